@@ -1,0 +1,367 @@
+#!/usr/bin/env python3
+"""Benchmark of the AbridgeKV attention hot path on one MI355X.
+
+Default workload (the metric's configuration): one decode step across all 36
+layers of a Qwen3-4B-shaped cache (32 query / 8 KV heads, d = 128, bf16) for 22
+sequences with prompts U[128, 512] and U[4096, 32768] generated tokens, blocks
+of C = 512 compressed to per-layer quotas (6 layers keep 256 rows per block, 12
+keep 64, 18 keep 128; which layers is a seeded permutation). A step is, per
+layer: append the current token (RoPE + write), then split-KV decode attention
+over the resident rows; any sequence whose block completes is compressed at
+every layer and its raw pages freed inside the step, as in serving. Inputs are
+synthetic and already resident in HBM when timing starts.
+
+Prints one JSON line: tokens/s, achieved HBM GB/s of the decode kernel against
+MI355X's 8 TB/s (HIP events around every decode launch in the timed region),
+the CPU oracle on a bounded sample, and the block-compression event (64
+sequences x 36 layers) with its MFMA-rate figures.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+L, HQ, HKV, D, C, PR = 36, 32, 8, 128, 512, 64
+METRIC = "decode-attn tokens/s + achieved HBM GB/s over AbridgeKV cache (36L quotas)"
+
+
+def layer_quotas(seed: int):
+    """Seeded permutation of the 36 layers: first 6 keep 256, next 12 keep 64,
+    the remaining 18 keep 128 (mean 128 rows per 512-token block)."""
+    perm = np.random.default_rng(seed).permutation(L)
+    q = np.empty(L, np.int32)
+    q[perm[:6]] = 256
+    q[perm[6:18]] = 64
+    q[perm[18:]] = 128
+    return q
+
+
+def decode_workload(seed: int = 2, batch: int = 22):
+    rng = np.random.default_rng(seed)
+    P = rng.integers(128, 512, batch, endpoint=True)
+    G = rng.integers(4096, 32768, batch, endpoint=True)
+    return layer_quotas(seed), P.astype(int), G.astype(int)
+
+
+def resident_rows(P, G, q, compress=True):
+    if not compress:
+        return P + G
+    nb = (G - 1) // C
+    return P + nb * q + (G - nb * C)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "kernels.h"):
+        with open(os.path.join(ROOT, "long_reasoning_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, launches_bytes: float):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/*.json),
+    or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------------
+
+def run_decode(args, torch, abk):
+    quotas, P, G = decode_workload(args.seed)
+    B = len(P)
+    Kp = int(quotas.max())
+    total_steps = args.warmup + args.steps
+    # pool: resident rows now plus growth over the run, in whole pages, with slack
+    pages = 0
+    for l in range(L):
+        R = resident_rows(P, G + total_steps, quotas[l])
+        pages += int(np.sum(np.ceil(R / PR) + 2 + C // PR))
+    page_bytes = HKV * PR * D * 2
+    pool = abk.Pool(num_layers=L, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_tokens=C,
+                    num_pause=Kp, layer_quota=quotas.tolist(), page_rows=PR, max_seqs=B,
+                    pool_bytes=2 * page_bytes * pages, max_position=33792, dtype="bf16",
+                    rope_base=1e6)
+    sids = []
+    for i in range(B):
+        s = pool.seq_create(int(P[i]))
+        pool.synth_fill(s, int(G[i]), (args.seed * 1000003 + i * 7919 + 17))
+        sids.append(s)
+    torch.cuda.synchronize()
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(args.seed)
+    bf = torch.bfloat16
+    q_in = torch.randn((total_steps, L, B, HQ, D), device="cuda", dtype=bf, generator=gen)
+    k_in = torch.randn((total_steps, L, B, HKV, D), device="cuda", dtype=bf, generator=gen)
+    v_in = torch.randn((total_steps, L, B, HKV, D), device="cuda", dtype=bf, generator=gen)
+    qp = torch.randn((B, Kp, HQ, D), device="cuda", dtype=bf, generator=gen)
+    kp = torch.randn((B, Kp, HKV, D), device="cuda", dtype=bf, generator=gen)
+    vp = torch.randn((B, Kp, HKV, D), device="cuda", dtype=bf, generator=gen)
+    out = torch.empty((B, HQ, D), device="cuda", dtype=bf)
+    lse = torch.empty((B, HQ), device="cuda", dtype=torch.float32)
+    cout = torch.empty((B, Kp, HQ, D), device="cuda", dtype=bf)
+    clse = torch.empty((B, Kp, HQ), device="cuda", dtype=torch.float32)
+
+    # host mirror of generated counts for the compress/free schedule and bytes
+    g = G.copy()
+    nb = (g - 1) // C
+
+    def step(t, rec):
+        full = [i for i in range(B) if g[i] - nb[i] * C == C]
+        if full:
+            ids = [sids[i] for i in full]
+            for l in range(L):
+                if rec is not None:
+                    rec["c0"].append(torch.cuda.Event(enable_timing=True))
+                    rec["c0"][-1].record()
+                pool.compress_block(l, ids, qp[:len(ids)], kp[:len(ids)], vp[:len(ids)],
+                                    cout[:len(ids)], clse[:len(ids)])
+                if rec is not None:
+                    rec["c1"].append(torch.cuda.Event(enable_timing=True))
+                    rec["c1"][-1].record()
+            pool.free_block(ids)
+            for i in full:
+                nb[i] += 1
+        for l in range(L):
+            pool.append_kv(l, sids, k_in[t, l], v_in[t, l])
+            if rec is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            pool.decode_attention(l, sids, q_in[t, l], out, lse)
+            if rec is not None:
+                e1 = torch.cuda.Event(enable_timing=True)
+                e1.record()
+                R = P + nb * quotas[l] + (g + 1 - nb * C)
+                rec["d"].append((e0, e1, int(R.sum())))
+        g[:] += 1
+
+    for t in range(args.warmup):
+        step(t, None)
+    torch.cuda.synchronize()
+    rec = {"d": [], "c0": [], "c1": []}
+    t0 = time.perf_counter()
+    for t in range(args.warmup, total_steps):
+        step(t, rec)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    # algorithmic bytes of one decode launch: every resident K and V row once,
+    # plus q, out (bf16) and lse (fp32)
+    row_bytes = 2 * HKV * D * 2
+    io_bytes = B * (2 * HQ * D * 2 + HQ * 4)
+    dec_ms = [e0.elapsed_time(e1) for e0, e1, _ in rec["d"]]
+    dec_bytes = [rows * row_bytes + io_bytes for _, _, rows in rec["d"]]
+    achieved = sum(dec_bytes) / (sum(dec_ms) * 1e-3) / 1e9
+    comp_ms = sum(a.elapsed_time(b) for a, b in zip(rec["c0"], rec["c1"]))
+    tokens = B * args.steps
+    resident = pool.stats()["resident_bytes"]
+    full_kv_rows = int(sum(resident_rows(P, g, quotas[l], compress=False).sum() for l in range(L)))
+    res = {
+        "value": tokens / wall,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "hbm_gbps": achieved,
+        "decode_ms_per_step": sum(dec_ms) / args.steps,
+        "compress_ms_in_timed_steps": comp_ms,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic_from_profiles("decode_split", float(np.mean(dec_bytes))),
+            "kernel": "decode_split_kernel<bf16,128,4> (+ split combine)",
+            "algorithmic_bytes_per_launch": float(np.mean(dec_bytes)),
+            "avg_launch_us": float(np.mean(dec_ms)) * 1e3,
+        },
+        "config": {
+            "workload": "36-layer per-layer-quota decode step (append + split-KV decode per "
+                        "layer; compress+free when a block completes), 22 sequences",
+            "layers": L, "batch": B, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
+            "block_tokens": C, "pause_tokens": Kp, "quotas": "6x256/12x64/18x128 (seeded)",
+            "prompt": "U[128,512]", "generated": "U[4096,32768]", "page_rows": PR,
+            "resident_kv_gb": resident / 1e9,
+            "full_kv_equivalent_gb": full_kv_rows * row_bytes / 1e9,
+        },
+    }
+    pool.close()
+    del q_in, k_in, v_in
+    return res, (quotas, P, G)
+
+
+def run_compress(args, torch, abk):
+    """One block-compression event: 64 sequences complete a 512-token block at
+    once; pause-token attention + code-row scatter at all 36 layers, then the
+    raw pages are freed."""
+    rng = np.random.default_rng(3)
+    quotas = layer_quotas(2)
+    B = 64
+    P = rng.integers(128, 512, B, endpoint=True)
+    b = rng.integers(0, 62, B, endpoint=True)
+    G = (b + 1) * C
+    Kp = 256
+    pages = 0
+    for l in range(L):
+        R = P + b * quotas[l] + C
+        pages += int(np.sum(np.ceil((P + (b + 1) * quotas[l]) / PR) + 1 + C // PR))
+    page_bytes = HKV * PR * D * 2
+    pool = abk.Pool(num_layers=L, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_tokens=C,
+                    num_pause=Kp, layer_quota=quotas.tolist(), page_rows=PR, max_seqs=B,
+                    pool_bytes=2 * page_bytes * pages, max_position=33792, dtype="bf16",
+                    rope_base=1e6)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    bf = torch.bfloat16
+    qp = torch.randn((L, B, Kp, HQ, D), device="cuda", dtype=bf, generator=gen)
+    kp = torch.randn((L, B, Kp, HKV, D), device="cuda", dtype=bf, generator=gen)
+    vp = torch.randn((L, B, Kp, HKV, D), device="cuda", dtype=bf, generator=gen)
+    out = torch.empty((B, Kp, HQ, D), device="cuda", dtype=bf)
+    lse = torch.empty((B, Kp, HQ), device="cuda", dtype=torch.float32)
+    times = []
+    for rep in range(args.compress_reps + 1):
+        sids = []
+        for i in range(B):
+            s = pool.seq_create(int(P[i]))
+            pool.synth_fill(s, int(G[i]), 3 * 1000003 + i)
+            sids.append(s)
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
+        e[0].record()
+        for l in range(L):
+            pool.compress_block(l, sids, qp[l], kp[l], vp[l], out, lse)
+            e[l + 1].record()
+        pool.free_block(sids)
+        torch.cuda.synchronize()
+        if rep > 0:
+            times.append([e[l].elapsed_time(e[l + 1]) for l in range(L)])
+        for s in sids:
+            pool.seq_release(s)
+    pool.close()
+    ms = np.mean([sum(t) for t in times])
+    # algorithmic flops: QK^T and PV over context N_l plus the causal pause part
+    flops = 0.0
+    nbytes = 0.0
+    for l in range(L):
+        N = P + b * quotas[l] + C
+        flops += float(np.sum(4.0 * HQ * Kp * D * (N + (Kp + 1) / 2.0)))
+        nbytes += float(np.sum(N)) * 2 * HKV * D * 2 + B * Kp * (2 * HQ + 2 * HKV) * D * 2
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": "block compressions/s (64 sequences x 36 layers per event)",
+        "events_per_s": 1e3 / ms, "ms_per_event": ms,
+        "blocks_per_s": B * 1e3 / ms,
+        "tflop_per_event": flops / 1e12, "gb_per_event": nbytes / 1e9,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None},
+        "config": {"workload": "block compression, 64 sequences, 36 layers, K=256 pause tokens "
+                               "(layer keeps quota prefix)", "prompt": "U[128,512]",
+                   "block_index": "U{0..62}"},
+    }
+
+
+def cpu_baseline(workload, budget_s: float):
+    """The CPU oracle as it stands, on a bounded sample of the decode step:
+    sequence 0 at one layer of each quota; cost scales with resident rows, so the
+    whole step's time is extrapolated by rows."""
+    import oracle
+    import synth
+    from oracle import TEXT, LayerView
+    quotas, P, G = workload
+    B = len(P)
+    layers = [int(np.where(quotas == q)[0][0]) for q in (256, 64, 128)]
+    seed = 2 * 1000003 + 17
+    sampled_rows = 0
+    secs = 0.0
+    for l in layers:
+        Lv = LayerView(int(P[0]), C, int(quotas.max()), int(quotas[l]))
+        nb = (int(G[0]) - 1) // C
+        cache = {}
+
+        def fetch(kind, a, b, which, l=l):
+            key = (which, len(kind))
+            if key not in cache:
+                w = synth.WHICH_K if which == "k" else synth.WHICH_V
+                out = np.empty((len(kind), HKV, D))
+                for kd in (0, 1, 2):
+                    m = kind == kd
+                    if m.any():
+                        out[m] = synth.rows(seed, l, kd, a[m], b[m], w, HKV, D, "bf16")
+                cache[key] = out
+            return cache[key]
+
+        q = synth.rows(seed, l, TEXT, [int(G[0]) - 1], 0, synth.WHICH_Q, HQ, D, "bf16")[0]
+        oracle.decode(Lv, int(G[0]), nb, q, fetch, oracle.BF16, 1e6)  # fills the input cache
+        t0 = time.perf_counter()
+        _, _, keys = oracle.decode(Lv, int(G[0]), nb, q, fetch, oracle.BF16, 1e6)
+        secs += time.perf_counter() - t0
+        sampled_rows += len(keys[0])
+        if secs > budget_s:
+            break
+    total_rows = sum(int(resident_rows(P, G, quotas[l]).sum()) for l in range(L))
+    step_s = secs * total_rows / sampled_rows
+    return {"value": B / step_s, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"sequence 0 (P={int(P[0])}, G={int(G[0])}) at layers {layers} "
+                      f"({sampled_rows} resident rows, {secs:.2f} s); extrapolated by rows to the "
+                      f"22-sequence 36-layer step ({total_rows} rows)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--compress-reps", type=int, default=2)
+    ap.add_argument("--no-compress", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import long_reasoning_kv_amd as abk
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    print(f"[bench] decode workload: 36 layers, 22 sequences, {args.warmup}+{args.steps} steps",
+          file=sys.stderr, flush=True)
+    res, workload = run_decode(args, torch, abk)
+    comp = None
+    if not args.no_compress:
+        print("[bench] compression event: 64 sequences x 36 layers", file=sys.stderr, flush=True)
+        comp = run_compress(args, torch, abk)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline (bounded sample)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(workload, args.cpu_budget_s)
+    line = {
+        "metric": METRIC, "value": res["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "config": res["config"], "hbm_gbps": res["hbm_gbps"],
+        "decode_ms_per_step": res["decode_ms_per_step"],
+        "compress_ms_in_timed_steps": res["compress_ms_in_timed_steps"],
+        "roofline": res["roofline"], "cpu_baseline": cpu, "compress": comp,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

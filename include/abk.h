@@ -1,0 +1,183 @@
+/* abk.h -- C ABI of the AbridgeKV attention hot path for MI355X (gfx950).
+ *
+ * What the library computes (sources are the pages on AbridgeKV, arXiv
+ * 2610.20641):
+ *  - Generated text is written in blocks of C tokens. When a block completes,
+ *    K learned pause tokens attend to it and their per-layer KV entries become
+ *    the block's "code rows"; then the block's raw KV rows are freed
+ *    (abstract; figure captions, Fig. 1(a)).
+ *  - The resident cache of a sequence at layer l is the prompt, quota[l] code
+ *    rows per finished block, and the open block's raw rows (AI Radio
+ *    transcript; news write-up, second and third details). Each layer has a
+ *    fixed budget; rows a layer does not keep are never allocated.
+ *  - Pause token k of block b is placed at RoPE position
+ *    P + b*C + bitrev(k)*C/K inside the block it replaces (Fig. 2(b)).
+ *  - Text tokens attend to the prompt, earlier code rows and causally to their
+ *    own block; pause tokens attend to the prompt, earlier code rows, their
+ *    whole block and causally to earlier pause tokens (Fig. 2(a)).
+ *
+ * Conventions for every call:
+ *  - Device buffers (q/k/v/out/lse and the pages) are plain device pointers;
+ *    the caller owns its buffers, the pool owns pages, tables and workspace.
+ *  - Row layouts are contiguous, row-major, in the pool's dtype unless stated.
+ *    Keys are given before RoPE; the library rotates them (rotate-half, angle
+ *    pos * rope_base^(-2i/d)) and stores the rotated row. Values are stored
+ *    as given. Queries are rotated in fp32 and never rounded.
+ *  - All device work is enqueued on the stream given at creation; calls
+ *    return without synchronising unless stated. Host bookkeeping updates
+ *    synchronously.
+ *  - Every check happens before anything is enqueued: a call that returns an
+ *    error has enqueued nothing and changed no state. abk_last_error() gives
+ *    the reason (thread-local text).
+ *  - One host thread per pool.
+ *  - Scores are q.k/sqrt(d); softmax runs in fp32; lse is the natural log of
+ *    the sum of exp(score) (so out = sum exp(score - lse) v).
+ */
+#ifndef ABK_H
+#define ABK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ABK_OK = 0,
+  ABK_ERR_INVALID_ARG = 1,  /* bad pointer, size, id or configuration */
+  ABK_ERR_OUT_OF_PAGES = 2, /* not enough free pages or sequence slots */
+  ABK_ERR_BAD_STATE = 3,    /* call out of protocol order (see each call) */
+  ABK_ERR_HIP = 4,          /* a HIP runtime call failed */
+  ABK_ERR_UNSUPPORTED = 5   /* valid but not built (shape/dtype), or host-only pool */
+} abk_status;
+
+typedef enum { ABK_F32 = 0, ABK_BF16 = 1 } abk_dtype;
+
+typedef struct abk_pool abk_pool; /* opaque; owned by the library */
+
+typedef struct {
+  int32_t num_layers;   /* L */
+  int32_t num_q_heads;  /* Hq; a multiple of num_kv_heads (GQA group g = Hq/Hkv in 1,2,4,8) */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_dim;     /* d in {16, 64, 128} */
+  int32_t block_tokens; /* C; a multiple of page_rows */
+  int32_t num_pause;    /* K pause tokens per compression; a power of two dividing C */
+  const int32_t* layer_quota; /* [L] code rows kept per block, 0 <= quota <= pause count (copied) */
+  const int32_t* layer_pause; /* optional [L] pause tokens run at each layer (power of two,
+                                 >= quota, divides C); NULL = num_pause at every layer */
+  int32_t page_rows;    /* rows per page, 1..64 */
+  int32_t max_seqs;     /* sequence slots */
+  int64_t pool_bytes;   /* device bytes for K and V pages together */
+  int32_t max_position; /* positions must stay below this (sizes the RoPE table) */
+  int32_t dtype;        /* abk_dtype of pages, q/k/v and out */
+  double rope_base;     /* e.g. 1e6 */
+  int32_t compress;     /* 1: AbridgeKV; 0: full-KV, blocks never close */
+  int32_t host_only;    /* 1: bookkeeping only (no device memory, no kernels; data
+                           pointers are ignored) -- for capacity planning and tests */
+  int32_t decode_split_rows; /* rows per split-KV work item of decode (0 = 512); rounded
+                                down to whole pages */
+} abk_pool_config;
+
+typedef struct {
+  int32_t prompt_len;    /* P */
+  int32_t generated;     /* rows appended at this layer (G) */
+  int32_t blocks_done;   /* blocks compressed and freed */
+  int32_t open_rows;     /* raw rows of the open block at this layer */
+  int32_t resident_rows; /* P + blocks_done*quota + open (compress); P + G (full-KV) */
+  int32_t n_pages;       /* pages this (sequence, layer) holds */
+} abk_seq_info;
+
+/* Create a pool: page storage, per-(sequence, layer) page tables, RoPE table.
+ * Page layout: K pages [page][kv_head][page_rows][d] and V pages likewise,
+ * plus an int32 position per (page, row). hip_stream: a hipStream_t (NULL =
+ * default stream). Errors: INVALID_ARG (config), HIP (allocation). */
+abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_pool** out);
+/* Synchronises the stream, then frees everything the pool owns. */
+abk_status abk_pool_destroy(abk_pool* p);
+
+/* Open a sequence with a prompt of prompt_len tokens: takes the lowest free
+ * slot and reserves ceil(P/page_rows) persistent pages in every layer (layers
+ * ascending, lowest page ids first). Errors: OUT_OF_PAGES (no slot or pages). */
+abk_status abk_seq_create(abk_pool* p, int32_t prompt_len, int32_t* seq_id);
+/* Return every page of the sequence and its slot. Enqueues nothing. */
+abk_status abk_seq_release(abk_pool* p, int32_t seq_id);
+
+/* Write the prompt rows of one layer: k, v [P, Hkv, d] device, k pre-RoPE,
+ * row i at position i. BAD_STATE once generation has started at that layer. */
+abk_status abk_write_prompt(abk_pool* p, int32_t seq_id, int32_t layer, const void* k,
+                            const void* v);
+
+/* Step a1: append the current token of each sequence at one layer. k, v
+ * [n, Hkv, d] device (k pre-RoPE); the row lands at position P + G (G counted
+ * before the call) in the open block (compress) or after the persistent rows
+ * (full-KV); a new page is taken when the row starts one. seq_ids: host array
+ * of n distinct ids. BAD_STATE if the prompt is not written, this layer is
+ * ahead of the others, or (compress) the open block already holds C rows. */
+abk_status abk_append_kv(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                         const void* k, const void* v);
+
+/* Steps a2+a3: GQA decode attention of the current token of each sequence at
+ * one layer, over its resident rows (prompt, code rows, open block).
+ * q [n, Hq, d] device, pre-RoPE, rotated at position P + G - 1; query head h
+ * reads KV head h / (Hq/Hkv). out [n, Hq, d] (pool dtype), lse [n, Hq] fp32.
+ * BAD_STATE unless the current token is appended at this layer and the layer
+ * is not between compression and free. */
+abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                                const void* q, void* out, float* lse);
+
+/* Steps a4-a6: compress the completed open block b of each sequence at one
+ * layer. q_pause [n, Kp, Hq, d], k_pause and v_pause [n, Kp, Hkv, d] device,
+ * pre-RoPE (Kp = the layer's pause count). Pause k is rotated at
+ * P + b*C + bitrev(k)*C/Kp and attends to the prompt, the retained code rows of
+ * earlier blocks, all C rows of block b, and pause keys j <= k. out [n, Kp, Hq,
+ * d], lse [n, Kp, Hq] fp32. Then the rows k < quota[layer] (rotated key, value,
+ * position) are appended to the layer's persistent rows in k order.
+ * BAD_STATE unless the open block holds exactly C rows at this layer and was
+ * not yet compressed there; BAD_STATE in full-KV mode. */
+abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                              const void* q_pause, const void* k_pause, const void* v_pause,
+                              void* out, float* lse);
+
+/* Step a7: after every layer is compressed, return the open block's pages of
+ * every layer to the free list and start the next block (its raw rows are no
+ * longer resident). BAD_STATE unless every layer of every sequence is
+ * compressed; BAD_STATE in full-KV mode. */
+abk_status abk_free_block(abk_pool* p, int32_t n, const int32_t* seq_ids);
+
+/* Host-side counters of one (sequence, layer). */
+abk_status abk_seq_query(const abk_pool* p, int32_t seq_id, int32_t layer, abk_seq_info* out);
+
+/* Read back the device page table (persistent pages, then open pages) and the
+ * stored position of every resident row, in row order (host buffers).
+ * Synchronises the stream. In a host-only pool returns the host mirror.
+ * INVALID_ARG if a capacity is too small. */
+abk_status abk_export_layout(const abk_pool* p, int32_t seq_id, int32_t layer, int32_t* page_ids,
+                             int32_t cap_pages, int32_t* positions, int32_t cap_rows);
+
+/* Copy resident rows [row0, row0 + nrows) of (sequence, layer) in row order
+ * into device buffers k_out, v_out [nrows, Hkv, d] (keys as stored, i.e.
+ * rotated). Enqueued on the stream. */
+abk_status abk_read_rows(const abk_pool* p, int32_t seq_id, int32_t layer, int32_t row0,
+                         int32_t nrows, void* k_out, void* v_out);
+
+/* Pool-wide counters. resident_bytes = K+V bytes of resident rows. */
+abk_status abk_pool_stats(const abk_pool* p, int64_t* pages_used, int64_t* pages_free,
+                          int64_t* resident_bytes);
+
+/* Bulk-build a fresh sequence's state after `generated` tokens with synthetic
+ * rows: every completed block except the last token's is compressed and
+ * freed. Row values are the seeded N(0,1) generator of the synth module (keyed
+ * by seed, layer and token identity), rounded to the pool dtype; keys are
+ * rotated at the row's position as by append/compress. Pages are taken per
+ * layer ascending, persistent before open. BAD_STATE unless the sequence is
+ * fresh (no prompt written, nothing appended). */
+abk_status abk_synth_fill(abk_pool* p, int32_t seq_id, int32_t generated, uint64_t seed);
+
+/* Thread-local text for the last non-OK status of this thread. */
+const char* abk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ABK_H */

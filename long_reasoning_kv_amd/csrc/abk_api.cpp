@@ -1,0 +1,538 @@
+// C ABI of the AbridgeKV attention hot path (declared in include/abk.h).
+//
+// Each call: check arguments, let the host pool validate the protocol and do
+// its bookkeeping (nothing changes on failure), then enqueue the device work
+// on the pool's stream. Hot-path calls (append, decode, free) pass their
+// per-call data in kernel arguments; the others upload a small descriptor
+// through a ring of pinned host buffers.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/abk.h"
+#include "kernels.h"
+#include "pool.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+abk_status set_err(abk_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+abk_status from_host(abk::Status st, const std::string& msg) {
+  return set_err((abk_status)st, msg);
+}
+
+#define ABK_HIP(call)                                                                    \
+  do {                                                                                   \
+    hipError_t e_ = (call);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return set_err(ABK_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_));    \
+  } while (0)
+
+constexpr int kRing = 8;
+
+struct PinnedSlot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+}  // namespace
+
+struct abk_pool {
+  abk::HostPool host;
+  abk::Shape shape;
+  bool host_only = false;
+  int32_t split_rows = 512;
+  hipStream_t stream = nullptr;
+  abk::DevPool dev{};
+  int32_t* quota_d = nullptr;
+  int32_t* pause_d = nullptr;
+  float* part = nullptr;
+  size_t part_bytes = 0;
+  void* kp_rot = nullptr;
+  size_t kp_rot_bytes = 0;
+  void* desc = nullptr;
+  size_t desc_bytes = 0;
+  int32_t* export_d = nullptr;
+  size_t export_ints = 0;
+  PinnedSlot ring[kRing];
+  int ring_next = 0;
+  std::vector<int32_t> scratch;  // host staging for descriptors
+};
+
+namespace {
+
+abk_status grow(abk_pool* p, void** buf, size_t* have, size_t need) {
+  if (need <= *have) return ABK_OK;
+  ABK_HIP(hipStreamSynchronize(p->stream));
+  if (*buf) ABK_HIP(hipFree(*buf));
+  *buf = nullptr;
+  *have = 0;
+  size_t cap = std::max(need, (size_t)1 << 20);
+  ABK_HIP(hipMalloc(buf, cap));
+  *have = cap;
+  return ABK_OK;
+}
+
+// Copy `bytes` of host data to the pool's device descriptor buffer, in stream
+// order, through a pinned slot that is reused only after its copy finished.
+abk_status upload_desc(abk_pool* p, const void* src, size_t bytes) {
+  if (bytes == 0) return ABK_OK;
+  if (abk_status st = grow(p, &p->desc, &p->desc_bytes, bytes)) return st;
+  PinnedSlot& s = p->ring[p->ring_next];
+  p->ring_next = (p->ring_next + 1) % kRing;
+  if (s.pending) ABK_HIP(hipEventSynchronize(s.ev));
+  s.pending = false;
+  if (s.cap < bytes) {
+    if (s.host) ABK_HIP(hipHostFree(s.host));
+    s.host = nullptr;
+    s.cap = 0;
+    size_t cap = std::max(bytes * 2, (size_t)1 << 16);
+    ABK_HIP(hipHostMalloc(&s.host, cap, hipHostMallocDefault));
+    s.cap = cap;
+  }
+  if (!s.ev) ABK_HIP(hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
+  std::memcpy(s.host, src, bytes);
+  ABK_HIP(hipMemcpyAsync(p->desc, s.host, bytes, hipMemcpyHostToDevice, p->stream));
+  ABK_HIP(hipEventRecord(s.ev, p->stream));
+  s.pending = true;
+  return ABK_OK;
+}
+
+abk_status check_pool(const abk_pool* p) {
+  return p ? ABK_OK : set_err(ABK_ERR_INVALID_ARG, "pool is NULL");
+}
+
+size_t row_elems(const abk::Shape& s) { return (size_t)s.Hkv * s.D; }
+
+}  // namespace
+
+extern "C" {
+
+const char* abk_last_error(void) { return g_err.c_str(); }
+
+abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_pool** out) {
+  if (!cfg || !out) return set_err(ABK_ERR_INVALID_ARG, "cfg/out is NULL");
+  *out = nullptr;
+  if (cfg->num_layers < 1 || cfg->num_layers > 4096) return set_err(ABK_ERR_INVALID_ARG, "num_layers");
+  if (!cfg->layer_quota) return set_err(ABK_ERR_INVALID_ARG, "layer_quota is NULL");
+  abk::Shape s;
+  s.L = cfg->num_layers;
+  s.Hq = cfg->num_q_heads;
+  s.Hkv = cfg->num_kv_heads;
+  s.D = cfg->head_dim;
+  s.C = cfg->block_tokens;
+  s.pr = cfg->page_rows;
+  s.max_seqs = cfg->max_seqs;
+  s.max_position = cfg->max_position;
+  s.dtype = cfg->dtype;
+  s.compress = cfg->compress ? 1 : 0;
+  s.rope_base = cfg->rope_base;
+  s.quota.assign(cfg->layer_quota, cfg->layer_quota + s.L);
+  if (cfg->layer_pause) s.pause.assign(cfg->layer_pause, cfg->layer_pause + s.L);
+  else s.pause.assign(s.L, cfg->num_pause);
+  if (s.Hkv < 1 || s.D < 1 || s.pr < 1 || (s.dtype != 0 && s.dtype != 1))
+    return set_err(ABK_ERR_INVALID_ARG, "bad shape or dtype");
+  const int64_t page_bytes = (int64_t)s.Hkv * s.pr * s.D * s.esize();
+  s.num_pages = cfg->pool_bytes / (2 * page_bytes);
+  abk_pool* p = new abk_pool();
+  std::string e;
+  if (abk::Status st = p->host.init(s, &e)) {
+    delete p;
+    return set_err((abk_status)st, e);
+  }
+  if (s.Hkv * s.D > 2048) {
+    delete p;
+    return set_err(ABK_ERR_UNSUPPORTED, "num_kv_heads * head_dim above 2048");
+  }
+  p->shape = s;
+  p->host_only = cfg->host_only != 0;
+  if (cfg->decode_split_rows < 0) {
+    delete p;
+    return set_err(ABK_ERR_INVALID_ARG, "decode_split_rows is negative");
+  }
+  p->split_rows = cfg->decode_split_rows > 0 ? cfg->decode_split_rows : 512;
+  p->stream = (hipStream_t)hip_stream;
+  if (p->host_only) {
+    *out = p;
+    return ABK_OK;
+  }
+  auto fail = [&](hipError_t err, const char* what) {
+    abk_pool_destroy(p);
+    return set_err(ABK_ERR_HIP, std::string(what) + ": " + hipGetErrorString(err));
+  };
+  hipError_t err;
+  const size_t pages = (size_t)s.num_pages;
+  const size_t tab_ints = (size_t)s.max_seqs * s.L * s.table_stride();
+  const size_t meta_ints = (size_t)s.max_seqs * s.L * 4;
+  const size_t rope_n = (size_t)s.max_position * (s.D / 2);
+  abk::DevPool& d = p->dev;
+  if ((err = hipMalloc(&d.kpool, pages * page_bytes))) return fail(err, "pages");
+  if ((err = hipMalloc(&d.vpool, pages * page_bytes))) return fail(err, "pages");
+  if ((err = hipMalloc(&d.pos, pages * s.pr * sizeof(int32_t)))) return fail(err, "positions");
+  if ((err = hipMalloc(&d.ptab, tab_ints * sizeof(int32_t)))) return fail(err, "page table");
+  if ((err = hipMalloc(&d.meta, meta_ints * sizeof(int32_t)))) return fail(err, "meta");
+  float2* rope = nullptr;
+  if ((err = hipMalloc(&rope, rope_n * sizeof(float2)))) return fail(err, "rope");
+  d.rope = rope;
+  if ((err = hipMalloc(&p->quota_d, s.L * sizeof(int32_t)))) return fail(err, "quota");
+  if ((err = hipMalloc(&p->pause_d, s.L * sizeof(int32_t)))) return fail(err, "pause");
+  p->export_ints = 4 + (size_t)s.table_stride() + s.max_position + s.C;
+  if ((err = hipMalloc(&p->export_d, p->export_ints * sizeof(int32_t)))) return fail(err, "export");
+  if ((err = hipMemset(d.kpool, 0, pages * page_bytes))) return fail(err, "memset");
+  if ((err = hipMemset(d.vpool, 0, pages * page_bytes))) return fail(err, "memset");
+  if ((err = hipMemset(d.pos, 0xff, pages * s.pr * sizeof(int32_t)))) return fail(err, "memset");
+  if ((err = hipMemset(d.ptab, 0xff, tab_ints * sizeof(int32_t)))) return fail(err, "memset");
+  if ((err = hipMemset(d.meta, 0, meta_ints * sizeof(int32_t)))) return fail(err, "memset");
+  // RoPE angles pos * base^(-2i/d) in double, stored as fp32 (cos, sin)
+  {
+    std::vector<float2> h(rope_n);
+    const int half = s.D / 2;
+    std::vector<double> inv(half);
+    for (int i = 0; i < half; ++i) inv[i] = std::pow(s.rope_base, -2.0 * i / s.D);
+    for (int64_t pos = 0; pos < s.max_position; ++pos)
+      for (int i = 0; i < half; ++i) {
+        double th = (double)pos * inv[i];
+        h[pos * half + i] = make_float2((float)std::cos(th), (float)std::sin(th));
+      }
+    if ((err = hipMemcpy(rope, h.data(), rope_n * sizeof(float2), hipMemcpyHostToDevice)))
+      return fail(err, "rope upload");
+  }
+  if ((err = hipMemcpy(p->quota_d, s.quota.data(), s.L * sizeof(int32_t), hipMemcpyHostToDevice)))
+    return fail(err, "quota upload");
+  if ((err = hipMemcpy(p->pause_d, s.pause.data(), s.L * sizeof(int32_t), hipMemcpyHostToDevice)))
+    return fail(err, "pause upload");
+  if ((err = hipDeviceSynchronize())) return fail(err, "init sync");
+  d.L = s.L;
+  d.Hkv = s.Hkv;
+  d.D = s.D;
+  d.pr = s.pr;
+  d.tstride = s.table_stride();
+  d.max_pers = s.max_pers_pages();
+  d.C = s.C;
+  d.dtype = s.dtype;
+  *out = p;
+  return ABK_OK;
+}
+
+abk_status abk_pool_destroy(abk_pool* p) {
+  if (!p) return ABK_OK;
+  if (!p->host_only) {
+    (void)hipStreamSynchronize(p->stream);
+    abk::DevPool& d = p->dev;
+    for (void* b : {(void*)d.kpool, (void*)d.vpool, (void*)d.pos, (void*)d.ptab, (void*)d.meta,
+                    (void*)d.rope, (void*)p->quota_d, (void*)p->pause_d, (void*)p->part,
+                    p->kp_rot, p->desc, (void*)p->export_d})
+      if (b) (void)hipFree(b);
+    for (auto& s : p->ring) {
+      if (s.host) (void)hipHostFree(s.host);
+      if (s.ev) (void)hipEventDestroy(s.ev);
+    }
+  }
+  delete p;
+  return ABK_OK;
+}
+
+abk_status abk_seq_create(abk_pool* p, int32_t prompt_len, int32_t* seq_id) {
+  if (abk_status st = check_pool(p)) return st;
+  if (abk::Status st = p->host.seq_create(prompt_len, seq_id)) return from_host(st, p->host.err);
+  return ABK_OK;
+}
+
+abk_status abk_seq_release(abk_pool* p, int32_t seq_id) {
+  if (abk_status st = check_pool(p)) return st;
+  if (abk::Status st = p->host.seq_release(seq_id)) return from_host(st, p->host.err);
+  return ABK_OK;
+}
+
+abk_status abk_write_prompt(abk_pool* p, int32_t seq_id, int32_t layer, const void* k,
+                            const void* v) {
+  if (abk_status st = check_pool(p)) return st;
+  if (p->host.check_seq(seq_id)) return set_err(ABK_ERR_INVALID_ARG, "unknown sequence id");
+  const int32_t P = p->host.seq(seq_id).P;
+  if (!p->host_only && P > 0 && (!k || !v)) return set_err(ABK_ERR_INVALID_ARG, "k/v is NULL");
+  if (abk::Status st = p->host.write_prompt(seq_id, layer)) return from_host(st, p->host.err);
+  if (p->host_only) return ABK_OK;
+  const auto& pages = p->host.seq(seq_id).layers[layer].pers_pages;
+  const int32_t np = (P + p->shape.pr - 1) / p->shape.pr;
+  if (abk_status st = upload_desc(p, pages.data(), np * sizeof(int32_t))) return st;
+  abk::PromptArgs a;
+  a.P = p->dev;
+  a.k = k;
+  a.v = v;
+  a.pages = (const int32_t*)p->desc;
+  a.slot = seq_id;
+  a.layer = layer;
+  a.prompt_len = P;
+  ABK_HIP(abk::launch_prompt(a, p->stream));
+  return ABK_OK;
+}
+
+abk_status abk_append_kv(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                         const void* k, const void* v) {
+  if (abk_status st = check_pool(p)) return st;
+  if (!p->host_only && n > 0 && (!k || !v)) return set_err(ABK_ERR_INVALID_ARG, "k/v is NULL");
+  std::vector<int32_t> new_page;
+  if (abk::Status st = p->host.append(layer, n, seq_ids, &new_page)) return from_host(st, p->host.err);
+  if (p->host_only) return ABK_OK;
+  const size_t rb = row_elems(p->shape) * p->shape.esize();
+  for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
+    const int32_t m = std::min(n - c0, abk::kMaxBatch);
+    abk::AppendArgs a;
+    a.P = p->dev;
+    a.k = (const char*)k + c0 * rb;
+    a.v = (const char*)v + c0 * rb;
+    a.layer = layer;
+    a.n = m;
+    a.compress = p->shape.compress;
+    for (int32_t i = 0; i < m; ++i) {
+      a.slot[i] = seq_ids[c0 + i];
+      a.new_page[i] = new_page[c0 + i];
+    }
+    ABK_HIP(abk::launch_append(a, p->stream));
+  }
+  return ABK_OK;
+}
+
+abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                                const void* q, void* out, float* lse) {
+  if (abk_status st = check_pool(p)) return st;
+  if (!p->host_only && n > 0 && (!q || !out || !lse))
+    return set_err(ABK_ERR_INVALID_ARG, "q/out/lse is NULL");
+  if (abk::Status st = p->host.check_decode(layer, n, seq_ids)) return from_host(st, p->host.err);
+  if (p->host_only || n == 0) return ABK_OK;
+  const abk::Shape& s = p->shape;
+  const int32_t G = s.Hq / s.Hkv;
+  const int32_t split_pages = std::max(1, p->split_rows / s.pr);
+  // size the partials for the whole call first (growing synchronises)
+  size_t need = 0;
+  std::vector<int32_t> splits(n);
+  for (int32_t i = 0; i < n; ++i) {
+    const auto& lay = p->host.seq(seq_ids[i]).layers[layer];
+    const int32_t nvp = (int32_t)(lay.pers_pages.size() + lay.open_pages.size());
+    splits[i] = (nvp + split_pages - 1) / split_pages;
+  }
+  for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
+    size_t t = 0;
+    for (int32_t i = c0; i < std::min(n, c0 + abk::kMaxBatch); ++i) t += splits[i];
+    need = std::max(need, t);
+  }
+  if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
+                           need * s.Hkv * G * (s.D + 2) * sizeof(float)))
+    return st;
+  const size_t qb = (size_t)s.Hq * s.D * s.esize();
+  for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
+    const int32_t m = std::min(n - c0, abk::kMaxBatch);
+    abk::DecodeArgs a;
+    a.P = p->dev;
+    a.q = (const char*)q + c0 * qb;
+    a.out = (char*)out + c0 * qb;
+    a.lse = lse + (size_t)c0 * s.Hq;
+    a.part = p->part;
+    a.layer = layer;
+    a.n = m;
+    a.G = G;
+    a.split_pages = split_pages;
+    a.prefix[0] = 0;
+    for (int32_t i = 0; i < m; ++i) {
+      a.slot[i] = seq_ids[c0 + i];
+      a.prefix[i + 1] = a.prefix[i] + splits[c0 + i];
+    }
+    ABK_HIP(abk::launch_decode(a, a.prefix[m], p->stream));
+  }
+  return ABK_OK;
+}
+
+abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                              const void* q_pause, const void* k_pause, const void* v_pause,
+                              void* out, float* lse) {
+  if (abk_status st = check_pool(p)) return st;
+  if (!p->host_only && n > 0 && (!q_pause || !k_pause || !v_pause || !out || !lse))
+    return set_err(ABK_ERR_INVALID_ARG, "a pause/out/lse pointer is NULL");
+  std::vector<abk::CompressPlan> plan;
+  if (abk::Status st = p->host.compress(layer, n, seq_ids, &plan)) return from_host(st, p->host.err);
+  if (p->host_only || n == 0) return ABK_OK;
+  const abk::Shape& s = p->shape;
+  const int32_t Kp = s.pause[layer];
+  std::vector<int32_t>& d = p->scratch;
+  d.assign((size_t)n * abk::kCompRec, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t* r = &d[(size_t)i * abk::kCompRec];
+    r[0] = plan[i].slot;
+    r[1] = plan[i].block;
+    r[2] = plan[i].pers_before;
+    r[3] = p->host.seq(plan[i].slot).P;
+    r[4] = (int32_t)d.size();
+    r[5] = (int32_t)plan[i].pages.size();
+    r[6] = plan[i].first_new;
+    d.insert(d.end(), plan[i].pages.begin(), plan[i].pages.end());
+  }
+  if (abk_status st = grow(p, &p->kp_rot, &p->kp_rot_bytes,
+                           (size_t)n * s.Hkv * Kp * s.D * s.esize()))
+    return st;
+  if (abk_status st = upload_desc(p, d.data(), d.size() * sizeof(int32_t))) return st;
+  abk::CompressArgs a;
+  a.P = p->dev;
+  a.qp = q_pause;
+  a.kp = k_pause;
+  a.vp = v_pause;
+  a.out = out;
+  a.lse = lse;
+  a.kp_rot = p->kp_rot;
+  a.desc = (const int32_t*)p->desc;
+  a.layer = layer;
+  a.n = n;
+  a.Hq = s.Hq;
+  a.G = s.Hq / s.Hkv;
+  a.Kp = Kp;
+  a.quota = s.quota[layer];
+  a.log2Kp = abk::log2_exact(Kp);
+  ABK_HIP(abk::launch_compress(a, p->stream));
+  return ABK_OK;
+}
+
+abk_status abk_free_block(abk_pool* p, int32_t n, const int32_t* seq_ids) {
+  if (abk_status st = check_pool(p)) return st;
+  if (abk::Status st = p->host.free_block(n, seq_ids)) return from_host(st, p->host.err);
+  if (p->host_only) return ABK_OK;
+  for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
+    abk::FreeArgs a;
+    a.P = p->dev;
+    a.n = std::min(n - c0, abk::kMaxBatch);
+    for (int32_t i = 0; i < a.n; ++i) a.slot[i] = seq_ids[c0 + i];
+    ABK_HIP(abk::launch_free(a, p->stream));
+  }
+  return ABK_OK;
+}
+
+abk_status abk_seq_query(const abk_pool* p, int32_t seq_id, int32_t layer, abk_seq_info* out) {
+  if (abk_status st = check_pool(p)) return st;
+  if (!out) return set_err(ABK_ERR_INVALID_ARG, "out is NULL");
+  if (p->host.check_seq(seq_id) || p->host.check_layer(layer))
+    return set_err(ABK_ERR_INVALID_ARG, "unknown sequence or layer");
+  const abk::SeqState& q = p->host.seq(seq_id);
+  const abk::LayerState& lay = q.layers[layer];
+  out->prompt_len = q.P;
+  out->generated = lay.G;
+  out->blocks_done = q.nb;
+  out->open_rows = p->host.open_rows(seq_id, layer);
+  out->resident_rows = p->host.resident_rows(seq_id, layer);
+  out->n_pages = (int32_t)(lay.pers_pages.size() + lay.open_pages.size());
+  return ABK_OK;
+}
+
+abk_status abk_export_layout(const abk_pool* cp, int32_t seq_id, int32_t layer, int32_t* page_ids,
+                             int32_t cap_pages, int32_t* positions, int32_t cap_rows) {
+  abk_pool* p = const_cast<abk_pool*>(cp);
+  if (abk_status st = check_pool(p)) return st;
+  if (p->host.check_seq(seq_id) || p->host.check_layer(layer))
+    return set_err(ABK_ERR_INVALID_ARG, "unknown sequence or layer");
+  const abk::LayerState& lay = p->host.seq(seq_id).layers[layer];
+  const int32_t npages = (int32_t)(lay.pers_pages.size() + lay.open_pages.size());
+  const int32_t rows = p->host.resident_rows(seq_id, layer);
+  if ((npages > 0 && (!page_ids || cap_pages < npages)) || (rows > 0 && (!positions || cap_rows < rows)))
+    return set_err(ABK_ERR_INVALID_ARG, "capacity too small");
+  if (p->host_only) {
+    int32_t j = 0;
+    for (int32_t pg : lay.pers_pages) page_ids[j++] = pg;
+    for (int32_t pg : lay.open_pages) page_ids[j++] = pg;
+    for (int32_t r = 0; r < rows; ++r) positions[r] = (int32_t)p->host.row_position(seq_id, layer, r);
+    return ABK_OK;
+  }
+  abk::ExportArgs a;
+  a.P = p->dev;
+  a.dst = p->export_d;
+  a.slot = seq_id;
+  a.layer = layer;
+  ABK_HIP(abk::launch_export(a, p->stream));
+  std::vector<int32_t> h(4 + npages + rows);
+  ABK_HIP(hipMemcpyAsync(h.data(), p->export_d, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                         p->stream));
+  ABK_HIP(hipStreamSynchronize(p->stream));
+  if (h[0] + h[1] != rows || h[3] != npages)
+    return set_err(ABK_ERR_BAD_STATE, "device layout disagrees with the host mirror");
+  std::memcpy(page_ids, h.data() + 4, npages * sizeof(int32_t));
+  std::memcpy(positions, h.data() + 4 + npages, rows * sizeof(int32_t));
+  return ABK_OK;
+}
+
+abk_status abk_read_rows(const abk_pool* cp, int32_t seq_id, int32_t layer, int32_t row0,
+                         int32_t nrows, void* k_out, void* v_out) {
+  abk_pool* p = const_cast<abk_pool*>(cp);
+  if (abk_status st = check_pool(p)) return st;
+  if (p->host.check_seq(seq_id) || p->host.check_layer(layer))
+    return set_err(ABK_ERR_INVALID_ARG, "unknown sequence or layer");
+  const int32_t rows = p->host.resident_rows(seq_id, layer);
+  if (row0 < 0 || nrows < 0 || (int64_t)row0 + nrows > rows)
+    return set_err(ABK_ERR_INVALID_ARG, "rows out of range");
+  if (p->host_only) return set_err(ABK_ERR_UNSUPPORTED, "host-only pool has no rows");
+  if (nrows > 0 && (!k_out || !v_out)) return set_err(ABK_ERR_INVALID_ARG, "k_out/v_out is NULL");
+  abk::ReadArgs a;
+  a.P = p->dev;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.slot = seq_id;
+  a.layer = layer;
+  a.row0 = row0;
+  a.nrows = nrows;
+  ABK_HIP(abk::launch_read(a, p->stream));
+  return ABK_OK;
+}
+
+abk_status abk_pool_stats(const abk_pool* p, int64_t* pages_used, int64_t* pages_free,
+                          int64_t* resident_bytes) {
+  if (abk_status st = check_pool(p)) return st;
+  const int64_t fr = p->host.pages_free();
+  if (pages_used) *pages_used = p->shape.num_pages - fr;
+  if (pages_free) *pages_free = fr;
+  if (resident_bytes)
+    *resident_bytes = p->host.resident_rows_total() * 2 * (int64_t)row_elems(p->shape) * p->shape.esize();
+  return ABK_OK;
+}
+
+abk_status abk_synth_fill(abk_pool* p, int32_t seq_id, int32_t generated, uint64_t seed) {
+  if (abk_status st = check_pool(p)) return st;
+  if (abk::Status st = p->host.fill(seq_id, generated)) return from_host(st, p->host.err);
+  if (p->host_only) return ABK_OK;
+  const abk::Shape& s = p->shape;
+  const abk::SeqState& q = p->host.seq(seq_id);
+  std::vector<int32_t>& d = p->scratch;
+  d.assign((size_t)4 * s.L, 0);
+  int32_t max_rows = 0;
+  for (int32_t l = 0; l < s.L; ++l) {
+    const auto& lay = q.layers[l];
+    d[4 * l + 0] = (int32_t)d.size();
+    d[4 * l + 1] = (int32_t)lay.pers_pages.size();
+    d.insert(d.end(), lay.pers_pages.begin(), lay.pers_pages.end());
+    d[4 * l + 2] = (int32_t)d.size();
+    d[4 * l + 3] = (int32_t)lay.open_pages.size();
+    d.insert(d.end(), lay.open_pages.begin(), lay.open_pages.end());
+    max_rows = std::max(max_rows, p->host.resident_rows(seq_id, l));
+  }
+  if (abk_status st = upload_desc(p, d.data(), d.size() * sizeof(int32_t))) return st;
+  abk::FillArgs a;
+  a.P = p->dev;
+  a.desc = (const int32_t*)p->desc;
+  a.quota = p->quota_d;
+  a.pause = p->pause_d;
+  a.seed = seed;
+  a.slot = seq_id;
+  a.prompt_len = q.P;
+  a.G = generated;
+  a.nb = q.nb;
+  a.compress = s.compress;
+  ABK_HIP(abk::launch_fill(a, max_rows, p->stream));
+  return ABK_OK;
+}
+
+}  // extern "C"

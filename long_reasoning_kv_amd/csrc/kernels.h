@@ -1,0 +1,116 @@
+// Launch interface between the C ABI (abk_api.cpp) and the HIP kernels
+// (kernels.hip). Hot-path launches (append, decode, free) carry their
+// per-call data by value in the kernel arguments and read the device-resident
+// per-(sequence, layer) metadata and page tables, so no host-to-device copy
+// sits between two layers. Rarer calls (prompt, compression, fills,
+// inspection) read a small descriptor uploaded to `desc`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace abk {
+
+constexpr int kMaxBatch = 256;  // sequences per hot-path launch (larger batches are split)
+
+// Device view of a pool. Pages: K [page][Hkv][pr][D], V likewise; pos
+// [page][pr]. ptab[(slot*L + l)*tstride + i]: persistent page i for
+// i < max_pers, open page j at max_pers + j. meta[(slot*L + l)*4 + f]:
+// f=0 persistent rows, f=1 open rows, f=2 position of the current token.
+struct DevPool {
+  void* kpool;
+  void* vpool;
+  int32_t* pos;
+  int32_t* ptab;
+  int32_t* meta;
+  const float2* rope;  // [max_position][D/2] (cos, sin)
+  int32_t L, Hkv, D, pr, tstride, max_pers, C, dtype;
+};
+
+struct AppendArgs {
+  DevPool P;
+  const void* k;
+  const void* v;
+  int32_t layer, n, compress;
+  int32_t slot[kMaxBatch];
+  int32_t new_page[kMaxBatch];  // page taken for this row, or -1
+};
+
+struct DecodeArgs {
+  DevPool P;
+  const void* q;
+  void* out;
+  float* lse;
+  float* part;  // split partials [work][Hkv][G][D + 2]
+  int32_t layer, n, G, split_pages;
+  int32_t slot[kMaxBatch];
+  int32_t prefix[kMaxBatch + 1];  // work items of sequence i: [prefix[i], prefix[i+1])
+};
+
+struct FreeArgs {
+  DevPool P;
+  int32_t n;
+  int32_t slot[kMaxBatch];
+};
+
+// Prompt write: rows 0..P-1 of (slot, layer); pages from desc.
+struct PromptArgs {
+  DevPool P;
+  const void* k;
+  const void* v;
+  const int32_t* pages;  // ceil(P/pr) ids (device)
+  int32_t slot, layer, prompt_len;
+};
+
+// One compression record per sequence in desc (ints):
+// {slot, block, pers_before, prompt_len, pages_off, npages, first_new, pad}
+constexpr int kCompRec = 8;
+struct CompressArgs {
+  DevPool P;
+  const void* qp;
+  const void* kp;
+  const void* vp;
+  void* out;
+  float* lse;
+  void* kp_rot;          // workspace [n][Hkv][Kp][D]: rotated pause keys
+  const int32_t* desc;   // n records, then page lists
+  int32_t layer, n, Hq, G, Kp, quota, log2Kp;
+};
+
+// Fill: desc holds per layer {pers_off, npers_pages, open_off, nopen_pages}
+// then the page lists.
+struct FillArgs {
+  DevPool P;
+  const int32_t* desc;
+  const int32_t* quota;  // [L] device
+  const int32_t* pause;  // [L] device
+  uint64_t seed;
+  int32_t slot, prompt_len, G, nb, compress;
+};
+
+// Gather rows [row0, row0+nrows) of (slot, layer) through the device page
+// table into k_out, v_out [nrows][Hkv][D].
+struct ReadArgs {
+  DevPool P;
+  void* k_out;
+  void* v_out;
+  int32_t slot, layer, row0, nrows;
+};
+
+// Export: writes {n_pers, n_open, qpos, npages, pages..., positions...}.
+struct ExportArgs {
+  DevPool P;
+  int32_t* dst;
+  int32_t slot, layer;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int32_t total_work, hipStream_t s);
+hipError_t launch_free(const FreeArgs& a, hipStream_t s);
+hipError_t launch_prompt(const PromptArgs& a, hipStream_t s);
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+hipError_t launch_fill(const FillArgs& a, int32_t max_rows, hipStream_t s);
+hipError_t launch_read(const ReadArgs& a, hipStream_t s);
+hipError_t launch_export(const ExportArgs& a, hipStream_t s);
+
+}  // namespace abk

@@ -1,0 +1,117 @@
+// Host bookkeeping of the paged AbridgeKV cache: page allocator, sequence
+// slots, per-(sequence, layer) row counts and page lists, protocol checks.
+// Plain C++ with no device calls; the C ABI drives it and mirrors its results
+// to the device. Every operation validates first and changes nothing on
+// failure.
+//
+// Cache structure (arXiv 2610.20641, abstract and Fig. 1 captions; AI Radio
+// transcript): per layer the resident rows are the prompt, quota[l] code rows
+// per finished block, and the open block's raw rows; rows a layer does not
+// keep are never allocated, and a finished block's raw rows are freed.
+#pragma once
+
+#include <cstdint>
+#include <functional>
+#include <queue>
+#include <string>
+#include <vector>
+
+namespace abk {
+
+enum Status : int32_t {
+  kOk = 0,
+  kInvalidArg = 1,
+  kOutOfPages = 2,
+  kBadState = 3,
+  kHipError = 4,
+  kUnsupported = 5,
+};
+
+struct Shape {
+  int32_t L = 0, Hq = 0, Hkv = 0, D = 0;
+  int32_t C = 0, pr = 0;  // block tokens, page rows
+  int32_t max_seqs = 0, max_position = 0, dtype = 0, compress = 1;
+  int64_t num_pages = 0;
+  double rope_base = 0.0;
+  std::vector<int32_t> quota, pause;  // per layer
+  int32_t esize() const { return dtype == 0 ? 4 : 2; }
+  int32_t max_pers_pages() const { return (max_position + pr - 1) / pr; }
+  int32_t max_open_pages() const { return compress ? C / pr : 0; }
+  int32_t table_stride() const { return max_pers_pages() + max_open_pages(); }
+};
+
+struct LayerState {
+  int32_t G = 0;          // generated rows appended at this layer
+  int32_t pers_rows = 0;  // prompt + code rows (compress) or prompt + text (full-KV)
+  std::vector<int32_t> pers_pages, open_pages;
+  bool compressed = false;  // current block compressed here, not yet freed
+  bool prompt_written = false;
+};
+
+struct SeqState {
+  bool live = false;
+  int32_t P = 0;
+  int32_t nb = 0;  // blocks compressed and freed
+  std::vector<LayerState> layers;
+};
+
+// What one sequence of a compress call needs on the device.
+struct CompressPlan {
+  int32_t slot, block, pers_before;
+  std::vector<int32_t> pages;  // pages covering rows [pers_before, pers_before + quota)
+  int32_t first_new;           // index in `pages` of the first newly taken page
+};
+
+class HostPool {
+ public:
+  Status init(const Shape& s, std::string* err);
+
+  const Shape& shape() const { return s_; }
+  const SeqState& seq(int32_t id) const { return seqs_[id]; }
+  int64_t pages_free() const { return (int64_t)free_pages_.size(); }
+  int32_t open_rows(int32_t id, int32_t l) const;
+  int32_t resident_rows(int32_t id, int32_t l) const;
+  int64_t resident_rows_total() const;
+
+  // Checks shared by the ABI.
+  Status check_seq(int32_t id) const;
+  Status check_layer(int32_t l) const;
+  Status check_batch(int32_t n, const int32_t* ids);
+
+  Status seq_create(int32_t P, int32_t* id);
+  Status seq_release(int32_t id);
+  Status write_prompt(int32_t id, int32_t l);
+  // new_page[i] = page taken for sequence i's row, or -1.
+  Status append(int32_t l, int32_t n, const int32_t* ids, std::vector<int32_t>* new_page);
+  Status check_decode(int32_t l, int32_t n, const int32_t* ids);
+  Status compress(int32_t l, int32_t n, const int32_t* ids, std::vector<CompressPlan>* plan);
+  Status free_block(int32_t n, const int32_t* ids);
+  Status fill(int32_t id, int32_t G);
+
+  // Position of resident row r of (id, l), from the host mirror.
+  int64_t row_position(int32_t id, int32_t l, int32_t r) const;
+
+  std::string err;  // reason of the last failure
+
+ private:
+  Status fail(Status st, const std::string& msg) {
+    err = msg;
+    return st;
+  }
+  int32_t take_page();
+  void give_page(int32_t p) { free_pages_.push(p); }
+  int32_t gmin(const SeqState& q) const;
+  int32_t gmax(const SeqState& q) const;
+
+  Shape s_;
+  std::vector<SeqState> seqs_;
+  std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_pages_;
+  std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_slots_;
+  std::vector<uint32_t> mark_;  // duplicate detection, stamped per call
+  uint32_t stamp_ = 0;
+};
+
+int32_t bitrev(int32_t k, int32_t nbits);
+int32_t log2_exact(int32_t x);  // -1 unless x is a power of two
+
+}  // namespace abk

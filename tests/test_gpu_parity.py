@@ -1,0 +1,284 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: bf16 pools (fp32 accumulation) max-abs 2e-2 on outputs and 1e-3 on lse;
+fp32 pools 1e-5 on both (the derivation: fp32 rounding of ~1e2-term sums of
+O(1) values); page tables, positions and row counts bit-exact; stored values
+bit-exact, stored rotated keys within one ulp of the storage type.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import PAUSE, PROMPT, TEXT
+from oracle.pagemodel import PageModel
+from tests.harness import Run, dev, host
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 1e-3), "f32": (1e-5, 1e-5)}
+
+
+def _close(name, got, want, tol):
+    err = float(np.abs(np.asarray(got) - np.asarray(want)).max()) if np.size(want) else 0.0
+    print(f"[parity] {name}: max-abs {err:.3e} (tol {tol:.0e})", flush=True)
+    assert err <= tol, f"{name}: max-abs {err} > {tol}"
+
+
+def _check_decode(run, sids, layer, q=None):
+    out, lse, q = run.decode(sids, layer, q)
+    to, tl = TOL[run.dtype]
+    for i, s in enumerate(sids):
+        o_ref, l_ref, keys = run.oracle_decode(s, layer, q[i])
+        _close(f"decode out seq{s} L{layer}", out[i], o_ref, to)
+        _close(f"decode lse seq{s} L{layer}", lse[i], l_ref, tl)
+        assert run.pool.seq_query(s, layer)["resident_rows"] == len(keys[0])
+    return out, lse
+
+
+def _check_layout(run, pm, sids):
+    for s in sids:
+        for l in range(run.L):
+            pages, pos = run.pool.export_layout(s, l)
+            mp, mpos, _ = pm.layout(s, l)
+            assert pages == mp, (s, l)
+            assert pos == mpos, (s, l)
+
+
+def _ulps_bf16(a, b):
+    ia = synth.bf16_bits_from_f32(np.asarray(a, np.float32)).astype(np.int32)
+    ib = synth.bf16_bits_from_f32(np.asarray(b, np.float32)).astype(np.int32)
+    return np.abs(ia - ib)
+
+
+# ---- the tiny fp32 case: 1 layer, d=16, P=2, C=8, K=4, 3 blocks + 5 open ------
+
+def test_tiny_fp32_decode_compress_free():
+    run = Run(L=1, Hq=2, Hkv=1, D=16, C=8, Kp=4, quota=[4], pr=4, dtype="f32", seed=0)
+    pm = PageModel(num_pages=run.pool.stats()["pages_free"], page_rows=4, num_layers=1, C=8,
+                   quotas=[4], pauses=[4], max_seqs=64)
+    s = run.new_seq(2, 0)
+    assert pm.seq_create(2) == s
+    run.write_prompts(s)
+    pm.write_prompt(s, 0)
+    # mirror every ABI step in the page model
+    for t in range(29):
+        if t > 0 and t % 8 == 0:
+            pm.compress(0, [s])
+            pm.free_block([s])
+        pm.append(0, [s])
+    run.grow({s: 29})
+    assert run.pool.seq_query(s, 0)["resident_rows"] == 19
+    _check_layout(run, pm, [s])
+    _check_decode(run, [s], 0)
+    # fill block 3 (G = 32), compress it, check outputs, code rows and layout
+    for _ in range(3):
+        pm.append(0, [s])
+    run.grow({s: 32})
+    assert run.pool.seq_query(s, 0)["resident_rows"] == 22
+    out, lse = run.compress_layer([s], 0)
+    torch.cuda.synchronize()
+    pm.compress(0, [s])
+    o_ref, l_ref, code = run.oracle_compress(s, 0)
+    _close("compress out", host(out)[0], o_ref, 1e-5)
+    _close("compress lse", host(lse)[0], l_ref, 1e-5)
+    assert [int(p) for p in code[3]] == [26, 30, 28, 32]  # bitrev positions in block 3
+    _check_layout(run, pm, [s])
+    k = torch.empty((4, 1, 16), device="cuda")
+    v = torch.empty((4, 1, 16), device="cuda")
+    run.pool.read_rows(s, 0, 14, 4, k, v)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(v), code[5])
+    _close("code rows k", host(k), code[4], 2e-6)
+    run.pool.free_block([s])
+    pm.free_block([s])
+    run.nb[s] += 1
+    assert run.pool.seq_query(s, 0)["resident_rows"] == 18
+    _check_layout(run, pm, [s])
+    # the next token decodes over the new code rows
+    pm.append(0, [s])
+    run.grow({s: 33})
+    _check_decode(run, [s], 0)
+    _check_layout(run, pm, [s])
+
+
+# ---- bf16 multi-tile, ragged, several blocks, through the ABI -----------------
+
+def _bf16_run(**kw):
+    base = dict(L=2, Hq=32, Hkv=8, D=128, C=64, Kp=16, quota=[16, 4], pr=16, dtype="bf16",
+                split_rows=32, seed=1)
+    base.update(kw)
+    return Run(**base)
+
+
+def test_bf16_ragged_history_decode_and_layout():
+    run = _bf16_run()
+    npages = run.pool.stats()["pages_free"]
+    Ps = [0, 3, 17, 40, 64]
+    Gs = [1, 63, 64, 65, 200]
+    sids = [run.new_seq(P, i) for i, P in enumerate(Ps)]
+    for s in sids:
+        run.write_prompts(s)
+    run.grow(dict(zip(sids, Gs)))
+    _check_decode(run, sids, 0)
+    _check_decode(run, sids, 1)
+    # row counts: prompt + quota per finished block + open rows
+    for s, P, G in zip(sids, Ps, Gs):
+        nb = (G - 1) // 64
+        for l, q in enumerate([16, 4]):
+            info = run.pool.seq_query(s, l)
+            assert info["resident_rows"] == P + nb * q + (G - nb * 64)
+    assert run.pool.stats()["pages_free"] < npages
+
+
+def test_bf16_compress_then_decode_uses_code_rows():
+    run = _bf16_run(seed=2)
+    Ps = [5, 64, 30]
+    sids = [run.new_seq(P, i) for i, P in enumerate(Ps)]
+    for s in sids:
+        run.write_prompts(s)
+    # second block complete: one block already compressed, this one open and full
+    run.grow({s: 128 for s in sids})
+    outs = [run.compress_layer(sids, l) for l in range(run.L)]
+    torch.cuda.synchronize()
+    for l, (out, lse) in enumerate(outs):
+        out, lse = host(out), host(lse)
+        for i, s in enumerate(sids):
+            o_ref, l_ref, code = run.oracle_compress(s, l)
+            _close(f"compress out seq{s} L{l}", out[i], o_ref, 2e-2)
+            _close(f"compress lse seq{s} L{l}", lse[i], l_ref, 1e-3)
+            # the kept rows: values bit-exact, rotated keys within one bf16 ulp
+            q = run.quota[l]
+            r0 = run.pool.seq_query(s, l)["resident_rows"] - 64 - q
+            k = torch.empty((q, run.Hkv, run.D), device="cuda", dtype=torch.bfloat16)
+            v = torch.empty_like(k)
+            run.pool.read_rows(s, l, r0, q, k, v)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(host(v), code[5])
+            assert _ulps_bf16(host(k), code[4]).max() <= 1
+    run.pool.free_block(sids)
+    for s in sids:
+        run.nb[s] += 1
+    run.grow({s: 129 for s in sids})
+    _check_decode(run, sids, 0)
+    _check_decode(run, sids, 1)
+
+
+def test_fill_equals_history_built_through_the_abi():
+    run = _bf16_run(seed=3)
+    a = run.new_seq(21, 0)
+    run.write_prompts(a)
+    run.grow({a: 150})
+    b = run.new_seq(21, 0)      # same synth seed as a
+    run.fill(b, 150)
+    for l in range(run.L):
+        oa, la, _ = run.decode([a], l)
+        ob, lb, _ = run.decode([b], l)
+        np.testing.assert_array_equal(oa, ob)
+        np.testing.assert_array_equal(la, lb)
+        n = run.pool.seq_query(a, l)["resident_rows"]
+        ka = torch.empty((n, run.Hkv, run.D), device="cuda", dtype=torch.bfloat16)
+        va, kb, vb = torch.empty_like(ka), torch.empty_like(ka), torch.empty_like(ka)
+        run.pool.read_rows(a, l, 0, n, ka, va)
+        run.pool.read_rows(b, l, 0, n, kb, vb)
+        torch.cuda.synchronize()
+        assert torch.equal(ka, kb) and torch.equal(va, vb)
+        assert run.pool.export_layout(a, l)[1] == run.pool.export_layout(b, l)[1]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 8, 64), (16, 8, 64), (16, 2, 128), (2, 1, 16)])
+def test_group_sizes_and_head_dims(Hq, Hkv, D):
+    run = _bf16_run(Hq=Hq, Hkv=Hkv, D=D, seed=4)
+    sids = [run.new_seq(P, i) for i, P in enumerate([7, 33])]
+    for s in sids:
+        run.fill(s, 150 if s == sids[0] else 77)
+    _check_decode(run, sids, 0)
+    _check_decode(run, sids, 1)
+
+
+def test_peaky_softmax_and_full_kv_mode():
+    run = _bf16_run(seed=5)
+    sids = [run.new_seq(P, i) for i, P in enumerate([12, 50])]
+    for s, G in zip(sids, [140, 190]):
+        run.fill(s, G)
+    q = np.stack([run.decode_query(s, 0, scale=8.0) for s in sids])
+    _check_decode(run, sids, 0, q)
+    full = _bf16_run(seed=5, compress=False)
+    fs = [full.new_seq(P, i) for i, P in enumerate([12, 50])]
+    for s, G in zip(fs, [140, 190]):
+        full.fill(s, G)
+    for s, G, P in zip(fs, [140, 190], [12, 50]):
+        assert full.pool.seq_query(s, 0)["resident_rows"] == P + G
+    _check_decode(full, fs, 0)
+    _check_decode(full, fs, 1)
+
+
+def test_planted_rows_are_found_at_every_position():
+    # q = RoPE^-1(alpha * k'_r) puts nearly all weight on row r: out ~ v_r
+    run = _bf16_run(seed=6, pr=16)
+    s = run.new_seq(37, 0)
+    run.fill(s, 64 * 3 + 20)
+    layer = 0
+    n = run.pool.seq_query(s, layer)["resident_rows"]
+    k = torch.empty((n, run.Hkv, run.D), device="cuda", dtype=torch.bfloat16)
+    v = torch.empty_like(k)
+    run.pool.read_rows(s, layer, 0, n, k, v)
+    torch.cuda.synchronize()
+    kh, vh = host(k), host(v)
+    qpos = run.P[s] + run.G[s] - 1
+    rows = sorted({0, 15, 16, 36, 37, 52, 53, 84, n - 20, n - 19, n - 2, n - 1})
+    for r in rows:
+        target = 8.0 * kh[r]                                   # [Hkv, d]
+        qk = np.repeat(target, run.Hq // run.Hkv, axis=0)      # [Hq, d]
+        q = oracle.rope_rows(qk[None], np.array([-qpos]), run.base)[0]
+        q = synth.to_storage(q, "bf16")
+        out, lse, _ = run.decode([s], layer, q[None])
+        o_ref, l_ref, _ = run.oracle_decode(s, layer, q)
+        _close(f"planted row {r}", out[0], o_ref, 2e-2)
+        _close(f"planted row {r} lse", lse[0], l_ref, 1e-3)
+        want = np.repeat(vh[r], run.Hq // run.Hkv, axis=0)
+        assert np.abs(out[0] - want).max() < 0.1, r
+
+
+def test_freed_raw_rows_are_not_attended():
+    run = _bf16_run(seed=7)
+    s = run.new_seq(9, 0)
+    run.write_prompts(s)
+    run.grow({s: 64})
+    layer = 0
+    # raw row of the block that is about to be freed (TEXT 10), rotated at its position
+    k10 = run.rows(s, layer, TEXT, [10], 0, synth.WHICH_K)[0]
+    run.grow({s: 65})  # compresses and frees block 0, appends token 64
+    qpos = run.P[s] + 64
+    kr = oracle.rope_rows(k10[None], np.array([run.P[s] + 10]), run.base)[0]
+    q = np.repeat(8.0 * kr, run.Hq // run.Hkv, axis=0)
+    q = synth.to_storage(oracle.rope_rows(q[None], np.array([-qpos]), run.base)[0], "bf16")
+    out, lse, _ = run.decode([s], layer, q[None])
+    o_ref, l_ref, keys = run.oracle_decode(s, layer, q)
+    assert not any((kd == TEXT and a == 10) for kd, a in zip(keys[0], keys[1]))
+    _close("freed row out", out[0], o_ref, 2e-2)
+    _close("freed row lse", lse[0], l_ref, 1e-3)
+    v10 = np.repeat(run.rows(s, layer, TEXT, [10], 0, synth.WHICH_V)[0], run.Hq // run.Hkv, 0)
+    assert np.abs(out[0] - v10).max() > 0.2
+
+
+# ---- full sizes ------------------------------------------------------------------
+
+def test_single_layer_bf16_full_size_sampled():
+    """16 sequences, prompt 256, 7,900 generated (15 blocks + 220 open), uniform
+    K = quota = 128, C = 512: every output against the oracle on 4 sequences."""
+    run = Run(L=1, Hq=32, Hkv=8, D=128, C=512, Kp=128, quota=[128], pr=64, dtype="bf16",
+              pool_bytes=1 << 30, seed=11)
+    sids = [run.new_seq(256, i) for i in range(16)]
+    for s in sids:
+        run.fill(s, 7900)
+        assert run.pool.seq_query(s, 0)["resident_rows"] == 2396
+    out, lse, q = run.decode(sids, 0)
+    for i in (0, 5, 10, 15):
+        o_ref, l_ref, _ = run.oracle_decode(sids[i], 0, q[i])
+        _close(f"full-size decode out seq{i}", out[i], o_ref, 2e-2)
+        _close(f"full-size decode lse seq{i}", lse[i], l_ref, 1e-3)
+    pos = run.pool.export_layout(sids[3], 0)[1]
+    want = oracle.visible_keys(run.view(sids[3], 0), 7900, 15, (TEXT, 7899, 0))[3]
+    assert pos == want.tolist()
