@@ -98,7 +98,7 @@ def run_decode(args, torch, abk):
     pool = abk.Pool(num_layers=L, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_tokens=C,
                     num_pause=Kp, layer_quota=quotas.tolist(), page_rows=PR, max_seqs=B,
                     pool_bytes=2 * page_bytes * pages, max_position=33792, dtype="bf16",
-                    rope_base=1e6)
+                    rope_base=1e6, decode_split_rows=args.split_rows)
     sids = []
     for i in range(B):
         s = pool.seq_create(int(P[i]))
@@ -326,20 +326,33 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--split-rows", type=int, default=0, help="rows per split-KV work item (0: library default)")
     ap.add_argument("--compress-reps", type=int, default=2)
     ap.add_argument("--no-compress", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see the sharding notes in DESIGN.md)", file=sys.stderr)
         sys.exit(2)
     import torch
-    import long_reasoning_kv_amd as abk
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration_mib:
+        # a plain copy of known size: reads and writes exactly n bytes each
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+    import long_reasoning_kv_amd as abk
     print(f"[bench] decode workload: 36 layers, 22 sequences, {args.warmup}+{args.steps} steps",
           file=sys.stderr, flush=True)
     res, workload = run_decode(args, torch, abk)

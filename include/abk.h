@@ -74,8 +74,10 @@ typedef struct {
   int32_t compress;     /* 1: AbridgeKV; 0: full-KV, blocks never close */
   int32_t host_only;    /* 1: bookkeeping only (no device memory, no kernels; data
                            pointers are ignored) -- for capacity planning and tests */
-  int32_t decode_split_rows; /* rows per split-KV work item of decode (0 = 512); rounded
-                                down to whole pages */
+  int32_t decode_split_rows; /* decode schedule: 0 = automatic (persistent, equal work per
+                                workgroup where the shape allows, else 512-row splits);
+                                > 0 = fixed split-KV work items of this many rows (whole
+                                pages) */
 } abk_pool_config;
 
 typedef struct {

@@ -12,7 +12,7 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libabk.so")
+LIB_PATH = os.environ.get("ABK_LIB") or os.path.join(_HERE, "libabk.so")
 
 OK, INVALID_ARG, OUT_OF_PAGES, BAD_STATE, HIP_ERROR, UNSUPPORTED = range(6)
 F32, BF16 = 0, 1

@@ -52,7 +52,8 @@ struct abk_pool {
   abk::HostPool host;
   abk::Shape shape;
   bool host_only = false;
-  int32_t split_rows = 512;
+  int32_t split_rows = 0;  // 0: automatic schedule; > 0: fixed split-KV work items of this many rows
+  int32_t stream_wgs = 0;  // resident workgroups of the stream-K decode (0: not used)
   hipStream_t stream = nullptr;
   abk::DevPool dev{};
   int32_t* quota_d = nullptr;
@@ -161,7 +162,7 @@ abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_poo
     delete p;
     return set_err(ABK_ERR_INVALID_ARG, "decode_split_rows is negative");
   }
-  p->split_rows = cfg->decode_split_rows > 0 ? cfg->decode_split_rows : 512;
+  p->split_rows = cfg->decode_split_rows;
   p->stream = (hipStream_t)hip_stream;
   if (p->host_only) {
     *out = p;
@@ -213,6 +214,18 @@ abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_poo
   if ((err = hipMemcpy(p->pause_d, s.pause.data(), s.L * sizeof(int32_t), hipMemcpyHostToDevice)))
     return fail(err, "pause upload");
   if ((err = hipDeviceSynchronize())) return fail(err, "init sync");
+  {
+    int dev = 0, cus = 0;
+    if ((err = hipGetDevice(&dev))) return fail(err, "device");
+    if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)))
+      return fail(err, "device attributes");
+    abk::DevPool probe = d;
+    probe.pr = s.pr;
+    probe.D = s.D;
+    probe.dtype = s.dtype;
+    if (abk::decode_stream_supported(probe, s.Hq / s.Hkv))
+      p->stream_wgs = cus * abk::decode_stream_blocks_per_cu(probe);
+  }
   d.L = s.L;
   d.Hkv = s.Hkv;
   d.D = s.D;
@@ -313,15 +326,65 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
   if (p->host_only || n == 0) return ABK_OK;
   const abk::Shape& s = p->shape;
   const int32_t G = s.Hq / s.Hkv;
-  const int32_t split_pages = std::max(1, p->split_rows / s.pr);
-  // size the partials for the whole call first (growing synchronises)
-  size_t need = 0;
+  const size_t qb = (size_t)s.Hq * s.D * s.esize();
+  if (p->stream_wgs > 0 && p->split_rows == 0) {
+    // stream-K: equal runs of 32-row units over the flattened (sequence, head, unit) work
+    const int32_t nq = s.pr / 32;
+    for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
+      const int32_t m = std::min(n - c0, abk::kMaxBatch);
+      abk::StreamArgs a;
+      a.useg[0] = 0;
+      for (int32_t i = 0; i < m; ++i) {
+        const auto& lay = p->host.seq(seq_ids[c0 + i]).layers[layer];
+        const int32_t units = (int32_t)(lay.pers_pages.size() + lay.open_pages.size()) * nq;
+        a.slot[i] = seq_ids[c0 + i];
+        a.useg[i + 1] = a.useg[i] + units * s.Hkv;
+      }
+      const int32_t U = a.useg[m];
+      const int32_t kMinUnits = 8;  // per workgroup, to amortise its set-up
+      int32_t W = std::max(1, std::min(p->stream_wgs, (U + kMinUnits - 1) / kMinUnits));
+      const int32_t T = (U + W - 1) / W;
+      W = (U + T - 1) / T;
+      int32_t maxp = 1;
+      for (int32_t i = 0; i < m; ++i) {
+        const int32_t units = (a.useg[i + 1] - a.useg[i]) / s.Hkv;
+        for (int32_t h = 0; h < s.Hkv; ++h) {
+          const int32_t S = a.useg[i] + h * units;
+          maxp = std::max(maxp, (S + units - 1) / T - S / T + 1);
+        }
+      }
+      if (maxp > abk::kMaxSplits) return set_err(ABK_ERR_UNSUPPORTED, "too many partials per head");
+      if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
+                               (size_t)m * s.Hkv * maxp * G * (s.D + 2) * sizeof(float)))
+        return st;
+      a.P = p->dev;
+      a.q = (const char*)q + c0 * qb;
+      a.out = (char*)out + c0 * qb;
+      a.lse = lse + (size_t)c0 * s.Hq;
+      a.part = p->part;
+      a.layer = layer;
+      a.n = m;
+      a.T = T;
+      a.U = U;
+      a.maxp = maxp;
+      ABK_HIP(abk::launch_decode_stream(a, W, p->stream));
+    }
+    return ABK_OK;
+  }
+  // pages per split-KV work item; widened when a sequence would need more
+  // than kMaxSplits of them
+  int32_t split_pages = std::max(1, (p->split_rows > 0 ? p->split_rows : 512) / s.pr);
   std::vector<int32_t> splits(n);
+  int32_t max_nvp = 0;
   for (int32_t i = 0; i < n; ++i) {
     const auto& lay = p->host.seq(seq_ids[i]).layers[layer];
-    const int32_t nvp = (int32_t)(lay.pers_pages.size() + lay.open_pages.size());
-    splits[i] = (nvp + split_pages - 1) / split_pages;
+    splits[i] = (int32_t)(lay.pers_pages.size() + lay.open_pages.size());
+    max_nvp = std::max(max_nvp, splits[i]);
   }
+  split_pages = std::max(split_pages, (max_nvp + abk::kMaxSplits - 1) / abk::kMaxSplits);
+  for (int32_t i = 0; i < n; ++i) splits[i] = (splits[i] + split_pages - 1) / split_pages;
+  // size the partials for the whole call first (growing synchronises)
+  size_t need = 0;
   for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
     size_t t = 0;
     for (int32_t i = c0; i < std::min(n, c0 + abk::kMaxBatch); ++i) t += splits[i];
@@ -330,7 +393,6 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
   if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
                            need * s.Hkv * G * (s.D + 2) * sizeof(float)))
     return st;
-  const size_t qb = (size_t)s.Hq * s.D * s.esize();
   for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
     const int32_t m = std::min(n - c0, abk::kMaxBatch);
     abk::DecodeArgs a;

@@ -11,7 +11,8 @@
 
 namespace abk {
 
-constexpr int kMaxBatch = 256;  // sequences per hot-path launch (larger batches are split)
+constexpr int kMaxBatch = 256;   // sequences per hot-path launch (larger batches are split)
+constexpr int kMaxSplits = 256;  // split-KV work items per sequence (the host sizes splits to fit)
 
 // Device view of a pool. Pages: K [page][Hkv][pr][D], V likewise; pos
 // [page][pr]. ptab[(slot*L + l)*tstride + i]: persistent page i for
@@ -45,6 +46,23 @@ struct DecodeArgs {
   int32_t layer, n, G, split_pages;
   int32_t slot[kMaxBatch];
   int32_t prefix[kMaxBatch + 1];  // work items of sequence i: [prefix[i], prefix[i+1])
+};
+
+// Persistent stream-K decode (bf16, d = 128, 4 query heads per KV head): the
+// flattened work (sequence i, KV head h, 32-row unit) is cut into equal runs of
+// T units, one per workgroup. useg[i] = first flattened unit of sequence i
+// (its units for head h follow at useg[i] + h * units_i). A (sequence, head)
+// whose units span workgroups wa..wb leaves partials in slots
+// ((i * Hkv + h) * maxp + (w - wa)) for the merge kernel.
+struct StreamArgs {
+  DevPool P;
+  const void* q;
+  void* out;
+  float* lse;
+  float* part;  // [n][Hkv][maxp][4][D + 2]
+  int32_t layer, n, T, U, maxp;
+  int32_t slot[kMaxBatch];
+  int32_t useg[kMaxBatch + 1];
 };
 
 struct FreeArgs {
@@ -106,6 +124,10 @@ struct ExportArgs {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int32_t total_work, hipStream_t s);
+// stream-K path: shapes it serves, workgroups per CU it keeps resident, launch
+bool decode_stream_supported(const DevPool& P, int32_t G);
+int32_t decode_stream_blocks_per_cu(const DevPool& P);
+hipError_t launch_decode_stream(const StreamArgs& a, int32_t nwg, hipStream_t s);
 hipError_t launch_free(const FreeArgs& a, hipStream_t s);
 hipError_t launch_prompt(const PromptArgs& a, hipStream_t s);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);

@@ -90,6 +90,25 @@ __device__ __forceinline__ float across_max(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over lane bits 3..5 (the 8 row slots of an 8-lanes-per-row
+// layout) without the LDS crossbar: DPP row_ror:8 pairs lanes i and i^8 inside
+// a 16-lane row, v_permlane16_swap exchanges neighbouring rows and
+// v_permlane32_swap the two halves of the wavefront.
+__device__ __forceinline__ float slots8_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false)));
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float slots8_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Rows are read 16 bytes per lane: EPL elements per lane, LPR lanes per row,
 // RPL rows per wavefront load, at most MAXCH loads per 64-row page.
 template <typename T, int D>
@@ -161,22 +180,81 @@ __global__ void __launch_bounds__(1024) append_kernel(AppendArgs a) {
   }
 }
 
-// ---- a2: split-KV decode partials -----------------------------------------------
+// ---- a2 + a3: split-KV decode ----------------------------------------------------
 //
-// Work item (sequence i, split s) x KV head h: 4 wavefronts take the split's
-// pages round-robin. A page is read 16 bytes per lane (LPR lanes per row);
-// each lane holds its slice of the G rotated queries, so one K load feeds G
-// dot products that are finished by a DPP group sum. Softmax is online per
-// page with a wavefront-uniform running max (log2 domain), V is accumulated
-// per lane and reduced across row groups and wavefronts at the end.
+// Work item (sequence i, split s) x KV head h. A split is a run of pages; a page
+// is cut into units of RW rows and wavefront w takes units w, w+4, ... so all
+// four wavefronts stream the same pages. A unit is read 16 bytes per lane (LPR
+// lanes per row, RPL rows per load): each lane holds its slice of the G
+// rotated queries, so one K load feeds G dot products finished by a DPP group
+// sum. The next unit's K and V are loaded into registers before the current
+// unit is computed. Softmax is online per unit with a wavefront-uniform running
+// max (log2 domain); V is accumulated per lane and reduced across row groups
+// and wavefronts at the end; a sequence with several splits leaves partials
+// (o, m, l) for the merge kernel.
+
+#ifndef ABK_UNIT_ROWS
+#define ABK_UNIT_ROWS 16  // rows of a page a wavefront reads per step
+#endif
+#ifndef ABK_PREFETCH_UNITS
+#define ABK_PREFETCH_UNITS 1  // units a wavefront keeps in flight while computing one
+#endif
+template <typename T, int D>
+struct UnitCfg {
+  using R = RowCfg<T, D>;
+  static constexpr int CW = R::RPL >= ABK_UNIT_ROWS ? 1 : ABK_UNIT_ROWS / R::RPL;  // loads/lane
+  static constexpr int RW = CW * R::RPL;                                            // rows/unit
+};
+
+__device__ __forceinline__ int sgpr(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// a3: merge the split partials of one (sequence, KV head): weights
+// exp2(m_s - M) / L per (split, query head) in LDS, then every output element
+// is one weighted sum over the splits.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(1024) decode_merge_kernel(DecodeArgs a) {
+  __shared__ float sm_pm[kMaxSplits * G], sm_pl[kMaxSplits * G], sm_M[G], sm_L[G];
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int b0 = a.prefix[i], ns = a.prefix[i + 1] - b0;
+  if (ns == 1) return;  // single split: the split kernel wrote out and lse
+  const int Hkv = a.P.Hkv, Hq = Hkv * G;
+  auto part = [&](int s, int g) { return a.part + (((size_t)(b0 + s) * Hkv + h) * G + g) * (D + 2); };
+  for (int t = threadIdx.x; t < ns * G; t += blockDim.x) {
+    const float* pp = part(t / G, t % G);
+    sm_pm[t] = pp[D];
+    sm_pl[t] = pp[D + 1];
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, sm_pm[s2 * G + g]);
+    float Ls = 0.f;
+    for (int s2 = 0; s2 < ns; ++s2) Ls += sm_pl[s2 * G + g] * fast_exp2(sm_pm[s2 * G + g] - M);
+    sm_M[g] = M;
+    sm_L[g] = Ls;
+    a.lse[(size_t)i * Hq + h * G + g] = (M + __log2f(Ls)) * 0.6931471805599453f;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < ns * G; t += blockDim.x)
+    sm_pm[t] = fast_exp2(sm_pm[t] - sm_M[t % G]) / sm_L[t % G];
+  __syncthreads();
+  for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
+    const int g = t / D, d = t % D;
+    float O = 0.f;
+    for (int s2 = 0; s2 < ns; ++s2) O += part(s2, g)[d] * sm_pm[s2 * G + g];
+    ((T*)a.out)[((size_t)i * Hq + h * G + g) * D + d] = from_f32<T>(O);
+  }
+}
 
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   using Cfg = RowCfg<T, D>;
-  constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPL = Cfg::RPL, MAXCH = Cfg::MAXCH;
+  constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPL = Cfg::RPL;
+  constexpr int CW = UnitCfg<T, D>::CW, RW = UnitCfg<T, D>::RW;
   const DevPool& P = a.P;
   const int w = blockIdx.x, h = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
   const int c = lane % LPR, grp = lane / LPR;
 
   int lo = 0, hi = a.n - 1;
@@ -185,27 +263,40 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     if (a.prefix[mid] <= w) lo = mid;
     else hi = mid - 1;
   }
-  const int i = lo, s = w - a.prefix[i], nsplit = a.prefix[i + 1] - a.prefix[i];
+  const int i = lo, s = w - a.prefix[i], b0 = a.prefix[i], nsplit = a.prefix[i + 1] - b0;
   const int slot = a.slot[i];
   const int32_t* meta = meta_of(P, slot, a.layer);
-  const int n_pers = meta[0], n_open = meta[1], qpos = meta[2];
+  const int n_pers = sgpr(meta[0]), n_open = sgpr(meta[1]), qpos = sgpr(meta[2]);
   const int pr = P.pr;
   const int npp = (n_pers + pr - 1) / pr, nop = (n_open + pr - 1) / pr;
   const int vp0 = s * a.split_pages, vp1 = min(npp + nop, vp0 + a.split_pages);
+  const int NQ = (pr + RW - 1) / RW;
+  const int nunits = (vp1 - vp0) * NQ;
   const int32_t* tab = ptab_of(P, slot, a.layer);
   const int Hq = P.Hkv * G;
 
-  // rotated, pre-scaled query slice: dims c*EPL .. c*EPL+EPL-1 of heads h*G+g
+  // rotated, pre-scaled query slice: dims c*EPL .. c*EPL+EPL-1 of heads h*G+g.
+  // Rotate-half pairs dim d with d +- D/2: the lane loads its own 16 bytes and
+  // its partner's, and the (cos, sin) of its dims, all unconditionally.
   float qv[G][EPL];
   {
-    const float2* rope = P.rope + (size_t)qpos * (D / 2);
+    constexpr int H = D / 2;
+    const int d0 = c * EPL;                 // first dim of this lane
+    const int dp = (d0 + H) % D;            // partner dims
+    const float sgn = d0 < H ? -1.f : 1.f;  // y = x cos + sgn * x_partner sin
+    const float2* rope = P.rope + (size_t)qpos * H + (d0 % H);
+    float2 cs[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) cs[e] = rope[e];
     const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const T* qh = (const T*)a.q + ((size_t)i * Hq + h * G + g) * D;
+      float x[EPL], xp[EPL];
+      unpack16(*(const uint4*)(qh + d0), x, T());
+      unpack16(*(const uint4*)(qh + dp), xp, T());
 #pragma unroll
-      for (int e = 0; e < EPL; ++e)
-        qv[g][e] = qs * rope_elem<D>([&](int d) { return to_f32(qh[d]); }, c * EPL + e, rope);
+      for (int e = 0; e < EPL; ++e) qv[g][e] = qs * (x[e] * cs[e].x + sgn * xp[e] * cs[e].y);
     }
   }
 
@@ -220,68 +311,108 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 
   const T* kpool = (const T*)P.kpool;
   const T* vpool = (const T*)P.vpool;
-  for (int vp = vp0 + wave; vp < vp1; vp += 4) {
+  // unit u -> (element offset of its first row for this lane, valid rows in it)
+  auto locate = [&](int u, size_t* off, int* nval) {
+    const int vp = vp0 + u / NQ, qq = u % NQ;
     int page, rows;
     if (vp < npp) {
-      page = tab[vp];
+      page = sgpr(tab[vp]);
       rows = (vp == npp - 1) ? n_pers - vp * pr : pr;
     } else {
       const int j = vp - npp;
-      page = tab[P.max_pers + j];
+      page = sgpr(tab[P.max_pers + j]);
       rows = (j == nop - 1) ? n_open - j * pr : pr;
     }
-    const size_t base = ((size_t)page * P.Hkv + h) * pr * D + c * EPL;
-    float sc[MAXCH][G];
+    *off = (((size_t)page * P.Hkv + h) * pr + (size_t)qq * RW) * D + c * EPL;
+    *nval = rows - qq * RW;  // rows of this unit that exist (may be <= 0)
+  };
+  auto load = [&](size_t off, int nval, uint4* kr, uint4* vr) {
 #pragma unroll
-    for (int ch = 0; ch < MAXCH; ++ch) {
-      if (ch * RPL < rows) {
-        const int r = ch * RPL + grp;
-        const bool valid = r < rows;
-        const int rl = valid ? r : rows - 1;
-        const uint4 kw = *(const uint4*)(kpool + base + (size_t)rl * D);
-        float kf[EPL];
-        unpack16(kw, kf, T());
+    for (int ch = 0; ch < CW; ++ch) {
+      int r = ch * RPL + grp;
+      r = r < nval ? r : (nval > 0 ? nval - 1 : 0);
+      kr[ch] = *(const uint4*)(kpool + off + (size_t)r * D);
+      vr[ch] = *(const uint4*)(vpool + off + (size_t)r * D);
+    }
+  };
+  auto compute = [&](int nval, const uint4* kr, const uint4* vr) {
+    float sc[CW][G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float acc = 0.f;
+    for (int ch = 0; ch < CW; ++ch) {
+      float kf[EPL];
+      unpack16(kr[ch], kf, T());
+      const bool valid = ch * RPL + grp < nval;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc += qv[g][e] * kf[e];
-          acc = group_sum<LPR>(acc);
-          sc[ch][g] = valid ? acc : -INFINITY;
-        }
-      } else {
+      for (int g = 0; g < G; ++g) {
+        float acc = 0.f;
 #pragma unroll
-        for (int g = 0; g < G; ++g) sc[ch][g] = -INFINITY;
+        for (int e = 0; e < EPL; ++e) acc += qv[g][e] * kf[e];
+        acc = group_sum<LPR>(acc);
+        sc[ch][g] = valid ? acc : -INFINITY;
       }
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float mx = sc[0][g];
 #pragma unroll
-      for (int ch = 1; ch < MAXCH; ++ch) mx = fmaxf(mx, sc[ch][g]);
-      mx = across_max<LPR>(mx);
-      const float mn = fmaxf(m_run[g], mx);
-      const float alpha = fast_exp2(m_run[g] - mn);
-      m_run[g] = mn;
-      l_run[g] *= alpha;
+      for (int ch = 1; ch < CW; ++ch) mx = fmaxf(mx, sc[ch][g]);
+      mx = across_max<LPR>(mx);  // finite: the unit has a valid row
+      // rescale only when the running max grows (wavefront-uniform branch)
+      if (mx > m_run[g]) {
+        const float alpha = fast_exp2(m_run[g] - mx);
+        m_run[g] = mx;
+        l_run[g] *= alpha;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[g][e] *= alpha;
+        for (int e = 0; e < EPL; ++e) o[g][e] *= alpha;
+      }
     }
 #pragma unroll
-    for (int ch = 0; ch < MAXCH; ++ch) {
-      if (ch * RPL < rows) {
-        const int r = ch * RPL + grp;
-        const int rl = r < rows ? r : rows - 1;
-        const uint4 vw = *(const uint4*)(vpool + base + (size_t)rl * D);
-        float vf[EPL];
-        unpack16(vw, vf, T());
+    for (int ch = 0; ch < CW; ++ch) {
+      float vf[EPL];
+      unpack16(vr[ch], vf, T());
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float p = fast_exp2(sc[ch][g] - m_run[g]);
-          l_run[g] += p;
+      for (int g = 0; g < G; ++g) {
+        const float p = fast_exp2(sc[ch][g] - m_run[g]);
+        l_run[g] += p;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) o[g][e] += p * vf[e];
+        for (int e = 0; e < EPL; ++e) o[g][e] += p * vf[e];
+      }
+    }
+  };
+
+  // ring of NB unit buffers: NB-1 units are in flight while one is computed
+  constexpr int NB = ABK_PREFETCH_UNITS + 1;
+  uint4 kb[NB][CW], vb[NB][CW];
+  size_t offb[NB];
+  int nvb[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    offb[b] = 0;
+    nvb[b] = 0;
+  }
+#pragma unroll
+  for (int b = 0; b < NB - 1; ++b) {
+    const int ub = wave + 4 * b;
+    if (ub < nunits) {
+      locate(ub, &offb[b], &nvb[b]);
+      load(offb[b], nvb[b], kb[b], vb[b]);
+    }
+  }
+  int u = wave;
+  bool more = u < nunits;
+  while (more) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (more) {
+        const int un = u + 4 * (NB - 1);
+        const int bn = (b + NB - 1) % NB;
+        if (un < nunits) {
+          locate(un, &offb[bn], &nvb[bn]);
+          load(offb[bn], nvb[bn], kb[bn], vb[bn]);
         }
+        if (nvb[b] > 0) compute(nvb[b], kb[b], vb[b]);
+        u += 4;
+        more = u < nunits;
       }
     }
   }
@@ -311,7 +442,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     float Ls = 0.f, O = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const float f = fast_exp2(sm_m[ww][g] - M);
+      // a wavefront that saw no rows has m = -inf, l = 0, o = 0
+      const float f = sm_m[ww][g] == -INFINITY ? 0.f : fast_exp2(sm_m[ww][g] - M);
       Ls += sm_l[ww][g] * f;
       O += sm_o[ww][g][d] * f;
     }
@@ -330,29 +462,773 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// ---- a3: merge split partials --------------------------------------------------
+// ---- a2, bf16 and d = 128: the streaming kernel -------------------------------------
+//
+// Same work items and output as decode_split_kernel, shaped for CDNA4's VALU:
+//  - 8 lanes per row; lane c holds dims [8c, 8c+8) and [64+8c, 64+8c+8), i.e.
+//    both halves of its rotate-half pairs, so each wavefront load is 8 rows x
+//    128 contiguous bytes;
+//  - q.k on v_dot2c_f32_bf16: the rotated, pre-scaled query is split into
+//    bf16 hi + lo parts (|q - hi - lo| <= 2^-16 |q|), keys are used as stored;
+//  - 3 DPP steps finish a row's dot product; 2 rows x G heads per lane per
+//    16-row unit need exp2, not 4 x G;
+//  - the unit's base address is wavefront-uniform, lane offsets are fixed, and
+//    only partial units clamp rows.
 
-template <typename T, int D, int G>
-__global__ void __launch_bounds__(1024) decode_combine_kernel(DecodeArgs a) {
-  const int i = blockIdx.x, h = blockIdx.y;
-  const int b0 = a.prefix[i], ns = a.prefix[i + 1] - b0;
-  if (ns == 1) return;
-  const int Hkv = a.P.Hkv, Hq = Hkv * G;
-  for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// nearest-even bf16 bits of a finite float (no NaN handling: queries are finite)
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int G>
+__global__ void __launch_bounds__(256) decode_bf16_d128_kernel(DecodeArgs a) {
+  constexpr int D = 128, UR = 16;  // rows per unit: 2 groups of 8
+  const DevPool& P = a.P;
+  const int w = blockIdx.x, h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
+  const int c8 = lane & 7, r8 = lane >> 3;
+
+  int lo = 0, hi = a.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.prefix[mid] <= w) lo = mid;
+    else hi = mid - 1;
+  }
+  const int i = lo, s = w - a.prefix[i], nsplit = a.prefix[i + 1] - a.prefix[i];
+  const int slot = a.slot[i];
+  const int32_t* meta = meta_of(P, slot, a.layer);
+  const int n_pers = sgpr(meta[0]), n_open = sgpr(meta[1]), qpos = sgpr(meta[2]);
+  const int pr = P.pr;
+  const int npp = (n_pers + pr - 1) / pr, nop = (n_open + pr - 1) / pr;
+  const int vp0 = s * a.split_pages, vp1 = min(npp + nop, vp0 + a.split_pages);
+  const int NQ = (pr + UR - 1) / UR;
+  const int nunits = (vp1 - vp0) * NQ;
+  const int32_t* tab = ptab_of(P, slot, a.layer);
+  const int Hq = P.Hkv * G;
+
+  // query: rotate dims (8c8+e, 64+8c8+e) together, scale, split into hi/lo bf16 pairs
+  uint32_t qh[G][8], ql[G][8];
+  {
+    const float2* rope = P.rope + (size_t)qpos * (D / 2) + 8 * c8;
+    float cs_c[8], cs_s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float2 t = rope[e];
+      cs_c[e] = t.x;
+      cs_s[e] = t.y;
+    }
+    const float qs = 1.4426950408889634f / sqrtf((float)D);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)i * Hq + h * G + g) * D;
+      float xa[8], xb[8], y[16];
+      unpack16(*(const uint4*)(qrow + 8 * c8), xa, bf16_t());
+      unpack16(*(const uint4*)(qrow + 64 + 8 * c8), xb, bf16_t());
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y[e] = qs * (xa[e] * cs_c[e] - xb[e] * cs_s[e]);
+        y[8 + e] = qs * (xb[e] * cs_c[e] + xa[e] * cs_s[e]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t h0 = bf16_bits(y[2 * j]), h1 = bf16_bits(y[2 * j + 1]);
+        const float r0 = y[2 * j] - __uint_as_float(h0 << 16);
+        const float r1 = y[2 * j + 1] - __uint_as_float(h1 << 16);
+        qh[g][j] = h0 | (h1 << 16);
+        ql[g][j] = bf16_bits(r0) | (bf16_bits(r1) << 16);
+      }
+    }
+  }
+
+  float m_run[G], l_run[G], o[G][16];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[g][e] = 0.f;
+  }
+
+  const char* kbase = (const char*)P.kpool;
+  const char* vbase = (const char*)P.vpool;
+  const uint32_t lane_off = (uint32_t)(r8 * D + 8 * c8) * 2;  // bytes, row r8 of a group
+  // unit u -> wavefront-uniform byte offset of its first row, rows present
+  auto locate = [&](int u, size_t* off, int* nval) {
+    const int vp = vp0 + u / NQ, qq = u % NQ;
+    int page, rows;
+    if (vp < npp) {
+      page = sgpr(tab[vp]);
+      rows = (vp == npp - 1) ? n_pers - vp * pr : pr;
+    } else {
+      const int j = vp - npp;
+      page = sgpr(tab[P.max_pers + j]);
+      rows = (j == nop - 1) ? n_open - j * pr : pr;
+    }
+    *off = ((((size_t)page * P.Hkv + h) * pr) + (size_t)qq * UR) * D * 2;
+    *nval = rows - qq * UR;
+  };
+  // kr[0..3]: group 0 dims lo/hi half, group 1 dims lo/hi half
+  auto load = [&](size_t off, int nval, uint4* kr, uint4* vr) {
+    const char* kb = kbase + off;
+    const char* vb = vbase + off;
+    if (nval >= UR) {
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        const uint32_t o2 = lane_off + rg * 8 * D * 2;
+        kr[2 * rg] = *(const uint4*)(kb + o2);
+        kr[2 * rg + 1] = *(const uint4*)(kb + o2 + 128);
+        vr[2 * rg] = *(const uint4*)(vb + o2);
+        vr[2 * rg + 1] = *(const uint4*)(vb + o2 + 128);
+      }
+    } else {
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        int r = rg * 8 + r8;
+        r = r < nval ? r : (nval > 0 ? nval - 1 : 0);
+        const uint32_t o2 = (uint32_t)(r * D + 8 * c8) * 2;
+        kr[2 * rg] = *(const uint4*)(kb + o2);
+        kr[2 * rg + 1] = *(const uint4*)(kb + o2 + 128);
+        vr[2 * rg] = *(const uint4*)(vb + o2);
+        vr[2 * rg + 1] = *(const uint4*)(vb + o2 + 128);
+      }
+    }
+  };
+  auto compute = [&](int nval, const uint4* kr, const uint4* vr) {
+    float sc[2][G];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      const uint32_t k[8] = {kr[2 * rg].x,     kr[2 * rg].y,     kr[2 * rg].z,     kr[2 * rg].w,
+                             kr[2 * rg + 1].x, kr[2 * rg + 1].y, kr[2 * rg + 1].z, kr[2 * rg + 1].w};
+      const bool valid = rg * 8 + r8 < nval;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          acc = dot2_bf16(k[j], qh[g][j], acc);
+          acc = dot2_bf16(k[j], ql[g][j], acc);
+        }
+        acc = group_sum<8>(acc);
+        sc[rg][g] = valid ? acc : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mx = across_max<8>(fmaxf(sc[0][g], sc[1][g]));
+      if (mx > m_run[g]) {  // wavefront-uniform
+        const float alpha = fast_exp2(m_run[g] - mx);
+        m_run[g] = mx;
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[g][e] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      float vf[16];
+      unpack16(vr[2 * rg], vf, bf16_t());
+      unpack16(vr[2 * rg + 1], vf + 8, bf16_t());
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = fast_exp2(sc[rg][g] - m_run[g]);
+        l_run[g] += p;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[g][e] += p * vf[e];
+      }
+    }
+  };
+
+  constexpr int NB = 2;
+  uint4 kb[NB][4], vb[NB][4];
+  size_t offb[NB] = {0, 0};
+  int nvb[NB] = {0, 0};
+  if (wave < nunits) {
+    locate(wave, &offb[0], &nvb[0]);
+    load(offb[0], nvb[0], kb[0], vb[0]);
+  }
+  int u = wave;
+  bool more = u < nunits;
+  while (more) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (more) {
+        const int un = u + 4;
+        const int bn = (b + 1) % NB;
+        if (un < nunits) {
+          locate(un, &offb[bn], &nvb[bn]);
+          load(offb[bn], nvb[bn], kb[bn], vb[bn]);
+        }
+        if (nvb[b] > 0) compute(nvb[b], kb[b], vb[b]);
+        u += 4;
+        more = u < nunits;
+      }
+    }
+  }
+
+  // reduce across the 8 row slots of the wavefront, then across wavefronts
+  __shared__ float sm_o[4][G][D];
+  __shared__ float sm_m[4][G], sm_l[4][G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float lw = across_sum<8>(l_run[g]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float oe = across_sum<8>(o[g][e]);
+      if (r8 == 0) sm_o[wave][g][(e < 8 ? 0 : 64) + 8 * c8 + (e & 7)] = oe;
+    }
+    if (lane == 0) {
+      sm_m[wave][g] = m_run[g];
+      sm_l[wave][g] = lw;
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < G * D; t += 256) {
     const int g = t / D, d = t % D;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s)
-      M = fmaxf(M, a.part[(((size_t)(b0 + s) * Hkv + h) * G + g) * (D + 2) + D]);
+    float M = sm_m[0][g];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][g]);
     float Ls = 0.f, O = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float* pp = a.part + (((size_t)(b0 + s) * Hkv + h) * G + g) * (D + 2);
-      const float f = fast_exp2(pp[D] - M);
-      Ls += pp[D + 1] * f;
-      O += pp[d] * f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float f = sm_m[ww][g] == -INFINITY ? 0.f : fast_exp2(sm_m[ww][g] - M);
+      Ls += sm_l[ww][g] * f;
+      O += sm_o[ww][g][d] * f;
     }
     const int hq = h * G + g;
-    ((T*)a.out)[((size_t)i * Hq + hq) * D + d] = from_f32<T>(O / Ls);
-    if (d == 0) a.lse[(size_t)i * Hq + hq] = (M + __log2f(Ls)) * 0.6931471805599453f;
+    if (nsplit == 1) {
+      ((bf16_t*)a.out)[((size_t)i * Hq + hq) * D + d] = from_f32<bf16_t>(O / Ls);
+      if (d == 0) a.lse[(size_t)i * Hq + hq] = (M + __log2f(Ls)) * 0.6931471805599453f;
+    } else {
+      float* pp = a.part + (((size_t)w * P.Hkv + h) * G + g) * (D + 2);
+      pp[d] = O;
+      if (d == 0) {
+        pp[D] = M;
+        pp[D + 1] = Ls;
+      }
+    }
+  }
+}
+
+// ---- a2, bf16, d = 128, four query heads per KV head: LDS-staged streaming -------
+//
+// The workgroup streams a split's pages in units of 32 rows: every thread loads
+// its 16-byte pieces of a later unit's K and V into registers (two stages in
+// flight), stores the next unit into one of two LDS buffers, and the four
+// wavefronts compute the current unit from LDS. Wavefront w takes query heads
+// {2(w&1), 2(w&1)+1} of the group over rows [16(w>>1), 16(w>>1)+16) of each
+// unit, so each V row is widened to fp32 twice (not once per head) and each
+// wavefront holds two heads' query (hi/lo bf16 pairs for v_dot2c_f32_bf16) and
+// accumulators. Lane (r, c) covers row r of each 8-row group and dims
+// [8c, 8c+8) and [64+8c, 64+8c+8) (rotate-half partners). LDS rows are stored
+// with their 16-byte chunks XOR-swizzled by (row & 7) so the 8 rows a
+// wavefront reads at once fall in different banks.
+
+template <int NQ>  // 32-row units per page (page_rows / 32)
+__global__ void __launch_bounds__(256) decode_bf16_d128_g4_kernel(DecodeArgs a) {
+  constexpr int D = 128, G = 4, RB = D * 2, UR = 32;  // 2 pieces of 16 B per thread
+  __shared__ uint4 lk[2][UR * RB / 16], lv[2][UR * RB / 16];
+  __shared__ float sm_o[2][G][D], sm_m[2][G], sm_l[2][G];
+  const DevPool& P = a.P;
+  const int w = blockIdx.x, h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
+  const int hp = wave & 1, half = wave >> 1;  // head pair, row half
+  const int c8 = lane & 7, r8 = lane >> 3;
+
+  int lo = 0, hi = a.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.prefix[mid] <= w) lo = mid;
+    else hi = mid - 1;
+  }
+  const int i = lo, s = w - a.prefix[i], nsplit = a.prefix[i + 1] - a.prefix[i];
+  const int slot = a.slot[i];
+  const int32_t* meta = meta_of(P, slot, a.layer);
+  const int n_pers = sgpr(meta[0]), n_open = sgpr(meta[1]), qpos = sgpr(meta[2]);
+  const int pr = NQ * UR;
+  const int npp = (n_pers + pr - 1) / pr, nop = (n_open + pr - 1) / pr;
+  const int vp0 = s * a.split_pages, vp1 = min(npp + nop, vp0 + a.split_pages);
+  const int nunits = (vp1 - vp0) * NQ;
+  const int32_t* tab = ptab_of(P, slot, a.layer);
+  const int Hq = P.Hkv * G;
+
+  // this wavefront's two query heads: rotate, scale, split into hi/lo bf16 pairs
+  uint32_t qh[2][8], ql[2][8];
+  {
+    const float2* rope = P.rope + (size_t)qpos * (D / 2) + 8 * c8;
+    float cs_c[8], cs_s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float2 t = rope[e];
+      cs_c[e] = t.x;
+      cs_s[e] = t.y;
+    }
+    const float qs = 1.4426950408889634f / sqrtf((float)D);
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+      const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)i * Hq + h * G + 2 * hp + j2) * D;
+      float xa[8], xb[8], y[16];
+      unpack16(*(const uint4*)(qrow + 8 * c8), xa, bf16_t());
+      unpack16(*(const uint4*)(qrow + 64 + 8 * c8), xb, bf16_t());
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y[e] = qs * (xa[e] * cs_c[e] - xb[e] * cs_s[e]);
+        y[8 + e] = qs * (xb[e] * cs_c[e] + xa[e] * cs_s[e]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t h0 = bf16_bits(y[2 * j]), h1 = bf16_bits(y[2 * j + 1]);
+        qh[j2][j] = h0 | (h1 << 16);
+        ql[j2][j] = bf16_bits(y[2 * j] - __uint_as_float(h0 << 16)) |
+                    (bf16_bits(y[2 * j + 1] - __uint_as_float(h1 << 16)) << 16);
+      }
+    }
+  }
+
+  // unit u -> wavefront-uniform byte offset of its first row, rows present
+  auto locate = [&](int u, size_t* off, int* nval) __attribute__((always_inline)) {
+    const int vp = vp0 + (NQ == 1 ? u : u >> 1), qq = NQ == 1 ? 0 : (u & 1);
+    int page, rows;
+    if (vp < npp) {
+      page = sgpr(tab[vp]);
+      rows = (vp == npp - 1) ? n_pers - vp * pr : pr;
+    } else {
+      const int j = vp - npp;
+      page = sgpr(tab[P.max_pers + j]);
+      rows = (j == nop - 1) ? n_open - j * pr : pr;
+    }
+    *off = ((((size_t)page * P.Hkv + h) * pr) + (size_t)qq * UR) * RB;
+    *nval = rows - qq * UR;
+  };
+  const char* kbase = (const char*)P.kpool;
+  const char* vbase = (const char*)P.vpool;
+  // piece ch of this thread: row (t + 256 ch) / 16, chunk (t + 256 ch) % 16
+  const int prow0 = threadIdx.x >> 4, pchunk = threadIdx.x & 15;
+  const int lds0 = prow0 * 16 + (pchunk ^ (prow0 & 7));  // swizzled LDS slot (rows +16 for ch 1)
+  uint4 ak0, av0, ak1, av1, bk0, bv0, bk1, bv1;
+  auto gload = [&](int u, uint4* k0, uint4* v0, uint4* k1, uint4* v1) __attribute__((always_inline)) {
+    size_t off;
+    int nval;
+    locate(u, &off, &nval);
+    int r0 = prow0, r1 = prow0 + 16;
+    if (nval < UR) {
+      const int last = nval > 0 ? nval - 1 : 0;
+      r0 = r0 < nval ? r0 : last;
+      r1 = r1 < nval ? r1 : last;
+    }
+    const char* kb = kbase + off + pchunk * 16;
+    const char* vb = vbase + off + pchunk * 16;
+    *k0 = *(const uint4*)(kb + r0 * RB);
+    *v0 = *(const uint4*)(vb + r0 * RB);
+    *k1 = *(const uint4*)(kb + r1 * RB);
+    *v1 = *(const uint4*)(vb + r1 * RB);
+  };
+  auto swrite = [&](int b, const uint4& k0, const uint4& v0, const uint4& k1, const uint4& v1)
+      __attribute__((always_inline)) {
+    lk[b][lds0] = k0;
+    lv[b][lds0] = v0;
+    lk[b][lds0 + 256] = k1;
+    lv[b][lds0 + 256] = v1;
+  };
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f}, o[2][16];
+#pragma unroll
+  for (int j2 = 0; j2 < 2; ++j2)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[j2][e] = 0.f;
+
+  auto compute = [&](int b, int nval) __attribute__((always_inline)) {
+    float sc[2][2];  // [row group][head]
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      const int row = half * 16 + rg * 8 + r8;
+      const int sw = r8;  // row & 7
+      const uint4 ka = lk[b][row * 16 + (c8 ^ sw)];
+      const uint4 kb = lk[b][row * 16 + 8 + (c8 ^ sw)];
+      const uint32_t k[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+      const bool valid = row < nval;
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          acc0 = dot2_bf16(k[j], qh[j2][j], acc0);
+          acc1 = dot2_bf16(k[j], ql[j2][j], acc1);
+        }
+        const float acc = group_sum<8>(acc0 + acc1);
+        sc[rg][j2] = valid ? acc : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+      const float mx = slots8_max(fmaxf(sc[0][j2], sc[1][j2]));
+      if (mx > m_run[j2]) {  // wavefront-uniform; -inf when this half has no rows
+        const float alpha = fast_exp2(m_run[j2] - mx);
+        m_run[j2] = mx;
+        l_run[j2] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[j2][e] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      const int row = half * 16 + rg * 8 + r8;
+      float vf[16];
+      unpack16(lv[b][row * 16 + (c8 ^ r8)], vf, bf16_t());
+      unpack16(lv[b][row * 16 + 8 + (c8 ^ r8)], vf + 8, bf16_t());
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        const float p = m_run[j2] == -INFINITY ? 0.f : fast_exp2(sc[rg][j2] - m_run[j2]);
+        l_run[j2] += p;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[j2][e] += p * vf[e];
+      }
+    }
+  };
+
+  // Prologue: unit 0 in LDS buffer 0, units 1 (stage a) and 2 (stage b) in
+  // flight. Every step issues the same loads and stores whatever the unit count
+  // (indices past the end re-read the last unit, which is still in L2), so the
+  // waits before each store can count exactly the newer stage's loads.
+  const int ulast = nunits - 1;
+  gload(0, &ak0, &av0, &ak1, &av1);
+  swrite(0, ak0, av0, ak1, av1);
+  gload(min(1, ulast), &ak0, &av0, &ak1, &av1);
+  gload(min(2, ulast), &bk0, &bv0, &bk1, &bv1);
+  __syncthreads();
+  auto step = [&](int u, uint4& k0, uint4& v0, uint4& k1, uint4& v1) __attribute__((always_inline)) {
+    const int b = u & 1;
+    swrite(b ^ 1, k0, v0, k1, v1);  // its buffer was last read before the previous barrier
+    gload(min(u + 3, ulast), &k0, &v0, &k1, &v1);
+    if (u < nunits) {
+      size_t off;
+      int nval;
+      locate(u, &off, &nval);
+      if (nval > half * 16) compute(b, nval);
+    }
+    __syncthreads();
+  };
+  for (int u = 0; u < nunits; u += 2) {
+    step(u, ak0, av0, ak1, av1);
+    step(u + 1, bk0, bv0, bk1, bv1);
+  }
+
+  // reduce over the 8 row slots, then merge the two row halves of each head
+#pragma unroll
+  for (int j2 = 0; j2 < 2; ++j2) {
+    const float lw = slots8_sum(l_run[j2]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float oe = slots8_sum(o[j2][e]);
+      if (r8 == 0) sm_o[half][2 * hp + j2][(e < 8 ? 0 : 64) + 8 * c8 + (e & 7)] = oe;
+    }
+    if (lane == 0) {
+      sm_m[half][2 * hp + j2] = m_run[j2];
+      sm_l[half][2 * hp + j2] = lw;
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < G * D; t += 256) {
+    const int g = t / D, d = t % D;
+    const float m0 = sm_m[0][g], m1 = sm_m[1][g];
+    const float M = fmaxf(m0, m1);
+    const float f0 = m0 == -INFINITY ? 0.f : fast_exp2(m0 - M);
+    const float f1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+    const float Ls = sm_l[0][g] * f0 + sm_l[1][g] * f1;
+    const float O = sm_o[0][g][d] * f0 + sm_o[1][g][d] * f1;
+    const int hq = h * G + g;
+    if (nsplit == 1) {
+      ((bf16_t*)a.out)[((size_t)i * Hq + hq) * D + d] = from_f32<bf16_t>(O / Ls);
+      if (d == 0) a.lse[(size_t)i * Hq + hq] = (M + __log2f(Ls)) * 0.6931471805599453f;
+    } else {
+      float* pp = a.part + (((size_t)w * P.Hkv + h) * G + g) * (D + 2);
+      pp[d] = O;
+      if (d == 0) {
+        pp[D] = M;
+        pp[D + 1] = Ls;
+      }
+    }
+  }
+}
+
+// ---- a2 + a3, persistent stream-K form of the kernel above ------------------------
+//
+// One resident wave of workgroups; workgroup w walks flattened units
+// [w*T, (w+1)*T), which cover one or a few (sequence, KV head) segments. Per
+// segment it runs the same LDS-staged pipeline and math as
+// decode_bf16_d128_g4_kernel, then writes the final output (segment inside
+// this workgroup) or a partial for decode_stream_merge_kernel. Every workgroup
+// does the same amount of streaming, and the per-workgroup set-up (sequence
+// lookup, metadata, query rotation, first loads) is paid per segment, not per
+// fixed-size split.
+
+template <int NQ>
+__global__ void __launch_bounds__(256) decode_stream_kernel(StreamArgs a) {
+  constexpr int D = 128, G = 4, RB = D * 2, UR = 32;
+  __shared__ uint4 lk[2][UR * RB / 16], lv[2][UR * RB / 16];
+  __shared__ float sm_o[2][G][D], sm_m[2][G], sm_l[2][G];
+  const DevPool& P = a.P;
+  const int w = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
+  const int hp = wave & 1, half = wave >> 1;
+  const int c8 = lane & 7, r8 = lane >> 3;
+  const int pr = NQ * UR;
+  const int Hq = P.Hkv * G;
+  const char* kbase = (const char*)P.kpool;
+  const char* vbase = (const char*)P.vpool;
+  const int prow0 = threadIdx.x >> 4, pchunk = threadIdx.x & 15;
+  const int lds0 = prow0 * 16 + (pchunk ^ (prow0 & 7));
+
+  int F = w * a.T;
+  const int Fend = min(a.U, F + a.T);
+  int i = 0;
+  while (F < Fend) {
+    while (a.useg[i + 1] <= F) ++i;  // sequence of flattened unit F (scalar)
+    const int units = (a.useg[i + 1] - a.useg[i]) / P.Hkv;
+    const int rel = F - a.useg[i];
+    const int h = rel / units, lu0 = rel % units;
+    const int segS = a.useg[i] + h * units;
+    const int F1 = min(Fend, segS + units);
+    const int nunits = F1 - F;
+    const int slot = a.slot[i];
+    const int32_t* meta = meta_of(P, slot, a.layer);
+    const int n_pers = sgpr(meta[0]), n_open = sgpr(meta[1]), qpos = sgpr(meta[2]);
+    const int npp = (n_pers + pr - 1) / pr, nop = (n_open + pr - 1) / pr;
+    const int32_t* tab = ptab_of(P, slot, a.layer);
+
+    uint32_t qh[2][8], ql[2][8];
+    {
+      const float2* rope = P.rope + (size_t)qpos * (D / 2) + 8 * c8;
+      float cs_c[8], cs_s[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 t = rope[e];
+        cs_c[e] = t.x;
+        cs_s[e] = t.y;
+      }
+      const float qs = 1.4426950408889634f / sqrtf((float)D);
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)i * Hq + h * G + 2 * hp + j2) * D;
+        float xa[8], xb[8], y[16];
+        unpack16(*(const uint4*)(qrow + 8 * c8), xa, bf16_t());
+        unpack16(*(const uint4*)(qrow + 64 + 8 * c8), xb, bf16_t());
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y[e] = qs * (xa[e] * cs_c[e] - xb[e] * cs_s[e]);
+          y[8 + e] = qs * (xb[e] * cs_c[e] + xa[e] * cs_s[e]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t h0 = bf16_bits(y[2 * j]), h1 = bf16_bits(y[2 * j + 1]);
+          qh[j2][j] = h0 | (h1 << 16);
+          ql[j2][j] = bf16_bits(y[2 * j] - __uint_as_float(h0 << 16)) |
+                      (bf16_bits(y[2 * j + 1] - __uint_as_float(h1 << 16)) << 16);
+        }
+      }
+    }
+
+    // segment-local unit u -> byte offset of its first row, rows present
+    auto locate = [&](int u, size_t* off, int* nval) __attribute__((always_inline)) {
+      const int lu = lu0 + u;
+      const int vp = NQ == 1 ? lu : lu >> 1, qq = NQ == 1 ? 0 : (lu & 1);
+      int page, rows;
+      if (vp < npp) {
+        page = sgpr(tab[vp]);
+        rows = (vp == npp - 1) ? n_pers - vp * pr : pr;
+      } else {
+        const int j = vp - npp;
+        page = sgpr(tab[P.max_pers + j]);
+        rows = (j == nop - 1) ? n_open - j * pr : pr;
+      }
+      *off = ((((size_t)page * P.Hkv + h) * pr) + (size_t)qq * UR) * RB;
+      *nval = rows - qq * UR;
+    };
+    uint4 ak0, av0, ak1, av1, bk0, bv0, bk1, bv1;
+    auto gload = [&](int u, uint4* k0, uint4* v0, uint4* k1, uint4* v1) __attribute__((always_inline)) {
+      size_t off;
+      int nval;
+      locate(u, &off, &nval);
+      int r0 = prow0, r1 = prow0 + 16;
+      if (nval < UR) {
+        const int last = nval > 0 ? nval - 1 : 0;
+        r0 = r0 < nval ? r0 : last;
+        r1 = r1 < nval ? r1 : last;
+      }
+      const char* kb = kbase + off + pchunk * 16;
+      const char* vb = vbase + off + pchunk * 16;
+      *k0 = *(const uint4*)(kb + r0 * RB);
+      *v0 = *(const uint4*)(vb + r0 * RB);
+      *k1 = *(const uint4*)(kb + r1 * RB);
+      *v1 = *(const uint4*)(vb + r1 * RB);
+    };
+    auto swrite = [&](int b, const uint4& k0, const uint4& v0, const uint4& k1, const uint4& v1)
+        __attribute__((always_inline)) {
+      lk[b][lds0] = k0;
+      lv[b][lds0] = v0;
+      lk[b][lds0 + 256] = k1;
+      lv[b][lds0 + 256] = v1;
+    };
+
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f}, o[2][16];
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[j2][e] = 0.f;
+
+    auto compute = [&](int b, int nval) __attribute__((always_inline)) {
+      float sc[2][2];
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        const int row = half * 16 + rg * 8 + r8;
+        const uint4 ka = lk[b][row * 16 + (c8 ^ r8)];
+        const uint4 kb = lk[b][row * 16 + 8 + (c8 ^ r8)];
+        const uint32_t k[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+        const bool valid = row < nval;
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+          float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            acc0 = dot2_bf16(k[j], qh[j2][j], acc0);
+            acc1 = dot2_bf16(k[j], ql[j2][j], acc1);
+          }
+          const float acc = group_sum<8>(acc0 + acc1);
+          sc[rg][j2] = valid ? acc : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        const float mx = slots8_max(fmaxf(sc[0][j2], sc[1][j2]));
+        if (mx > m_run[j2]) {
+          const float alpha = fast_exp2(m_run[j2] - mx);
+          m_run[j2] = mx;
+          l_run[j2] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[j2][e] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        const int row = half * 16 + rg * 8 + r8;
+        float vf[16];
+        unpack16(lv[b][row * 16 + (c8 ^ r8)], vf, bf16_t());
+        unpack16(lv[b][row * 16 + 8 + (c8 ^ r8)], vf + 8, bf16_t());
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+          const float p = m_run[j2] == -INFINITY ? 0.f : fast_exp2(sc[rg][j2] - m_run[j2]);
+          l_run[j2] += p;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[j2][e] += p * vf[e];
+        }
+      }
+    };
+
+    const int ulast = nunits - 1;
+    gload(0, &ak0, &av0, &ak1, &av1);
+    swrite(0, ak0, av0, ak1, av1);
+    gload(min(1, ulast), &ak0, &av0, &ak1, &av1);
+    gload(min(2, ulast), &bk0, &bv0, &bk1, &bv1);
+    __syncthreads();
+    auto step = [&](int u, uint4& k0, uint4& v0, uint4& k1, uint4& v1) __attribute__((always_inline)) {
+      const int b = u & 1;
+      swrite(b ^ 1, k0, v0, k1, v1);
+      gload(min(u + 3, ulast), &k0, &v0, &k1, &v1);
+      if (u < nunits) {
+        size_t off;
+        int nval;
+        locate(u, &off, &nval);
+        if (nval > half * 16) compute(b, nval);
+      }
+      __syncthreads();
+    };
+    for (int u = 0; u < nunits; u += 2) {
+      step(u, ak0, av0, ak1, av1);
+      step(u + 1, bk0, bv0, bk1, bv1);
+    }
+
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+      const float lw = slots8_sum(l_run[j2]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float oe = slots8_sum(o[j2][e]);
+        if (r8 == 0) sm_o[half][2 * hp + j2][(e < 8 ? 0 : 64) + 8 * c8 + (e & 7)] = oe;
+      }
+      if (lane == 0) {
+        sm_m[half][2 * hp + j2] = m_run[j2];
+        sm_l[half][2 * hp + j2] = lw;
+      }
+    }
+    __syncthreads();
+    const int wa = segS / a.T, wb = (segS + units - 1) / a.T;
+    for (int t = threadIdx.x; t < G * D; t += 256) {
+      const int g = t / D, d = t % D;
+      const float m0 = sm_m[0][g], m1 = sm_m[1][g];
+      const float M = fmaxf(m0, m1);
+      const float f0 = m0 == -INFINITY ? 0.f : fast_exp2(m0 - M);
+      const float f1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+      const float Ls = sm_l[0][g] * f0 + sm_l[1][g] * f1;
+      const float O = sm_o[0][g][d] * f0 + sm_o[1][g][d] * f1;
+      const int hq = h * G + g;
+      if (wa == wb) {
+        ((bf16_t*)a.out)[((size_t)i * Hq + hq) * D + d] = from_f32<bf16_t>(O / Ls);
+        if (d == 0) a.lse[(size_t)i * Hq + hq] = (M + __log2f(Ls)) * 0.6931471805599453f;
+      } else {
+        float* pp = a.part + ((((size_t)i * P.Hkv + h) * a.maxp + (w - wa)) * G + g) * (D + 2);
+        pp[d] = O;
+        if (d == 0) {
+          pp[D] = M;
+          pp[D + 1] = Ls;
+        }
+      }
+    }
+    __syncthreads();  // LDS (buffers and merge area) is reused by the next segment
+    F = F1;
+  }
+}
+
+// Merge the partials of (sequence i, KV head h) written by workgroups wa..wb.
+__global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) {
+  constexpr int D = 128, G = 4;
+  __shared__ float sm_w[kMaxSplits * G], sm_M[G], sm_L[G];
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int Hkv = a.P.Hkv, Hq = Hkv * G;
+  const int units = (a.useg[i + 1] - a.useg[i]) / Hkv;
+  const int segS = a.useg[i] + h * units;
+  const int wa = segS / a.T, wb = (segS + units - 1) / a.T;
+  const int ns = wb - wa + 1;
+  if (ns == 1) return;
+  auto part = [&](int s, int g) {
+    return a.part + ((((size_t)i * Hkv + h) * a.maxp + s) * G + g) * (D + 2);
+  };
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, part(s2, g)[D]);
+    float Ls = 0.f;
+    for (int s2 = 0; s2 < ns; ++s2) {
+      const float f = fast_exp2(part(s2, g)[D] - M);
+      sm_w[s2 * G + g] = f;
+      Ls += part(s2, g)[D + 1] * f;
+    }
+    sm_M[g] = M;
+    sm_L[g] = Ls;
+    a.lse[(size_t)i * Hq + h * G + g] = (M + __log2f(Ls)) * 0.6931471805599453f;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
+    const int g = t / D, d = t % D;
+    float O = 0.f;
+    for (int s2 = 0; s2 < ns; ++s2) O += part(s2, g)[d] * sm_w[s2 * G + g];
+    ((bf16_t*)a.out)[((size_t)i * Hq + h * G + g) * D + d] = from_f32<bf16_t>(O / sm_L[g]);
   }
 }
 
@@ -719,12 +1595,12 @@ template <typename T, int D>
 static hipError_t decode_g(const DecodeArgs& a, int32_t total, hipStream_t s) {
   const dim3 grid(total, a.P.Hkv);
   switch (a.G) {
-#define ABK_G(GG)                                                                          \
-  case GG:                                                                                 \
-    hipLaunchKernelGGL((decode_split_kernel<T, D, GG>), grid, dim3(256), 0, s, a);         \
-    if (total > a.n)                                                                       \
-      hipLaunchKernelGGL((decode_combine_kernel<T, D, GG>), dim3(a.n, a.P.Hkv),            \
-                         dim3(GG * D < 1024 ? GG * D : 1024), 0, s, a);                    \
+#define ABK_G(GG)                                                                  \
+  case GG:                                                                         \
+    hipLaunchKernelGGL((decode_split_kernel<T, D, GG>), grid, dim3(256), 0, s, a); \
+    if (total > a.n)                                                               \
+      hipLaunchKernelGGL((decode_merge_kernel<T, D, GG>), dim3(a.n, a.P.Hkv),      \
+                         dim3(GG * D < 1024 ? GG * D : 1024), 0, s, a);            \
     break;
     ABK_G(1) ABK_G(2) ABK_G(4) ABK_G(8)
 #undef ABK_G
@@ -734,8 +1610,39 @@ static hipError_t decode_g(const DecodeArgs& a, int32_t total, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int GG>
+static void decode_bf16_d128(const DecodeArgs& a, int32_t total, hipStream_t s) {
+  hipLaunchKernelGGL((decode_bf16_d128_kernel<GG>), dim3(total, a.P.Hkv), dim3(256), 0, s, a);
+  if (total > a.n)
+    hipLaunchKernelGGL((decode_merge_kernel<bf16_t, 128, GG>), dim3(a.n, a.P.Hkv),
+                       dim3(GG * 128 < 1024 ? GG * 128 : 1024), 0, s, a);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int32_t total_work, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
+#ifndef ABK_DECODE_GENERIC_ONLY
+  if (a.P.dtype == 1 && a.P.D == 128 && a.G == 4 && (a.P.pr == 32 || a.P.pr == 64)) {
+    const dim3 grid(total_work, a.P.Hkv);
+    if (a.P.pr == 64)
+      hipLaunchKernelGGL((decode_bf16_d128_g4_kernel<2>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_bf16_d128_g4_kernel<1>), grid, dim3(256), 0, s, a);
+    if (total_work > a.n)
+      hipLaunchKernelGGL((decode_merge_kernel<bf16_t, 128, 4>), dim3(a.n, a.P.Hkv), dim3(512), 0,
+                         s, a);
+    return hipGetLastError();
+  }
+  if (a.P.dtype == 1 && a.P.D == 128) {
+    switch (a.G) {
+      case 1: decode_bf16_d128<1>(a, total_work, s); break;
+      case 2: decode_bf16_d128<2>(a, total_work, s); break;
+      case 4: decode_bf16_d128<4>(a, total_work, s); break;
+      case 8: decode_bf16_d128<8>(a, total_work, s); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+#endif
   ABK_DISPATCH_TD(a.P.dtype, a.P.D, return decode_g<T, DD>(a, total_work, s));
   return hipSuccess;
 }
@@ -776,6 +1683,29 @@ hipError_t launch_read(const ReadArgs& a, hipStream_t s) {
   if (a.nrows == 0) return hipSuccess;
   ABK_DISPATCH_TD(a.P.dtype, a.P.D,
                   hipLaunchKernelGGL((read_rows_kernel<T, DD>), dim3(a.nrows), dim3(256), 0, s, a));
+  return hipGetLastError();
+}
+
+bool decode_stream_supported(const DevPool& P, int32_t G) {
+  return P.dtype == 1 && P.D == 128 && G == 4 && (P.pr == 32 || P.pr == 64);
+}
+
+int32_t decode_stream_blocks_per_cu(const DevPool& P) {
+  int nb = 0;
+  hipError_t e = P.pr == 64
+                     ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_stream_kernel<2>, 256, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_stream_kernel<1>, 256, 0);
+  return (e == hipSuccess && nb > 0) ? nb : 1;
+}
+
+hipError_t launch_decode_stream(const StreamArgs& a, int32_t nwg, hipStream_t s) {
+  if (a.n == 0 || nwg == 0) return hipSuccess;
+  if (a.P.pr == 64)
+    hipLaunchKernelGGL((decode_stream_kernel<2>), dim3(nwg), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<1>), dim3(nwg), dim3(256), 0, s, a);
+  if (a.maxp > 1)
+    hipLaunchKernelGGL(decode_stream_merge_kernel, dim3(a.n, a.P.Hkv), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -112,8 +112,10 @@ def _bf16_run(**kw):
     return Run(**base)
 
 
-def test_bf16_ragged_history_decode_and_layout():
-    run = _bf16_run()
+@pytest.mark.parametrize("pr,split", [(16, 32), (32, 64), (64, 128), (32, 0), (64, 0)])
+def test_bf16_ragged_history_decode_and_layout(pr, split):
+    # split 0: the automatic (persistent) schedule; > 0: fixed split-KV items
+    run = _bf16_run(pr=pr, split_rows=split)
     npages = run.pool.stats()["pages_free"]
     Ps = [0, 3, 17, 40, 64]
     Gs = [1, 63, 64, 65, 200]
@@ -214,9 +216,10 @@ def test_peaky_softmax_and_full_kv_mode():
     _check_decode(full, fs, 1)
 
 
-def test_planted_rows_are_found_at_every_position():
+@pytest.mark.parametrize("pr,split", [(16, 32), (32, 64), (64, 128), (32, 0), (64, 0)])
+def test_planted_rows_are_found_at_every_position(pr, split):
     # q = RoPE^-1(alpha * k'_r) puts nearly all weight on row r: out ~ v_r
-    run = _bf16_run(seed=6, pr=16)
+    run = _bf16_run(seed=6, pr=pr, split_rows=split)
     s = run.new_seq(37, 0)
     run.fill(s, 64 * 3 + 20)
     layer = 0
@@ -227,7 +230,8 @@ def test_planted_rows_are_found_at_every_position():
     torch.cuda.synchronize()
     kh, vh = host(k), host(v)
     qpos = run.P[s] + run.G[s] - 1
-    rows = sorted({0, 15, 16, 36, 37, 52, 53, 84, n - 20, n - 19, n - 2, n - 1})
+    rows = sorted({0, 15, 16, 17, 31, 32, 33, 36, 37, 47, 48, 52, 53, 63, 64, 65, 84, 100,
+                   n - 20, n - 19, n - 2, n - 1})
     for r in rows:
         target = 8.0 * kh[r]                                   # [Hkv, d]
         qk = np.repeat(target, run.Hq // run.Hkv, axis=0)      # [Hq, d]
