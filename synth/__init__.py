@@ -4,8 +4,9 @@ This module holds no attention arithmetic: it only turns a seed and a token's
 identity into normally distributed numbers, so that both sides can be fed the
 same values without either one importing the other.
 
-Definition (implemented twice from the same published sources: here in numpy
-for the host, and in ``synth_rng.h`` for device-side bulk fills):
+Definition (implemented three times from the same published sources: here in
+numpy, in ``synth_host.c`` for fast host-side generation, and in
+``synth_rng.h`` for device-side bulk fills):
 
 * splitmix64 (S. Vigna, "splitmix64.c", public domain): the n-th output
   (n >= 1) of a stream whose state starts at ``s`` is ``mix(s + n*GAMMA)``,
@@ -28,6 +29,10 @@ Token identity (``kind``, ``a``, ``b``): PROMPT (0, i, 0), TEXT (1, j, 0) with
 identity with ``which = 2``.
 """
 from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
 
 import numpy as np
 
@@ -107,10 +112,54 @@ def to_storage(x64: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_CLIB_PATH = os.path.join(_HERE, "libsynth.so")
+_clib = None
+
+
+def build_c(verbose: bool = False) -> str:
+    """Compile the C implementation (gcc, OpenMP)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", _CLIB_PATH + ".tmp",
+           os.path.join(_HERE, "synth_host.c"), "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    os.replace(_CLIB_PATH + ".tmp", _CLIB_PATH)
+    return _CLIB_PATH
+
+
+def _c():
+    global _clib
+    if _clib is None:
+        if not os.path.exists(_CLIB_PATH):
+            build_c()
+        L = ctypes.CDLL(_CLIB_PATH)
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        L.synth_rows_c.argtypes = [ctypes.c_uint64, i64, i64, vp, vp, i64, i64, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_double, vp]
+        L.synth_rows_c.restype = None
+        _clib = L
+    return _clib
+
+
 def rows(seed, layer, kind, a, b, which, heads: int, d: int, dtype: str, scale: float = 1.0):
     """Values of token rows: shape [len(a), heads, d] (doubles exactly
     representable in ``dtype``). ``a`` and ``b`` broadcast against each other;
-    ``scale`` multiplies the normals before storage rounding."""
+    ``scale`` multiplies the normals before storage rounding. Computed by the C
+    implementation (``synth_host.c``); :func:`rows_numpy` is the same generator
+    in numpy."""
+    a = np.ascontiguousarray(np.atleast_1d(np.asarray(a, dtype=np.int64)))
+    b = np.ascontiguousarray(np.broadcast_to(np.asarray(b, dtype=np.int64), a.shape))
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(dtype)
+    out = np.empty((len(a), heads, d), dtype=np.float64)
+    _c().synth_rows_c(seed & 0xFFFFFFFFFFFFFFFF, layer, kind, a.ctypes.data, b.ctypes.data, len(a),
+                      which, heads, d, int(dtype == "bf16"), scale, out.ctypes.data)
+    return out
+
+
+def rows_numpy(seed, layer, kind, a, b, which, heads: int, d: int, dtype: str, scale: float = 1.0):
+    """numpy implementation of :func:`rows`."""
     a = np.atleast_1d(np.asarray(a, dtype=np.int64))
     b = np.broadcast_to(np.asarray(b, dtype=np.int64), a.shape)
     h = np.arange(heads, dtype=np.int64)

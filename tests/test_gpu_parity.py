@@ -134,14 +134,21 @@ def test_bf16_ragged_history_decode_and_layout(pr, split):
     assert run.pool.stats()["pages_free"] < npages
 
 
-def test_bf16_compress_then_decode_uses_code_rows():
-    run = _bf16_run(seed=2)
+# (page rows, C, K, quotas): 16-row pages take the SIMT kernel; 64-row pages the
+# MFMA kernel with 1, 2 and 4 query tiles and partial causal pause tiles
+COMPRESS_CASES = [(16, 64, 16, [16, 4]), (64, 128, 32, [32, 8]), (64, 128, 64, [64, 16]),
+                  (64, 256, 128, [128, 32])]
+
+
+@pytest.mark.parametrize("pr,C,Kp,quota", COMPRESS_CASES)
+def test_bf16_compress_then_decode_uses_code_rows(pr, C, Kp, quota):
+    run = _bf16_run(seed=2, pr=pr, C=C, Kp=Kp, quota=quota, split_rows=0)
     Ps = [5, 64, 30]
     sids = [run.new_seq(P, i) for i, P in enumerate(Ps)]
     for s in sids:
         run.write_prompts(s)
     # second block complete: one block already compressed, this one open and full
-    run.grow({s: 128 for s in sids})
+    run.grow({s: 2 * C for s in sids})
     outs = [run.compress_layer(sids, l) for l in range(run.L)]
     torch.cuda.synchronize()
     for l, (out, lse) in enumerate(outs):
@@ -152,7 +159,7 @@ def test_bf16_compress_then_decode_uses_code_rows():
             _close(f"compress lse seq{s} L{l}", lse[i], l_ref, 1e-3)
             # the kept rows: values bit-exact, rotated keys within one bf16 ulp
             q = run.quota[l]
-            r0 = run.pool.seq_query(s, l)["resident_rows"] - 64 - q
+            r0 = run.pool.seq_query(s, l)["resident_rows"] - C - q
             k = torch.empty((q, run.Hkv, run.D), device="cuda", dtype=torch.bfloat16)
             v = torch.empty_like(k)
             run.pool.read_rows(s, l, r0, q, k, v)
@@ -162,7 +169,7 @@ def test_bf16_compress_then_decode_uses_code_rows():
     run.pool.free_block(sids)
     for s in sids:
         run.nb[s] += 1
-    run.grow({s: 129 for s in sids})
+    run.grow({s: 2 * C + 1 for s in sids})
     _check_decode(run, sids, 0)
     _check_decode(run, sids, 1)
 
