@@ -61,9 +61,17 @@ def resident_rows(P, G, q, compress=True):
     return P + nb * q + (G - nb * C)
 
 
-def kernel_source_hash():
+KERNEL_SOURCES = {
+    "decode_stream": ("decode.hip", "common.h", "kernels.h"),
+    "compress_attn_mfma": ("compress.hip", "common.h", "kernels.h"),
+}
+
+
+def kernel_source_hash(kernel: str):
+    """Hash of the sources a kernel family is built from: counters taken on
+    other sources no longer describe it."""
     h = hashlib.sha256()
-    for f in ("kernels.hip", "kernels.h"):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "long_reasoning_kv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -77,7 +85,7 @@ def traffic_from_profiles(kernel: str, launches_bytes: float):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return t.get("bytes_per_launch")
 
@@ -183,8 +191,8 @@ def run_decode(args, torch, abk):
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": traffic_from_profiles("decode_split", float(np.mean(dec_bytes))),
-            "kernel": "decode_split_kernel<bf16,128,4> (+ split combine)",
+            "traffic": traffic_from_profiles("decode_stream", float(np.mean(dec_bytes))),
+            "kernel": "decode_stream_kernel (+ split merge)",
             "algorithmic_bytes_per_launch": float(np.mean(dec_bytes)),
             "avg_launch_us": float(np.mean(dec_ms)) * 1e3,
         },

@@ -1,184 +1,15 @@
-// HIP kernels of the AbridgeKV attention hot path, written for CDNA4 (gfx950):
-// 64-lane wavefronts, DPP row reductions, 16-byte coalesced page loads.
-//
-// What is computed follows the pages on AbridgeKV (arXiv 2610.20641): the
-// abstract and Fig. 1(a) (code rows written by pause tokens, raw block rows
-// freed), Fig. 2(a) (the block mask) and Fig. 2(b) (pause token k of block b
-// at position P + b*C + bitrev(k)*C/K). RoPE is rotate-half; stored keys are
-// rotated once, in fp32, and rounded to the pool dtype.
+// Decode attention of the AbridgeKV hot path (steps a2 and a3): the current
+// token of each sequence attends to its resident rows (prompt, code rows of
+// finished blocks, the open block) through the per-(sequence, layer) page
+// table. See the pages on AbridgeKV (arXiv 2610.20641): the abstract and
+// Fig. 1 captions (what stays resident), Fig. 2(a) (text tokens see the
+// prompt, earlier code rows and their own block).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../synth/synth_rng.h"
-#include "kernels.h"
+#include "common.h"
 
 namespace abk {
-
-// ---- element types ------------------------------------------------------------
-
-struct bf16_t {
-  uint16_t u;
-};
-
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.u << 16); }
-
-template <typename T>
-__device__ __forceinline__ T from_f32(float x);
-template <>
-__device__ __forceinline__ float from_f32<float>(float x) {
-  return x;
-}
-template <>
-__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t{(uint16_t)((u >> 16) | 0x40)};  // NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return bf16_t{(uint16_t)(u >> 16)};
-}
-
-// 16 bytes of a row -> floats (8 for bf16, 4 for fp32).
-__device__ __forceinline__ void unpack16(const uint4& w, float* f, bf16_t) {
-  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(x[i] << 16);
-    f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ void unpack16(const uint4& w, float* f, float) {
-  f[0] = __uint_as_float(w.x);
-  f[1] = __uint_as_float(w.y);
-  f[2] = __uint_as_float(w.z);
-  f[3] = __uint_as_float(w.w);
-}
-
-// ---- wavefront reductions -------------------------------------------------------
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// Sum over aligned groups of N lanes (N = 1..64, a power of two); every lane of
-// a group ends with the group's sum. Within 16 lanes the DPP row operations do
-// it: swap neighbours, swap pairs, mirror 8, mirror 16.
-template <int N>
-__device__ __forceinline__ float group_sum(float x) {
-  if constexpr (N >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-  if constexpr (N >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-  if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror
-  if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32);
-  return x;
-}
-
-// Reduce across the lane bits above log2(STRIDE) (sum or max).
-template <int STRIDE>
-__device__ __forceinline__ float across_sum(float x) {
-#pragma unroll
-  for (int o = STRIDE; o < 64; o <<= 1) x += __shfl_xor(x, o);
-  return x;
-}
-template <int STRIDE>
-__device__ __forceinline__ float across_max(float x) {
-#pragma unroll
-  for (int o = STRIDE; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Reductions over lane bits 3..5 (the 8 row slots of an 8-lanes-per-row
-// layout) without the LDS crossbar: DPP row_ror:8 pairs lanes i and i^8 inside
-// a 16-lane row, v_permlane16_swap exchanges neighbouring rows and
-// v_permlane32_swap the two halves of the wavefront.
-__device__ __forceinline__ float slots8_max(float x) {
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false)));
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float slots8_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// Rows are read 16 bytes per lane: EPL elements per lane, LPR lanes per row,
-// RPL rows per wavefront load, at most MAXCH loads per 64-row page.
-template <typename T, int D>
-struct RowCfg {
-  static constexpr int EPL = 16 / (int)sizeof(T);
-  static constexpr int LPR = D / EPL;
-  static constexpr int RPL = 64 / LPR;
-  static constexpr int MAXCH = (64 + RPL - 1) / RPL;
-  static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "row shape");
-};
-
-__device__ __forceinline__ const int32_t* meta_of(const DevPool& P, int slot, int layer) {
-  return P.meta + (slot * P.L + layer) * 4;
-}
-__device__ __forceinline__ int32_t* ptab_of(const DevPool& P, int slot, int layer) {
-  return P.ptab + (size_t)(slot * P.L + layer) * P.tstride;
-}
-
-// Rotate-half RoPE of element d of a row x (D elements, any layout via lambda).
-template <int D, typename F>
-__device__ __forceinline__ float rope_elem(F x, int d, const float2* rope_row) {
-  constexpr int H = D / 2;
-  if (d < H) {
-    float2 cs = rope_row[d];
-    return x(d) * cs.x - x(d + H) * cs.y;
-  }
-  float2 cs = rope_row[d - H];
-  return x(d) * cs.x + x(d - H) * cs.y;
-}
-
-// ---- a1: append the current token (RoPE k at its position, write k and v) ----
-
-template <typename T, int D>
-__global__ void __launch_bounds__(1024) append_kernel(AppendArgs a) {
-  const DevPool P = a.P;
-  const int i = blockIdx.x;
-  const int slot = a.slot[i];
-  const int fresh_page = a.new_page[i];
-  int32_t* meta = P.meta + (slot * P.L + a.layer) * 4;
-  const int n_pers = meta[0], n_open = meta[1], qpos = meta[2];
-  const int r = a.compress ? n_open : n_pers;
-  int32_t* tab = ptab_of(P, slot, a.layer) + (a.compress ? P.max_pers : 0);
-  const int pidx = r / P.pr, srow = r % P.pr;
-  const int page = srow == 0 ? fresh_page : tab[pidx];
-  const int pos = qpos + 1;
-  const T* k = (const T*)a.k + (size_t)i * P.Hkv * D;
-  const T* v = (const T*)a.v + (size_t)i * P.Hkv * D;
-  T* kd = (T*)P.kpool + ((size_t)page * P.Hkv * P.pr + srow) * D;
-  T* vd = (T*)P.vpool + ((size_t)page * P.Hkv * P.pr + srow) * D;
-  const float2* rope = P.rope + (size_t)pos * (D / 2);
-  for (int t = threadIdx.x; t < P.Hkv * (D / 2); t += blockDim.x) {
-    const int hh = t / (D / 2), j = t % (D / 2);
-    const T* kr = k + hh * D;
-    const float x1 = to_f32(kr[j]), x2 = to_f32(kr[j + D / 2]);
-    const float2 cs = rope[j];
-    T* kdst = kd + (size_t)hh * P.pr * D;
-    kdst[j] = from_f32<T>(x1 * cs.x - x2 * cs.y);
-    kdst[j + D / 2] = from_f32<T>(x2 * cs.x + x1 * cs.y);
-    T* vdst = vd + (size_t)hh * P.pr * D;
-    vdst[j] = v[hh * D + j];
-    vdst[j + D / 2] = v[hh * D + j + D / 2];
-  }
-  __syncthreads();  // every thread has read meta and the table
-  if (threadIdx.x == 0) {
-    P.pos[(size_t)page * P.pr + srow] = pos;
-    if (srow == 0) tab[pidx] = page;
-    meta[a.compress ? 1 : 0] += 1;
-    meta[2] = pos;
-  }
-}
 
 // ---- a2 + a3: split-KV decode ----------------------------------------------------
 //
@@ -206,46 +37,6 @@ struct UnitCfg {
   static constexpr int RW = CW * R::RPL;                                            // rows/unit
 };
 
-__device__ __forceinline__ int sgpr(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// a3: merge the split partials of one (sequence, KV head): weights
-// exp2(m_s - M) / L per (split, query head) in LDS, then every output element
-// is one weighted sum over the splits.
-template <typename T, int D, int G>
-__global__ void __launch_bounds__(1024) decode_merge_kernel(DecodeArgs a) {
-  __shared__ float sm_pm[kMaxSplits * G], sm_pl[kMaxSplits * G], sm_M[G], sm_L[G];
-  const int i = blockIdx.x, h = blockIdx.y;
-  const int b0 = a.prefix[i], ns = a.prefix[i + 1] - b0;
-  if (ns == 1) return;  // single split: the split kernel wrote out and lse
-  const int Hkv = a.P.Hkv, Hq = Hkv * G;
-  auto part = [&](int s, int g) { return a.part + (((size_t)(b0 + s) * Hkv + h) * G + g) * (D + 2); };
-  for (int t = threadIdx.x; t < ns * G; t += blockDim.x) {
-    const float* pp = part(t / G, t % G);
-    sm_pm[t] = pp[D];
-    sm_pl[t] = pp[D + 1];
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, sm_pm[s2 * G + g]);
-    float Ls = 0.f;
-    for (int s2 = 0; s2 < ns; ++s2) Ls += sm_pl[s2 * G + g] * fast_exp2(sm_pm[s2 * G + g] - M);
-    sm_M[g] = M;
-    sm_L[g] = Ls;
-    a.lse[(size_t)i * Hq + h * G + g] = (M + __log2f(Ls)) * 0.6931471805599453f;
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < ns * G; t += blockDim.x)
-    sm_pm[t] = fast_exp2(sm_pm[t] - sm_M[t % G]) / sm_L[t % G];
-  __syncthreads();
-  for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
-    const int g = t / D, d = t % D;
-    float O = 0.f;
-    for (int s2 = 0; s2 < ns; ++s2) O += part(s2, g)[d] * sm_pm[s2 * G + g];
-    ((T*)a.out)[((size_t)i * Hq + h * G + g) * D + d] = from_f32<T>(O);
-  }
-}
 
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
@@ -475,18 +266,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 //  - the unit's base address is wavefront-uniform, lane offsets are fixed, and
 //    only partial units clamp rows.
 
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
 
-// nearest-even bf16 bits of a finite float (no NaN handling: queries are finite)
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
 
 template <int G>
 __global__ void __launch_bounds__(256) decode_bf16_d128_kernel(DecodeArgs a) {
@@ -1232,671 +1013,7 @@ __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) 
   }
 }
 
-// ---- a7: the open block's rows leave the device view -----------------------------
-
-__global__ void free_kernel(FreeArgs a) {
-  const int i = blockIdx.x;
-  for (int l = threadIdx.x; l < a.P.L; l += blockDim.x)
-    a.P.meta[(a.slot[i] * a.P.L + l) * 4 + 1] = 0;
-}
-
-// ---- prompt rows -----------------------------------------------------------------
-
-template <typename T, int D>
-__global__ void __launch_bounds__(1024) prompt_kernel(PromptArgs a) {
-  const DevPool& P = a.P;
-  const int r = blockIdx.x;
-  if (r == 0 && threadIdx.x == 0) {
-    int32_t* meta = P.meta + (a.slot * P.L + a.layer) * 4;
-    meta[0] = a.prompt_len;
-    meta[1] = 0;
-    meta[2] = a.prompt_len - 1;
-  }
-  if (r == 0) {
-    int32_t* tab = ptab_of(P, a.slot, a.layer);
-    for (int t = threadIdx.x; t < (a.prompt_len + P.pr - 1) / P.pr; t += blockDim.x)
-      tab[t] = a.pages[t];
-  }
-  if (r >= a.prompt_len) return;
-  const int page = a.pages[r / P.pr], srow = r % P.pr;
-  const T* k = (const T*)a.k + (size_t)r * P.Hkv * D;
-  const T* v = (const T*)a.v + (size_t)r * P.Hkv * D;
-  const float2* rope = P.rope + (size_t)r * (D / 2);
-  for (int t = threadIdx.x; t < P.Hkv * (D / 2); t += blockDim.x) {
-    const int hh = t / (D / 2), j = t % (D / 2);
-    const float x1 = to_f32(k[hh * D + j]), x2 = to_f32(k[hh * D + j + D / 2]);
-    const float2 cs = rope[j];
-    const size_t o = (((size_t)page * P.Hkv + hh) * P.pr + srow) * D;
-    ((T*)P.kpool)[o + j] = from_f32<T>(x1 * cs.x - x2 * cs.y);
-    ((T*)P.kpool)[o + j + D / 2] = from_f32<T>(x2 * cs.x + x1 * cs.y);
-    ((T*)P.vpool)[o + j] = v[hh * D + j];
-    ((T*)P.vpool)[o + j + D / 2] = v[hh * D + j + D / 2];
-  }
-  if (threadIdx.x == 0) P.pos[(size_t)page * P.pr + srow] = r;
-}
-
-// ---- a4 + a6: pause RoPE at bit-reversed in-block positions, code-row scatter ----
-
-__device__ __forceinline__ int bitrev_dev(int k, int nbits) {
-  return nbits == 0 ? 0 : (int)(__brev((unsigned)k) >> (32 - nbits));
-}
-
-template <typename T, int D>
-__global__ void __launch_bounds__(1024) pause_rope_scatter_kernel(CompressArgs a) {
-  const DevPool& P = a.P;
-  const int k = blockIdx.x, i = blockIdx.y;
-  const int32_t* rec = a.desc + i * kCompRec;
-  const int slot = rec[0], blk = rec[1], pers_before = rec[2], prompt = rec[3];
-  const int pages_off = rec[4], npages = rec[5], first_new = rec[6];
-  const int pos = prompt + blk * P.C + bitrev_dev(k, a.log2Kp) * (P.C / a.Kp);
-  const T* kin = (const T*)a.kp + ((size_t)i * a.Kp + k) * P.Hkv * D;
-  const T* vin = (const T*)a.vp + ((size_t)i * a.Kp + k) * P.Hkv * D;
-  const float2* rope = P.rope + (size_t)pos * (D / 2);
-  const bool keep = k < a.quota;
-  int page = 0, srow = 0;
-  if (keep) {
-    const int row = pers_before + k;
-    page = a.desc[pages_off + row / P.pr - pers_before / P.pr];
-    srow = row % P.pr;
-  }
-  for (int t = threadIdx.x; t < P.Hkv * (D / 2); t += blockDim.x) {
-    const int hh = t / (D / 2), j = t % (D / 2);
-    const float x1 = to_f32(kin[hh * D + j]), x2 = to_f32(kin[hh * D + j + D / 2]);
-    const float2 cs = rope[j];
-    const T y1 = from_f32<T>(x1 * cs.x - x2 * cs.y);
-    const T y2 = from_f32<T>(x2 * cs.x + x1 * cs.y);
-    T* kr = (T*)a.kp_rot + (((size_t)i * P.Hkv + hh) * a.Kp + k) * D;
-    kr[j] = y1;
-    kr[j + D / 2] = y2;
-    if (keep) {
-      const size_t o = (((size_t)page * P.Hkv + hh) * P.pr + srow) * D;
-      ((T*)P.kpool)[o + j] = y1;
-      ((T*)P.kpool)[o + j + D / 2] = y2;
-      ((T*)P.vpool)[o + j] = vin[hh * D + j];
-      ((T*)P.vpool)[o + j + D / 2] = vin[hh * D + j + D / 2];
-    }
-  }
-  if (keep && threadIdx.x == 0) P.pos[(size_t)page * P.pr + srow] = pos;
-  if (k == 0 && threadIdx.x == 0) {
-    int32_t* tab = ptab_of(P, slot, a.layer);
-    const int first_idx = pers_before / P.pr;
-    for (int j = first_new; j < npages; ++j) tab[first_idx + j] = a.desc[pages_off + j];
-    P.meta[(slot * P.L + a.layer) * 4 + 0] = pers_before + a.quota;
-  }
-}
-
-// ---- a5: pause-token attention under the block mask (SIMT form) -------------------
-//
-// One wavefront per (sequence, pause j, query head). Keys: the sequence's
-// resident rows at this layer (prompt, earlier code rows, the whole block)
-// followed by the rotated pause keys 0..j. 64 keys per step: one lane per key
-// scores it, the wavefront takes the step's max, and each lane accumulates
-// its D/64 output dims over the step.
-
-template <typename T, int D>
-__global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) {
-  const DevPool& P = a.P;
-  const int j = blockIdx.x, hq = blockIdx.y, i = blockIdx.z;
-  const int lane = threadIdx.x;
-  const int hk = hq / a.G;
-  const int32_t* rec = a.desc + i * kCompRec;
-  const int slot = rec[0], blk = rec[1], n_pers = rec[2], prompt = rec[3];
-  const int n_ctx = n_pers + P.C;
-  const int n_keys = n_ctx + j + 1;
-  const int32_t* tab = ptab_of(P, slot, a.layer);
-  const int pos = prompt + blk * P.C + bitrev_dev(j, a.log2Kp) * (P.C / a.Kp);
-
-  __shared__ float qs[D];
-  __shared__ float ps[64];
-  {
-    const float2* rope = P.rope + (size_t)pos * (D / 2);
-    const T* qh = (const T*)a.qp + (((size_t)i * a.Kp + j) * a.Hq + hq) * D;
-    const float sc = 1.4426950408889634f / sqrtf((float)D);
-    for (int d = lane; d < D; d += 64)
-      qs[d] = sc * rope_elem<D>([&](int e) { return to_f32(qh[e]); }, d, rope);
-  }
-  __syncthreads();
-
-  auto key_row = [&](int r, const T** kr, const T** vr) {
-    if (r < n_ctx) {
-      int page, srow;
-      if (r < n_pers) {
-        page = tab[r / P.pr];
-        srow = r % P.pr;
-      } else {
-        const int o = r - n_pers;
-        page = tab[P.max_pers + o / P.pr];
-        srow = o % P.pr;
-      }
-      const size_t off = (((size_t)page * P.Hkv + hk) * P.pr + srow) * D;
-      *kr = (const T*)P.kpool + off;
-      *vr = (const T*)P.vpool + off;
-    } else {
-      const int kk = r - n_ctx;
-      *kr = (const T*)a.kp_rot + (((size_t)i * P.Hkv + hk) * a.Kp + kk) * D;
-      *vr = (const T*)a.vp + (((size_t)i * a.Kp + kk) * P.Hkv + hk) * D;
-    }
-  };
-
-  constexpr int DPL = (D + 63) / 64;
-  float m = -INFINITY, l = 0.f, o[DPL];
-#pragma unroll
-  for (int t = 0; t < DPL; ++t) o[t] = 0.f;
-  for (int r0 = 0; r0 < n_keys; r0 += 64) {
-    const int r = r0 + lane;
-    float s = -INFINITY;
-    if (r < n_keys) {
-      const T *kr, *vr;
-      key_row(r, &kr, &vr);
-      float acc = 0.f;
-      for (int d = 0; d < D; ++d) acc += qs[d] * to_f32(kr[d]);
-      s = acc;
-    }
-    float mx = s;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    const float mn = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mn);
-    m = mn;
-    const float p = fast_exp2(s - mn);
-    float psum = p;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) psum += __shfl_xor(psum, off);
-    l = l * alpha + psum;
-    __syncthreads();
-    ps[lane] = p;
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < DPL; ++t) o[t] *= alpha;
-    const int nr = min(64, n_keys - r0);
-    for (int rr = 0; rr < nr; ++rr) {
-      const T *kr, *vr;
-      key_row(r0 + rr, &kr, &vr);
-      const float pr_ = ps[rr];
-#pragma unroll
-      for (int t = 0; t < DPL; ++t) {
-        const int d = lane + 64 * t;
-        if (d < D) o[t] += pr_ * to_f32(vr[d]);
-      }
-    }
-  }
-  T* out = (T*)a.out + (((size_t)i * a.Kp + j) * a.Hq + hq) * D;
-#pragma unroll
-  for (int t = 0; t < DPL; ++t) {
-    const int d = lane + 64 * t;
-    if (d < D) out[d] = from_f32<T>(o[t] / l);
-  }
-  if (lane == 0) a.lse[((size_t)i * a.Kp + j) * a.Hq + hq] = (m + __log2f(l)) * 0.6931471805599453f;
-}
-
-// ---- a5 on bf16 MFMA (d = 128, four query heads per KV head, 64-row pages) -------
-//
-// Workgroup = (sequence, KV head, tile of 128 query rows); query row r is pause
-// r/4, head 4h + r%4. Each of the 4 wavefronts owns 32 query rows (two 16-row
-// N-blocks). For every 64-key tile (a context page, then pause-key tiles):
-//   S^T = K Q^T   with v_mfma_f32_16x16x32_bf16: A = K rows from LDS, B = the
-//                 rotated query (hi + lo bf16 parts, so the product keeps fp32
-//                 accuracy), C lane l = keys 4(l/16)+i x query l%16;
-//   online softmax per query column, all lane-local plus permlane swaps;
-//   O^T += V^T P^T: B = P^T straight from the S^T registers (bf16), A = V^T
-//                 from a transposed LDS tile.
-// The M-blocks of S^T take keys 32(mb/2) + 8(m/4) + 4(mb%2) + m%4 so that for
-// each 32-key step a lane's 8 probabilities are 8 consecutive keys, which is
-// one 16-byte read of the transposed V tile. K rows in LDS have their 16-byte
-// chunks XOR-swizzled by row so the 16 rows an A-operand read touches use
-// different banks. The next tile is loaded into registers while the current
-// one is computed; LDS is double-buffered (64 KB).
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
-
-__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-// max / sum over the four 16-lane rows of a wavefront (lane bits 4 and 5)
-__device__ __forceinline__ float rows4_max(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows4_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-__global__ void __launch_bounds__(256) compress_attn_mfma_kernel(CompressArgs a) {
-  constexpr int D = 128, G = 4, TK = 64, RB = D * 2;
-  __shared__ uint4 lk[2][TK * RB / 16];   // K rows, chunks swizzled by (row & 15)
-  __shared__ uint4 lvt[2][D * TK * 2 / 16];  // V^T: [dim][64 keys] bf16, 128 B per dim
-  const DevPool& P = a.P;
-  const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
-  const int l16 = lane & 15, g4 = lane >> 4;
-  // workgroup -> (pair = sequence x KV head, query tile); the tiles of one pair
-  // share blockIdx.x mod 8, i.e. one XCD and its L2
-  const int ntq = (4 * a.Kp + 127) / 128;
-  const int npair = a.n * P.Hkv;
-  const int b = blockIdx.x, xcd = b & 7, jj = b >> 3;
-  const int pair = (jj / ntq) * 8 + xcd, qt = jj % ntq;
-  if (pair >= npair) return;
-  const int i = pair / P.Hkv, hk = pair % P.Hkv;
-  const int32_t* rec = a.desc + i * kCompRec;
-  const int slot = rec[0], blk = rec[1], n_pers = rec[2], prompt = rec[3];
-  const int32_t* tab = ptab_of(P, slot, a.layer);
-  const int npp = (n_pers + TK - 1) / TK, nop = P.C / TK;
-  const int ntc = npp + nop;  // context tiles
-  const int q0 = qt * 128;    // first query row of the workgroup
-  const int nq = min(128, 4 * a.Kp - q0);
-  const int last_pause = (q0 + nq - 1) >> 2;
-  const int ntp = last_pause / TK + 1;  // pause-key tiles
-  const int ntiles = ntc + ntp;
-
-  // ---- the wavefront's query rows: rotate at the bitrev position, scale, hi/lo
-  uint4 qh[2][4], ql[2][4];  // [N-block][k-step]: dims 32ks + 8 g4 + 0..7
-  int qpause[2];
-  {
-    const float qs = 1.4426950408889634f / sqrtf((float)D);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      int r = q0 + wave * 32 + nb * 16 + l16;
-      const bool rv = r < q0 + nq;
-      r = rv ? r : q0;
-      const int pz = r >> 2, hh = r & 3;
-      qpause[nb] = rv ? pz : -1;
-      const int pos = prompt + blk * P.C + bitrev_dev(pz, a.log2Kp) * (P.C / a.Kp);
-      const bf16_t* qrow = (const bf16_t*)a.qp + (((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh) * D;
-      float x[4][8];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) unpack16(*(const uint4*)(qrow + 32 * ks + 8 * g4), x[ks], bf16_t());
-      const float2* rope = P.rope + (size_t)pos * (D / 2);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        float y0[8], y1[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float2 cs = rope[32 * ks + 8 * g4 + j];
-          y0[j] = qs * (x[ks][j] * cs.x - x[ks + 2][j] * cs.y);
-          y1[j] = qs * (x[ks + 2][j] * cs.x + x[ks][j] * cs.y);
-        }
-        uint32_t h0[4], l0[4], h1[4], l1[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t a0 = bf16_bits(y0[2 * j]), a1 = bf16_bits(y0[2 * j + 1]);
-          h0[j] = a0 | (a1 << 16);
-          l0[j] = bf16_bits(y0[2 * j] - __uint_as_float(a0 << 16)) |
-                  (bf16_bits(y0[2 * j + 1] - __uint_as_float(a1 << 16)) << 16);
-          a0 = bf16_bits(y1[2 * j]);
-          a1 = bf16_bits(y1[2 * j + 1]);
-          h1[j] = a0 | (a1 << 16);
-          l1[j] = bf16_bits(y1[2 * j] - __uint_as_float(a0 << 16)) |
-                  (bf16_bits(y1[2 * j + 1] - __uint_as_float(a1 << 16)) << 16);
-        }
-        qh[nb][ks] = make_uint4(h0[0], h0[1], h0[2], h0[3]);
-        ql[nb][ks] = make_uint4(l0[0], l0[1], l0[2], l0[3]);
-        qh[nb][ks + 2] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
-        ql[nb][ks + 2] = make_uint4(l1[0], l1[1], l1[2], l1[3]);
-      }
-    }
-  }
-
-  // ---- tile t -> rows: thread t loads rows (tid/16 + 16 c), chunk tid%16
-  const int trow = threadIdx.x >> 4, tchunk = threadIdx.x & 15;
-  // staged rows of the next tile, named so they stay in registers
-  uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
-  auto tile_src = [&](int t, const char** kb, const char** vb, size_t* kstride, size_t* vstride,
-                      int* nval) __attribute__((always_inline)) {
-    if (t < ntc) {
-      int page, rows;
-      if (t < npp) {
-        page = sgpr(tab[t]);
-        rows = (t == npp - 1) ? n_pers - t * TK : TK;
-      } else {
-        page = sgpr(tab[P.max_pers + (t - npp)]);
-        rows = TK;
-      }
-      const size_t off = (((size_t)page * P.Hkv + hk) * TK) * RB;
-      *kb = (const char*)P.kpool + off;
-      *vb = (const char*)P.vpool + off;
-      *kstride = RB;
-      *vstride = RB;
-      *nval = rows;
-    } else {
-      const int k0 = (t - ntc) * TK;
-      *kb = (const char*)a.kp_rot + (((size_t)i * P.Hkv + hk) * a.Kp + k0) * RB;
-      *vb = (const char*)a.vp + (((size_t)i * a.Kp + k0) * P.Hkv + hk) * RB;
-      *kstride = RB;
-      *vstride = (size_t)P.Hkv * RB;
-      *nval = min(TK, a.Kp - k0);
-    }
-  };
-  auto gload = [&](int t) __attribute__((always_inline)) {
-    const char *kb, *vb;
-    size_t ks, vs;
-    int nval;
-    tile_src(t, &kb, &vb, &ks, &vs, &nval);
-    auto piece = [&](int c, uint4& kx, uint4& vx) __attribute__((always_inline)) {
-      int r = trow + 16 * c;
-      r = r < nval ? r : nval - 1;
-      kx = *(const uint4*)(kb + r * ks + tchunk * 16);
-      vx = *(const uint4*)(vb + r * vs + tchunk * 16);
-    };
-    piece(0, sk0, sv0);
-    piece(1, sk1, sv1);
-    piece(2, sk2, sv2);
-    piece(3, sk3, sv3);
-  };
-  auto swrite = [&](int buf) __attribute__((always_inline)) {
-    uint16_t* vt = (uint16_t*)lvt[buf];
-    auto piece = [&](int c, const uint4& kx, const uint4& vx) __attribute__((always_inline)) {
-      const int r = trow + 16 * c;
-      lk[buf][r * 16 + (tchunk ^ (r & 15))] = kx;
-      // V^T: dims 8 tchunk .. +8 of key r -> [dim][key]
-      const int d0 = 8 * tchunk;
-      vt[(d0 + 0) * TK + r] = (uint16_t)vx.x;
-      vt[(d0 + 1) * TK + r] = (uint16_t)(vx.x >> 16);
-      vt[(d0 + 2) * TK + r] = (uint16_t)vx.y;
-      vt[(d0 + 3) * TK + r] = (uint16_t)(vx.y >> 16);
-      vt[(d0 + 4) * TK + r] = (uint16_t)vx.z;
-      vt[(d0 + 5) * TK + r] = (uint16_t)(vx.z >> 16);
-      vt[(d0 + 6) * TK + r] = (uint16_t)vx.w;
-      vt[(d0 + 7) * TK + r] = (uint16_t)(vx.w >> 16);
-    };
-    piece(0, sk0, sv0);
-    piece(1, sk1, sv1);
-    piece(2, sk2, sv2);
-    piece(3, sk3, sv3);
-  };
-
-  // key of S^T M-block mb, row m (see above)
-  auto keyof = [](int mb, int m) { return 32 * (mb >> 1) + 8 * (m >> 2) + 4 * (mb & 1) + (m & 3); };
-
-  f32x4_t acc_o[2][8];  // [N-block][dim block]
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int db = 0; db < 8; ++db) acc_o[nb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-
-  auto compute = [&](int t, int buf) __attribute__((always_inline)) {
-    const bool ctx = t < ntc;
-    int nval;
-    {
-      const char *kb, *vb;
-      size_t ks, vs;
-      tile_src(t, &kb, &vb, &ks, &vs, &nval);
-    }
-    const int kbase = ctx ? 0 : (t - ntc) * TK;  // pause index of key 0 of a pause tile
-    f32x4_t s[4][2];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int kr = keyof(mb, l16);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 ka = lk[buf][kr * 16 + ((4 * ks + g4) ^ (kr & 15))];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          s[mb][nb] = mfma_bf16(ka, qh[nb][ks], s[mb][nb]);
-          s[mb][nb] = mfma_bf16(ka, ql[nb][ks], s[mb][nb]);
-        }
-      }
-    }
-    // mask, online softmax per query column (lane-local after the row swaps)
-    uint4 pb[2][2];  // [N-block][32-key step]: bf16 probabilities, 8 keys
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = keyof(mb, 4 * g4 + e);
-          bool ok = key < nval;
-          if (!ctx) ok = ok && (kbase + key <= qpause[nb]);
-          const float v = ok ? s[mb][nb][e] : -INFINITY;
-          s[mb][nb][e] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = rows4_max(mx);
-      const float mn = fmaxf(m_run[nb], mx);
-      const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_run[nb] - mn);
-      m_run[nb] = mn;
-      float ps = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = mn == -INFINITY ? 0.f : fast_exp2(s[mb][nb][e] - mn);
-          s[mb][nb][e] = p;  // the score register now holds its probability
-          ps += p;
-        }
-      l_run[nb] = l_run[nb] * alpha + ps;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) acc_o[nb][db] *= alpha;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // keys 32kk + 8 g4 + j: j < 4 from M-block 2kk, j >= 4 from 2kk+1
-        const f32x4_t u0 = s[2 * kk][nb], u1 = s[2 * kk + 1][nb];
-        pb[nb][kk] = make_uint4(bf16_bits(u0[0]) | (bf16_bits(u0[1]) << 16),
-                                bf16_bits(u0[2]) | (bf16_bits(u0[3]) << 16),
-                                bf16_bits(u1[0]) | (bf16_bits(u1[1]) << 16),
-                                bf16_bits(u1[2]) | (bf16_bits(u1[3]) << 16));
-      }
-    }
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const int d = 16 * db + l16;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint4 va = lvt[buf][(d * TK + 32 * kk + 8 * g4) / 8];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc_o[nb][db] = mfma_bf16(va, pb[nb][kk], acc_o[nb][db]);
-      }
-    }
-  };
-
-  gload(0);
-  swrite(0);
-  if (ntiles > 1) gload(1);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) {
-      swrite(buf ^ 1);  // last read before the previous barrier
-      if (t + 2 < ntiles) gload(t + 2);
-    }
-    compute(t, buf);
-    __syncthreads();
-  }
-
-  // ---- output: O^T / l; lane holds dims 16 db + 4 g4 + e of query l16
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float L = rows4_sum(l_run[nb]);
-    const int r = q0 + wave * 32 + nb * 16 + l16;
-    if (r >= q0 + nq) continue;
-    const int pz = r >> 2, hh = r & 3;
-    bf16_t* dst = (bf16_t*)a.out + (((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh) * D;
-    const float inv = 1.f / L;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const uint32_t lo = bf16_bits(acc_o[nb][db][0] * inv) | (bf16_bits(acc_o[nb][db][1] * inv) << 16);
-      const uint32_t hi = bf16_bits(acc_o[nb][db][2] * inv) | (bf16_bits(acc_o[nb][db][3] * inv) << 16);
-      *(uint2*)(dst + 16 * db + 4 * g4) = make_uint2(lo, hi);
-    }
-    if (g4 == 0)
-      a.lse[((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh] = (m_run[nb] + __log2f(L)) * 0.6931471805599453f;
-  }
-}
-
-// ---- synthetic fill --------------------------------------------------------------
-
-template <typename T, int D>
-__global__ void __launch_bounds__(512) fill_kernel(FillArgs a) {
-  const DevPool& P = a.P;
-  const int r = blockIdx.x, l = blockIdx.y;
-  const int32_t* hdr = a.desc + 4 * l;
-  const int pers_off = hdr[0], npers = hdr[1], open_off = hdr[2], nopen = hdr[3];
-  const int q = a.quota[l], Kp = a.pause[l];
-  const int pers_rows = a.compress ? a.prompt_len + a.nb * q : a.prompt_len + a.G;
-  const int open_rows = a.compress ? a.G - a.nb * P.C : 0;
-  if (r == 0) {
-    int32_t* tab = ptab_of(P, a.slot, l);
-    for (int t = threadIdx.x; t < npers; t += blockDim.x) tab[t] = a.desc[pers_off + t];
-    for (int t = threadIdx.x; t < nopen; t += blockDim.x) tab[P.max_pers + t] = a.desc[open_off + t];
-    if (threadIdx.x == 0) {
-      int32_t* meta = P.meta + (a.slot * P.L + l) * 4;
-      meta[0] = pers_rows;
-      meta[1] = open_rows;
-      meta[2] = a.prompt_len + a.G - 1;
-    }
-  }
-  if (r >= pers_rows + open_rows) return;
-  int kind, ia, ib, pos, page, srow;
-  if (r < a.prompt_len) {
-    kind = 0; ia = r; ib = 0; pos = r;
-  } else if (r < pers_rows) {
-    const int c = r - a.prompt_len;
-    if (a.compress) {
-      kind = 2; ia = c / q; ib = c % q;
-      int nbits = 0;
-      while ((1 << nbits) < Kp) ++nbits;
-      pos = a.prompt_len + ia * P.C + bitrev_dev(ib, nbits) * (P.C / Kp);
-    } else {
-      kind = 1; ia = c; ib = 0; pos = r;
-    }
-  } else {
-    kind = 1; ia = a.nb * P.C + (r - pers_rows); ib = 0; pos = a.prompt_len + ia;
-  }
-  if (r < pers_rows) {
-    page = a.desc[pers_off + r / P.pr];
-    srow = r % P.pr;
-  } else {
-    page = a.desc[open_off + (r - pers_rows) / P.pr];
-    srow = (r - pers_rows) % P.pr;
-  }
-  // generate the raw row (stored type) into LDS, then rotate the key
-  __shared__ float kraw[1024 * 2];  // up to Hkv*D = 1024 elements
-  const int n = P.Hkv * D;
-  for (int t = threadIdx.x; t < n / 2; t += blockDim.x) {
-    const int hh = t / (D / 2), e = t % (D / 2);
-    double z0, z1;
-    synth_pair(synth_row_key(a.seed, l, kind, ia, ib, 0, hh), e, &z0, &z1);
-    kraw[hh * D + 2 * e] = to_f32(from_f32<T>((float)z0));
-    kraw[hh * D + 2 * e + 1] = to_f32(from_f32<T>((float)z1));
-    synth_pair(synth_row_key(a.seed, l, kind, ia, ib, 1, hh), e, &z0, &z1);
-    const size_t o = (((size_t)page * P.Hkv + hh) * P.pr + srow) * D;
-    ((T*)P.vpool)[o + 2 * e] = from_f32<T>((float)z0);
-    ((T*)P.vpool)[o + 2 * e + 1] = from_f32<T>((float)z1);
-  }
-  __syncthreads();
-  const float2* rope = P.rope + (size_t)pos * (D / 2);
-  for (int t = threadIdx.x; t < n / 2; t += blockDim.x) {
-    const int hh = t / (D / 2), j = t % (D / 2);
-    const float x1 = kraw[hh * D + j], x2 = kraw[hh * D + j + D / 2];
-    const float2 cs = rope[j];
-    const size_t o = (((size_t)page * P.Hkv + hh) * P.pr + srow) * D;
-    ((T*)P.kpool)[o + j] = from_f32<T>(x1 * cs.x - x2 * cs.y);
-    ((T*)P.kpool)[o + j + D / 2] = from_f32<T>(x2 * cs.x + x1 * cs.y);
-  }
-  if (threadIdx.x == 0) P.pos[(size_t)page * P.pr + srow] = pos;
-}
-
-// ---- inspection ------------------------------------------------------------------
-
-template <typename T, int D>
-__global__ void read_rows_kernel(ReadArgs a) {
-  const DevPool& P = a.P;
-  const int rr = blockIdx.x, r = a.row0 + rr;
-  const int32_t* meta = meta_of(P, a.slot, a.layer);
-  const int32_t* tab = ptab_of(P, a.slot, a.layer);
-  const int n_pers = meta[0];
-  int page, srow;
-  if (r < n_pers) {
-    page = tab[r / P.pr];
-    srow = r % P.pr;
-  } else {
-    page = tab[P.max_pers + (r - n_pers) / P.pr];
-    srow = (r - n_pers) % P.pr;
-  }
-  for (int t = threadIdx.x; t < P.Hkv * D; t += blockDim.x) {
-    const int hh = t / D, d = t % D;
-    const size_t o = (((size_t)page * P.Hkv + hh) * P.pr + srow) * D + d;
-    ((T*)a.k_out)[(size_t)rr * P.Hkv * D + t] = ((const T*)P.kpool)[o];
-    ((T*)a.v_out)[(size_t)rr * P.Hkv * D + t] = ((const T*)P.vpool)[o];
-  }
-}
-
-__global__ void export_kernel(ExportArgs a) {
-  const DevPool& P = a.P;
-  const int32_t* meta = meta_of(P, a.slot, a.layer);
-  const int32_t* tab = ptab_of(P, a.slot, a.layer);
-  const int n_pers = meta[0], n_open = meta[1];
-  const int npp = (n_pers + P.pr - 1) / P.pr, nop = (n_open + P.pr - 1) / P.pr;
-  if (threadIdx.x == 0) {
-    a.dst[0] = n_pers;
-    a.dst[1] = n_open;
-    a.dst[2] = meta[2];
-    a.dst[3] = npp + nop;
-  }
-  for (int t = threadIdx.x; t < npp; t += blockDim.x) a.dst[4 + t] = tab[t];
-  for (int t = threadIdx.x; t < nop; t += blockDim.x) a.dst[4 + npp + t] = tab[P.max_pers + t];
-  int32_t* posd = a.dst + 4 + npp + nop;
-  for (int r = threadIdx.x; r < n_pers + n_open; r += blockDim.x) {
-    int page, srow;
-    if (r < n_pers) {
-      page = tab[r / P.pr];
-      srow = r % P.pr;
-    } else {
-      page = tab[P.max_pers + (r - n_pers) / P.pr];
-      srow = (r - n_pers) % P.pr;
-    }
-    posd[r] = P.pos[(size_t)page * P.pr + srow];
-  }
-}
-
-// ---- dispatch ----------------------------------------------------------------------
-
-template <template <typename, int> class K>
-struct Nop {};
-
-#define ABK_DISPATCH_TD(dtype, D, ...)                                  \
-  do {                                                                  \
-    if (dtype == 0) {                                                   \
-      using T = float;                                                  \
-      if (D == 16) { constexpr int DD = 16; __VA_ARGS__; }              \
-      else if (D == 64) { constexpr int DD = 64; __VA_ARGS__; }         \
-      else if (D == 128) { constexpr int DD = 128; __VA_ARGS__; }       \
-      else return hipErrorInvalidValue;                                 \
-    } else {                                                            \
-      using T = bf16_t;                                                 \
-      if (D == 16) { constexpr int DD = 16; __VA_ARGS__; }              \
-      else if (D == 64) { constexpr int DD = 64; __VA_ARGS__; }         \
-      else if (D == 128) { constexpr int DD = 128; __VA_ARGS__; }       \
-      else return hipErrorInvalidValue;                                 \
-    }                                                                   \
-  } while (0)
-
-static int threads_for(int Hkv, int D) {
-  int t = Hkv * (D / 2);
-  t = t < 64 ? 64 : t;
-  return t > 1024 ? 1024 : t;
-}
-
-hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
-  if (a.n == 0) return hipSuccess;
-  const int th = threads_for(a.P.Hkv, a.P.D);
-  ABK_DISPATCH_TD(a.P.dtype, a.P.D,
-                  hipLaunchKernelGGL((append_kernel<T, DD>), dim3(a.n), dim3(th), 0, s, a));
-  return hipGetLastError();
-}
+// ---- launchers ---------------------------------------------------------------------
 
 template <typename T, int D>
 static hipError_t decode_g(const DecodeArgs& a, int32_t total, hipStream_t s) {
@@ -1954,54 +1071,6 @@ hipError_t launch_decode(const DecodeArgs& a, int32_t total_work, hipStream_t s)
   return hipSuccess;
 }
 
-hipError_t launch_free(const FreeArgs& a, hipStream_t s) {
-  if (a.n == 0) return hipSuccess;
-  hipLaunchKernelGGL(free_kernel, dim3(a.n), dim3(64), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_prompt(const PromptArgs& a, hipStream_t s) {
-  const int th = threads_for(a.P.Hkv, a.P.D);
-  const int rows = a.prompt_len > 0 ? a.prompt_len : 1;
-  ABK_DISPATCH_TD(a.P.dtype, a.P.D,
-                  hipLaunchKernelGGL((prompt_kernel<T, DD>), dim3(rows), dim3(th), 0, s, a));
-  return hipGetLastError();
-}
-
-hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
-  if (a.n == 0) return hipSuccess;
-  const int th = threads_for(a.P.Hkv, a.P.D);
-  const bool mfma = a.P.dtype == 1 && a.P.D == 128 && a.G == 4 && a.P.pr == 64;
-  ABK_DISPATCH_TD(a.P.dtype, a.P.D, {
-    hipLaunchKernelGGL((pause_rope_scatter_kernel<T, DD>), dim3(a.Kp, a.n), dim3(th), 0, s, a);
-    if (!mfma)
-      hipLaunchKernelGGL((compress_attn_simt_kernel<T, DD>), dim3(a.Kp, a.Hq, a.n), dim3(64), 0,
-                         s, a);
-  });
-  if (mfma) {
-    // tiles of one (sequence, KV head) pair share blockIdx.x mod 8 (one XCD)
-    const int ntq = (4 * a.Kp + 127) / 128;
-    const int npair = a.n * a.P.Hkv;
-    const int nwg = ((npair + 7) / 8) * 8 * ntq;
-    hipLaunchKernelGGL(compress_attn_mfma_kernel, dim3(nwg), dim3(256), 0, s, a);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_fill(const FillArgs& a, int32_t max_rows, hipStream_t s) {
-  const int rows = max_rows > 0 ? max_rows : 1;
-  ABK_DISPATCH_TD(a.P.dtype, a.P.D,
-                  hipLaunchKernelGGL((fill_kernel<T, DD>), dim3(rows, a.P.L), dim3(512), 0, s, a));
-  return hipGetLastError();
-}
-
-hipError_t launch_read(const ReadArgs& a, hipStream_t s) {
-  if (a.nrows == 0) return hipSuccess;
-  ABK_DISPATCH_TD(a.P.dtype, a.P.D,
-                  hipLaunchKernelGGL((read_rows_kernel<T, DD>), dim3(a.nrows), dim3(256), 0, s, a));
-  return hipGetLastError();
-}
-
 bool decode_stream_supported(const DevPool& P, int32_t G) {
   return P.dtype == 1 && P.D == 128 && G == 4 && (P.pr == 32 || P.pr == 64);
 }
@@ -2024,10 +1093,4 @@ hipError_t launch_decode_stream(const StreamArgs& a, int32_t nwg, hipStream_t s)
     hipLaunchKernelGGL(decode_stream_merge_kernel, dim3(a.n, a.P.Hkv), dim3(512), 0, s, a);
   return hipGetLastError();
 }
-
-hipError_t launch_export(const ExportArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(export_kernel, dim3(1), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 }  // namespace abk

@@ -1,5 +1,5 @@
 // Launch interface between the C ABI (abk_api.cpp) and the HIP kernels
-// (kernels.hip). Hot-path launches (append, decode, free) carry their
+// (pool_kernels.hip, decode.hip, compress.hip). Hot-path launches (append, decode, free) carry their
 // per-call data by value in the kernel arguments and read the device-resident
 // per-(sequence, layer) metadata and page tables, so no host-to-device copy
 // sits between two layers. Rarer calls (prompt, compression, fills,
