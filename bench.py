@@ -90,6 +90,169 @@ def traffic_from_profiles(kernel: str, launches_bytes: float):
     return t.get("bytes_per_launch")
 
 
+# ---- rocprofv3 summaries ----------------------------------------------------------
+
+NUM_XCD, NUM_CU, SIMD_PER_CU = 8, 256, 4
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    return None
+
+
+def _cmd(d, name):
+    path = os.path.join(d, name + ".cmd")
+    return open(path).read().strip() if os.path.exists(path) else "(command not recorded)"
+
+
+def _counters(d, name, counter, match):
+    """Per-dispatch values of one counter for kernels whose name contains ``match``."""
+    path = _find(os.path.join(d, name), "counter_collection.csv")
+    if path is None:
+        return []
+    return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in _csv_rows(path)
+            if r["Counter_Name"] == counter and match in r["Kernel_Name"]]
+
+
+def _calibration(d):
+    """KiB that FETCH_SIZE / WRITE_SIZE read for one plain device copy of known
+    size: the scale from counter units to HBM bytes."""
+    info = os.path.join(d, "copy_fetch.json")
+    n = json.load(open(info))["copy_bytes"] if os.path.exists(info) else 1 << 30
+    out = {"copy_bytes": n}
+    for which, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        vals = sorted(v for _, v in _counters(d, "copy_" + which, counter, "copyBuffer"))[-3:]
+        kib = float(np.mean(vals)) if vals else float("nan")
+        out[which + "_kib_per_copy"] = kib
+        out[which + "_scale"] = (n / 1024.0) / kib if vals else float("nan")
+    return out
+
+
+def _stats_table(d, name, match):
+    path = _find(os.path.join(d, name), "kernel_stats.csv")
+    lines = []
+    for r in _csv_rows(path) if path else []:
+        if any(m in r["Name"] for m in match):
+            lines.append(f"  {r['Name'][:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.1f} "
+                         f"{float(r['MinNs']) / 1e3:9.1f} {float(r['MaxNs']) / 1e3:9.1f} "
+                         f"{float(r['TotalDurationNs']) / 1e6:10.2f}")
+    head = f"  {'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_ms':>10s}"
+    return [head] + lines, path
+
+
+def profile_summary(d):
+    """Write profiles/*.txt and profiles/*_traffic.json from a directory of
+    rocprofv3 runs (one sub-directory per pass, ``<pass>.cmd`` holding the
+    command of each pass, ``<pass>.json`` the JSON line bench printed)."""
+    cal = _calibration(d)
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    cal_lines = [
+        f"calibration: a plain device copy of {cal['copy_bytes']} B reads FETCH_SIZE "
+        f"{cal['fetch_kib_per_copy']:.1f} KiB and WRITE_SIZE {cal['write_kib_per_copy']:.1f} KiB per "
+        f"dispatch -> scale {cal['fetch_scale']:.3f} (fetch), {cal['write_scale']:.3f} (write)",
+        f"  fetch pass: {_cmd(d, 'copy_fetch')}",
+        f"  write pass: {_cmd(d, 'copy_write')}",
+    ]
+    for fam, tag, trace, prefix, match, what in (
+            ("decode_stream", "decode_stream_36L_22seq", "dec_trace", "dec", "decode_stream",
+             "decode step of the 36-layer per-layer-quota workload, 22 sequences, bf16, d = 128, "
+             "32 q / 8 KV heads, 64-row pages (bench.py default workload)"),
+            ("compress_attn_mfma", "compress_attn_mfma_64seq_36L", "cmp_trace", "cmp",
+             "compress_attn_mfma",
+             "block compression event: 64 sequences x 36 layers, K = 256 pause tokens, bf16, "
+             "d = 128, 32 q / 8 KV heads (bench.py compression event)")):
+        if not os.path.isdir(os.path.join(d, prefix + "_fetch")):
+            continue
+        table, _ = _stats_table(d, trace, [match, "append_kernel", "pause_rope"])
+        fetch = _counters(d, prefix + "_fetch", "FETCH_SIZE", match)
+        write = _counters(d, prefix + "_write", "WRITE_SIZE", match)
+        by = {}
+        for nm, v in fetch:
+            by.setdefault(nm, [[], []])[0].append(v)
+        for nm, v in write:
+            by.setdefault(nm, [[], []])[1].append(v)
+        # one call = one dispatch of each kernel of the family
+        per_call = 0.0
+        cnt_lines = [f"  {'kernel':60s} {'dispatches':>10s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} "
+                     f"{'HBM MB':>10s}"]
+        fetch_kib = write_kib = 0.0
+        for nm, (fv, wv) in sorted(by.items()):
+            f_, w_ = float(np.mean(fv)), float(np.mean(wv))
+            mb = (f_ * cal["fetch_scale"] + w_ * cal["write_scale"]) * 1024 / 1e6
+            per_call += mb * 1e6
+            fetch_kib += f_
+            write_kib += w_
+            cnt_lines.append(f"  {nm[:60]:60s} {len(fv):10d} {f_:12.1f} {w_:12.1f} {mb:10.2f}")
+        bench_json = os.path.join(d, trace + ".json")
+        bj = json.load(open(bench_json)) if os.path.exists(bench_json) else None
+        extra = []
+        if fam == "decode_stream" and bj:
+            rf = bj["roofline"]
+            extra = [f"bench.py in the traced run: {rf['avg_launch_us']:.1f} us per decode call "
+                     f"(HIP events around decode + merge), algorithmic "
+                     f"{rf['algorithmic_bytes_per_launch'] / 1e6:.1f} MB per call, "
+                     f"{rf['achieved']:.0f} GB/s = {100 * rf['frac']:.1f}% of 8 TB/s",
+                     f"counted HBM bytes / algorithmic bytes: "
+                     f"{per_call / rf['algorithmic_bytes_per_launch']:.3f}"]
+        if fam == "compress_attn_mfma":
+            sq = {}
+            for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_MFMA",
+                      "SQ_INSTS_VALU", "SQ_WAVES"):
+                v = _counters(d, "cmp_sq", c, match)
+                if v:
+                    sq[c] = float(np.mean([x for _, x in v]))
+            g = _counters(d, "cmp_grbm", "GRBM_GUI_ACTIVE", match)
+            if g and sq:
+                gui = float(np.mean([x for _, x in g])) / NUM_XCD
+                extra.append(f"per dispatch: GRBM_GUI_ACTIVE {gui * NUM_XCD:.4g} (summed over "
+                             f"{NUM_XCD} XCDs: {gui:.4g} cycles each)")
+                for c, v in sq.items():
+                    extra.append(f"  {c} {v:.4g}")
+                extra.append(f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {NUM_CU} CUs x "
+                             f"{SIMD_PER_CU} SIMDs) = "
+                             f"{100 * sq['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * NUM_CU * SIMD_PER_CU):.1f}%")
+                extra.append(f"CU busy = SQ_BUSY_CU_CYCLES / (cycles x {NUM_CU}) = "
+                             f"{100 * sq['SQ_BUSY_CU_CYCLES'] / (gui * NUM_CU):.1f}%")
+                extra.append(f"VALU instructions per MFMA: {sq['SQ_INSTS_VALU'] / sq['SQ_INSTS_MFMA']:.2f}")
+                extra.append(f"  sq pass:   {_cmd(d, 'cmp_sq')}")
+                extra.append(f"  grbm pass: {_cmd(d, 'cmp_grbm')}")
+            if bj and bj.get("compress"):
+                c = bj["compress"]
+                extra.append(f"bench.py in the traced run: {c['ms_per_event']:.1f} ms per event, "
+                             f"{c['roofline']['achieved']:.0f} TFLOP/s algorithmic = "
+                             f"{100 * c['roofline']['frac']:.1f}% of 2.5 PFLOP/s bf16")
+        text = [f"{fam} -- {what}", "",
+                "Commands (run from the repository root with TMPDIR=/tmp; "
+                "the library built in-tree beforehand):",
+                f"  trace pass: {_cmd(d, trace)}",
+                f"  fetch pass: {_cmd(d, prefix + '_fetch')}",
+                f"  write pass: {_cmd(d, prefix + '_write')}", "",
+                "rocprofv3 --kernel-trace --stats (durations in us):"] + table + [
+                "", "Counters, mean per dispatch (FETCH_SIZE and WRITE_SIZE in KiB, scaled to HBM "
+                "bytes with the copy calibration):"] + cnt_lines + [
+                f"HBM bytes per call (one dispatch of each kernel above): {per_call / 1e6:.2f} MB", ""
+                ] + cal_lines + ([""] + extra if extra else [])
+        with open(os.path.join(prof, tag + ".txt"), "w") as f:
+            f.write("\n".join(text) + "\n")
+        rec = {"kernel": fam, "kernel_source_hash": kernel_source_hash(fam),
+               "bytes_per_launch": per_call, "fetch_kib_per_launch": fetch_kib,
+               "write_kib_per_launch": write_kib, "fetch_scale": cal["fetch_scale"],
+               "write_scale": cal["write_scale"], "summary": f"profiles/{tag}.txt"}
+        with open(os.path.join(prof, fam + "_traffic.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(f"wrote profiles/{tag}.txt and profiles/{fam}_traffic.json")
+
+
 # ---------------------------------------------------------------------------------
 
 def run_decode(args, torch, abk):
@@ -131,6 +294,12 @@ def run_decode(args, torch, abk):
     # host mirror of generated counts for the compress/free schedule and bytes
     g = G.copy()
     nb = (g - 1) // C
+    # per-layer views and events made before the timed region, so that the host
+    # stays well ahead of the GPU inside it
+    views = [[(q_in[t, l], k_in[t, l], v_in[t, l]) for l in range(L)] for t in range(total_steps)]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(L)] for _ in range(args.steps)]
+    cev = []
 
     def step(t, rec):
         full = [i for i in range(B) if g[i] - nb[i] * C == C]
@@ -138,36 +307,35 @@ def run_decode(args, torch, abk):
             ids = [sids[i] for i in full]
             for l in range(L):
                 if rec is not None:
-                    rec["c0"].append(torch.cuda.Event(enable_timing=True))
-                    rec["c0"][-1].record()
+                    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    c0.record()
                 pool.compress_block(l, ids, qp[:len(ids)], kp[:len(ids)], vp[:len(ids)],
                                     cout[:len(ids)], clse[:len(ids)])
                 if rec is not None:
-                    rec["c1"].append(torch.cuda.Event(enable_timing=True))
-                    rec["c1"][-1].record()
+                    c1.record()
+                    cev.append((c0, c1))
             pool.free_block(ids)
             for i in full:
                 nb[i] += 1
         for l in range(L):
-            pool.append_kv(l, sids, k_in[t, l], v_in[t, l])
+            q, k, v = views[t][l]
+            pool.append_kv(l, sids, k, v)
             if rec is not None:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-            pool.decode_attention(l, sids, q_in[t, l], out, lse)
+                rec[l][0].record()
+            pool.decode_attention(l, sids, q, out, lse)
             if rec is not None:
-                e1 = torch.cuda.Event(enable_timing=True)
-                e1.record()
-                R = P + nb * quotas[l] + (g + 1 - nb * C)
-                rec["d"].append((e0, e1, int(R.sum())))
+                rec[l][1].record()
+        if rec is not None:
+            rows_log.append([int((P + nb * quotas[l] + (g + 1 - nb * C)).sum()) for l in range(L)])
         g[:] += 1
 
+    rows_log = []
     for t in range(args.warmup):
         step(t, None)
     torch.cuda.synchronize()
-    rec = {"d": [], "c0": [], "c1": []}
     t0 = time.perf_counter()
     for t in range(args.warmup, total_steps):
-        step(t, rec)
+        step(t, ev[t - args.warmup])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
@@ -175,10 +343,10 @@ def run_decode(args, torch, abk):
     # plus q, out (bf16) and lse (fp32)
     row_bytes = 2 * HKV * D * 2
     io_bytes = B * (2 * HQ * D * 2 + HQ * 4)
-    dec_ms = [e0.elapsed_time(e1) for e0, e1, _ in rec["d"]]
-    dec_bytes = [rows * row_bytes + io_bytes for _, _, rows in rec["d"]]
+    dec_ms = [e0.elapsed_time(e1) for evs in ev for e0, e1 in evs]
+    dec_bytes = [rows * row_bytes + io_bytes for rl in rows_log for rows in rl]
     achieved = sum(dec_bytes) / (sum(dec_ms) * 1e-3) / 1e9
-    comp_ms = sum(a.elapsed_time(b) for a, b in zip(rec["c0"], rec["c1"]))
+    comp_ms = sum(a.elapsed_time(b) for a, b in cev)
     tokens = B * args.steps
     resident = pool.stats()["resident_bytes"]
     full_kv_rows = int(sum(resident_rows(P, g, quotas[l], compress=False).sum() for l in range(L)))
@@ -345,7 +513,12 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--profile-summary", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 runs under DIR (no GPU needed)")
     args = ap.parse_args()
+    if args.profile_summary:
+        profile_summary(args.profile_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see the sharding notes in DESIGN.md)", file=sys.stderr)
