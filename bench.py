@@ -451,20 +451,21 @@ def run_compress(args, torch, abk):
 
 def cpu_baseline(workload, budget_s: float):
     """The CPU oracle as it stands, on a bounded sample of the decode step:
-    sequence 0 at one layer of each quota; cost scales with resident rows, so the
-    whole step's time is extrapolated by rows."""
+    (sequence, layer) pairs until the time budget is spent; cost scales with
+    resident rows, so the whole step's time is extrapolated by rows."""
     import oracle
     import synth
     from oracle import TEXT, LayerView
     quotas, P, G = workload
     B = len(P)
-    layers = [int(np.where(quotas == q)[0][0]) for q in (256, 64, 128)]
     sampled_rows = 0
     secs = 0.0
     npairs = 0
-    # one layer of each quota class first, then more (sequence, layer) pairs
-    # until the oracle has spent budget_s seconds
-    pairs = [(0, l) for l in layers] + [(si, l) for si in range(1, B) for l in layers]
+    # (sequence, layer) pairs in a seeded order: the oracle decodes them one by
+    # one until it has spent budget_s seconds
+    pairs = [(si, l) for si in range(B) for l in range(L)]
+    order = np.random.default_rng(12345).permutation(len(pairs))
+    pairs = [pairs[k] for k in order]
     for si, l in pairs:
         Lv = LayerView(int(P[si]), C, int(quotas.max()), int(quotas[l]))
         g, nb = int(G[si]), (int(G[si]) - 1) // C
@@ -495,8 +496,8 @@ def cpu_baseline(workload, budget_s: float):
     step_s = secs * total_rows / sampled_rows
     return {"value": B / step_s, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{npairs} (sequence, layer) pairs of the step, one layer per quota class "
-                      f"per sequence ({sampled_rows} resident rows, {secs:.2f} s of oracle time); "
+            "sample": f"{npairs} (sequence, layer) pairs of the step in a seeded random order "
+                      f"({sampled_rows} resident rows, {secs:.2f} s of oracle time); "
                       f"extrapolated by rows to the 22-sequence 36-layer step ({total_rows} rows)"}
 
 
@@ -510,7 +511,7 @@ def main():
     ap.add_argument("--compress-reps", type=int, default=2)
     ap.add_argument("--no-compress", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=10.0)
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--profile-summary", metavar="DIR",
