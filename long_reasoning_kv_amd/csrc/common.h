@@ -185,10 +185,14 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// nearest-even bf16 bits of a finite float (no NaN handling: queries are finite)
+// bf16 bits of a float, rounded to nearest even by the hardware conversion
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)x);  // v_cvt_pk_bf16_f32: nearest even
+}
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 pair (a in the low half), nearest even, one instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 __device__ __forceinline__ int bitrev_dev(int k, int nbits) {

@@ -169,23 +169,50 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
 //   S^T = K Q^T   with v_mfma_f32_16x16x32_bf16: A = K rows from LDS, B = the
 //                 rotated query (hi + lo bf16 parts, so the product keeps fp32
 //                 accuracy), C lane l = keys 4(l/16)+i x query l%16;
-//   online softmax per query column, all lane-local plus permlane swaps;
+//   online softmax per query column, all lane-local plus permlane swaps; the
+//                 running maximum is only moved (and O^T rescaled) when a
+//                 tile's maximum exceeds it by more than 2^8, which keeps the
+//                 result exact and makes rescales rare;
 //   O^T += V^T P^T: B = P^T straight from the S^T registers (bf16), A = V^T
-//                 from a transposed LDS tile.
+//                 read from the row-major V tile with ds_read_b64_tr_b16.
 // The M-blocks of S^T take keys 32(mb/2) + 8(m/4) + 4(mb%2) + m%4 so that for
 // each 32-key step a lane's 8 probabilities are 8 consecutive keys, which is
-// one 16-byte read of the transposed V tile. K rows in LDS have their 16-byte
-// chunks XOR-swizzled by row so the 16 rows an A-operand read touches use
-// different banks. The next tile is loaded into registers while the current
-// one is computed; LDS is double-buffered (64 KB).
+// what two transposing reads of V deliver. K and V rows in LDS have their
+// 16-byte chunks XOR-swizzled by row (K: row & 15; V: bits 0, 1 and 3 of the
+// row) so that an A-operand read of either touches every bank evenly. The next
+// tile is loaded into registers while the current one is computed; LDS is
+// double-buffered (64 KB). Masks are applied only to partial and pause tiles.
 
+// V^T operand of O^T += V^T P^T for dims 16db + l%16 and keys k0 + 8(l/16) + 0..7
+// of a row-major, swizzled 64-key V tile: two ds_read_b64_tr_b16. Within each
+// 16-lane group, lane s supplies row k0 + 8g + 4hh + s/4 at dims 16db + 4(s%4)
+// and receives 4 keys of dim 16db + s.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int vt_swz(int row) { return 2 * ((row & 3) | ((row >> 1) & 4)); }
+__device__ __forceinline__ uint4 vt_operand(const uint4* __restrict__ tile, int db, int k0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  uint32_t w[4];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int row = k0 + 8 * g + 4 * hh + (s >> 2);
+    const int dim = 16 * db + 4 * (s & 3);
+    const int chunk = (dim >> 3) ^ vt_swz(row);
+    const char* addr = (const char*)(tile + row * 16 + chunk) + 2 * (dim & 7);
+    const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(addr));
+    const uint2 u = __builtin_bit_cast(uint2, r);
+    w[2 * hh] = u.x;
+    w[2 * hh + 1] = u.y;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
 
-
-
-__global__ void __launch_bounds__(256) compress_attn_mfma_kernel(CompressArgs a) {
+__global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs a) {
   constexpr int D = 128, G = 4, TK = 64, RB = D * 2;
-  __shared__ uint4 lk[2][TK * RB / 16];   // K rows, chunks swizzled by (row & 15)
-  __shared__ uint4 lvt[2][D * TK * 2 / 16];  // V^T: [dim][64 keys] bf16, 128 B per dim
+  // K rows (chunks swizzled by row & 15) and V rows (swizzled by vt_swz), two
+  // buffers each; separate arrays so that the compiler can tell them apart
+  __shared__ uint4 lk0[TK * RB / 16], lk1[TK * RB / 16];
+  __shared__ uint4 lv0[TK * RB / 16], lv1[TK * RB / 16];
   const DevPool& P = a.P;
   const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -256,72 +283,58 @@ __global__ void __launch_bounds__(256) compress_attn_mfma_kernel(CompressArgs a)
     }
   }
 
-  // ---- tile t -> rows: thread t loads rows (tid/16 + 16 c), chunk tid%16
-  const int trow = threadIdx.x >> 4, tchunk = threadIdx.x & 15;
-  // staged rows of the next tile, named so they stay in registers
-  uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
-  auto tile_src = [&](int t, const char** kb, const char** vb, size_t* kstride, size_t* vstride,
-                      int* nval) __attribute__((always_inline)) {
+  // ---- tile t: 64 K rows and 64 V rows (a context page, or pause keys). The
+  // page table is read through the constant address space (scalar loads: it
+  // does not change while the kernel runs), one tile ahead of its use.
+  const __attribute__((address_space(4))) int32_t* ctab =
+      (const __attribute__((address_space(4))) int32_t*)tab;
+  auto page_of = [&](int t) __attribute__((always_inline)) {
+    const int idx = t < npp ? t : P.max_pers + min(t - npp, nop - 1);
+    return ctab[idx];
+  };
+  struct TileSrc {
+    const char* kb;
+    const char* vb;
+    int kstride, vstride, nval;
+  };
+  auto tile_src = [&](int t, int page) __attribute__((always_inline)) {
+    TileSrc ts;
     if (t < ntc) {
-      int page, rows;
-      if (t < npp) {
-        page = sgpr(tab[t]);
-        rows = (t == npp - 1) ? n_pers - t * TK : TK;
-      } else {
-        page = sgpr(tab[P.max_pers + (t - npp)]);
-        rows = TK;
-      }
       const size_t off = (((size_t)page * P.Hkv + hk) * TK) * RB;
-      *kb = (const char*)P.kpool + off;
-      *vb = (const char*)P.vpool + off;
-      *kstride = RB;
-      *vstride = RB;
-      *nval = rows;
+      ts.kb = (const char*)P.kpool + off;
+      ts.vb = (const char*)P.vpool + off;
+      ts.kstride = RB;
+      ts.vstride = RB;
+      ts.nval = (t == npp - 1) ? n_pers - t * TK : TK;
     } else {
       const int k0 = (t - ntc) * TK;
-      *kb = (const char*)a.kp_rot + (((size_t)i * P.Hkv + hk) * a.Kp + k0) * RB;
-      *vb = (const char*)a.vp + (((size_t)i * a.Kp + k0) * P.Hkv + hk) * RB;
-      *kstride = RB;
-      *vstride = (size_t)P.Hkv * RB;
-      *nval = min(TK, a.Kp - k0);
+      ts.kb = (const char*)a.kp_rot + (((size_t)i * P.Hkv + hk) * a.Kp + k0) * RB;
+      ts.vb = (const char*)a.vp + (((size_t)i * a.Kp + k0) * P.Hkv + hk) * RB;
+      ts.kstride = RB;
+      ts.vstride = P.Hkv * RB;
+      ts.nval = min(TK, a.Kp - k0);
     }
+    return ts;
   };
-  auto gload = [&](int t) __attribute__((always_inline)) {
-    const char *kb, *vb;
-    size_t ks, vs;
-    int nval;
-    tile_src(t, &kb, &vb, &ks, &vs, &nval);
-    auto piece = [&](int c, uint4& kx, uint4& vx) __attribute__((always_inline)) {
-      int r = trow + 16 * c;
-      r = r < nval ? r : nval - 1;
-      kx = *(const uint4*)(kb + r * ks + tchunk * 16);
-      vx = *(const uint4*)(vb + r * vs + tchunk * 16);
-    };
-    piece(0, sk0, sv0);
-    piece(1, sk1, sv1);
-    piece(2, sk2, sv2);
-    piece(3, sk3, sv3);
-  };
-  auto swrite = [&](int buf) __attribute__((always_inline)) {
-    uint16_t* vt = (uint16_t*)lvt[buf];
-    auto piece = [&](int c, const uint4& kx, const uint4& vx) __attribute__((always_inline)) {
-      const int r = trow + 16 * c;
-      lk[buf][r * 16 + (tchunk ^ (r & 15))] = kx;
-      // V^T: dims 8 tchunk .. +8 of key r -> [dim][key]
-      const int d0 = 8 * tchunk;
-      vt[(d0 + 0) * TK + r] = (uint16_t)vx.x;
-      vt[(d0 + 1) * TK + r] = (uint16_t)(vx.x >> 16);
-      vt[(d0 + 2) * TK + r] = (uint16_t)vx.y;
-      vt[(d0 + 3) * TK + r] = (uint16_t)(vx.y >> 16);
-      vt[(d0 + 4) * TK + r] = (uint16_t)vx.z;
-      vt[(d0 + 5) * TK + r] = (uint16_t)(vx.z >> 16);
-      vt[(d0 + 6) * TK + r] = (uint16_t)vx.w;
-      vt[(d0 + 7) * TK + r] = (uint16_t)(vx.w >> 16);
-    };
-    piece(0, sk0, sv0);
-    piece(1, sk1, sv1);
-    piece(2, sk2, sv2);
-    piece(3, sk3, sv3);
+  // Tile t straight from global memory into LDS (global_load_lds_dwordx4): in
+  // load j of wavefront w, lane l fills LDS chunk 256j + 64w + l, i.e. row
+  // 16j + 4w + l/16 at swizzled position l%16, so it fetches the source chunk
+  // that belongs there. Rows past the tile's valid count repeat its last row.
+  const int r_in = 4 * wave + (lane >> 4);
+  const int kchunk = (lane & 15) ^ (r_in & 15);
+  const int vchunk = (lane & 15) ^ vt_swz(r_in);
+  auto issue = [&](int t, int page, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
+    const TileSrc ts = tile_src(t, page);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = min(16 * j + r_in, ts.nval - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(ts.kb + row * ts.kstride + 16 * kchunk),
+                                       (__attribute__((address_space(3))) void*)(dk + 256 * j + 64 * wave),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(ts.vb + row * ts.vstride + 16 * vchunk),
+                                       (__attribute__((address_space(3))) void*)(dv + 256 * j + 64 * wave),
+                                       16, 0, 0);
+    }
   };
 
   // key of S^T M-block mb, row m (see above)
@@ -332,16 +345,24 @@ __global__ void __launch_bounds__(256) compress_attn_mfma_kernel(CompressArgs a)
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc_o[nb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // running maximum (log2 units) and sum per query column; the finite start
+  // keeps exp2(s - m) well defined while a column has seen only masked keys
+  float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
 
-  auto compute = [&](int t, int buf) __attribute__((always_inline)) {
+  // One tile: start loading tile t+1 into (nk, nv), compute tile t from
+  // (ck, cv). The restrict qualifiers tell the compiler that the loads in
+  // flight do not write the buffers being read, so it waits for them only at
+  // the barrier that ends the step. The load is unconditional (the last one
+  // repeats the last tile into the spare buffer): a load issued on one path
+  // only makes the compiler wait for it before every later LDS read.
+  int page_next = page_of(min(1, ntiles - 1));
+  auto step = [&](int t, const uint4* __restrict__ ck, const uint4* __restrict__ cv,
+                  uint4* __restrict__ nk, uint4* __restrict__ nv) __attribute__((always_inline)) {
+    const int tn = min(t + 1, ntiles - 1);
+    issue(tn, page_next, nk, nv);
+    page_next = page_of(min(t + 2, ntiles - 1));
     const bool ctx = t < ntc;
-    int nval;
-    {
-      const char *kb, *vb;
-      size_t ks, vs;
-      tile_src(t, &kb, &vb, &ks, &vs, &nval);
-    }
+    const int nval = ctx ? (t == npp - 1 ? n_pers - t * TK : TK) : min(TK, a.Kp - (t - ntc) * TK);
     const int kbase = ctx ? 0 : (t - ntc) * TK;  // pause index of key 0 of a pause tile
     f32x4_t s[4][2];
 #pragma unroll
@@ -353,7 +374,7 @@ __global__ void __launch_bounds__(256) compress_attn_mfma_kernel(CompressArgs a)
       const int kr = keyof(mb, l16);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint4 ka = lk[buf][kr * 16 + ((4 * ks + g4) ^ (kr & 15))];
+        const uint4 ka = ck[kr * 16 + ((4 * ks + g4) ^ (kr & 15))];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           s[mb][nb] = mfma_bf16(ka, qh[nb][ks], s[mb][nb]);
@@ -361,71 +382,83 @@ __global__ void __launch_bounds__(256) compress_attn_mfma_kernel(CompressArgs a)
         }
       }
     }
-    // mask, online softmax per query column (lane-local after the row swaps)
-    uint4 pb[2][2];  // [N-block][32-key step]: bf16 probabilities, 8 keys
+    // mask (partial context pages and pause tiles only; the test is uniform)
+    if (!ctx || nval < TK) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = keyof(mb, 4 * g4 + e);
+            const bool ok = key < nval && (ctx || kbase + key <= qpause[nb]);
+            s[mb][nb][e] = ok ? s[mb][nb][e] : -INFINITY;
+          }
+    }
+    // online softmax per query column (lane-local after the row swaps)
+    float mn[2], alpha[2];
+    bool moved = false;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = keyof(mb, 4 * g4 + e);
-          bool ok = key < nval;
-          if (!ctx) ok = ok && (kbase + key <= qpause[nb]);
-          const float v = ok ? s[mb][nb][e] : -INFINITY;
-          s[mb][nb][e] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[mb][nb][e]);
       mx = rows4_max(mx);
-      const float mn = fmaxf(m_run[nb], mx);
-      const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_run[nb] - mn);
-      m_run[nb] = mn;
+      const bool up = mx > m_run[nb] + 8.f;
+      mn[nb] = up ? mx : m_run[nb];
+      alpha[nb] = fast_exp2(m_run[nb] - mn[nb]);
+      moved = moved || up;
+      m_run[nb] = mn[nb];
+    }
+    if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        l_run[nb] *= alpha[nb];
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc_o[nb][db] *= alpha[nb];
+      }
+    }
+    uint4 pb[2][2];  // [N-block][32-key step]: bf16 probabilities, 8 keys
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
       float ps = 0.f;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = mn == -INFINITY ? 0.f : fast_exp2(s[mb][nb][e] - mn);
+          const float p = fast_exp2(s[mb][nb][e] - mn[nb]);
           s[mb][nb][e] = p;  // the score register now holds its probability
           ps += p;
         }
-      l_run[nb] = l_run[nb] * alpha + ps;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) acc_o[nb][db] *= alpha;
+      l_run[nb] += ps;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         // keys 32kk + 8 g4 + j: j < 4 from M-block 2kk, j >= 4 from 2kk+1
         const f32x4_t u0 = s[2 * kk][nb], u1 = s[2 * kk + 1][nb];
-        pb[nb][kk] = make_uint4(bf16_bits(u0[0]) | (bf16_bits(u0[1]) << 16),
-                                bf16_bits(u0[2]) | (bf16_bits(u0[3]) << 16),
-                                bf16_bits(u1[0]) | (bf16_bits(u1[1]) << 16),
-                                bf16_bits(u1[2]) | (bf16_bits(u1[3]) << 16));
+        pb[nb][kk] = make_uint4(pack_bf16x2(u0[0], u0[1]), pack_bf16x2(u0[2], u0[3]),
+                                pack_bf16x2(u1[0], u1[1]), pack_bf16x2(u1[2], u1[3]));
       }
     }
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const int d = 16 * db + l16;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint4 va = lvt[buf][(d * TK + 32 * kk + 8 * g4) / 8];
+        const uint4 va = vt_operand(cv, db, 32 * kk, lane);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc_o[nb][db] = mfma_bf16(va, pb[nb][kk], acc_o[nb][db]);
       }
     }
   };
 
-  gload(0);
-  swrite(0);
-  if (ntiles > 1) gload(1);
+  issue(0, page_of(0), lk0, lv0);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) {
-      swrite(buf ^ 1);  // last read before the previous barrier
-      if (t + 2 < ntiles) gload(t + 2);
-    }
-    compute(t, buf);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, lk0, lv0, lk1, lv1);
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    step(t + 1, lk1, lv1, lk0, lv0);
     __syncthreads();
   }
 
