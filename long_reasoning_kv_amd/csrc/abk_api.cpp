@@ -54,6 +54,7 @@ struct abk_pool {
   bool host_only = false;
   int32_t split_rows = 0;  // 0: automatic schedule; > 0: fixed split-KV work items of this many rows
   int32_t stream_wgs = 0;  // resident workgroups of the stream-K decode (0: not used)
+  int32_t mfma_waves = 0;  // resident wavefronts of the MFMA decode (0: not used)
   hipStream_t stream = nullptr;
   abk::DevPool dev{};
   int32_t* quota_d = nullptr;
@@ -223,7 +224,9 @@ abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_poo
     probe.pr = s.pr;
     probe.D = s.D;
     probe.dtype = s.dtype;
-    if (abk::decode_stream_supported(probe, s.Hq / s.Hkv))
+    if (abk::decode_mfma_supported(probe, s.Hq / s.Hkv))
+      p->mfma_waves = cus * abk::decode_mfma_waves_per_cu();
+    else if (abk::decode_stream_supported(probe, s.Hq / s.Hkv))
       p->stream_wgs = cus * abk::decode_stream_blocks_per_cu(probe);
   }
   d.L = s.L;
@@ -327,6 +330,54 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
   const abk::Shape& s = p->shape;
   const int32_t G = s.Hq / s.Hkv;
   const size_t qb = (size_t)s.Hq * s.D * s.esize();
+  if (p->mfma_waves > 0 && p->split_rows == 0) {
+    // MFMA decode: equal runs of 32-row tiles per wavefront over the flattened
+    // (sequence, head, tile) work; a sequence's tiles cover its persistent rows,
+    // then its open rows
+    constexpr int32_t TK = 32;
+    for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
+      const int32_t m = std::min(n - c0, abk::kMaxBatch);
+      abk::StreamArgs a;
+      a.useg[0] = 0;
+      for (int32_t i = 0; i < m; ++i) {
+        const int32_t id = seq_ids[c0 + i];
+        const int32_t pers = p->host.seq(id).layers[layer].pers_rows;
+        const int32_t open = p->host.open_rows(id, layer);
+        const int32_t units = (pers + TK - 1) / TK + (open + TK - 1) / TK;
+        a.slot[i] = id;
+        a.useg[i + 1] = a.useg[i] + units * s.Hkv;
+      }
+      const int32_t U = a.useg[m];
+      const int32_t kMinUnits = 4;  // per wavefront, to amortise its set-up
+      int32_t W = std::max(1, std::min(p->mfma_waves, (U + kMinUnits - 1) / kMinUnits));
+      const int32_t T = (U + W - 1) / W;
+      W = (U + T - 1) / T;
+      int32_t maxp = 1;
+      for (int32_t i = 0; i < m; ++i) {
+        const int32_t units = (a.useg[i + 1] - a.useg[i]) / s.Hkv;
+        for (int32_t h = 0; h < s.Hkv; ++h) {
+          const int32_t S = a.useg[i] + h * units;
+          maxp = std::max(maxp, (S + units - 1) / T - S / T + 1);
+        }
+      }
+      if (maxp > abk::kMaxSplits) return set_err(ABK_ERR_UNSUPPORTED, "too many partials per head");
+      if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
+                               (size_t)m * s.Hkv * maxp * G * (s.D + 2) * sizeof(float)))
+        return st;
+      a.P = p->dev;
+      a.q = (const char*)q + c0 * qb;
+      a.out = (char*)out + c0 * qb;
+      a.lse = lse + (size_t)c0 * s.Hq;
+      a.part = p->part;
+      a.layer = layer;
+      a.n = m;
+      a.T = T;
+      a.U = U;
+      a.maxp = maxp;
+      ABK_HIP(abk::launch_decode_mfma(a, W, p->stream));
+    }
+    return ABK_OK;
+  }
   if (p->stream_wgs > 0 && p->split_rows == 0) {
     // stream-K: equal runs of 32-row units over the flattened (sequence, head, unit) work
     const int32_t nq = s.pr / 32;

@@ -201,6 +201,7 @@ __device__ __forceinline__ int bitrev_dev(int k, int nbits) {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));  // ds_read_b64_tr_b16 result
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),

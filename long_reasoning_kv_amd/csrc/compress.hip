@@ -187,7 +187,6 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
 // of a row-major, swizzled 64-key V tile: two ds_read_b64_tr_b16. Within each
 // 16-lane group, lane s supplies row k0 + 8g + 4hh + s/4 at dims 16db + 4(s%4)
 // and receives 4 keys of dim 16db + s.
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int vt_swz(int row) { return 2 * ((row & 3) | ((row >> 1) & 4)); }
 __device__ __forceinline__ uint4 vt_operand(const uint4* __restrict__ tile, int db, int k0, int lane) {
   const int g = lane >> 4, s = lane & 15;

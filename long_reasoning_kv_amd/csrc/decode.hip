@@ -1013,6 +1013,276 @@ __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) 
   }
 }
 
+// ---- a2 + a3 on bf16 MFMA: wavefront-level stream-K over 32-row tiles ------------
+//
+// Every wavefront is an independent stream over an equal run of the flattened
+// (sequence, KV head, 32-row tile) work, so no barrier is needed anywhere. A
+// tile's 32 K rows and 32 V rows go straight from HBM into the wavefront's own
+// 16 KB of LDS (global_load_lds_dwordx4). The wavefront first reads the whole
+// tile into registers (K as MFMA A operands, V through ds_read_b64_tr_b16 as
+// V^T operands), then starts loading the next tile into the same LDS and
+// computes while it is in flight:
+//   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, two M-blocks of 16 keys; B = the
+//                 four rotated query heads of the KV head (hi + lo bf16 parts)
+//                 in columns 0..3; M-block mb row m is key 8(m/4) + 4mb + m%4,
+//                 so lane l ends up with the 8 consecutive keys 8(l/16)+0..7 of
+//                 head l%16;
+//   online softmax per head column (lane-local, then permlane swaps); the
+//                 running maximum only moves when a tile exceeds it by 2^8;
+//   O^T += V^T P^T  v_mfma_f32_16x16x32_bf16; B = P^T straight from the S^T
+//                 registers, A = V^T (dims 16db + l%16, keys 8(l/16) + 0..7).
+// K rows in LDS have their 16-byte chunks XOR-swizzled by bits 0,1,3,4 of the
+// row and V rows by 2*(bits 0,1,3), so both operand reads touch every bank
+// evenly. A segment inside one wavefront's run writes out and lse; other pieces
+// write partials for decode_stream_merge_kernel (index = wavefront - first).
+
+__device__ __forceinline__ int dm_kswz(int row) { return (((row >> 3) & 3) << 2) | (row & 3); }
+__device__ __forceinline__ int dm_vswz(int row) { return 2 * ((row & 3) | ((row >> 1) & 4)); }
+
+__global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
+  constexpr int D = 128, G = 4, TK = 32, RB = D * 2, PR = 64;
+  constexpr int WCH = TK * RB / 16;  // 16-byte chunks of one tile (K or V) = 512
+  __shared__ uint4 lk[4 * WCH], lv[4 * WCH];  // one 8 KB K slice and V slice per wavefront
+  const DevPool& P = a.P;
+  const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int w = blockIdx.x * 4 + wave;  // wavefront id in the stream-K order
+  const int Hq = P.Hkv * G;
+  const int F0 = w * a.T;
+  const int Fend = min(a.U, F0 + a.T);
+  if (F0 >= Fend) return;
+  const char* kpool = (const char*)P.kpool;
+  const char* vpool = (const char*)P.vpool;
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+
+  // ---- cursor over (sequence, KV head, tile); all fields wave-uniform
+  struct Cur {
+    int i, h, lu, units, ptiles, n_pers, n_open, slot;
+  };
+  auto load_seq = [&](Cur& c) __attribute__((always_inline)) {
+    c.units = (a.useg[c.i + 1] - a.useg[c.i]) / P.Hkv;
+    c.slot = a.slot[c.i];
+    cptr meta = (cptr)meta_of(P, c.slot, a.layer);
+    c.n_pers = meta[0];
+    c.n_open = meta[1];
+    c.ptiles = (c.n_pers + TK - 1) / TK;
+  };
+  auto cursor_at = [&](int F) __attribute__((always_inline)) {
+    Cur c;
+    c.i = 0;
+    while (a.useg[c.i + 1] <= F) ++c.i;
+    load_seq(c);
+    const int rel = F - a.useg[c.i];
+    c.h = rel / c.units;
+    c.lu = rel % c.units;
+    return c;
+  };
+  auto advance = [&](Cur& c) __attribute__((always_inline)) {
+    if (++c.lu == c.units) {
+      c.lu = 0;
+      if (++c.h == P.Hkv) {
+        c.h = 0;
+        ++c.i;
+        if (c.i < a.n) load_seq(c);
+      }
+    }
+  };
+  // byte offset of the tile's first row in the pools, and its valid rows
+  auto locate = [&](const Cur& c, size_t* off, int* nval) __attribute__((always_inline)) {
+    cptr tab = (cptr)ptab_of(P, c.slot, a.layer);
+    int page, r0;
+    if (c.lu < c.ptiles) {
+      page = tab[c.lu >> 1];
+      r0 = (c.lu & 1) * TK;
+      *nval = min(TK, c.n_pers - c.lu * TK);
+    } else {
+      const int j = c.lu - c.ptiles;
+      page = tab[P.max_pers + (j >> 1)];
+      r0 = (j & 1) * TK;
+      *nval = min(TK, c.n_open - j * TK);
+    }
+    *off = (((size_t)page * P.Hkv + c.h) * PR + r0) * RB;
+  };
+
+  // ---- loads: load j of the wavefront fills chunks 64j.. of its slice, i.e.
+  // row 4j + lane/16 at swizzled position lane%16; rows past the valid count
+  // repeat the last valid row
+  const int dr = lane >> 4;
+  auto issue = [&](const Cur& c) __attribute__((always_inline)) {
+    size_t off;
+    int nval;
+    locate(c, &off, &nval);
+#pragma unroll
+    for (int j = 0; j < TK / 4; ++j) {
+      const int row = 4 * j + dr;
+      const int rc = min(row, nval - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(kpool + off + rc * RB + 16 * ((lane & 15) ^ dm_kswz(row))),
+          (__attribute__((address_space(3))) void*)(lk + wave * WCH + 64 * j), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(vpool + off + rc * RB + 16 * ((lane & 15) ^ dm_vswz(row))),
+          (__attribute__((address_space(3))) void*)(lv + wave * WCH + 64 * j), 16, 0, 0);
+    }
+  };
+
+  // ---- per-segment state
+  uint4 qh[4], ql[4];  // B operand of S^T: head l16 (< 4), dims 32ks + 8g4 + 0..7
+  f32x4_t acc[8];      // O^T: dims 16db + 4g4 + i of head l16
+  float m_run = -1e30f, l_run = 0.f;
+  auto start_segment = [&](const Cur& c) __attribute__((always_inline)) {
+    cptr meta = (cptr)meta_of(P, c.slot, a.layer);
+    const int qpos = meta[2];
+    const float qs = 1.4426950408889634f / sqrtf((float)D);
+    const int hh = l16 < G ? l16 : 0;
+    const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)c.i * Hq + c.h * G + hh) * D;
+    const float2* rope = P.rope + (size_t)qpos * (D / 2);
+    float x[4][8];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) unpack16(*(const uint4*)(qrow + 32 * ks + 8 * g4), x[ks], bf16_t());
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float y0[8], y1[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float2 cs = rope[32 * ks + 8 * g4 + j];
+        y0[j] = l16 < G ? qs * (x[ks][j] * cs.x - x[ks + 2][j] * cs.y) : 0.f;
+        y1[j] = l16 < G ? qs * (x[ks + 2][j] * cs.x + x[ks][j] * cs.y) : 0.f;
+      }
+      uint32_t h0[4], o0[4], h1[4], o1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h0[j] = pack_bf16x2(y0[2 * j], y0[2 * j + 1]);
+        h1[j] = pack_bf16x2(y1[2 * j], y1[2 * j + 1]);
+        o0[j] = pack_bf16x2(y0[2 * j] - __uint_as_float(h0[j] << 16),
+                            y0[2 * j + 1] - __uint_as_float(h0[j] & 0xffff0000u));
+        o1[j] = pack_bf16x2(y1[2 * j] - __uint_as_float(h1[j] << 16),
+                            y1[2 * j + 1] - __uint_as_float(h1[j] & 0xffff0000u));
+      }
+      qh[ks] = make_uint4(h0[0], h0[1], h0[2], h0[3]);
+      ql[ks] = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+      qh[ks + 2] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
+      ql[ks + 2] = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run = -1e30f;
+    l_run = 0.f;
+  };
+  auto end_segment = [&](const Cur& c) __attribute__((always_inline)) {
+    const float L = rows4_sum(l_run);
+    const int segS = a.useg[c.i] + c.h * c.units;
+    const int wa = segS / a.T, wb = (segS + c.units - 1) / a.T;
+    if (l16 < G) {
+      const int hq = c.h * G + l16;
+      if (wa == wb) {
+        const float inv = 1.f / L;
+        bf16_t* dst = (bf16_t*)a.out + ((size_t)c.i * Hq + hq) * D;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          *(uint2*)(dst + 16 * db + 4 * g4) =
+              make_uint2(pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv),
+                         pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv));
+        if (g4 == 0) a.lse[(size_t)c.i * Hq + hq] = (m_run + __log2f(L)) * 0.6931471805599453f;
+      } else {
+        float* pp = a.part + ((((size_t)c.i * P.Hkv + c.h) * a.maxp + (w - wa)) * G + l16) * (D + 2);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) *(f32x4_t*)(pp + 16 * db + 4 * g4) = acc[db];
+        if (g4 == 0) {
+          pp[D] = m_run;
+          pp[D + 1] = L;
+        }
+      }
+    }
+  };
+
+  Cur cc = cursor_at(F0);  // tile being computed
+  Cur ci = cc;             // tile being loaded
+  issue(ci);
+  int last_i = -1, last_h = -1;
+  const int vrow0 = 8 * g4 + (l16 >> 2);  // V^T operand rows (+4 for the second half)
+  for (int t = F0; t < Fend; ++t) {
+    if (cc.i != last_i || cc.h != last_h) {  // query loads join the tile's wait
+      start_segment(cc);
+      last_i = cc.i;
+      last_h = cc.h;
+    }
+    // ---- the whole tile from LDS into registers
+    uint4 ka[2][4], va[8];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int kr = 8 * (l16 >> 2) + 4 * mb + (l16 & 3);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) ka[mb][ks] = lk[wave * WCH + kr * 16 + ((4 * ks + g4) ^ dm_kswz(kr))];
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      uint32_t wv[4];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = vrow0 + 4 * hh;
+        const int chunk = (2 * db + ((l16 & 3) >> 1)) ^ dm_vswz(row);
+        const int boff = (wave * WCH + row * 16 + chunk) * 16 + 8 * (l16 & 1);
+        const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)((const char*)lv + boff));
+        const uint2 u = __builtin_bit_cast(uint2, r);
+        wv[2 * hh] = u.x;
+        wv[2 * hh + 1] = u.y;
+      }
+      va[db] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    size_t off;
+    int nval;
+    locate(cc, &off, &nval);
+    // ---- the next tile into the same LDS (once every read above has landed)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    if (t + 1 < Fend) advance(ci);
+    issue(ci);  // unconditional: past the end it repeats the last tile
+    // ---- S^T, softmax, O^T
+    f32x4_t sc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      sc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        sc[mb] = mfma_bf16(ka[mb][ks], qh[ks], sc[mb]);
+        sc[mb] = mfma_bf16(ka[mb][ks], ql[ks], sc[mb]);
+      }
+    }
+    if (nval < TK) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[mb][e] = 8 * g4 + 4 * mb + e < nval ? sc[mb][e] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = rows4_max(mx);
+    const bool up = mx > m_run + 8.f;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float mn = up ? mx : m_run;
+      const float alpha = fast_exp2(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+    }
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] = fast_exp2(sc[0][e] - m_run);
+      p[4 + e] = fast_exp2(sc[1][e] - m_run);
+    }
+    l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    const uint4 pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] = mfma_bf16(va[db], pb, acc[db]);
+    if (cc.lu == cc.units - 1 || t == Fend - 1) end_segment(cc);
+    advance(cc);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may land in LDS after the wavefront ends
+}
+
 // ---- launchers ---------------------------------------------------------------------
 
 template <typename T, int D>
@@ -1081,6 +1351,24 @@ int32_t decode_stream_blocks_per_cu(const DevPool& P) {
                      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_stream_kernel<2>, 256, 0)
                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_stream_kernel<1>, 256, 0);
   return (e == hipSuccess && nb > 0) ? nb : 1;
+}
+
+bool decode_mfma_supported(const DevPool& P, int32_t G) {
+  return P.dtype == 1 && P.D == 128 && G == 4 && P.pr == 64;
+}
+
+int32_t decode_mfma_waves_per_cu() {
+  int nb = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_mfma_kernel, 256, 0);
+  return 4 * ((e == hipSuccess && nb > 0) ? nb : 1);
+}
+
+hipError_t launch_decode_mfma(const StreamArgs& a, int32_t nwaves, hipStream_t s) {
+  if (a.n == 0 || nwaves == 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_mfma_kernel, dim3((nwaves + 3) / 4), dim3(256), 0, s, a);
+  if (a.maxp > 1)
+    hipLaunchKernelGGL(decode_stream_merge_kernel, dim3(a.n, a.P.Hkv), dim3(512), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_stream(const StreamArgs& a, int32_t nwg, hipStream_t s) {

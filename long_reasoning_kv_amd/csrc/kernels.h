@@ -128,6 +128,11 @@ hipError_t launch_decode(const DecodeArgs& a, int32_t total_work, hipStream_t s)
 bool decode_stream_supported(const DevPool& P, int32_t G);
 int32_t decode_stream_blocks_per_cu(const DevPool& P);
 hipError_t launch_decode_stream(const StreamArgs& a, int32_t nwg, hipStream_t s);
+// bf16, d = 128, four query heads per KV head, 64-row pages: MFMA decode with
+// wavefront-level stream-K over 16-row tiles (U, T, useg in tiles; T per wavefront)
+bool decode_mfma_supported(const DevPool& P, int32_t G);
+int32_t decode_mfma_waves_per_cu();
+hipError_t launch_decode_mfma(const StreamArgs& a, int32_t nwaves, hipStream_t s);
 hipError_t launch_free(const FreeArgs& a, hipStream_t s);
 hipError_t launch_prompt(const PromptArgs& a, hipStream_t s);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
