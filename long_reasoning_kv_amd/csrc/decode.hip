@@ -976,10 +976,13 @@ __global__ void __launch_bounds__(256) decode_stream_kernel(StreamArgs a) {
   }
 }
 
-// Merge the partials of (sequence i, KV head h) written by workgroups wa..wb.
+// Merge the partials of (sequence i, KV head h) written by stream-K workers
+// wa..wb (workgroups of decode_stream_kernel, wavefronts of decode_mfma_kernel).
+// Every partial's maximum and sum are fetched at once, so the merge costs a few
+// dependent loads however many partials there are.
 __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) {
   constexpr int D = 128, G = 4;
-  __shared__ float sm_w[kMaxSplits * G], sm_M[G], sm_L[G];
+  __shared__ float sm_w[kMaxSplits * G], sm_l[kMaxSplits * G];
   const int i = blockIdx.x, h = blockIdx.y;
   const int Hkv = a.P.Hkv, Hq = Hkv * G;
   const int units = (a.useg[i + 1] - a.useg[i]) / Hkv;
@@ -987,29 +990,30 @@ __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) 
   const int wa = segS / a.T, wb = (segS + units - 1) / a.T;
   const int ns = wb - wa + 1;
   if (ns == 1) return;
-  auto part = [&](int s, int g) {
-    return a.part + ((((size_t)i * Hkv + h) * a.maxp + s) * G + g) * (D + 2);
-  };
+  const float* base = a.part + ((size_t)i * Hkv + h) * a.maxp * G * (D + 2);
+  for (int t = threadIdx.x; t < ns * G; t += blockDim.x) {
+    sm_w[t] = base[t * (D + 2) + D];
+    sm_l[t] = base[t * (D + 2) + D + 1];
+  }
+  __syncthreads();
   if (threadIdx.x < G) {
     const int g = threadIdx.x;
     float M = -INFINITY;
-    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, part(s2, g)[D]);
+    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, sm_w[s2 * G + g]);
     float Ls = 0.f;
-    for (int s2 = 0; s2 < ns; ++s2) {
-      const float f = fast_exp2(part(s2, g)[D] - M);
-      sm_w[s2 * G + g] = f;
-      Ls += part(s2, g)[D + 1] * f;
-    }
-    sm_M[g] = M;
-    sm_L[g] = Ls;
+    for (int s2 = 0; s2 < ns; ++s2) Ls += sm_l[s2 * G + g] * fast_exp2(sm_w[s2 * G + g] - M);
+    const float inv = 1.f / Ls;
+    for (int s2 = 0; s2 < ns; ++s2) sm_w[s2 * G + g] = fast_exp2(sm_w[s2 * G + g] - M) * inv;
     a.lse[(size_t)i * Hq + h * G + g] = (M + __log2f(Ls)) * 0.6931471805599453f;
   }
   __syncthreads();
   for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
     const int g = t / D, d = t % D;
+    const float* pp = base + g * (D + 2) + d;
     float O = 0.f;
-    for (int s2 = 0; s2 < ns; ++s2) O += part(s2, g)[d] * sm_w[s2 * G + g];
-    ((bf16_t*)a.out)[((size_t)i * Hq + h * G + g) * D + d] = from_f32<bf16_t>(O / sm_L[g]);
+#pragma unroll 4
+    for (int s2 = 0; s2 < ns; ++s2) O += pp[(size_t)s2 * G * (D + 2)] * sm_w[s2 * G + g];
+    ((bf16_t*)a.out)[((size_t)i * Hq + h * G + g) * D + d] = from_f32<bf16_t>(O);
   }
 }
 
