@@ -62,7 +62,7 @@ def resident_rows(P, G, q, compress=True):
 
 
 KERNEL_SOURCES = {
-    "decode_stream": ("decode.hip", "common.h", "kernels.h"),
+    "decode_mfma": ("decode.hip", "common.h", "kernels.h"),
     "compress_attn_mfma": ("compress.hip", "common.h", "kernels.h"),
 }
 
@@ -164,7 +164,7 @@ def profile_summary(d):
         f"  write pass: {_cmd(d, 'copy_write')}",
     ]
     for fam, tag, trace, prefix, match, what in (
-            ("decode_stream", "decode_stream_36L_22seq", "dec_trace", "dec", "decode_stream",
+            ("decode_mfma", "decode_mfma_36L_22seq", "dec_trace", "dec", "decode_",
              "decode step of the 36-layer per-layer-quota workload, 22 sequences, bf16, d = 128, "
              "32 q / 8 KV heads, 64-row pages (bench.py default workload)"),
             ("compress_attn_mfma", "compress_attn_mfma_64seq_36L", "cmp_trace", "cmp",
@@ -196,7 +196,7 @@ def profile_summary(d):
         bench_json = os.path.join(d, trace + ".json")
         bj = json.load(open(bench_json)) if os.path.exists(bench_json) else None
         extra = []
-        if fam == "decode_stream" and bj:
+        if fam == "decode_mfma" and bj:
             rf = bj["roofline"]
             extra = [f"bench.py in the traced run: {rf['avg_launch_us']:.1f} us per decode call "
                      f"(HIP events around decode + merge), algorithmic "
@@ -359,8 +359,8 @@ def run_decode(args, torch, abk):
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": traffic_from_profiles("decode_stream", float(np.mean(dec_bytes))),
-            "kernel": "decode_stream_kernel (+ split merge)",
+            "traffic": traffic_from_profiles("decode_mfma", float(np.mean(dec_bytes))),
+            "kernel": "decode_mfma_kernel (+ decode_stream_merge_kernel)",
             "algorithmic_bytes_per_launch": float(np.mean(dec_bytes)),
             "avg_launch_us": float(np.mean(dec_ms)) * 1e3,
         },

@@ -978,11 +978,11 @@ __global__ void __launch_bounds__(256) decode_stream_kernel(StreamArgs a) {
 
 // Merge the partials of (sequence i, KV head h) written by stream-K workers
 // wa..wb (workgroups of decode_stream_kernel, wavefronts of decode_mfma_kernel).
-// Every partial's maximum and sum are fetched at once, so the merge costs a few
-// dependent loads however many partials there are.
+// Thread (g, d) fetches, for sixteen partials at a time, their maximum, sum and
+// its own output element in one round of independent loads, then combines
+// them online; with up to sixteen partials the merge is one memory round trip.
 __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) {
-  constexpr int D = 128, G = 4;
-  __shared__ float sm_w[kMaxSplits * G], sm_l[kMaxSplits * G];
+  constexpr int D = 128, G = 4, K = 16;
   const int i = blockIdx.x, h = blockIdx.y;
   const int Hkv = a.P.Hkv, Hq = Hkv * G;
   const int units = (a.useg[i + 1] - a.useg[i]) / Hkv;
@@ -991,29 +991,34 @@ __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) 
   const int ns = wb - wa + 1;
   if (ns == 1) return;
   const float* base = a.part + ((size_t)i * Hkv + h) * a.maxp * G * (D + 2);
-  for (int t = threadIdx.x; t < ns * G; t += blockDim.x) {
-    sm_w[t] = base[t * (D + 2) + D];
-    sm_l[t] = base[t * (D + 2) + D + 1];
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, sm_w[s2 * G + g]);
-    float Ls = 0.f;
-    for (int s2 = 0; s2 < ns; ++s2) Ls += sm_l[s2 * G + g] * fast_exp2(sm_w[s2 * G + g] - M);
-    const float inv = 1.f / Ls;
-    for (int s2 = 0; s2 < ns; ++s2) sm_w[s2 * G + g] = fast_exp2(sm_w[s2 * G + g] - M) * inv;
-    a.lse[(size_t)i * Hq + h * G + g] = (M + __log2f(Ls)) * 0.6931471805599453f;
-  }
-  __syncthreads();
   for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
     const int g = t / D, d = t % D;
-    const float* pp = base + g * (D + 2) + d;
-    float O = 0.f;
-#pragma unroll 4
-    for (int s2 = 0; s2 < ns; ++s2) O += pp[(size_t)s2 * G * (D + 2)] * sm_w[s2 * G + g];
-    ((bf16_t*)a.out)[((size_t)i * Hq + h * G + g) * D + d] = from_f32<bf16_t>(O);
+    float M = -INFINITY, Ls = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += K) {
+      float mv[K], lv[K], ov[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float* pp = base + (min(s0 + k, ns - 1) * G + g) * (D + 2);
+        mv[k] = pp[D];
+        lv[k] = pp[D + 1];
+        ov[k] = pp[d];
+      }
+      float cm = M;
+#pragma unroll
+      for (int k = 0; k < K; ++k) cm = s0 + k < ns ? fmaxf(cm, mv[k]) : cm;
+      const float r = fast_exp2(M - cm);  // first round: M = -inf, r = 0
+      Ls *= r;
+      O *= r;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float wgt = s0 + k < ns ? fast_exp2(mv[k] - cm) : 0.f;
+        Ls += wgt * lv[k];
+        O += wgt * ov[k];
+      }
+      M = cm;
+    }
+    ((bf16_t*)a.out)[((size_t)i * Hq + h * G + g) * D + d] = from_f32<bf16_t>(O / Ls);
+    if (d == 0) a.lse[(size_t)i * Hq + h * G + g] = (M + __log2f(Ls)) * 0.6931471805599453f;
   }
 }
 
