@@ -193,24 +193,27 @@ def decode(L: LayerView, G: int, nb: int, q_raw: np.ndarray, fetch, dtype: int, 
 
 
 def compress(L: LayerView, G: int, nb: int, block: int, q_raw: np.ndarray, fetch, dtype: int,
-             base: float):
+             base: float, queries=None):
     """Pause-token attention of one compression of ``block`` at one layer.
 
     q_raw [Kp, Hq, d] are the pause queries (pre-RoPE). Returns (out [Kp,Hq,d],
     lse [Kp,Hq], code) where code = (kind, a, b, pos, k_cached, v) of the rows
-    this layer keeps: pause k < quota, in k order.
+    this layer keeps: pause k < quota, in k order. ``queries`` (optional) lists
+    the pause indices to compute; out and lse then hold those rows, in order.
     """
     Kp = L.Kp
-    lists = [visible_keys(L, G, nb, (PAUSE, block, j)) for j in range(Kp)]
+    queries = list(range(Kp)) if queries is None else [int(j) for j in queries]
+    q_raw = np.asarray(q_raw)[queries]
+    lists = [visible_keys(L, G, nb, (PAUSE, block, j)) for j in queries]
     kind = np.concatenate([t[0] for t in lists])
     a = np.concatenate([t[1] for t in lists])
     b = np.concatenate([t[2] for t in lists])
     pos = np.concatenate([t[3] for t in lists])
-    off = np.zeros(Kp + 1, np.int64)
+    off = np.zeros(len(queries) + 1, np.int64)
     off[1:] = np.cumsum([len(t[0]) for t in lists])
     k = rope_rows(fetch(kind, a, b, "k"), pos, base, dtype)
     v = fetch(kind, a, b, "v")
-    qpos = np.array([position(L, PAUSE, block, j) for j in range(Kp)], np.int64)
+    qpos = np.array([position(L, PAUSE, block, j) for j in queries], np.int64)
     qr = rope_rows(q_raw, qpos, base, -1)
     out, lse = attention_batch(qr, off, k, v)
     ck = np.arange(min(L.quota, Kp))

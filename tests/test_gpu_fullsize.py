@@ -1,0 +1,135 @@
+"""GPU parity at the benchmark's full sizes, in the launch configuration that
+bench.py times (bf16, d = 128, 32 q / 8 KV heads, 64-row pages, C = 512, the
+automatic decode schedule), on outputs the oracle computes one by one.
+
+- The 36-layer per-layer-quota decode step: 22 sequences, prompts U[128, 512],
+  U[4096, 32768] generated tokens, quotas 6x256 / 12x64 / 18x128 (seeded).
+- The block-compression event: 64 sequences completing a block at once, all
+  36 layers, K = 256 pause tokens.
+
+Bars as everywhere: out max-abs 2e-2, lse 1e-3; stored values bit-exact,
+rotated keys within the fp32 rotation's rounding bound (one bf16 ulp away from
+cancellation); row counts and positions bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import oracle
+import synth
+from oracle import PAUSE, TEXT
+from tests.harness import Run, host, rotated_key_bound
+
+pytestmark = pytest.mark.gpu
+
+L, HQ, HKV, D, C, PR, KP = 36, 32, 8, 128, 512, 64, 256
+
+
+def _close(name, got, want, tol):
+    err = float(np.abs(np.asarray(got) - np.asarray(want)).max())
+    print(f"[parity] {name}: max-abs {err:.3e} (tol {tol:.0e})", flush=True)
+    assert err <= tol, f"{name}: max-abs {err} > {tol}"
+
+
+def _pool_bytes(P, Gmax, quotas, compressed_blocks=None):
+    page_bytes = HKV * PR * D * 2
+    pages = 0
+    for q in quotas:
+        nb = (Gmax - 1) // C if compressed_blocks is None else compressed_blocks
+        R = P + nb * q + C
+        pages += int(np.sum(np.ceil(R / PR) + 2 + C // PR))
+    return 2 * page_bytes * pages
+
+
+def _sample_layers(quotas):
+    """Two layers of each quota class."""
+    out = []
+    for q in (64, 128, 256):
+        out += [int(l) for l in np.where(quotas == q)[0][:2]]
+    return out
+
+
+def test_36_layer_quota_decode_step_sampled():
+    quotas, P, G = bench.decode_workload(2)
+    B = len(P)
+    run = Run(L=L, Hq=HQ, Hkv=HKV, D=D, C=C, Kp=int(quotas.max()), quota=quotas.tolist(), pr=PR,
+              dtype="bf16", max_seqs=B, pool_bytes=_pool_bytes(P, G + 1, quotas),
+              max_position=33792, seed=2)
+    sids = [run.new_seq(int(P[i]), i) for i in range(B)]
+    for s, g in zip(sids, G):
+        run.fill(s, int(g))
+    # the step's token at every layer (a full open block is compressed first)
+    run.grow({s: int(g) + 1 for s, g in zip(sids, G)})
+    print(f"[fullsize] 36-layer step: {B} sequences filled and appended", flush=True)
+    layers = _sample_layers(quotas)
+    seqs = (0, 11, 21)
+    for l in range(L):
+        out, lse, q = run.decode(sids, l)
+        assert np.isfinite(out).all() and np.isfinite(lse).all(), l
+        for i, s in enumerate(sids):
+            nb = run.nb[s]
+            want = int(P[i]) + nb * int(quotas[l]) + (run.G[s] - nb * C)
+            assert run.pool.seq_query(s, l)["resident_rows"] == want, (i, l)
+        if l in layers:
+            for i in seqs:
+                o_ref, l_ref, keys = run.oracle_decode(sids[i], l, q[i])
+                _close(f"36L decode out seq{i} L{l} q{quotas[l]}", out[i], o_ref, 2e-2)
+                _close(f"36L decode lse seq{i} L{l} q{quotas[l]}", lse[i], l_ref, 1e-3)
+    # positions of one sampled (sequence, layer), bit-exact
+    s, l = sids[11], layers[-1]
+    pos = run.pool.export_layout(s, l)[1]
+    want = oracle.visible_keys(run.view(s, l), run.G[s], run.nb[s], (TEXT, run.G[s] - 1, 0))[3]
+    assert pos == want.tolist()
+
+
+def test_block_compression_event_sampled():
+    rng = np.random.default_rng(3)
+    quotas = bench.layer_quotas(2)
+    B = 64
+    P = rng.integers(128, 512, B, endpoint=True)
+    b = rng.integers(0, 62, B, endpoint=True)
+    G = (b + 1) * C
+    run = Run(L=L, Hq=HQ, Hkv=HKV, D=D, C=C, Kp=KP, quota=quotas.tolist(), pr=PR, dtype="bf16",
+              max_seqs=B, pool_bytes=_pool_bytes(P, G, quotas, compressed_blocks=b + 1),
+              max_position=33792, seed=3)
+    sids = [run.new_seq(int(P[i]), i) for i in range(B)]
+    for s, g in zip(sids, G):
+        run.fill(s, int(g))
+    print("[fullsize] compression event: 64 sequences filled", flush=True)
+    layers = _sample_layers(quotas)
+    seqs = (0, 31, 63)
+    queries = [0, 1, 100, 255]
+    kept = {}
+    before = {(i, l): run.pool.seq_query(sids[i], l)["resident_rows"] for i in seqs for l in layers}
+    for l in range(L):
+        out, lse = run.compress_layer(sids, l)
+        if l in layers:
+            kept[l] = (host(out[list(seqs)][:, queries]), host(lse[list(seqs)][:, queries]))
+    torch.cuda.synchronize()
+    for l in layers:
+        q_l = int(quotas[l])
+        for n, i in enumerate(seqs):
+            s = sids[i]
+            qraw = run.rows(s, l, PAUSE, np.full(KP, b[i]), np.arange(KP), synth.WHICH_Q)
+            o_ref, l_ref, code = oracle.compress(run.view(s, l), run.G[s], run.nb[s], run.nb[s], qraw,
+                                                 run.fetch(s, l), oracle.BF16, run.base, queries=queries)
+            _close(f"event out seq{i} L{l} q{q_l}", kept[l][0][n], o_ref, 2e-2)
+            _close(f"event lse seq{i} L{l} q{q_l}", kept[l][1][n], l_ref, 1e-3)
+            # the layer's new code rows: values bit-exact, rotated keys within one ulp
+            rows = run.pool.seq_query(s, l)["resident_rows"]
+            assert rows == before[(i, l)] + q_l
+            r0 = rows - C - q_l
+            k = torch.empty((q_l, HKV, D), device="cuda", dtype=torch.bfloat16)
+            v = torch.empty_like(k)
+            run.pool.read_rows(s, l, r0, q_l, k, v)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(host(v), code[5])
+            k_raw = run.rows(s, l, PAUSE, np.full(q_l, b[i]), np.arange(q_l), synth.WHICH_K)
+            assert (np.abs(host(k) - code[4]) <= rotated_key_bound(k_raw, code[4])).all()
+            pos = run.pool.export_layout(s, l)[1]
+            assert pos[r0:r0 + q_l] == code[3].tolist()
+    run.pool.free_block(sids)
+    for i, s in enumerate(sids):
+        for l in (0, L - 1):
+            assert run.pool.seq_query(s, l)["resident_rows"] == int(P[i]) + (int(b[i]) + 1) * int(quotas[l])

@@ -326,3 +326,21 @@ def test_quota_table_golden():
     assert sum(n for _, n in table) == 36
     total = sum(r * n for r, n in table)
     assert total == 36 * mean and C // mean == 4
+
+
+def test_compress_query_subset_equals_full():
+    """Sampling pause queries selects rows of the full computation unchanged."""
+    Lv = LayerView(3, 8, 4, 2)
+    G, nb = 24, 2
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((4, 2, 16))
+
+    def fetch(kind, a, b, which):
+        # any deterministic rows keyed by identity
+        key = kind * 100000 + a * 100 + b + (7 if which == "k" else 0)
+        return np.sin(key[:, None, None] * 0.37 + np.arange(16)[None, None, :] * 0.11) * np.ones((1, 1, 16))
+
+    full = oracle.compress(Lv, G, nb, nb, q, fetch, oracle.F32, 1e6)
+    part = oracle.compress(Lv, G, nb, nb, q, fetch, oracle.F32, 1e6, queries=[3, 0])
+    np.testing.assert_array_equal(part[0], full[0][[3, 0]])
+    np.testing.assert_array_equal(part[1], full[1][[3, 0]])
