@@ -184,8 +184,8 @@ abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_poo
   if ((err = hipMalloc(&d.pos, pages * s.pr * sizeof(int32_t)))) return fail(err, "positions");
   if ((err = hipMalloc(&d.ptab, tab_ints * sizeof(int32_t)))) return fail(err, "page table");
   if ((err = hipMalloc(&d.meta, meta_ints * sizeof(int32_t)))) return fail(err, "meta");
-  float2* rope = nullptr;
-  if ((err = hipMalloc(&rope, rope_n * sizeof(float2)))) return fail(err, "rope");
+  double2* rope = nullptr;
+  if ((err = hipMalloc(&rope, rope_n * sizeof(double2)))) return fail(err, "rope");
   d.rope = rope;
   if ((err = hipMalloc(&p->quota_d, s.L * sizeof(int32_t)))) return fail(err, "quota");
   if ((err = hipMalloc(&p->pause_d, s.L * sizeof(int32_t)))) return fail(err, "pause");
@@ -196,18 +196,18 @@ abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_poo
   if ((err = hipMemset(d.pos, 0xff, pages * s.pr * sizeof(int32_t)))) return fail(err, "memset");
   if ((err = hipMemset(d.ptab, 0xff, tab_ints * sizeof(int32_t)))) return fail(err, "memset");
   if ((err = hipMemset(d.meta, 0, meta_ints * sizeof(int32_t)))) return fail(err, "memset");
-  // RoPE angles pos * base^(-2i/d) in double, stored as fp32 (cos, sin)
+  // RoPE (cos, sin) of the angles pos * base^(-2i/d), in fp64
   {
-    std::vector<float2> h(rope_n);
+    std::vector<double2> h(rope_n);
     const int half = s.D / 2;
     std::vector<double> inv(half);
     for (int i = 0; i < half; ++i) inv[i] = std::pow(s.rope_base, -2.0 * i / s.D);
     for (int64_t pos = 0; pos < s.max_position; ++pos)
       for (int i = 0; i < half; ++i) {
         double th = (double)pos * inv[i];
-        h[pos * half + i] = make_float2((float)std::cos(th), (float)std::sin(th));
+        h[pos * half + i] = make_double2(std::cos(th), std::sin(th));
       }
-    if ((err = hipMemcpy(rope, h.data(), rope_n * sizeof(float2), hipMemcpyHostToDevice)))
+    if ((err = hipMemcpy(rope, h.data(), rope_n * sizeof(double2), hipMemcpyHostToDevice)))
       return fail(err, "rope upload");
   }
   if ((err = hipMemcpy(p->quota_d, s.quota.data(), s.L * sizeof(int32_t), hipMemcpyHostToDevice)))

@@ -123,16 +123,26 @@ __device__ __forceinline__ int32_t* ptab_of(const DevPool& P, int slot, int laye
   return P.ptab + (size_t)(slot * P.L + layer) * P.tstride;
 }
 
+// ---- RoPE in fp64 ---------------------------------------------------------------
+// The (cos, sin) table is fp64, computed on the host as cos/sin(pos *
+// base^(-2i/d)). Rotations run in fp64 without contraction and are rounded once
+// to the storage type, so stored keys and rotated queries are the correctly
+// rounded values of the exact rotation of the stored inputs.
+// rotate-half pair (a, b) = (x_i, x_{i+d/2}) -> (a cos - b sin, b cos + a sin)
+__device__ __forceinline__ double rot_first(double a, double b, double2 cs) {
+#pragma clang fp contract(off)
+  return a * cs.x - b * cs.y;
+}
+__device__ __forceinline__ double rot_second(double a, double b, double2 cs) {
+#pragma clang fp contract(off)
+  return b * cs.x + a * cs.y;
+}
 // Rotate-half RoPE of element d of a row x (D elements, any layout via lambda).
 template <int D, typename F>
-__device__ __forceinline__ float rope_elem(F x, int d, const float2* rope_row) {
+__device__ __forceinline__ double rope_elem(F x, int d, const double2* rope_row) {
   constexpr int H = D / 2;
-  if (d < H) {
-    float2 cs = rope_row[d];
-    return x(d) * cs.x - x(d + H) * cs.y;
-  }
-  float2 cs = rope_row[d - H];
-  return x(d) * cs.x + x(d - H) * cs.y;
+  if (d < H) return rot_first(x(d), x(d + H), rope_row[d]);
+  return rot_second(x(d - H), x(d), rope_row[d - H]);
 }
 
 // ---- small helpers -----------------------------------------------------------------
@@ -188,6 +198,34 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // bf16 bits of a float, rounded to nearest even by the hardware conversion
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);  // v_cvt_pk_bf16_f32: nearest even
+}
+// double -> float rounded to odd (the neighbour toward zero, last bit forced
+// to 1, when inexact): a later nearest-even rounding to a format at least two
+// bits narrower then equals a single nearest-even rounding of the double
+__device__ __forceinline__ float f64_to_f32_odd(double d) {
+  float f = (float)d;
+  if ((double)f != d) {
+    uint32_t b = __float_as_uint(f);
+    if (fabs((double)f) > fabs(d)) b -= 1;
+    f = __uint_as_float(b | 1u);
+  }
+  return f;
+}
+// a double rounded once (nearest even) to the storage type T
+template <typename T>
+__device__ __forceinline__ T from_f64(double d);
+template <>
+__device__ __forceinline__ float from_f64<float>(double d) { return (float)d; }
+template <>
+__device__ __forceinline__ bf16_t from_f64<bf16_t>(double d) {
+  return bf16_t{(uint16_t)bf16_bits(f64_to_f32_odd(d))};
+}
+// ... and widened back to float: the rotated query in the pool dtype
+template <typename T>
+__device__ __forceinline__ float round_to(double d) { return to_f32(from_f64<T>(d)); }
+// two doubles -> packed bf16 pair (a in the low half), each rounded once
+__device__ __forceinline__ uint32_t pack_bf16x2_f64(double a, double b) {
+  return bf16_bits(f64_to_f32_odd(a)) | (bf16_bits(f64_to_f32_odd(b)) << 16);
 }
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // two floats -> packed bf16 pair (a in the low half), nearest even, one instruction

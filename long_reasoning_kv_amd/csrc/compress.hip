@@ -23,7 +23,7 @@ __global__ void __launch_bounds__(1024) pause_rope_scatter_kernel(CompressArgs a
   const int pos = prompt + blk * P.C + bitrev_dev(k, a.log2Kp) * (P.C / a.Kp);
   const T* kin = (const T*)a.kp + ((size_t)i * a.Kp + k) * P.Hkv * D;
   const T* vin = (const T*)a.vp + ((size_t)i * a.Kp + k) * P.Hkv * D;
-  const float2* rope = P.rope + (size_t)pos * (D / 2);
+  const double2* rope = P.rope + (size_t)pos * (D / 2);
   const bool keep = k < a.quota;
   int page = 0, srow = 0;
   if (keep) {
@@ -33,10 +33,10 @@ __global__ void __launch_bounds__(1024) pause_rope_scatter_kernel(CompressArgs a
   }
   for (int t = threadIdx.x; t < P.Hkv * (D / 2); t += blockDim.x) {
     const int hh = t / (D / 2), j = t % (D / 2);
-    const float x1 = to_f32(kin[hh * D + j]), x2 = to_f32(kin[hh * D + j + D / 2]);
-    const float2 cs = rope[j];
-    const T y1 = from_f32<T>(x1 * cs.x - x2 * cs.y);
-    const T y2 = from_f32<T>(x2 * cs.x + x1 * cs.y);
+    const double x1 = to_f32(kin[hh * D + j]), x2 = to_f32(kin[hh * D + j + D / 2]);
+    const double2 cs = rope[j];
+    const T y1 = from_f64<T>(rot_first(x1, x2, cs));
+    const T y2 = from_f64<T>(rot_second(x1, x2, cs));
     T* kr = (T*)a.kp_rot + (((size_t)i * P.Hkv + hh) * a.Kp + k) * D;
     kr[j] = y1;
     kr[j + D / 2] = y2;
@@ -81,11 +81,11 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
   __shared__ float qs[D];
   __shared__ float ps[64];
   {
-    const float2* rope = P.rope + (size_t)pos * (D / 2);
+    const double2* rope = P.rope + (size_t)pos * (D / 2);
     const T* qh = (const T*)a.qp + (((size_t)i * a.Kp + j) * a.Hq + hq) * D;
     const float sc = 1.4426950408889634f / sqrtf((float)D);
     for (int d = lane; d < D; d += 64)
-      qs[d] = sc * rope_elem<D>([&](int e) { return to_f32(qh[e]); }, d, rope);
+      qs[d] = sc * round_to<T>(rope_elem<D>([&](int e) { return (double)to_f32(qh[e]); }, d, rope));
   }
   __syncthreads();
 
@@ -167,8 +167,9 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
 // r/4, head 4h + r%4. Each of the 4 wavefronts owns 32 query rows (two 16-row
 // N-blocks). For every 64-key tile (a context page, then pause-key tiles):
 //   S^T = K Q^T   with v_mfma_f32_16x16x32_bf16: A = K rows from LDS, B = the
-//                 rotated query (hi + lo bf16 parts, so the product keeps fp32
-//                 accuracy), C lane l = keys 4(l/16)+i x query l%16;
+//                 rotated query rounded once to bf16 (like stored keys; the
+//                 softmax scale goes on the fp32 scores), C lane l = keys
+//                 4(l/16)+i x query l%16;
 //   online softmax per query column, all lane-local plus permlane swaps; the
 //                 running maximum is only moved (and O^T rescaled) when a
 //                 tile's maximum exceeds it by more than 2^8, which keeps the
@@ -234,11 +235,12 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   const int ntp = last_pause / TK + 1;  // pause-key tiles
   const int ntiles = ntc + ntp;
 
-  // ---- the wavefront's query rows: rotate at the bitrev position, scale, hi/lo
-  uint4 qh[2][4], ql[2][4];  // [N-block][k-step]: dims 32ks + 8 g4 + 0..7
+  // ---- the wavefront's query rows: rotated at the bitrev position, rounded
+  // once to bf16 (like stored keys); the softmax scale goes on the fp32 scores
+  const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
+  uint4 qh[2][4];  // [N-block][k-step]: dims 32ks + 8 g4 + 0..7
   int qpause[2];
   {
-    const float qs = 1.4426950408889634f / sqrtf((float)D);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       int r = q0 + wave * 32 + nb * 16 + l16;
@@ -251,33 +253,20 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
       float x[4][8];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) unpack16(*(const uint4*)(qrow + 32 * ks + 8 * g4), x[ks], bf16_t());
-      const float2* rope = P.rope + (size_t)pos * (D / 2);
+      const double2* rope = P.rope + (size_t)pos * (D / 2);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        float y0[8], y1[8];
+        double y0[8], y1[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float2 cs = rope[32 * ks + 8 * g4 + j];
-          y0[j] = qs * (x[ks][j] * cs.x - x[ks + 2][j] * cs.y);
-          y1[j] = qs * (x[ks + 2][j] * cs.x + x[ks][j] * cs.y);
+          const double2 cs = rope[32 * ks + 8 * g4 + j];
+          y0[j] = rot_first(x[ks][j], x[ks + 2][j], cs);
+          y1[j] = rot_second(x[ks][j], x[ks + 2][j], cs);
         }
-        uint32_t h0[4], l0[4], h1[4], l1[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t a0 = bf16_bits(y0[2 * j]), a1 = bf16_bits(y0[2 * j + 1]);
-          h0[j] = a0 | (a1 << 16);
-          l0[j] = bf16_bits(y0[2 * j] - __uint_as_float(a0 << 16)) |
-                  (bf16_bits(y0[2 * j + 1] - __uint_as_float(a1 << 16)) << 16);
-          a0 = bf16_bits(y1[2 * j]);
-          a1 = bf16_bits(y1[2 * j + 1]);
-          h1[j] = a0 | (a1 << 16);
-          l1[j] = bf16_bits(y1[2 * j] - __uint_as_float(a0 << 16)) |
-                  (bf16_bits(y1[2 * j + 1] - __uint_as_float(a1 << 16)) << 16);
-        }
-        qh[nb][ks] = make_uint4(h0[0], h0[1], h0[2], h0[3]);
-        ql[nb][ks] = make_uint4(l0[0], l0[1], l0[2], l0[3]);
-        qh[nb][ks + 2] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
-        ql[nb][ks + 2] = make_uint4(l1[0], l1[1], l1[2], l1[3]);
+        qh[nb][ks] = make_uint4(pack_bf16x2_f64(y0[0], y0[1]), pack_bf16x2_f64(y0[2], y0[3]),
+                                pack_bf16x2_f64(y0[4], y0[5]), pack_bf16x2_f64(y0[6], y0[7]));
+        qh[nb][ks + 2] = make_uint4(pack_bf16x2_f64(y1[0], y1[1]), pack_bf16x2_f64(y1[2], y1[3]),
+                                    pack_bf16x2_f64(y1[4], y1[5]), pack_bf16x2_f64(y1[6], y1[7]));
       }
     }
   }
@@ -375,10 +364,7 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
       for (int ks = 0; ks < 4; ++ks) {
         const uint4 ka = ck[kr * 16 + ((4 * ks + g4) ^ (kr & 15))];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          s[mb][nb] = mfma_bf16(ka, qh[nb][ks], s[mb][nb]);
-          s[mb][nb] = mfma_bf16(ka, ql[nb][ks], s[mb][nb]);
-        }
+        for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma_bf16(ka, qh[nb][ks], s[mb][nb]);
       }
     }
     // mask (partial context pages and pause tiles only; the test is uniform)
@@ -404,7 +390,7 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[mb][nb][e]);
-      mx = rows4_max(mx);
+      mx = rows4_max(mx) * qs;  // log2 units
       const bool up = mx > m_run[nb] + 8.f;
       mn[nb] = up ? mx : m_run[nb];
       alpha[nb] = fast_exp2(m_run[nb] - mn[nb]);
@@ -427,7 +413,7 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = fast_exp2(s[mb][nb][e] - mn[nb]);
+          const float p = fast_exp2(fmaf(s[mb][nb][e], qs, -mn[nb]));
           s[mb][nb][e] = p;  // the score register now holds its probability
           ps += p;
         }

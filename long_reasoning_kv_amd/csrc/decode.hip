@@ -75,8 +75,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     const int d0 = c * EPL;                 // first dim of this lane
     const int dp = (d0 + H) % D;            // partner dims
     const float sgn = d0 < H ? -1.f : 1.f;  // y = x cos + sgn * x_partner sin
-    const float2* rope = P.rope + (size_t)qpos * H + (d0 % H);
-    float2 cs[EPL];
+    const double2* rope = P.rope + (size_t)qpos * H + (d0 % H);
+    double2 cs[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) cs[e] = rope[e];
     const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
@@ -87,7 +87,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
       unpack16(*(const uint4*)(qh + d0), x, T());
       unpack16(*(const uint4*)(qh + dp), xp, T());
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) qv[g][e] = qs * (x[e] * cs[e].x + sgn * xp[e] * cs[e].y);
+      for (int e = 0; e < EPL; ++e)
+        qv[g][e] = qs * round_to<T>(sgn < 0.f ? rot_first(x[e], xp[e], cs[e]) : rot_second(xp[e], x[e], cs[e]));
     }
   }
 
@@ -259,8 +260,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 //  - 8 lanes per row; lane c holds dims [8c, 8c+8) and [64+8c, 64+8c+8), i.e.
 //    both halves of its rotate-half pairs, so each wavefront load is 8 rows x
 //    128 contiguous bytes;
-//  - q.k on v_dot2c_f32_bf16: the rotated, pre-scaled query is split into
-//    bf16 hi + lo parts (|q - hi - lo| <= 2^-16 |q|), keys are used as stored;
+//  - q.k on v_dot2c_f32_bf16: the rotated query, rounded once to bf16 and then
+//    scaled, is split into bf16 hi + lo parts (|q - hi - lo| <= 2^-16 |q|), so
+//    the scale costs no precision; keys are used as stored;
 //  - 3 DPP steps finish a row's dot product; 2 rows x G heads per lane per
 //    16-row unit need exp2, not 4 x G;
 //  - the unit's base address is wavefront-uniform, lane offsets are fixed, and
@@ -298,14 +300,10 @@ __global__ void __launch_bounds__(256) decode_bf16_d128_kernel(DecodeArgs a) {
   // query: rotate dims (8c8+e, 64+8c8+e) together, scale, split into hi/lo bf16 pairs
   uint32_t qh[G][8], ql[G][8];
   {
-    const float2* rope = P.rope + (size_t)qpos * (D / 2) + 8 * c8;
-    float cs_c[8], cs_s[8];
+    const double2* rope = P.rope + (size_t)qpos * (D / 2) + 8 * c8;
+    double2 cs[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float2 t = rope[e];
-      cs_c[e] = t.x;
-      cs_s[e] = t.y;
-    }
+    for (int e = 0; e < 8; ++e) cs[e] = rope[e];
     const float qs = 1.4426950408889634f / sqrtf((float)D);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -315,8 +313,8 @@ __global__ void __launch_bounds__(256) decode_bf16_d128_kernel(DecodeArgs a) {
       unpack16(*(const uint4*)(qrow + 64 + 8 * c8), xb, bf16_t());
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        y[e] = qs * (xa[e] * cs_c[e] - xb[e] * cs_s[e]);
-        y[8 + e] = qs * (xb[e] * cs_c[e] + xa[e] * cs_s[e]);
+        y[e] = qs * round_to<bf16_t>(rot_first(xa[e], xb[e], cs[e]));
+        y[8 + e] = qs * round_to<bf16_t>(rot_second(xa[e], xb[e], cs[e]));
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -543,14 +541,10 @@ __global__ void __launch_bounds__(256) decode_bf16_d128_g4_kernel(DecodeArgs a) 
   // this wavefront's two query heads: rotate, scale, split into hi/lo bf16 pairs
   uint32_t qh[2][8], ql[2][8];
   {
-    const float2* rope = P.rope + (size_t)qpos * (D / 2) + 8 * c8;
-    float cs_c[8], cs_s[8];
+    const double2* rope = P.rope + (size_t)qpos * (D / 2) + 8 * c8;
+    double2 cs[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float2 t = rope[e];
-      cs_c[e] = t.x;
-      cs_s[e] = t.y;
-    }
+    for (int e = 0; e < 8; ++e) cs[e] = rope[e];
     const float qs = 1.4426950408889634f / sqrtf((float)D);
 #pragma unroll
     for (int j2 = 0; j2 < 2; ++j2) {
@@ -560,8 +554,8 @@ __global__ void __launch_bounds__(256) decode_bf16_d128_g4_kernel(DecodeArgs a) 
       unpack16(*(const uint4*)(qrow + 64 + 8 * c8), xb, bf16_t());
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        y[e] = qs * (xa[e] * cs_c[e] - xb[e] * cs_s[e]);
-        y[8 + e] = qs * (xb[e] * cs_c[e] + xa[e] * cs_s[e]);
+        y[e] = qs * round_to<bf16_t>(rot_first(xa[e], xb[e], cs[e]));
+        y[8 + e] = qs * round_to<bf16_t>(rot_second(xa[e], xb[e], cs[e]));
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -786,14 +780,10 @@ __global__ void __launch_bounds__(256) decode_stream_kernel(StreamArgs a) {
 
     uint32_t qh[2][8], ql[2][8];
     {
-      const float2* rope = P.rope + (size_t)qpos * (D / 2) + 8 * c8;
-      float cs_c[8], cs_s[8];
+      const double2* rope = P.rope + (size_t)qpos * (D / 2) + 8 * c8;
+      double2 cs[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 t = rope[e];
-        cs_c[e] = t.x;
-        cs_s[e] = t.y;
-      }
+      for (int e = 0; e < 8; ++e) cs[e] = rope[e];
       const float qs = 1.4426950408889634f / sqrtf((float)D);
 #pragma unroll
       for (int j2 = 0; j2 < 2; ++j2) {
@@ -803,8 +793,8 @@ __global__ void __launch_bounds__(256) decode_stream_kernel(StreamArgs a) {
         unpack16(*(const uint4*)(qrow + 64 + 8 * c8), xb, bf16_t());
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          y[e] = qs * (xa[e] * cs_c[e] - xb[e] * cs_s[e]);
-          y[8 + e] = qs * (xb[e] * cs_c[e] + xa[e] * cs_s[e]);
+          y[e] = qs * round_to<bf16_t>(rot_first(xa[e], xb[e], cs[e]));
+          y[8 + e] = qs * round_to<bf16_t>(rot_second(xa[e], xb[e], cs[e]));
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -1032,8 +1022,9 @@ __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) 
 // V^T operands), then starts loading the next tile into the same LDS and
 // computes while it is in flight:
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, two M-blocks of 16 keys; B = the
-//                 four rotated query heads of the KV head (hi + lo bf16 parts)
-//                 in columns 0..3; M-block mb row m is key 8(m/4) + 4mb + m%4,
+//                 four rotated query heads of the KV head (bf16, rounded once
+//                 like stored keys) in columns 0..3; the softmax scale is
+//                 applied to the fp32 scores; M-block mb row m is key 8(m/4) + 4mb + m%4,
 //                 so lane l ends up with the 8 consecutive keys 8(l/16)+0..7 of
 //                 head l%16;
 //   online softmax per head column (lane-local, then permlane swaps); the
@@ -1062,6 +1053,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
   if (F0 >= Fend) return;
   const char* kpool = (const char*)P.kpool;
   const char* vpool = (const char*)P.vpool;
+  const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
   typedef const __attribute__((address_space(4))) int32_t* cptr;
 
   // ---- cursor over (sequence, KV head, tile); all fields wave-uniform
@@ -1135,42 +1127,31 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
   };
 
   // ---- per-segment state
-  uint4 qh[4], ql[4];  // B operand of S^T: head l16 (< 4), dims 32ks + 8g4 + 0..7
+  uint4 qh[4];  // B operand of S^T: bf16 rotated query, head l16 (< 4), dims 32ks + 8g4 + 0..7
   f32x4_t acc[8];      // O^T: dims 16db + 4g4 + i of head l16
   float m_run = -1e30f, l_run = 0.f;
   auto start_segment = [&](const Cur& c) __attribute__((always_inline)) {
     cptr meta = (cptr)meta_of(P, c.slot, a.layer);
     const int qpos = meta[2];
-    const float qs = 1.4426950408889634f / sqrtf((float)D);
     const int hh = l16 < G ? l16 : 0;
     const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)c.i * Hq + c.h * G + hh) * D;
-    const float2* rope = P.rope + (size_t)qpos * (D / 2);
+    const double2* rope = P.rope + (size_t)qpos * (D / 2);
     float x[4][8];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) unpack16(*(const uint4*)(qrow + 32 * ks + 8 * g4), x[ks], bf16_t());
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      float y0[8], y1[8];
+      double y0[8], y1[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float2 cs = rope[32 * ks + 8 * g4 + j];
-        y0[j] = l16 < G ? qs * (x[ks][j] * cs.x - x[ks + 2][j] * cs.y) : 0.f;
-        y1[j] = l16 < G ? qs * (x[ks + 2][j] * cs.x + x[ks][j] * cs.y) : 0.f;
+        const double2 cs = rope[32 * ks + 8 * g4 + j];
+        y0[j] = l16 < G ? rot_first(x[ks][j], x[ks + 2][j], cs) : 0.0;
+        y1[j] = l16 < G ? rot_second(x[ks][j], x[ks + 2][j], cs) : 0.0;
       }
-      uint32_t h0[4], o0[4], h1[4], o1[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h0[j] = pack_bf16x2(y0[2 * j], y0[2 * j + 1]);
-        h1[j] = pack_bf16x2(y1[2 * j], y1[2 * j + 1]);
-        o0[j] = pack_bf16x2(y0[2 * j] - __uint_as_float(h0[j] << 16),
-                            y0[2 * j + 1] - __uint_as_float(h0[j] & 0xffff0000u));
-        o1[j] = pack_bf16x2(y1[2 * j] - __uint_as_float(h1[j] << 16),
-                            y1[2 * j + 1] - __uint_as_float(h1[j] & 0xffff0000u));
-      }
-      qh[ks] = make_uint4(h0[0], h0[1], h0[2], h0[3]);
-      ql[ks] = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-      qh[ks + 2] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
-      ql[ks + 2] = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+      qh[ks] = make_uint4(pack_bf16x2_f64(y0[0], y0[1]), pack_bf16x2_f64(y0[2], y0[3]),
+                          pack_bf16x2_f64(y0[4], y0[5]), pack_bf16x2_f64(y0[6], y0[7]));
+      qh[ks + 2] = make_uint4(pack_bf16x2_f64(y1[0], y1[1]), pack_bf16x2_f64(y1[2], y1[3]),
+                              pack_bf16x2_f64(y1[4], y1[5]), pack_bf16x2_f64(y1[6], y1[7]));
     }
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1252,10 +1233,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
     for (int mb = 0; mb < 2; ++mb) {
       sc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        sc[mb] = mfma_bf16(ka[mb][ks], qh[ks], sc[mb]);
-        sc[mb] = mfma_bf16(ka[mb][ks], ql[ks], sc[mb]);
-      }
+      for (int ks = 0; ks < 4; ++ks) sc[mb] = mfma_bf16(ka[mb][ks], qh[ks], sc[mb]);
     }
     if (nval < TK) {
 #pragma unroll
@@ -1263,9 +1241,10 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[mb][e] = 8 * g4 + 4 * mb + e < nval ? sc[mb][e] : -INFINITY;
     }
+    // scores in log2 units: q.k * log2(e)/sqrt(d), folded into the exponent below
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mx = rows4_max(mx);
+    mx = rows4_max(mx) * qs;
     const bool up = mx > m_run + 8.f;
     if (__builtin_amdgcn_ballot_w64(up)) {
       const float mn = up ? mx : m_run;
@@ -1278,8 +1257,8 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
     float p[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      p[e] = fast_exp2(sc[0][e] - m_run);
-      p[4 + e] = fast_exp2(sc[1][e] - m_run);
+      p[e] = fast_exp2(fmaf(sc[0][e], qs, -m_run));
+      p[4 + e] = fast_exp2(fmaf(sc[1][e], qs, -m_run));
     }
     l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     const uint4 pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),

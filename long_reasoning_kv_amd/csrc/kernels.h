@@ -24,7 +24,7 @@ struct DevPool {
   int32_t* pos;
   int32_t* ptab;
   int32_t* meta;
-  const float2* rope;  // [max_position][D/2] (cos, sin)
+  const double2* rope;  // [max_position][D/2] (cos, sin), fp64
   int32_t L, Hkv, D, pr, tstride, max_pers, C, dtype;
 };
 

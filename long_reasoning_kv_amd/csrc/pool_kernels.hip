@@ -34,15 +34,15 @@ __global__ void __launch_bounds__(1024) append_kernel(AppendArgs a) {
   const T* v = (const T*)a.v + (size_t)i * P.Hkv * D;
   T* kd = (T*)P.kpool + ((size_t)page * P.Hkv * P.pr + srow) * D;
   T* vd = (T*)P.vpool + ((size_t)page * P.Hkv * P.pr + srow) * D;
-  const float2* rope = P.rope + (size_t)pos * (D / 2);
+  const double2* rope = P.rope + (size_t)pos * (D / 2);
   for (int t = threadIdx.x; t < P.Hkv * (D / 2); t += blockDim.x) {
     const int hh = t / (D / 2), j = t % (D / 2);
     const T* kr = k + hh * D;
-    const float x1 = to_f32(kr[j]), x2 = to_f32(kr[j + D / 2]);
-    const float2 cs = rope[j];
+    const double x1 = to_f32(kr[j]), x2 = to_f32(kr[j + D / 2]);
+    const double2 cs = rope[j];
     T* kdst = kd + (size_t)hh * P.pr * D;
-    kdst[j] = from_f32<T>(x1 * cs.x - x2 * cs.y);
-    kdst[j + D / 2] = from_f32<T>(x2 * cs.x + x1 * cs.y);
+    kdst[j] = from_f64<T>(rot_first(x1, x2, cs));
+    kdst[j + D / 2] = from_f64<T>(rot_second(x1, x2, cs));
     T* vdst = vd + (size_t)hh * P.pr * D;
     vdst[j] = v[hh * D + j];
     vdst[j + D / 2] = v[hh * D + j + D / 2];
@@ -85,14 +85,14 @@ __global__ void __launch_bounds__(1024) prompt_kernel(PromptArgs a) {
   const int page = a.pages[r / P.pr], srow = r % P.pr;
   const T* k = (const T*)a.k + (size_t)r * P.Hkv * D;
   const T* v = (const T*)a.v + (size_t)r * P.Hkv * D;
-  const float2* rope = P.rope + (size_t)r * (D / 2);
+  const double2* rope = P.rope + (size_t)r * (D / 2);
   for (int t = threadIdx.x; t < P.Hkv * (D / 2); t += blockDim.x) {
     const int hh = t / (D / 2), j = t % (D / 2);
-    const float x1 = to_f32(k[hh * D + j]), x2 = to_f32(k[hh * D + j + D / 2]);
-    const float2 cs = rope[j];
+    const double x1 = to_f32(k[hh * D + j]), x2 = to_f32(k[hh * D + j + D / 2]);
+    const double2 cs = rope[j];
     const size_t o = (((size_t)page * P.Hkv + hh) * P.pr + srow) * D;
-    ((T*)P.kpool)[o + j] = from_f32<T>(x1 * cs.x - x2 * cs.y);
-    ((T*)P.kpool)[o + j + D / 2] = from_f32<T>(x2 * cs.x + x1 * cs.y);
+    ((T*)P.kpool)[o + j] = from_f64<T>(rot_first(x1, x2, cs));
+    ((T*)P.kpool)[o + j + D / 2] = from_f64<T>(rot_second(x1, x2, cs));
     ((T*)P.vpool)[o + j] = v[hh * D + j];
     ((T*)P.vpool)[o + j + D / 2] = v[hh * D + j + D / 2];
   }
@@ -160,14 +160,14 @@ __global__ void __launch_bounds__(512) fill_kernel(FillArgs a) {
     ((T*)P.vpool)[o + 2 * e + 1] = from_f32<T>((float)z1);
   }
   __syncthreads();
-  const float2* rope = P.rope + (size_t)pos * (D / 2);
+  const double2* rope = P.rope + (size_t)pos * (D / 2);
   for (int t = threadIdx.x; t < n / 2; t += blockDim.x) {
     const int hh = t / (D / 2), j = t % (D / 2);
-    const float x1 = kraw[hh * D + j], x2 = kraw[hh * D + j + D / 2];
-    const float2 cs = rope[j];
+    const double x1 = kraw[hh * D + j], x2 = kraw[hh * D + j + D / 2];
+    const double2 cs = rope[j];
     const size_t o = (((size_t)page * P.Hkv + hh) * P.pr + srow) * D;
-    ((T*)P.kpool)[o + j] = from_f32<T>(x1 * cs.x - x2 * cs.y);
-    ((T*)P.kpool)[o + j + D / 2] = from_f32<T>(x2 * cs.x + x1 * cs.y);
+    ((T*)P.kpool)[o + j] = from_f64<T>(rot_first(x1, x2, cs));
+    ((T*)P.kpool)[o + j + D / 2] = from_f64<T>(rot_second(x1, x2, cs));
   }
   if (threadIdx.x == 0) P.pos[(size_t)page * P.pr + srow] = pos;
 }

@@ -11,7 +11,8 @@ module marshals arguments and composes the steps in the order the method
 states them:
 
 * decode (one text query): visible keys by the mask -> cached keys
-  RoPE(k) rounded to storage -> rotated query -> softmax attention;
+  RoPE(k) rounded to storage -> rotated query RoPE(q), rounded to storage the
+  same way -> softmax attention (scale 1/sqrt(d) on the fp64 scores);
 * compression of block b: every pause query PAUSE(b, j) with its own visible
   key set (prompt, retained code rows, the whole block, pause keys k <= j),
   then the code rows k < quota are what the layer keeps.
@@ -187,7 +188,7 @@ def decode(L: LayerView, G: int, nb: int, q_raw: np.ndarray, fetch, dtype: int, 
     k = rope_rows(fetch(kind, a, b, "k"), pos, base, dtype)
     v = fetch(kind, a, b, "v")
     qpos = np.array([position(L, *query)], np.int64)
-    qr = rope_rows(q_raw[None], qpos, base, -1)[0]
+    qr = rope_rows(q_raw[None], qpos, base, dtype)[0]  # rounded once, like stored keys
     out, lse = attention(qr, k, v)
     return out, lse, (kind, a, b, pos)
 
@@ -214,7 +215,7 @@ def compress(L: LayerView, G: int, nb: int, block: int, q_raw: np.ndarray, fetch
     k = rope_rows(fetch(kind, a, b, "k"), pos, base, dtype)
     v = fetch(kind, a, b, "v")
     qpos = np.array([position(L, PAUSE, block, j) for j in queries], np.int64)
-    qr = rope_rows(q_raw, qpos, base, -1)
+    qr = rope_rows(q_raw, qpos, base, dtype)  # rounded once, like stored keys
     out, lse = attention_batch(qr, off, k, v)
     ck = np.arange(min(L.quota, Kp))
     cpos = np.array([position(L, PAUSE, block, j) for j in ck], np.int64)

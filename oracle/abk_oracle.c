@@ -23,7 +23,9 @@
  *  - Pause tokens see all C rows of their block (they run after it completes).
  *  - Layer l keeps the prefix k < quota[l] of the K pause tokens' rows.
  *  - RoPE is rotate-half with theta_i = pos * base^(-2i/d); V is not rotated.
- *  - Cached keys are RoPE(k) rounded once to the cache's storage type.
+ *  - Cached keys are RoPE(k) rounded once to the cache's storage type; the
+ *    rotated query is rounded once to the same type (the attention takes
+ *    storage-type operands with fp64 accumulation here, fp32 on the device).
  *  - Scores are q'.k'/sqrt(d); lse is the natural log of sum exp(score).
  */
 #include <math.h>
