@@ -161,19 +161,3 @@ class Run:
         return oracle.compress(self.view(sid, layer), self.G[sid], b, b, q, self.fetch(sid, layer),
                                ORC_DT[self.dtype], self.base)
 
-
-def rotated_key_bound(k_raw: np.ndarray, k_ref: np.ndarray) -> np.ndarray:
-    """Largest admissible |stored - oracle| of rotated keys, per element.
-
-    The library rotates in fp32 (fp32 cos/sin table, two products and a sum:
-    at most 4 roundings of relative size 2^-24 over |x| + |y|, x and y the
-    rotate-half partners) and rounds once to bf16; the oracle rotates exactly
-    and rounds once. Rounding each side to bf16 adds at most one bf16 ulp of
-    the larger magnitude, so the bound is e + ulp(|ref| + e) with
-    e = 4 * 2^-24 * (|x| + |y|). Away from cancellation this is one ulp."""
-    half = k_raw.shape[-1] // 2
-    partner = np.concatenate([k_raw[..., half:], k_raw[..., :half]], axis=-1)
-    e = 4.0 * 2.0 ** -24 * (np.abs(k_raw) + np.abs(partner))
-    mag = np.abs(k_ref) + e
-    ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-300))) - 7), 2.0 ** -133)
-    return e + ulp
