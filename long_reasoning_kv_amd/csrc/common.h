@@ -123,6 +123,12 @@ __device__ __forceinline__ int32_t* ptab_of(const DevPool& P, int slot, int laye
   return P.ptab + (size_t)(slot * P.L + layer) * P.tstride;
 }
 
+// XOR swizzle of a 16-byte chunk position by bits 0, 1, 3 and 4 of a K row: the
+// 16 rows that one quarter of an MFMA A-operand read touches (keys 8a + 4m + b,
+// a, b in 0..3, for a fixed m) land on 16 different chunk positions, so the
+// 256 bytes they read hit every bank once
+__device__ __forceinline__ int kswz(int row) { return (((row >> 3) & 3) << 2) | (row & 3); }
+
 // ---- RoPE in fp64 ---------------------------------------------------------------
 // The (cos, sin) table is fp64, computed on the host as cos/sin(pos *
 // base^(-2i/d)). Rotations run in fp64 without contraction and are rounded once

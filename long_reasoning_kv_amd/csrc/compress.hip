@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
 // The M-blocks of S^T take keys 32(mb/2) + 8(m/4) + 4(mb%2) + m%4 so that for
 // each 32-key step a lane's 8 probabilities are 8 consecutive keys, which is
 // what two transposing reads of V deliver. K and V rows in LDS have their
-// 16-byte chunks XOR-swizzled by row (K: row & 15; V: bits 0, 1 and 3 of the
+// 16-byte chunks XOR-swizzled by row (K: bits 0, 1, 3, 4; V: bits 0, 1 and 3 of the
 // row) so that an A-operand read of either touches every bank evenly. The next
 // tile is loaded into registers while the current one is computed; LDS is
 // double-buffered (64 KB). Masks are applied only to partial and pause tiles.
@@ -209,7 +209,7 @@ __device__ __forceinline__ uint4 vt_operand(const uint4* __restrict__ tile, int 
 
 __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs a) {
   constexpr int D = 128, G = 4, TK = 64, RB = D * 2;
-  // K rows (chunks swizzled by row & 15) and V rows (swizzled by vt_swz), two
+  // K rows (chunks swizzled by kswz) and V rows (swizzled by vt_swz), two
   // buffers each; separate arrays so that the compiler can tell them apart
   __shared__ uint4 lk0[TK * RB / 16], lk1[TK * RB / 16];
   __shared__ uint4 lv0[TK * RB / 16], lv1[TK * RB / 16];
@@ -309,13 +309,13 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   // 16j + 4w + l/16 at swizzled position l%16, so it fetches the source chunk
   // that belongs there. Rows past the tile's valid count repeat its last row.
   const int r_in = 4 * wave + (lane >> 4);
-  const int kchunk = (lane & 15) ^ (r_in & 15);
-  const int vchunk = (lane & 15) ^ vt_swz(r_in);
+  const int vchunk = (lane & 15) ^ vt_swz(r_in);  // bits 0, 1, 3 of 16j + r_in are r_in's
   auto issue = [&](int t, int page, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
     const TileSrc ts = tile_src(t, page);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = min(16 * j + r_in, ts.nval - 1);
+      const int kchunk = (lane & 15) ^ kswz(16 * j + r_in);
       __builtin_amdgcn_global_load_lds((const void*)(ts.kb + row * ts.kstride + 16 * kchunk),
                                        (__attribute__((address_space(3))) void*)(dk + 256 * j + 64 * wave),
                                        16, 0, 0);
@@ -362,7 +362,7 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
       const int kr = keyof(mb, l16);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint4 ka = ck[kr * 16 + ((4 * ks + g4) ^ (kr & 15))];
+        const uint4 ka = ck[kr * 16 + ((4 * ks + g4) ^ kswz(kr))];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma_bf16(ka, qh[nb][ks], s[mb][nb]);
       }

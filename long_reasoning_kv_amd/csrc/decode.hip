@@ -1036,7 +1036,6 @@ __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) 
 // evenly. A segment inside one wavefront's run writes out and lse; other pieces
 // write partials for decode_stream_merge_kernel (index = wavefront - first).
 
-__device__ __forceinline__ int dm_kswz(int row) { return (((row >> 3) & 3) << 2) | (row & 3); }
 __device__ __forceinline__ int dm_vswz(int row) { return 2 * ((row & 3) | ((row >> 1) & 4)); }
 
 __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
@@ -1118,7 +1117,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
       const int row = 4 * j + dr;
       const int rc = min(row, nval - 1);
       __builtin_amdgcn_global_load_lds(
-          (const void*)(kpool + off + rc * RB + 16 * ((lane & 15) ^ dm_kswz(row))),
+          (const void*)(kpool + off + rc * RB + 16 * ((lane & 15) ^ kswz(row))),
           (__attribute__((address_space(3))) void*)(lk + wave * WCH + 64 * j), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(
           (const void*)(vpool + off + rc * RB + 16 * ((lane & 15) ^ dm_vswz(row))),
@@ -1202,7 +1201,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
     for (int mb = 0; mb < 2; ++mb) {
       const int kr = 8 * (l16 >> 2) + 4 * mb + (l16 & 3);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) ka[mb][ks] = lk[wave * WCH + kr * 16 + ((4 * ks + g4) ^ dm_kswz(kr))];
+      for (int ks = 0; ks < 4; ++ks) ka[mb][ks] = lk[wave * WCH + kr * 16 + ((4 * ks + g4) ^ kswz(kr))];
     }
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
