@@ -426,6 +426,23 @@ def run_compress(args, torch, abk):
             times.append([e[l].elapsed_time(e[l + 1]) for l in range(L)])
         for s in sids:
             pool.seq_release(s)
+    # one sequence completing its last block alone (the common serving case):
+    # the context of each query tile is split over several workgroups
+    single = []
+    for rep in range(args.compress_reps + 1):
+        s = pool.seq_create(int(P[0]))
+        pool.synth_fill(s, 63 * C, 3 * 1000003 + 999)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for l in range(L):
+            pool.compress_block(l, [s], qp[l][:1], kp[l][:1], vp[l][:1], out[:1], lse[:1])
+        e1.record()
+        pool.free_block([s])
+        torch.cuda.synchronize()
+        if rep > 0:
+            single.append(e0.elapsed_time(e1))
+        pool.seq_release(s)
     pool.close()
     ms = np.mean([sum(t) for t in times])
     # algorithmic flops: QK^T and PV over context N_l plus the causal pause part
@@ -446,6 +463,8 @@ def run_compress(args, torch, abk):
         "config": {"workload": "block compression, 64 sequences, 36 layers, K=256 pause tokens "
                                "(layer keeps quota prefix)", "prompt": "U[128,512]",
                    "block_index": "U{0..62}"},
+        "single_sequence_ms": float(np.mean(single)),
+        "single_sequence": f"one sequence (prompt {int(P[0])}) compressing block 62 alone, 36 layers",
     }
 
 

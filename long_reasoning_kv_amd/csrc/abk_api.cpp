@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <climits>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -55,6 +56,7 @@ struct abk_pool {
   int32_t split_rows = 0;  // 0: automatic schedule; > 0: fixed split-KV work items of this many rows
   int32_t stream_wgs = 0;  // resident workgroups of the stream-K decode (0: not used)
   int32_t mfma_waves = 0;  // resident wavefronts of the MFMA decode (0: not used)
+  int32_t cus = 0;         // compute units of the device
   hipStream_t stream = nullptr;
   abk::DevPool dev{};
   int32_t* quota_d = nullptr;
@@ -224,6 +226,7 @@ abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_poo
     probe.pr = s.pr;
     probe.D = s.D;
     probe.dtype = s.dtype;
+    p->cus = cus;
     if (abk::decode_mfma_supported(probe, s.Hq / s.Hkv))
       p->mfma_waves = cus * abk::decode_mfma_waves_per_cu();
     else if (abk::decode_stream_supported(probe, s.Hq / s.Hkv))
@@ -510,6 +513,26 @@ abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32
   a.Kp = Kp;
   a.quota = s.quota[layer];
   a.log2Kp = abk::log2_exact(Kp);
+  a.part = nullptr;
+  a.nsplit = 1;
+  if (abk::compress_mfma_supported(p->dev, a.G)) {
+    // few sequences: split each query tile's context over several workgroups so
+    // that about two per CU run, keeping at least 4 context tiles per split
+    const int32_t ntq = (4 * Kp + 127) / 128;
+    const int32_t wgs = (n * s.Hkv + 7) / 8 * 8 * ntq;
+    int32_t min_ntc = INT32_MAX;
+    for (int32_t i = 0; i < n; ++i)
+      min_ntc = std::min(min_ntc, (plan[i].pers_before + 63) / 64 + s.C / 64);
+    const int32_t target = 2 * std::max(1, p->cus);
+    if (wgs < target)
+      a.nsplit = std::max(1, std::min({(target + wgs - 1) / wgs, min_ntc / 4, 16}));
+    if (a.nsplit > 1) {
+      if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
+                               (size_t)n * s.Hkv * ntq * a.nsplit * 128 * (s.D + 2) * sizeof(float)))
+        return st;
+      a.part = p->part;
+    }
+  }
   ABK_HIP(abk::launch_compress(a, p->stream));
   return ABK_OK;
 }

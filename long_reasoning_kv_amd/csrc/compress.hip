@@ -216,12 +216,13 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   const DevPool& P = a.P;
   const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  // workgroup -> (pair = sequence x KV head, query tile); the tiles of one pair
-  // share blockIdx.x mod 8, i.e. one XCD and its L2
+  // workgroup -> (pair = sequence x KV head, query tile, context split); the
+  // workgroups of one pair share blockIdx.x mod 8, i.e. one XCD and its L2
   const int ntq = (4 * a.Kp + 127) / 128;
+  const int ns = a.nsplit;
   const int npair = a.n * P.Hkv;
   const int b = blockIdx.x, xcd = b & 7, jj = b >> 3;
-  const int pair = (jj / ntq) * 8 + xcd, qt = jj % ntq;
+  const int pair = (jj / (ntq * ns)) * 8 + xcd, qt = (jj % (ntq * ns)) / ns, sp = jj % ns;
   if (pair >= npair) return;
   const int i = pair / P.Hkv, hk = pair % P.Hkv;
   const int32_t* rec = a.desc + i * kCompRec;
@@ -232,8 +233,15 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   const int q0 = qt * 128;    // first query row of the workgroup
   const int nq = min(128, 4 * a.Kp - q0);
   const int last_pause = (q0 + nq - 1) >> 2;
-  const int ntp = last_pause / TK + 1;  // pause-key tiles
-  const int ntiles = ntc + ntp;
+  // this split's tiles: context tiles [tc0, tc1), then, in the last split, the
+  // pause-key tiles; local tile u maps to tile index gt(u) (pause tiles follow
+  // the ntc context tiles)
+  const int cps = (ntc + ns - 1) / ns;
+  const int tc0 = min(ntc, sp * cps), tc1 = min(ntc, tc0 + cps);
+  const int nct = tc1 - tc0;
+  const int ntp = sp == ns - 1 ? last_pause / TK + 1 : 0;  // pause-key tiles
+  const int ntiles = nct + ntp;
+  auto gt = [&](int u) { return u < nct ? tc0 + u : ntc + (u - nct); };
 
   // ---- the wavefront's query rows: rotated at the bitrev position, rounded
   // once to bf16 (like stored keys); the softmax scale goes on the fp32 scores
@@ -343,12 +351,12 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   // the barrier that ends the step. The load is unconditional (the last one
   // repeats the last tile into the spare buffer): a load issued on one path
   // only makes the compiler wait for it before every later LDS read.
-  int page_next = page_of(min(1, ntiles - 1));
-  auto step = [&](int t, const uint4* __restrict__ ck, const uint4* __restrict__ cv,
+  int page_next = page_of(gt(min(1, ntiles - 1)));
+  auto step = [&](int u, const uint4* __restrict__ ck, const uint4* __restrict__ cv,
                   uint4* __restrict__ nk, uint4* __restrict__ nv) __attribute__((always_inline)) {
-    const int tn = min(t + 1, ntiles - 1);
-    issue(tn, page_next, nk, nv);
-    page_next = page_of(min(t + 2, ntiles - 1));
+    const int t = gt(u);
+    issue(gt(min(u + 1, ntiles - 1)), page_next, nk, nv);
+    page_next = page_of(gt(min(u + 2, ntiles - 1)));
     const bool ctx = t < ntc;
     const int nval = ctx ? (t == npp - 1 ? n_pers - t * TK : TK) : min(TK, a.Kp - (t - ntc) * TK);
     const int kbase = ctx ? 0 : (t - ntc) * TK;  // pause index of key 0 of a pause tile
@@ -437,17 +445,36 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
     }
   };
 
-  issue(0, page_of(0), lk0, lv0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, lk0, lv0, lk1, lv1);
+  if (ntiles > 0) {
+    issue(gt(0), page_of(gt(0)), lk0, lv0);
     __syncthreads();
-    if (t + 1 >= ntiles) break;
-    step(t + 1, lk1, lv1, lk0, lv0);
-    __syncthreads();
+    for (int u = 0; u < ntiles; u += 2) {
+      step(u, lk0, lv0, lk1, lv1);
+      __syncthreads();
+      if (u + 1 >= ntiles) break;
+      step(u + 1, lk1, lv1, lk0, lv0);
+      __syncthreads();
+    }
   }
 
-  // ---- output: O^T / l; lane holds dims 16 db + 4 g4 + e of query l16
+  // ---- output: O^T / l; lane holds dims 16 db + 4 g4 + e of query l16. With
+  // context splits: the unnormalised partial (O, m, l) for compress_merge_kernel
+  if (ns > 1) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float L = rows4_sum(l_run[nb]);
+      const int rl = wave * 32 + nb * 16 + l16;
+      if (rl >= nq) continue;
+      float* pp = a.part + (((((size_t)i * P.Hkv + hk) * ntq + qt) * ns + sp) * 128 + rl) * (D + 2);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *(f32x4_t*)(pp + 16 * db + 4 * g4) = acc_o[nb][db];
+      if (g4 == 0) {
+        pp[D] = m_run[nb];
+        pp[D + 1] = L;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const float L = rows4_sum(l_run[nb]);
@@ -467,7 +494,42 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   }
 }
 
+// ---- context splits: merge the partials of one (sequence, KV head, query tile) -------
+//
+// Workgroup = (pair, query tile); 8 rows x 32 threads at a time, each thread 4
+// dims: out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s.
+__global__ void __launch_bounds__(256) compress_merge_kernel(CompressArgs a) {
+  constexpr int D = 128, G = 4;
+  const int ntq = (4 * a.Kp + 127) / 128, ns = a.nsplit;
+  const int pair = blockIdx.x / ntq, qt = blockIdx.x % ntq;
+  const int i = pair / a.P.Hkv, hk = pair % a.P.Hkv;
+  const int q0 = qt * 128, nq = min(128, 4 * a.Kp - q0);
+  const float* base = a.part + (((size_t)i * a.P.Hkv + hk) * ntq + qt) * ns * 128 * (D + 2);
+  const int d = 4 * (threadIdx.x & 31);
+  for (int rl = threadIdx.x >> 5; rl < nq; rl += 8) {
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, base[((size_t)s2 * 128 + rl) * (D + 2) + D]);
+    float Ls = 0.f;
+    f32x4_t O = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s2 = 0; s2 < ns; ++s2) {
+      const float* pp = base + ((size_t)s2 * 128 + rl) * (D + 2);
+      const float wgt = fast_exp2(pp[D] - M);
+      Ls += wgt * pp[D + 1];
+      O += wgt * *(const f32x4_t*)(pp + d);
+    }
+    const int r = q0 + rl, pz = r >> 2, hh = r & 3;
+    const float inv = 1.f / Ls;
+    bf16_t* dst = (bf16_t*)a.out + (((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh) * D + d;
+    *(uint2*)dst = make_uint2(pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv));
+    if (d == 0) a.lse[((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh] = (M + __log2f(Ls)) * 0.6931471805599453f;
+  }
+}
+
 // ---- launcher ----------------------------------------------------------------------
+
+bool compress_mfma_supported(const DevPool& P, int32_t G) {
+  return P.dtype == 1 && P.D == 128 && G == 4 && P.pr == 64;
+}
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
@@ -483,8 +545,10 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
     // tiles of one (sequence, KV head) pair share blockIdx.x mod 8 (one XCD)
     const int ntq = (4 * a.Kp + 127) / 128;
     const int npair = a.n * a.P.Hkv;
-    const int nwg = ((npair + 7) / 8) * 8 * ntq;
+    const int nwg = ((npair + 7) / 8) * 8 * ntq * a.nsplit;
     hipLaunchKernelGGL(compress_attn_mfma_kernel, dim3(nwg), dim3(256), 0, s, a);
+    if (a.nsplit > 1)
+      hipLaunchKernelGGL(compress_merge_kernel, dim3(npair * ntq), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -92,7 +92,9 @@ struct CompressArgs {
   float* lse;
   void* kp_rot;          // workspace [n][Hkv][Kp][D]: rotated pause keys
   const int32_t* desc;   // n records, then page lists
+  float* part;           // nsplit > 1: [n][Hkv][query tiles][nsplit][128][D + 2] partials
   int32_t layer, n, Hq, G, Kp, quota, log2Kp;
+  int32_t nsplit;        // MFMA path: context splits per query tile (1 = none)
 };
 
 // Fill: desc holds per layer {pers_off, npers_pages, open_off, nopen_pages}
@@ -136,6 +138,7 @@ hipError_t launch_decode_mfma(const StreamArgs& a, int32_t nwaves, hipStream_t s
 hipError_t launch_free(const FreeArgs& a, hipStream_t s);
 hipError_t launch_prompt(const PromptArgs& a, hipStream_t s);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+bool compress_mfma_supported(const DevPool& P, int32_t G);
 hipError_t launch_fill(const FillArgs& a, int32_t max_rows, hipStream_t s);
 hipError_t launch_read(const ReadArgs& a, hipStream_t s);
 hipError_t launch_export(const ExportArgs& a, hipStream_t s);

@@ -132,3 +132,35 @@ def test_block_compression_event_sampled():
     for i, s in enumerate(sids):
         for l in (0, L - 1):
             assert run.pool.seq_query(s, l)["resident_rows"] == int(P[i]) + (int(b[i]) + 1) * int(quotas[l])
+
+
+def test_compression_of_few_sequences_splits_the_context():
+    """One or two sequences completing a block: the context of each query tile
+    is split over several workgroups and merged; same bars as above."""
+    quotas = [256, 64]
+    for Ps, bs in (([300], [20]), ([130, 500], [3, 41])):
+        run = Run(L=2, Hq=HQ, Hkv=HKV, D=D, C=C, Kp=KP, quota=quotas, pr=PR, dtype="bf16",
+                  max_seqs=4, pool_bytes=1 << 30, max_position=33792, seed=5)
+        sids = [run.new_seq(P, i) for i, P in enumerate(Ps)]
+        for s, b in zip(sids, bs):
+            run.fill(s, (b + 1) * C)
+        queries = [0, 5, 128, 255]
+        for l in range(2):
+            out, lse = run.compress_layer(sids, l)
+            out, lse = host(out), host(lse)
+            for n, s in enumerate(sids):
+                b = run.nb[s]
+                qraw = run.rows(s, l, PAUSE, np.full(KP, b), np.arange(KP), synth.WHICH_Q)
+                o_ref, l_ref, code = oracle.compress(run.view(s, l), run.G[s], b, b, qraw, run.fetch(s, l),
+                                                     oracle.BF16, run.base, queries=queries)
+                _close(f"split compress out P{Ps[n]} b{b} L{l}", out[n][queries], o_ref, 2e-2)
+                _close(f"split compress lse P{Ps[n]} b{b} L{l}", lse[n][queries], l_ref, 1e-3)
+                q_l = quotas[l]
+                r0 = run.pool.seq_query(s, l)["resident_rows"] - C - q_l
+                k = torch.empty((q_l, HKV, D), device="cuda", dtype=torch.bfloat16)
+                v = torch.empty_like(k)
+                run.pool.read_rows(s, l, r0, q_l, k, v)
+                torch.cuda.synchronize()
+                np.testing.assert_array_equal(host(v), code[5])
+                np.testing.assert_array_equal(host(k), code[4])
+        run.pool.close()
