@@ -319,10 +319,16 @@ def run_decode(args, torch, abk):
                 nb[i] += 1
         for l in range(L):
             q, k, v = views[t][l]
-            pool.append_kv(l, sids, k, v)
-            if rec is not None:
-                rec[l][0].record()
-            pool.decode_attention(l, sids, q, out, lse)
+            if args.separate_append:
+                # the events bracket the decode call alone
+                pool.append_kv(l, sids, k, v)
+                if rec is not None:
+                    rec[l][0].record()
+                pool.decode_attention(l, sids, q, out, lse)
+            else:
+                if rec is not None:
+                    rec[l][0].record()
+                pool.append_decode(l, sids, k, v, q, out, lse)
             if rec is not None:
                 rec[l][1].record()
         if rec is not None:
@@ -339,10 +345,11 @@ def run_decode(args, torch, abk):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    # algorithmic bytes of one decode launch: every resident K and V row once,
-    # plus q, out (bf16) and lse (fp32)
+    # algorithmic bytes of one decode call: every resident K and V row once,
+    # plus q, out (bf16) and lse (fp32); a fused call also reads the new k, v
+    # and writes them as the new row
     row_bytes = 2 * HKV * D * 2
-    io_bytes = B * (2 * HQ * D * 2 + HQ * 4)
+    io_bytes = B * (2 * HQ * D * 2 + HQ * 4) + (0 if args.separate_append else B * 2 * row_bytes)
     dec_ms = [e0.elapsed_time(e1) for evs in ev for e0, e1 in evs]
     dec_bytes = [rows * row_bytes + io_bytes for rl in rows_log for rows in rl]
     achieved = sum(dec_bytes) / (sum(dec_ms) * 1e-3) / 1e9
@@ -360,13 +367,15 @@ def run_decode(args, torch, abk):
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic_from_profiles("decode_mfma", float(np.mean(dec_bytes))),
-            "kernel": "decode_mfma_kernel (+ decode_stream_merge_kernel)",
+            "kernel": ("decode_mfma_kernel (+ decode_stream_merge_kernel)" if args.separate_append else
+                       "decode_mfma_kernel with fused append (+ decode_stream_merge_kernel)"),
             "algorithmic_bytes_per_launch": float(np.mean(dec_bytes)),
             "avg_launch_us": float(np.mean(dec_ms)) * 1e3,
         },
         "config": {
             "workload": "36-layer per-layer-quota decode step (append + split-KV decode per "
-                        "layer; compress+free when a block completes), 22 sequences",
+                        "layer, one fused call each; compress+free when a block completes), "
+                        "22 sequences",
             "layers": L, "batch": B, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
             "block_tokens": C, "pause_tokens": Kp, "quotas": "6x256/12x64/18x128 (seeded)",
             "prompt": "U[128,512]", "generated": "U[4096,32768]", "page_rows": PR,
@@ -527,6 +536,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--split-rows", type=int, default=0, help="rows per split-KV work item (0: library default)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append and decode as two calls per layer (default: abk_append_decode)")
     ap.add_argument("--compress-reps", type=int, default=2)
     ap.add_argument("--no-compress", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")

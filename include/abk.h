@@ -127,6 +127,17 @@ abk_status abk_append_kv(abk_pool* p, int32_t layer, int32_t n, const int32_t* s
 abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
                                 const void* q, void* out, float* lse);
 
+/* Steps a1 + a2 + a3 in one call: append the current token (k, v as for
+ * abk_append_kv) and decode with q (as for abk_decode_attention) at one layer.
+ * The result equals the two calls in sequence. For bf16 pools with d = 128,
+ * four query heads per KV head, 64-row pages and the automatic schedule it is
+ * one decode launch that also writes the new row (plus the split-merge
+ * launch), saving the append launch per layer; other configurations issue the
+ * two steps. Errors as for the two calls; on the fused path every check
+ * happens before anything changes. */
+abk_status abk_append_decode(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                             const void* k, const void* v, const void* q, void* out, float* lse);
+
 /* Steps a4-a6: compress the completed open block b of each sequence at one
  * layer. q_pause [n, Kp, Hq, d], k_pause and v_pause [n, Kp, Hkv, d] device,
  * pre-RoPE (Kp = the layer's pause count). Pause k is rotated at

@@ -19,7 +19,8 @@ F32, BF16 = 0, 1
 
 SYMBOLS = [
     "abk_pool_create", "abk_pool_destroy", "abk_seq_create", "abk_seq_release",
-    "abk_write_prompt", "abk_append_kv", "abk_decode_attention", "abk_compress_block",
+    "abk_write_prompt", "abk_append_kv", "abk_decode_attention", "abk_append_decode",
+    "abk_compress_block",
     "abk_free_block", "abk_seq_query", "abk_export_layout", "abk_read_rows",
     "abk_pool_stats", "abk_synth_fill", "abk_last_error",
 ]
@@ -70,6 +71,7 @@ def lib():
             "abk_write_prompt": [vp, i32, i32, vp, vp],
             "abk_append_kv": [vp, i32, i32, ip, vp, vp],
             "abk_decode_attention": [vp, i32, i32, ip, vp, vp, vp],
+            "abk_append_decode": [vp, i32, i32, ip, vp, vp, vp, vp, vp],
             "abk_compress_block": [vp, i32, i32, ip, vp, vp, vp, vp, vp],
             "abk_free_block": [vp, i32, ip],
             "abk_seq_query": [vp, i32, i32, ctypes.POINTER(SeqInfo)],
@@ -161,6 +163,11 @@ class Pool:
     def decode_attention(self, layer, seq_ids, q, out, lse):
         n, ids = _ids(seq_ids)
         _check(lib().abk_decode_attention(self._h, layer, n, ids, _ptr(q), _ptr(out), _ptr(lse)))
+
+    def append_decode(self, layer, seq_ids, k, v, q, out, lse):
+        n, ids = _ids(seq_ids)
+        _check(lib().abk_append_decode(self._h, layer, n, ids, _ptr(k), _ptr(v), _ptr(q), _ptr(out),
+                                       _ptr(lse)))
 
     def compress_block(self, layer, seq_ids, q_pause, k_pause, v_pause, out, lse):
         n, ids = _ids(seq_ids)

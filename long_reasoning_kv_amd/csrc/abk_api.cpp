@@ -323,6 +323,89 @@ abk_status abk_append_kv(abk_pool* p, int32_t layer, int32_t n, const int32_t* s
   return ABK_OK;
 }
 
+namespace {
+
+// MFMA decode schedule: equal runs of 32-row tiles per wavefront over the
+// flattened (sequence, head, tile) work; a sequence's tiles cover its
+// persistent rows, then its open rows. `before_append`: counts exclude the
+// token a fused call is about to append (which the kernel handles itself), and
+// a sequence with no rows yet gets one empty tile. Fails (UNSUPPORTED) before
+// anything changes if a head would need more than kMaxSplits partials.
+abk_status mfma_schedule(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                         bool before_append, std::vector<abk::StreamArgs>* chunks) {
+  const abk::Shape& s = p->shape;
+  constexpr int32_t TK = 32;
+  chunks->clear();
+  for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
+    const int32_t m = std::min(n - c0, abk::kMaxBatch);
+    chunks->emplace_back();
+    abk::StreamArgs& a = chunks->back();
+    a.useg[0] = 0;
+    for (int32_t i = 0; i < m; ++i) {
+      const int32_t id = seq_ids[c0 + i];
+      const int32_t pers = p->host.seq(id).layers[layer].pers_rows;
+      const int32_t open = p->host.open_rows(id, layer);
+      int32_t units = (pers + TK - 1) / TK + (open + TK - 1) / TK;
+      if (before_append && units == 0) units = 1;
+      a.slot[i] = id;
+      a.useg[i + 1] = a.useg[i] + units * s.Hkv;
+    }
+    const int32_t U = a.useg[m];
+    const int32_t kMinUnits = 4;  // per wavefront, to amortise its set-up
+    int32_t W = std::max(1, std::min(p->mfma_waves, (U + kMinUnits - 1) / kMinUnits));
+    const int32_t T = (U + W - 1) / W;
+    int32_t maxp = 1;
+    for (int32_t i = 0; i < m; ++i) {
+      const int32_t units = (a.useg[i + 1] - a.useg[i]) / s.Hkv;
+      for (int32_t h = 0; h < s.Hkv; ++h) {
+        const int32_t S = a.useg[i] + h * units;
+        maxp = std::max(maxp, (S + units - 1) / T - S / T + 1);
+      }
+    }
+    if (maxp > abk::kMaxSplits) return set_err(ABK_ERR_UNSUPPORTED, "too many partials per head");
+    a.n = m;
+    a.T = T;
+    a.U = U;
+    a.maxp = maxp;
+  }
+  return ABK_OK;
+}
+
+// Launch the scheduled chunks; k/v/new_page non-null: fused append of the
+// current token.
+abk_status launch_mfma_chunks(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                              const void* q, void* out, float* lse, const void* k, const void* v,
+                              const int32_t* new_page, std::vector<abk::StreamArgs>* chunks) {
+  const abk::Shape& s = p->shape;
+  const int32_t G = s.Hq / s.Hkv;
+  const size_t qb = (size_t)s.Hq * s.D * s.esize();
+  const size_t kb = (size_t)s.Hkv * s.D * s.esize();
+  size_t need = 0;
+  for (const auto& a : *chunks) need = std::max(need, (size_t)a.n * s.Hkv * a.maxp * G * (s.D + 2));
+  if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes, need * sizeof(float))) return st;
+  for (size_t c = 0; c < chunks->size(); ++c) {
+    abk::StreamArgs& a = (*chunks)[c];
+    const int32_t c0 = (int32_t)c * abk::kMaxBatch;
+    const int32_t W = (a.U + a.T - 1) / a.T;
+    a.P = p->dev;
+    a.q = (const char*)q + c0 * qb;
+    a.out = (char*)out + c0 * qb;
+    a.lse = lse + (size_t)c0 * s.Hq;
+    a.part = p->part;
+    a.layer = layer;
+    a.compress = s.compress;
+    a.fused = k != nullptr;
+    a.k = k ? (const char*)k + c0 * kb : nullptr;
+    a.v = v ? (const char*)v + c0 * kb : nullptr;
+    for (int32_t i = 0; i < a.n; ++i) a.new_page[i] = new_page ? new_page[c0 + i] : -1;
+    (void)seq_ids;
+    ABK_HIP(abk::launch_decode_mfma(a, W, p->stream));
+  }
+  return ABK_OK;
+}
+
+}  // namespace
+
 abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
                                 const void* q, void* out, float* lse) {
   if (abk_status st = check_pool(p)) return st;
@@ -334,52 +417,9 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
   const int32_t G = s.Hq / s.Hkv;
   const size_t qb = (size_t)s.Hq * s.D * s.esize();
   if (p->mfma_waves > 0 && p->split_rows == 0) {
-    // MFMA decode: equal runs of 32-row tiles per wavefront over the flattened
-    // (sequence, head, tile) work; a sequence's tiles cover its persistent rows,
-    // then its open rows
-    constexpr int32_t TK = 32;
-    for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
-      const int32_t m = std::min(n - c0, abk::kMaxBatch);
-      abk::StreamArgs a;
-      a.useg[0] = 0;
-      for (int32_t i = 0; i < m; ++i) {
-        const int32_t id = seq_ids[c0 + i];
-        const int32_t pers = p->host.seq(id).layers[layer].pers_rows;
-        const int32_t open = p->host.open_rows(id, layer);
-        const int32_t units = (pers + TK - 1) / TK + (open + TK - 1) / TK;
-        a.slot[i] = id;
-        a.useg[i + 1] = a.useg[i] + units * s.Hkv;
-      }
-      const int32_t U = a.useg[m];
-      const int32_t kMinUnits = 4;  // per wavefront, to amortise its set-up
-      int32_t W = std::max(1, std::min(p->mfma_waves, (U + kMinUnits - 1) / kMinUnits));
-      const int32_t T = (U + W - 1) / W;
-      W = (U + T - 1) / T;
-      int32_t maxp = 1;
-      for (int32_t i = 0; i < m; ++i) {
-        const int32_t units = (a.useg[i + 1] - a.useg[i]) / s.Hkv;
-        for (int32_t h = 0; h < s.Hkv; ++h) {
-          const int32_t S = a.useg[i] + h * units;
-          maxp = std::max(maxp, (S + units - 1) / T - S / T + 1);
-        }
-      }
-      if (maxp > abk::kMaxSplits) return set_err(ABK_ERR_UNSUPPORTED, "too many partials per head");
-      if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
-                               (size_t)m * s.Hkv * maxp * G * (s.D + 2) * sizeof(float)))
-        return st;
-      a.P = p->dev;
-      a.q = (const char*)q + c0 * qb;
-      a.out = (char*)out + c0 * qb;
-      a.lse = lse + (size_t)c0 * s.Hq;
-      a.part = p->part;
-      a.layer = layer;
-      a.n = m;
-      a.T = T;
-      a.U = U;
-      a.maxp = maxp;
-      ABK_HIP(abk::launch_decode_mfma(a, W, p->stream));
-    }
-    return ABK_OK;
+    std::vector<abk::StreamArgs> chunks;
+    if (abk_status st = mfma_schedule(p, layer, n, seq_ids, false, &chunks)) return st;
+    return launch_mfma_chunks(p, layer, n, seq_ids, q, out, lse, nullptr, nullptr, nullptr, &chunks);
   }
   if (p->stream_wgs > 0 && p->split_rows == 0) {
     // stream-K: equal runs of 32-row units over the flattened (sequence, head, unit) work
@@ -387,6 +427,9 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
     for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
       const int32_t m = std::min(n - c0, abk::kMaxBatch);
       abk::StreamArgs a;
+      a.fused = 0;
+      a.compress = s.compress;
+      a.k = a.v = nullptr;
       a.useg[0] = 0;
       for (int32_t i = 0; i < m; ++i) {
         const auto& lay = p->host.seq(seq_ids[c0 + i]).layers[layer];
@@ -467,6 +510,25 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
     ABK_HIP(abk::launch_decode(a, a.prefix[m], p->stream));
   }
   return ABK_OK;
+}
+
+abk_status abk_append_decode(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                             const void* k, const void* v, const void* q, void* out, float* lse) {
+  if (abk_status st = check_pool(p)) return st;
+  if (!p->host_only && n > 0 && (!k || !v || !q || !out || !lse))
+    return set_err(ABK_ERR_INVALID_ARG, "k/v/q/out/lse is NULL");
+  if (p->host_only || n == 0 || p->mfma_waves == 0 || p->split_rows != 0) {
+    // other shapes and schedules: the two steps as separate launches
+    if (abk_status st = abk_append_kv(p, layer, n, seq_ids, k, v)) return st;
+    return abk_decode_attention(p, layer, n, seq_ids, q, out, lse);
+  }
+  if (p->host.check_layer(layer)) return set_err(ABK_ERR_INVALID_ARG, "bad layer");
+  if (abk::Status st = p->host.check_batch(n, seq_ids)) return from_host(st, p->host.err);
+  std::vector<abk::StreamArgs> chunks;
+  if (abk_status st = mfma_schedule(p, layer, n, seq_ids, true, &chunks)) return st;
+  std::vector<int32_t> new_page;
+  if (abk::Status st = p->host.append(layer, n, seq_ids, &new_page)) return from_host(st, p->host.err);
+  return launch_mfma_chunks(p, layer, n, seq_ids, q, out, lse, k, v, new_page.data(), &chunks);
 }
 
 abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,

@@ -979,6 +979,12 @@ __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) 
   const int segS = a.useg[i] + h * units;
   const int wa = segS / a.T, wb = (segS + units - 1) / a.T;
   const int ns = wb - wa + 1;
+  if (a.fused && h == 0 && threadIdx.x == 0) {
+    // the fused append's row is now in place: advance the counts and position
+    int32_t* meta = a.P.meta + (a.slot[i] * a.P.L + a.layer) * 4;
+    meta[a.compress ? 1 : 0] += 1;
+    meta[2] += 1;
+  }
   if (ns == 1) return;
   const float* base = a.part + ((size_t)i * Hkv + h) * a.maxp * G * (D + 2);
   for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
@@ -1097,9 +1103,10 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
       *nval = min(TK, c.n_pers - c.lu * TK);
     } else {
       const int j = c.lu - c.ptiles;
-      page = tab[P.max_pers + (j >> 1)];
-      r0 = (j & 1) * TK;
       *nval = min(TK, c.n_open - j * TK);
+      // a fused call's only tile of a sequence with no rows yet is empty
+      page = *nval > 0 ? tab[P.max_pers + (j >> 1)] : 0;
+      r0 = (j & 1) * TK;
     }
     *off = (((size_t)page * P.Hkv + c.h) * PR + r0) * RB;
   };
@@ -1112,6 +1119,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
     size_t off;
     int nval;
     locate(c, &off, &nval);
+    if (nval <= 0) return;  // empty tile: nothing to load
 #pragma unroll
     for (int j = 0; j < TK / 4; ++j) {
       const int row = 4 * j + dr;
@@ -1131,7 +1139,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
   float m_run = -1e30f, l_run = 0.f;
   auto start_segment = [&](const Cur& c) __attribute__((always_inline)) {
     cptr meta = (cptr)meta_of(P, c.slot, a.layer);
-    const int qpos = meta[2];
+    const int qpos = meta[2] + (a.fused ? 1 : 0);  // fused: the token appended here
     const int hh = l16 < G ? l16 : 0;
     const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)c.i * Hq + c.h * G + hh) * D;
     const double2* rope = P.rope + (size_t)qpos * (D / 2);
@@ -1156,6 +1164,65 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
     for (int db = 0; db < 8; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     m_run = -1e30f;
     l_run = 0.f;
+    if (!a.fused || c.lu != 0) return;
+    // fused append, first piece of the segment: rotate the current token's key
+    // (fp64, rounded once to bf16 like every stored key), write its K and V row
+    // of this KV head, and start the softmax with it (p = 1, O = v)
+    const bf16_t* krow = (const bf16_t*)a.k + ((size_t)c.i * P.Hkv + c.h) * D;
+    const bf16_t* vrow = (const bf16_t*)a.v + ((size_t)c.i * P.Hkv + c.h) * D;
+    float kx[4][8];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) unpack16(*(const uint4*)(krow + 32 * ks + 8 * g4), kx[ks], bf16_t());
+    uint4 kw[4];
+    float dotp = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      double y0[8], y1[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double2 cs = rope[32 * ks + 8 * g4 + j];
+        y0[j] = rot_first(kx[ks][j], kx[ks + 2][j], cs);
+        y1[j] = rot_second(kx[ks][j], kx[ks + 2][j], cs);
+      }
+      kw[ks] = make_uint4(pack_bf16x2_f64(y0[0], y0[1]), pack_bf16x2_f64(y0[2], y0[3]),
+                          pack_bf16x2_f64(y0[4], y0[5]), pack_bf16x2_f64(y0[6], y0[7]));
+      kw[ks + 2] = make_uint4(pack_bf16x2_f64(y1[0], y1[1]), pack_bf16x2_f64(y1[2], y1[3]),
+                              pack_bf16x2_f64(y1[4], y1[5]), pack_bf16x2_f64(y1[6], y1[7]));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float qf[8], kf[8];
+      unpack16(qh[ks], qf, bf16_t());
+      unpack16(kw[ks], kf, bf16_t());
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dotp = fmaf(qf[j], kf[j], dotp);
+    }
+    m_run = rows4_sum(dotp) * qs;
+    l_run = g4 == 0 ? 1.f : 0.f;  // the lane groups' sums are added at the end
+    uint2 vw[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      vw[db] = *(const uint2*)(vrow + 16 * db + 4 * g4);
+      acc[db] = f32x4_t{__uint_as_float(vw[db].x << 16), __uint_as_float(vw[db].x & 0xffff0000u),
+                        __uint_as_float(vw[db].y << 16), __uint_as_float(vw[db].y & 0xffff0000u)};
+    }
+    // the row: open block (or persistent list in full-KV mode), row r
+    const int r = a.compress ? c.n_open : c.n_pers;
+    const int tbase = a.compress ? P.max_pers : 0;
+    int32_t* tabw = ptab_of(P, c.slot, a.layer) + tbase;
+    const int pidx = r / PR, srow = r % PR;
+    const int page = srow == 0 ? a.new_page[c.i] : ((cptr)tabw)[pidx];
+    if (l16 == 0) {
+      const size_t o = (((size_t)page * P.Hkv + c.h) * PR + srow) * D;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) *(uint4*)((bf16_t*)P.kpool + o + 32 * ks + 8 * g4) = kw[ks];
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *(uint2*)((bf16_t*)P.vpool + o + 16 * db + 4 * g4) = vw[db];
+    }
+    if (c.h == 0 && lane == 0) {
+      P.pos[(size_t)page * PR + srow] = qpos;
+      if (srow == 0) tabw[pidx] = page;
+    }
   };
   auto end_segment = [&](const Cur& c) __attribute__((always_inline)) {
     const float L = rows4_sum(l_run);
@@ -1195,8 +1262,15 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
       last_i = cc.i;
       last_h = cc.h;
     }
-    // ---- the whole tile from LDS into registers
+    size_t off;
+    int nval;
+    locate(cc, &off, &nval);
+    // ---- the whole tile from LDS into registers, once its load has landed. The
+    // wait is explicit: the load is issued on a conditional path, which the
+    // compiler's own tracking of loads into LDS does not follow
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     uint4 ka[2][4], va[8];
+    if (nval > 0) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int kr = 8 * (l16 >> 2) + 4 * mb + (l16 & 3);
@@ -1219,14 +1293,13 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
       }
       va[db] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
-    size_t off;
-    int nval;
-    locate(cc, &off, &nval);
+    }
     // ---- the next tile into the same LDS (once every read above has landed)
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     if (t + 1 < Fend) advance(ci);
     issue(ci);  // unconditional: past the end it repeats the last tile
     // ---- S^T, softmax, O^T
+    if (nval > 0) {
     f32x4_t sc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -1264,6 +1337,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc[db] = mfma_bf16(va[db], pb, acc[db]);
+    }
     if (cc.lu == cc.units - 1 || t == Fend - 1) end_segment(cc);
     advance(cc);
   }
@@ -1353,7 +1427,7 @@ int32_t decode_mfma_waves_per_cu() {
 hipError_t launch_decode_mfma(const StreamArgs& a, int32_t nwaves, hipStream_t s) {
   if (a.n == 0 || nwaves == 0) return hipSuccess;
   hipLaunchKernelGGL(decode_mfma_kernel, dim3((nwaves + 3) / 4), dim3(256), 0, s, a);
-  if (a.maxp > 1)
+  if (a.maxp > 1 || a.fused)
     hipLaunchKernelGGL(decode_stream_merge_kernel, dim3(a.n, a.P.Hkv), dim3(512), 0, s, a);
   return hipGetLastError();
 }

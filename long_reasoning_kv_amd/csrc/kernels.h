@@ -60,9 +60,16 @@ struct StreamArgs {
   void* out;
   float* lse;
   float* part;  // [n][Hkv][maxp][4][D + 2]
+  // fused append (decode_mfma_kernel only): the current token's k, v [n][Hkv][D]
+  // are written and attended here; counts in meta are the ones before it, and
+  // decode_stream_merge_kernel advances them afterwards
+  const void* k;
+  const void* v;
+  int32_t fused, compress;
   int32_t layer, n, T, U, maxp;
   int32_t slot[kMaxBatch];
   int32_t useg[kMaxBatch + 1];
+  int32_t new_page[kMaxBatch];  // fused: page taken for the current row, or -1
 };
 
 struct FreeArgs {
@@ -134,7 +141,7 @@ hipError_t launch_decode_stream(const StreamArgs& a, int32_t nwg, hipStream_t s)
 // wavefront-level stream-K over 16-row tiles (U, T, useg in tiles; T per wavefront)
 bool decode_mfma_supported(const DevPool& P, int32_t G);
 int32_t decode_mfma_waves_per_cu();
-hipError_t launch_decode_mfma(const StreamArgs& a, int32_t nwaves, hipStream_t s);
+hipError_t launch_decode_mfma(const StreamArgs& a, int32_t nwaves, hipStream_t s);  // + merge (always when fused)
 hipError_t launch_free(const FreeArgs& a, hipStream_t s);
 hipError_t launch_prompt(const PromptArgs& a, hipStream_t s);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);

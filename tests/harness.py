@@ -149,6 +149,36 @@ class Run:
         torch.cuda.synchronize()
         return host(out), host(lse), q
 
+    def step_fused(self, sids):
+        """One token of every sequence through abk_append_decode at every layer;
+        returns [(out, lse, q)] per layer."""
+        res = []
+        for l in range(self.L):
+            k = np.stack([self.rows(s, l, TEXT, [self.G[s]], 0, synth.WHICH_K)[0] for s in sids])
+            v = np.stack([self.rows(s, l, TEXT, [self.G[s]], 0, synth.WHICH_V)[0] for s in sids])
+            q = np.stack([self.rows(s, l, TEXT, [self.G[s]], 0, synth.WHICH_Q)[0] for s in sids])
+            out = torch.empty((len(sids), self.Hq, self.D), device="cuda", dtype=TORCH_DT[self.dtype])
+            lse = torch.empty((len(sids), self.Hq), device="cuda", dtype=torch.float32)
+            self.pool.append_decode(l, sids, dev(k, self.dtype), dev(v, self.dtype), dev(q, self.dtype),
+                                    out, lse)
+            torch.cuda.synchronize()
+            res.append((host(out), host(lse), q))
+        for s in sids:
+            self.G[s] += 1
+        return res
+
+    def step_separate(self, sids):
+        """The same step as step_fused through abk_append_kv + abk_decode_attention."""
+        self.append_token(sids)
+        return [self.decode(sids, l) for l in range(self.L)]
+
+    def compress_and_free(self, sids):
+        for l in range(self.L):
+            self.compress_layer(sids, l)
+        self.pool.free_block(sids)
+        for s in sids:
+            self.nb[s] += 1
+
     def oracle_decode(self, sid, layer, q):
         return oracle.decode(self.view(sid, layer), self.G[sid], self.nb[sid], q, self.fetch(sid, layer),
                              ORC_DT[self.dtype], self.base)

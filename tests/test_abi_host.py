@@ -83,8 +83,14 @@ def _both(pool, pm, fpool, fmodel):
     return r1
 
 
+def _append_then_decode(pm, l, sids):
+    pm.append(l, sids)
+    return pm.check_decode(l, sids)
+
+
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("compress", [True, False])
-def test_host_pool_matches_page_model(compress):
+def test_host_pool_matches_page_model(compress, fused):
     pool = _pool(compress=compress, _pages=160)
     pm = PageModel(num_pages=160, page_rows=4, num_layers=3, C=8, quotas=[4, 2, 1],
                    pauses=[4, 4, 4], max_seqs=4, compress=compress)
@@ -96,6 +102,11 @@ def test_host_pool_matches_page_model(compress):
                   lambda s=s, l=l: pm.write_prompt(s, l))
     for t in range(30):
         for l in range(3):
+            if fused:
+                # abk_append_decode: the append's bookkeeping, then the decode's checks
+                _both(pool, pm, lambda l=l: pool.append_decode(l, sids, None, None, None, None, None),
+                      lambda l=l: _append_then_decode(pm, l, sids))
+                continue
             _both(pool, pm, lambda l=l: pool.append_kv(l, sids, None, None),
                   lambda l=l: pm.append(l, sids))
             _both(pool, pm, lambda l=l: pool.decode_attention(l, sids, None, None, None),

@@ -50,7 +50,8 @@ def _sample_layers(quotas):
     return out
 
 
-def test_36_layer_quota_decode_step_sampled():
+@pytest.mark.parametrize("fused", [False, True])
+def test_36_layer_quota_decode_step_sampled(fused):
     quotas, P, G = bench.decode_workload(2)
     B = len(P)
     run = Run(L=L, Hq=HQ, Hkv=HKV, D=D, C=C, Kp=int(quotas.max()), quota=quotas.tolist(), pr=PR,
@@ -59,13 +60,21 @@ def test_36_layer_quota_decode_step_sampled():
     sids = [run.new_seq(int(P[i]), i) for i in range(B)]
     for s, g in zip(sids, G):
         run.fill(s, int(g))
-    # the step's token at every layer (a full open block is compressed first)
-    run.grow({s: int(g) + 1 for s, g in zip(sids, G)})
-    print(f"[fullsize] 36-layer step: {B} sequences filled and appended", flush=True)
     layers = _sample_layers(quotas)
     seqs = (0, 11, 21)
+    if fused:
+        # the step through abk_append_decode, as bench.py runs it (a full open
+        # block is compressed and freed first)
+        full = [s for s in sids if run.G[s] - run.nb[s] * C == C]
+        if full:
+            run.compress_and_free(full)
+        results = run.step_fused(sids)
+    else:
+        run.grow({s: int(g) + 1 for s, g in zip(sids, G)})
+        results = None
+    print(f"[fullsize] 36-layer step: {B} sequences filled and appended (fused={fused})", flush=True)
     for l in range(L):
-        out, lse, q = run.decode(sids, l)
+        out, lse, q = results[l] if fused else run.decode(sids, l)
         assert np.isfinite(out).all() and np.isfinite(lse).all(), l
         for i, s in enumerate(sids):
             nb = run.nb[s]

@@ -287,3 +287,56 @@ def test_single_layer_bf16_full_size_sampled():
     pos = run.pool.export_layout(sids[3], 0)[1]
     want = oracle.visible_keys(run.view(sids[3], 0), 7900, 15, (TEXT, 7899, 0))[3]
     assert pos == want.tolist()
+
+
+# ---- fused append + decode -------------------------------------------------------
+
+@pytest.mark.parametrize("compress", [True, False])
+def test_fused_append_decode_equals_two_calls(compress):
+    """abk_append_decode against abk_append_kv + abk_decode_attention on twin
+    pools: outputs agree (and match the oracle), and so does every stored row,
+    position and count afterwards. Covers a sequence with no rows yet, a row in
+    the middle of a page, a row that starts a fresh page, the first row after a
+    block is freed, and a second step that relies on the advanced counts."""
+    kw = dict(L=2, Hq=32, Hkv=8, D=128, C=128, Kp=32, quota=[32, 8], pr=64, dtype="bf16",
+              split_rows=0, seed=9, compress=compress, pool_bytes=256 << 20)
+    twins = [_bf16_run(**kw), _bf16_run(**kw)]
+    Ps, Gs = [0, 5, 64, 100], [0, 63, 64, 256]
+    sids = []
+    for run in twins:
+        ids = [run.new_seq(P, i) for i, P in enumerate(Ps)]
+        for s, G in zip(ids, Gs):
+            run.write_prompts(s)
+            run.grow({s: G})
+        if compress:
+            run.compress_and_free([ids[3]])  # its block is full: the next row opens a new one
+        sids.append(ids)
+    for step in range(2):
+        sep = twins[0].step_separate(sids[0])
+        fus = twins[1].step_fused(sids[1])
+        to, tl = TOL["bf16"]
+        for l in range(2):
+            # the fused path starts the softmax at the current token (p = 1, exact),
+            # the separate path reaches it through bf16 probabilities from another
+            # running maximum: differences of the order of bf16 rounding of P
+            # (2^-9 relative), bounded by 1e-2 or one bf16 ulp of out
+            a, b = fus[l][0], sep[l][0]
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.maximum(np.abs(a), np.abs(b)), 2.0 ** -20))) - 7)
+            assert (np.abs(a - b) <= np.maximum(ulp, 1e-2)).all(), f"fused vs separate out L{l} step{step}"
+            _close(f"fused vs separate lse L{l} step{step}", fus[l][1], sep[l][1], 1e-5)
+            for i, s in enumerate(sids[1]):
+                o_ref, l_ref, keys = twins[1].oracle_decode(s, l, fus[l][2][i])
+                _close(f"fused out seq{i} L{l}", fus[l][0][i], o_ref, to)
+                _close(f"fused lse seq{i} L{l}", fus[l][1][i], l_ref, tl)
+        for sa, sb in zip(*sids):
+            for l in range(2):
+                qa, qb = twins[0].pool.seq_query(sa, l), twins[1].pool.seq_query(sb, l)
+                assert qa == qb, (l, qa, qb)
+                assert twins[0].pool.export_layout(sa, l) == twins[1].pool.export_layout(sb, l)
+                n = qa["resident_rows"]
+                ka = torch.empty((n, 8, 128), device="cuda", dtype=torch.bfloat16)
+                va, kb, vb = torch.empty_like(ka), torch.empty_like(ka), torch.empty_like(ka)
+                twins[0].pool.read_rows(sa, l, 0, n, ka, va)
+                twins[1].pool.read_rows(sb, l, 0, n, kb, vb)
+                torch.cuda.synchronize()
+                assert torch.equal(ka, kb) and torch.equal(va, vb), (l,)
