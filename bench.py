@@ -374,8 +374,8 @@ def run_decode(args, torch, abk):
         },
         "config": {
             "workload": "36-layer per-layer-quota decode step (append + split-KV decode per "
-                        "layer, one fused call each; compress+free when a block completes), "
-                        "22 sequences",
+                        "layer, " + ("two calls" if args.separate_append else "one fused call") +
+                        " each; compress+free when a block completes), 22 sequences",
             "layers": L, "batch": B, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
             "block_tokens": C, "pause_tokens": Kp, "quotas": "6x256/12x64/18x128 (seeded)",
             "prompt": "U[128,512]", "generated": "U[4096,32768]", "page_rows": PR,

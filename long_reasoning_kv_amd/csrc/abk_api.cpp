@@ -381,7 +381,8 @@ abk_status launch_mfma_chunks(abk_pool* p, int32_t layer, int32_t n, const int32
   const size_t qb = (size_t)s.Hq * s.D * s.esize();
   const size_t kb = (size_t)s.Hkv * s.D * s.esize();
   size_t need = 0;
-  for (const auto& a : *chunks) need = std::max(need, (size_t)a.n * s.Hkv * a.maxp * G * (s.D + 2));
+  const size_t extra = k != nullptr;  // a fused call's partial of the current token
+  for (const auto& a : *chunks) need = std::max(need, (size_t)a.n * s.Hkv * (a.maxp + extra) * G * (s.D + 2));
   if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes, need * sizeof(float))) return st;
   for (size_t c = 0; c < chunks->size(); ++c) {
     abk::StreamArgs& a = (*chunks)[c];

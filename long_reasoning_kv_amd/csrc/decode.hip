@@ -978,7 +978,8 @@ __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) 
   const int units = (a.useg[i + 1] - a.useg[i]) / Hkv;
   const int segS = a.useg[i] + h * units;
   const int wa = segS / a.T, wb = (segS + units - 1) / a.T;
-  const int ns = wb - wa + 1;
+  // a fused call adds the current token's partial after the tiles' ones
+  const int ns = wb - wa + 1 + a.fused;
   if (a.fused && h == 0 && threadIdx.x == 0) {
     // the fused append's row is now in place: advance the counts and position
     int32_t* meta = a.P.meta + (a.slot[i] * a.P.L + a.layer) * 4;
@@ -986,7 +987,7 @@ __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) 
     meta[2] += 1;
   }
   if (ns == 1) return;
-  const float* base = a.part + ((size_t)i * Hkv + h) * a.maxp * G * (D + 2);
+  const float* base = a.part + ((size_t)i * Hkv + h) * (a.maxp + a.fused) * G * (D + 2);
   for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
     const int g = t / D, d = t % D;
     float M = -INFINITY, Ls = 0.f, O = 0.f;
@@ -1055,7 +1056,6 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
   const int Hq = P.Hkv * G;
   const int F0 = w * a.T;
   const int Fend = min(a.U, F0 + a.T);
-  if (F0 >= Fend) return;
   const char* kpool = (const char*)P.kpool;
   const char* vpool = (const char*)P.vpool;
   const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
@@ -1164,65 +1164,6 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
     for (int db = 0; db < 8; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     m_run = -1e30f;
     l_run = 0.f;
-    if (!a.fused || c.lu != 0) return;
-    // fused append, first piece of the segment: rotate the current token's key
-    // (fp64, rounded once to bf16 like every stored key), write its K and V row
-    // of this KV head, and start the softmax with it (p = 1, O = v)
-    const bf16_t* krow = (const bf16_t*)a.k + ((size_t)c.i * P.Hkv + c.h) * D;
-    const bf16_t* vrow = (const bf16_t*)a.v + ((size_t)c.i * P.Hkv + c.h) * D;
-    float kx[4][8];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) unpack16(*(const uint4*)(krow + 32 * ks + 8 * g4), kx[ks], bf16_t());
-    uint4 kw[4];
-    float dotp = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      double y0[8], y1[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double2 cs = rope[32 * ks + 8 * g4 + j];
-        y0[j] = rot_first(kx[ks][j], kx[ks + 2][j], cs);
-        y1[j] = rot_second(kx[ks][j], kx[ks + 2][j], cs);
-      }
-      kw[ks] = make_uint4(pack_bf16x2_f64(y0[0], y0[1]), pack_bf16x2_f64(y0[2], y0[3]),
-                          pack_bf16x2_f64(y0[4], y0[5]), pack_bf16x2_f64(y0[6], y0[7]));
-      kw[ks + 2] = make_uint4(pack_bf16x2_f64(y1[0], y1[1]), pack_bf16x2_f64(y1[2], y1[3]),
-                              pack_bf16x2_f64(y1[4], y1[5]), pack_bf16x2_f64(y1[6], y1[7]));
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      float qf[8], kf[8];
-      unpack16(qh[ks], qf, bf16_t());
-      unpack16(kw[ks], kf, bf16_t());
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dotp = fmaf(qf[j], kf[j], dotp);
-    }
-    m_run = rows4_sum(dotp) * qs;
-    l_run = g4 == 0 ? 1.f : 0.f;  // the lane groups' sums are added at the end
-    uint2 vw[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      vw[db] = *(const uint2*)(vrow + 16 * db + 4 * g4);
-      acc[db] = f32x4_t{__uint_as_float(vw[db].x << 16), __uint_as_float(vw[db].x & 0xffff0000u),
-                        __uint_as_float(vw[db].y << 16), __uint_as_float(vw[db].y & 0xffff0000u)};
-    }
-    // the row: open block (or persistent list in full-KV mode), row r
-    const int r = a.compress ? c.n_open : c.n_pers;
-    const int tbase = a.compress ? P.max_pers : 0;
-    int32_t* tabw = ptab_of(P, c.slot, a.layer) + tbase;
-    const int pidx = r / PR, srow = r % PR;
-    const int page = srow == 0 ? a.new_page[c.i] : ((cptr)tabw)[pidx];
-    if (l16 == 0) {
-      const size_t o = (((size_t)page * P.Hkv + c.h) * PR + srow) * D;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) *(uint4*)((bf16_t*)P.kpool + o + 32 * ks + 8 * g4) = kw[ks];
-#pragma unroll
-      for (int db = 0; db < 8; ++db) *(uint2*)((bf16_t*)P.vpool + o + 16 * db + 4 * g4) = vw[db];
-    }
-    if (c.h == 0 && lane == 0) {
-      P.pos[(size_t)page * PR + srow] = qpos;
-      if (srow == 0) tabw[pidx] = page;
-    }
   };
   auto end_segment = [&](const Cur& c) __attribute__((always_inline)) {
     const float L = rows4_sum(l_run);
@@ -1230,7 +1171,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
     const int wa = segS / a.T, wb = (segS + c.units - 1) / a.T;
     if (l16 < G) {
       const int hq = c.h * G + l16;
-      if (wa == wb) {
+      if (wa == wb && !a.fused) {
         const float inv = 1.f / L;
         bf16_t* dst = (bf16_t*)a.out + ((size_t)c.i * Hq + hq) * D;
 #pragma unroll
@@ -1240,7 +1181,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
                          pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv));
         if (g4 == 0) a.lse[(size_t)c.i * Hq + hq] = (m_run + __log2f(L)) * 0.6931471805599453f;
       } else {
-        float* pp = a.part + ((((size_t)c.i * P.Hkv + c.h) * a.maxp + (w - wa)) * G + l16) * (D + 2);
+        float* pp = a.part + ((((size_t)c.i * P.Hkv + c.h) * (a.maxp + a.fused) + (w - wa)) * G + l16) * (D + 2);
 #pragma unroll
         for (int db = 0; db < 8; ++db) *(f32x4_t*)(pp + 16 * db + 4 * g4) = acc[db];
         if (g4 == 0) {
@@ -1251,9 +1192,77 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
     }
   };
 
-  Cur cc = cursor_at(F0);  // tile being computed
-  Cur ci = cc;             // tile being loaded
-  issue(ci);
+  // ---- fused append: the current token's row of (sequence i, KV head h), one
+  // per wavefront spread over the grid, done while the first tile loads. Lane l
+  // rotates the dimension pair (l, l + 64) of the key in fp64 (rounded once to
+  // bf16, like every stored key), writes the K and V row, and scores the key
+  // against the four rotated queries of the head; the result goes to the
+  // merge as one more partial of the head (maximum = score, sum = 1, O = v)
+  auto fused_row = [&](int x) __attribute__((always_inline)) {
+    const int i = x / P.Hkv, h = x % P.Hkv;
+    const int slot = a.slot[i];
+    cptr meta = (cptr)meta_of(P, slot, a.layer);
+    const int n_pers = meta[0], n_open = meta[1], pos = meta[2] + 1;
+    const double2 cs = P.rope[(size_t)pos * (D / 2) + lane];
+    const size_t kvo = ((size_t)i * P.Hkv + h) * D;
+    const bf16_t* kin = (const bf16_t*)a.k + kvo;
+    const bf16_t* vin = (const bf16_t*)a.v + kvo;
+    const double k1 = to_f32(kin[lane]), k2 = to_f32(kin[lane + 64]);
+    const bf16_t kr1 = from_f64<bf16_t>(rot_first(k1, k2, cs));
+    const bf16_t kr2 = from_f64<bf16_t>(rot_second(k1, k2, cs));
+    const bf16_t v1 = vin[lane], v2 = vin[lane + 64];
+    // the row: next row of the open block (persistent list in full-KV mode)
+    const int r = a.compress ? n_open : n_pers;
+    int32_t* tab = ptab_of(P, slot, a.layer) + (a.compress ? P.max_pers : 0);
+    const int pidx = r / PR, srow = r % PR;
+    const int page = srow == 0 ? a.new_page[i] : ((cptr)tab)[pidx];
+    const size_t o = (((size_t)page * P.Hkv + h) * PR + srow) * D;
+    bf16_t* kd = (bf16_t*)P.kpool + o;
+    bf16_t* vd = (bf16_t*)P.vpool + o;
+    kd[lane] = kr1;
+    kd[lane + 64] = kr2;
+    vd[lane] = v1;
+    vd[lane + 64] = v2;
+    if (h == 0 && lane == 0) {
+      P.pos[(size_t)page * PR + srow] = pos;
+      if (srow == 0) tab[pidx] = page;
+    }
+    const float kf1 = to_f32(kr1), kf2 = to_f32(kr2);
+    const int units = (a.useg[i + 1] - a.useg[i]) / P.Hkv;
+    const int segS = a.useg[i] + h * units;
+    const int ns = (segS + units - 1) / a.T - segS / a.T + 1;  // the tiles' partials
+    float* pp = a.part + (((size_t)i * P.Hkv + h) * (a.maxp + 1) + ns) * G * (D + 2);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const bf16_t* qin = (const bf16_t*)a.q + ((size_t)i * Hq + h * G + g) * D;
+      const double q1 = to_f32(qin[lane]), q2 = to_f32(qin[lane + 64]);
+      const float sc = group_sum<64>(round_to<bf16_t>(rot_first(q1, q2, cs)) * kf1 +
+                                     round_to<bf16_t>(rot_second(q1, q2, cs)) * kf2);
+      float* pg = pp + g * (D + 2);
+      pg[lane] = to_f32(v1);
+      pg[lane + 64] = to_f32(v2);
+      if (lane == 0) {
+        pg[D] = sc * qs;
+        pg[D + 1] = 1.f;
+      }
+    }
+  };
+
+  const bool has_tiles = F0 < Fend;
+  Cur cc, ci;  // tile being computed, tile being loaded
+  if (has_tiles) {
+    cc = cursor_at(F0);
+    ci = cc;
+    issue(ci);
+  }
+  if (a.fused) {
+    // rows x at wavefronts x * (waves / rows) when there are fewer rows than
+    // wavefronts, else rows w, w + waves, ...
+    const int nit = a.n * P.Hkv, nw = gridDim.x * 4;
+    const int st = nit <= nw ? nw / nit : 1;
+    for (int x = w % st == 0 ? w / st : nit; x < nit; x += nw) fused_row(x);
+  }
+  if (!has_tiles) return;
   int last_i = -1, last_h = -1;
   const int vrow0 = 8 * g4 + (l16 >> 2);  // V^T operand rows (+4 for the second half)
   for (int t = F0; t < Fend; ++t) {

@@ -59,10 +59,10 @@ struct StreamArgs {
   const void* q;
   void* out;
   float* lse;
-  float* part;  // [n][Hkv][maxp][4][D + 2]
+  float* part;  // [n][Hkv][maxp + fused][4][D + 2]
   // fused append (decode_mfma_kernel only): the current token's k, v [n][Hkv][D]
-  // are written and attended here; counts in meta are the ones before it, and
-  // decode_stream_merge_kernel advances them afterwards
+  // are written there and scored as one extra partial per head; counts in meta
+  // are the ones before it, and decode_stream_merge_kernel advances them
   const void* k;
   const void* v;
   int32_t fused, compress;
