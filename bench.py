@@ -477,6 +477,120 @@ def run_compress(args, torch, abk):
     }
 
 
+def serving_mix_admit(quotas, steps: int, compress: bool, pool_pages: int, seed: int = 4):
+    """Admit sequences (P ~ U[128, 512], G ~ U[1024, 32768], seeded) while the
+    pool holds each one's largest footprint over the run: its persistent rows
+    after the blocks it completes during the run, plus a whole open block per
+    layer (compressed before its pages are freed), or in full-KV mode all its
+    rows at the end. Both modes draw the same sequence stream."""
+    rng = np.random.default_rng(seed)
+    Ps, Gs, used = [], [], 0
+    while True:
+        P = int(rng.integers(128, 512, endpoint=True))
+        G = int(rng.integers(1024, 32768, endpoint=True))
+        if compress:
+            nb_end = (G + steps - 1) // C
+            need = int(sum(-(-(P + nb_end * int(q)) // PR) + C // PR for q in quotas))
+        else:
+            need = L * (-(-(P + G + steps) // PR))
+        if used + need > pool_pages:
+            break
+        Ps.append(P)
+        Gs.append(G)
+        used += need
+    return np.array(Ps, dtype=np.int64), np.array(Gs, dtype=np.int64), used
+
+
+def run_serving_mix(args, torch, abk, compress: bool):
+    """The saturated serving mix: a 200 GiB pool filled with as many sequences
+    as fit, then `steps` decode steps of all of them (one fused append + decode
+    call per layer); a sequence whose block completes is compressed at every
+    layer and freed inside the step. Full-KV mode runs the same kernels with
+    compression off."""
+    steps, warm = args.serving_mix_steps, 2
+    quotas = layer_quotas(2)
+    Kp = int(quotas.max())
+    page_bytes = HKV * PR * D * 2
+    pool_bytes = 200 << 30
+    pool_pages = pool_bytes // (2 * page_bytes)
+    P, G, used = serving_mix_admit(quotas, steps + warm, compress, pool_pages)
+    B = len(P)
+    pool = abk.Pool(num_layers=L, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_tokens=C,
+                    num_pause=Kp, layer_quota=quotas.tolist(), page_rows=PR, max_seqs=B,
+                    pool_bytes=pool_bytes, max_position=33792, dtype="bf16", rope_base=1e6,
+                    compress=compress)
+    sids = []
+    for i in range(B):
+        s = pool.seq_create(int(P[i]))
+        pool.synth_fill(s, int(G[i]), 4 * 1000003 + i * 7919 + 17)
+        sids.append(s)
+    torch.cuda.synchronize()
+    print(f"[bench] serving mix ({'AbridgeKV' if compress else 'full KV'}): {B} sequences, "
+          f"{used} of {pool_pages} pages at their largest", file=sys.stderr, flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    bf = torch.bfloat16
+    nsets = 2  # step inputs alternate between two random sets (values do not affect timing)
+    q_in = torch.randn((nsets, L, B, HQ, D), device="cuda", dtype=bf, generator=gen)
+    k_in = torch.randn((nsets, L, B, HKV, D), device="cuda", dtype=bf, generator=gen)
+    v_in = torch.randn((nsets, L, B, HKV, D), device="cuda", dtype=bf, generator=gen)
+    g = G.copy()
+    nb = (g - 1) // C if compress else np.zeros_like(g)
+    full_max = 1
+    if compress:
+        for t in range(steps + warm):
+            full_max = max(full_max, int(np.sum((g + t) - ((g + t - 1) // C) * C == C)))
+    qp = torch.randn((full_max, Kp, HQ, D), device="cuda", dtype=bf, generator=gen)
+    kp = torch.randn((full_max, Kp, HKV, D), device="cuda", dtype=bf, generator=gen)
+    vp = torch.randn((full_max, Kp, HKV, D), device="cuda", dtype=bf, generator=gen)
+    cout = torch.empty((full_max, Kp, HQ, D), device="cuda", dtype=bf)
+    clse = torch.empty((full_max, Kp, HQ), device="cuda", dtype=torch.float32)
+    out = torch.empty((B, HQ, D), device="cuda", dtype=bf)
+    lse = torch.empty((B, HQ), device="cuda", dtype=torch.float32)
+    views = [[(q_in[t, l], k_in[t, l], v_in[t, l]) for l in range(L)] for t in range(nsets)]
+    stats = {"compressions": 0, "rows": 0}
+
+    def step(t, count):
+        if compress:
+            full = [i for i in range(B) if g[i] - nb[i] * C == C]
+            if full:
+                ids = [sids[i] for i in full]
+                m = len(ids)
+                for l in range(L):
+                    pool.compress_block(l, ids, qp[:m], kp[:m], vp[:m], cout[:m], clse[:m])
+                pool.free_block(ids)
+                for i in full:
+                    nb[i] += 1
+                if count:
+                    stats["compressions"] += m
+        if count:
+            # resident rows the step's decode reads (the current token included)
+            stats["rows"] += int(sum(resident_rows(P, g + 1, int(q), compress).sum() for q in quotas))
+        for l in range(L):
+            q, k, v = views[t % nsets][l]
+            pool.append_decode(l, sids, k, v, q, out, lse)
+        g[:] += 1
+
+    for t in range(warm):
+        step(t, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(steps):
+        step(warm + t, True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = pool.stats()
+    pool.close()
+    del q_in, k_in, v_in
+    torch.cuda.empty_cache()
+    row_bytes = 2 * HKV * D * 2
+    return {"sequences_resident": B, "tokens_per_s": B * steps / dt, "ms_per_step": 1e3 * dt / steps,
+            "steps": steps, "compressions_in_timed_steps": stats["compressions"],
+            "decode_kv_gb_per_step": stats["rows"] * row_bytes / steps / 1e9,
+            "kv_gbps_incl_compression": stats["rows"] * row_bytes / dt / 1e9,
+            "pool_pages_used_at_end": st["pages_used"], "pool_pages": int(pool_pages)}
+
+
 def cpu_baseline(workload, budget_s: float):
     """The CPU oracle as it stands, on a bounded sample of the decode step:
     (sequence, layer) pairs until the time budget is spent; cost scales with
@@ -544,6 +658,9 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--serving-mix", action="store_true",
+                    help="only run the saturated serving mix (200 GiB pool, AbridgeKV and full KV)")
+    ap.add_argument("--serving-mix-steps", type=int, default=512)
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 runs under DIR (no GPU needed)")
     args = ap.parse_args()
@@ -569,6 +686,21 @@ def main():
         print(json.dumps({"copy_bytes": n, "launches": 3}))
         return
     import long_reasoning_kv_amd as abk
+    if args.serving_mix:
+        mix = {"abridgekv": run_serving_mix(args, torch, abk, True),
+               "full_kv": run_serving_mix(args, torch, abk, False)}
+        a, f = mix["abridgekv"], mix["full_kv"]
+        print(json.dumps({
+            "metric": "serving mix: decode tokens/s and sequences resident, AbridgeKV vs full KV",
+            "unit": "tokens/s", "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "saturated serving mix: 200 GiB paged pool, 36 layers, quotas "
+                                   "6x256/12x64/18x128, P ~ U[128,512], G ~ U[1024,32768], one fused "
+                                   "append+decode call per layer per step, compress+free at block "
+                                   "boundaries inside the steps"},
+            "abridgekv": a, "full_kv": f,
+            "tokens_per_s_ratio": a["tokens_per_s"] / f["tokens_per_s"],
+            "sequences_ratio": a["sequences_resident"] / f["sequences_resident"]}), flush=True)
+        return
     print(f"[bench] decode workload: 36 layers, 22 sequences, {args.warmup}+{args.steps} steps",
           file=sys.stderr, flush=True)
     res, workload = run_decode(args, torch, abk)

@@ -5,7 +5,10 @@ automatic decode schedule), on outputs the oracle computes one by one.
 - The 36-layer per-layer-quota decode step: 22 sequences, prompts U[128, 512],
   U[4096, 32768] generated tokens, quotas 6x256 / 12x64 / 18x128 (seeded).
 - The block-compression event: 64 sequences completing a block at once, all
-  36 layers, K = 256 pause tokens.
+  36 layers, K = 256 pause tokens; and one or two sequences alone (the
+  context-split schedule).
+- The serving mix's shape: more sequences than one launch takes, fused calls,
+  blocks completing between steps; AbridgeKV and full-KV modes.
 
 Bars as everywhere: out max-abs 2e-2, lse 1e-3; stored values and rotated keys
 bit-exact (both sides round the same fp64 rotation once); row counts and
@@ -173,3 +176,53 @@ def test_compression_of_few_sequences_splits_the_context():
                 np.testing.assert_array_equal(host(v), code[5])
                 np.testing.assert_array_equal(host(k), code[4])
         run.pool.close()
+
+
+@pytest.mark.parametrize("compress", [True, False])
+def test_serving_mix_more_sequences_than_one_launch(compress):
+    """The serving mix's shape at a size the oracle checks: 300 sequences (two
+    launches per call, split at 256) of one fused append + decode call per layer
+    per step, with blocks completing between the steps (compressed at every
+    layer and freed, as in serving). Sampled sequences on both sides of the
+    launch split against the oracle; row counts of every sequence exact."""
+    rng = np.random.default_rng(4)
+    B, steps = 300, 3
+    quotas = [256, 64]
+    P = rng.integers(128, 512, B, endpoint=True)
+    G = rng.integers(1024, 4096, B, endpoint=True)
+    # a few sequences reach a block boundary during the steps
+    G[::23] = (G[::23] // C) * C + C - rng.integers(0, steps, len(G[::23]))
+    if compress:
+        pool_bytes = _pool_bytes(P, G + steps + 1, np.array(quotas))
+    else:
+        pool_bytes = 2 * HKV * PR * D * 2 * 2 * int(np.sum(np.ceil((P + G + steps) / PR) + 1))
+    run = Run(L=2, Hq=HQ, Hkv=HKV, D=D, C=C, Kp=KP, quota=quotas, pr=PR, dtype="bf16",
+              compress=compress, max_seqs=B, pool_bytes=pool_bytes, max_position=33792, seed=4)
+    sids = [run.new_seq(int(P[i]), i) for i in range(B)]
+    for s, g in zip(sids, G):
+        run.fill(s, int(g))
+    print(f"[fullsize] serving mix (compress={compress}): {B} sequences filled", flush=True)
+    crossed = set()
+    for t in range(steps):
+        if compress:
+            full = [s for s in sids if run.G[s] - run.nb[s] * C == C]
+            if full:
+                run.compress_and_free(full)
+                crossed.update(full)
+        results = run.step_fused(sids)
+    if compress:
+        assert crossed, "no sequence completed a block"
+    check = sorted(set([0, 137, 255, 256, 299] + sorted(crossed)[:2]))
+    for l in range(2):
+        out, lse, q = results[l]
+        assert np.isfinite(out).all() and np.isfinite(lse).all()
+        for i, s in enumerate(sids):
+            nb = run.nb[s]
+            want = int(P[i]) + (nb * quotas[l] + (run.G[s] - nb * C) if compress else run.G[s])
+            assert run.pool.seq_query(s, l)["resident_rows"] == want, (i, l)
+        for s in check:
+            i = sids.index(s)
+            o_ref, l_ref, _ = run.oracle_decode(s, l, q[i])
+            _close(f"mix out seq{i} L{l}", out[i], o_ref, 2e-2)
+            _close(f"mix lse seq{i} L{l}", lse[i], l_ref, 1e-3)
+    run.pool.close()
