@@ -375,18 +375,20 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
         for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma_bf16(ka, qh[nb][ks], s[mb][nb]);
       }
     }
-    // mask (partial context pages and pause tiles only; the test is uniform)
+    // mask (partial context pages and pause tiles only; the test is uniform).
+    // Key keyof(mb, 4 g4 + e) = 8 g4 + (32(mb/2) + 4(mb%2) + e) is kept when it
+    // is a valid row and, in a pause tile, not after the query's own pause
+    // token: one limit per query column, one compare per element
     if (!ctx || nval < TK) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < 2; ++nb) {
+        const int lim = (ctx ? nval : min(nval, qpause[nb] - kbase + 1)) - 8 * g4;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = keyof(mb, 4 * g4 + e);
-            const bool ok = key < nval && (ctx || kbase + key <= qpause[nb]);
-            s[mb][nb][e] = ok ? s[mb][nb][e] : -INFINITY;
-          }
+          for (int e = 0; e < 4; ++e)
+            s[mb][nb][e] = 32 * (mb >> 1) + 4 * (mb & 1) + e < lim ? s[mb][nb][e] : -INFINITY;
+      }
     }
     // online softmax per query column (lane-local after the row swaps)
     float mn[2], alpha[2];
