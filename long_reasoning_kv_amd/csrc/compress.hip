@@ -318,16 +318,38 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   // that belongs there. Rows past the tile's valid count repeat its last row.
   const int r_in = 4 * wave + (lane >> 4);
   const int vchunk = (lane & 15) ^ vt_swz(r_in);  // bits 0, 1, 3 of 16j + r_in are r_in's
+  // byte offsets of a whole context page's loads (rows 64 x 256 B): the same
+  // for every such tile, so computed once; 32-bit offsets from a uniform base
+  // let the loads take the scalar-base form
+  uint32_t kof_full[4], vof_full[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    kof_full[j] = (16 * j + r_in) * RB + 16 * ((lane & 15) ^ kswz(16 * j + r_in));
+    vof_full[j] = (16 * j + r_in) * RB + 16 * vchunk;
+  }
   auto issue = [&](int t, int page, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
     const TileSrc ts = tile_src(t, page);
+    uint32_t kof[4], vof[4];
+    if (ts.nval == TK && ts.vstride == RB) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kof[j] = kof_full[j];
+        vof[j] = vof_full[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = min(16 * j + r_in, ts.nval - 1);
+        kof[j] = row * ts.kstride + 16 * ((lane & 15) ^ kswz(16 * j + r_in));
+        vof[j] = row * ts.vstride + 16 * vchunk;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = min(16 * j + r_in, ts.nval - 1);
-      const int kchunk = (lane & 15) ^ kswz(16 * j + r_in);
-      __builtin_amdgcn_global_load_lds((const void*)(ts.kb + row * ts.kstride + 16 * kchunk),
+      __builtin_amdgcn_global_load_lds((const void*)(ts.kb + kof[j]),
                                        (__attribute__((address_space(3))) void*)(dk + 256 * j + 64 * wave),
                                        16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(ts.vb + row * ts.vstride + 16 * vchunk),
+      __builtin_amdgcn_global_load_lds((const void*)(ts.vb + vof[j]),
                                        (__attribute__((address_space(3))) void*)(dv + 256 * j + 64 * wave),
                                        16, 0, 0);
     }
