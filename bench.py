@@ -438,7 +438,7 @@ def run_compress(args, torch, abk):
     # one sequence completing its last block alone (the common serving case):
     # the context of each query tile is split over several workgroups
     single = []
-    for rep in range(args.compress_reps + 1):
+    for rep in range(0 if args.no_single_sequence else args.compress_reps + 1):
         s = pool.seq_create(int(P[0]))
         pool.synth_fill(s, 63 * C, 3 * 1000003 + 999)
         torch.cuda.synchronize()
@@ -468,11 +468,13 @@ def run_compress(args, torch, abk):
         "blocks_per_s": B * 1e3 / ms,
         "tflop_per_event": flops / 1e12, "gb_per_event": nbytes / 1e9,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS,
+                     # HBM bytes per launch (one layer of the event), from the counters
+                     "traffic": traffic_from_profiles("compress_attn_mfma", nbytes / L)},
         "config": {"workload": "block compression, 64 sequences, 36 layers, K=256 pause tokens "
                                "(layer keeps quota prefix)", "prompt": "U[128,512]",
                    "block_index": "U{0..62}"},
-        "single_sequence_ms": float(np.mean(single)),
+        "single_sequence_ms": float(np.mean(single)) if single else None,
         "single_sequence": f"one sequence (prompt {int(P[0])}) compressing block 62 alone, 36 layers",
     }
 
@@ -654,6 +656,8 @@ def main():
                     help="append and decode as two calls per layer (default: abk_append_decode)")
     ap.add_argument("--compress-reps", type=int, default=2)
     ap.add_argument("--no-compress", action="store_true")
+    ap.add_argument("--no-single-sequence", action="store_true",
+                    help="skip the single-sequence compression latency (profiled runs of the event)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
