@@ -15,7 +15,10 @@ states them:
   same way -> softmax attention (scale 1/sqrt(d) on the fp64 scores);
 * compression of block b: every pause query PAUSE(b, j) with its own visible
   key set (prompt, retained code rows, the whole block, pause keys k <= j),
-  then the code rows k < quota are what the layer keeps.
+  then the code rows k < quota are what the layer keeps;
+* block-mask prefill (training-forward attention): every token of a sequence
+  laid out in training order (prompt, then each block's text followed by its
+  pause tokens once the block is complete) as a query with its own visible set.
 """
 from __future__ import annotations
 
@@ -224,3 +227,50 @@ def compress(L: LayerView, G: int, nb: int, block: int, q_raw: np.ndarray, fetch
     code_k = rope_rows(fetch(ckind, cb, ck, "k"), cpos, base, dtype)
     code_v = fetch(ckind, cb, ck, "v")
     return out, lse, (ckind, cb, ck, cpos, code_k, code_v)
+
+
+def training_tokens(L: LayerView, G: int):
+    """Token identities (kind, a, b) of a sequence with G text tokens in
+    training order (the creation order of Fig. 2(a) in the figure captions):
+    the prompt, then per block its C text tokens, followed, when the block is
+    complete and compression is on, by its Kp pause tokens."""
+    kind, a, b = [PROMPT] * L.P, list(range(L.P)), [0] * L.P
+    nb = G // L.C if L.compress else 0
+    for blk in range((G + L.C - 1) // L.C):
+        n = min(L.C, G - blk * L.C)
+        kind += [TEXT] * n
+        a += list(range(blk * L.C, blk * L.C + n))
+        b += [0] * n
+        if blk < nb:
+            kind += [PAUSE] * L.Kp
+            a += [blk] * L.Kp
+            b += list(range(L.Kp))
+    return np.array(kind, np.int32), np.array(a, np.int64), np.array(b, np.int64)
+
+
+def blockmask_prefill(L: LayerView, G: int, q_raw: np.ndarray, fetch, dtype: int, base: float,
+                      rows=None):
+    """Attention of the tokens of a training-order sequence under the block mask
+    (Fig. 2(a) of the figure captions), one layer.
+
+    q_raw [T, Hq, d]: pre-RoPE queries of all T tokens in training order.
+    ``fetch`` as in :func:`decode`. ``rows`` (optional) lists the token indices
+    to compute. Each query attends to the keys the mask shows it among the
+    tokens created before it, every key and query rotated at its own position
+    and rounded once to the storage dtype. Returns (out [n, Hq, d], lse [n, Hq]).
+    """
+    kind, a, b = training_tokens(L, G)
+    nb = G // L.C if L.compress else 0
+    rows = list(range(len(kind))) if rows is None else [int(r) for r in rows]
+    lists = [visible_keys(L, G, nb, (int(kind[r]), int(a[r]), int(b[r]))) for r in rows]
+    kk = np.concatenate([t[0] for t in lists])
+    ka = np.concatenate([t[1] for t in lists])
+    kb = np.concatenate([t[2] for t in lists])
+    kpos = np.concatenate([t[3] for t in lists])
+    off = np.zeros(len(rows) + 1, np.int64)
+    off[1:] = np.cumsum([len(t[0]) for t in lists])
+    k = rope_rows(fetch(kk, ka, kb, "k"), kpos, base, dtype)
+    v = fetch(kk, ka, kb, "v")
+    qpos = np.array([position(L, int(kind[r]), int(a[r]), int(b[r])) for r in rows], np.int64)
+    qr = rope_rows(np.asarray(q_raw)[rows], qpos, base, dtype)
+    return attention_batch(qr, off, k, v)

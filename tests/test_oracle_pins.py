@@ -344,3 +344,98 @@ def test_compress_query_subset_equals_full():
     part = oracle.compress(Lv, G, nb, nb, q, fetch, oracle.F32, 1e6, queries=[3, 0])
     np.testing.assert_array_equal(part[0], full[0][[3, 0]])
     np.testing.assert_array_equal(part[1], full[1][[3, 0]])
+
+
+# ---- block-mask prefill (training-forward attention) ---------------------------
+
+def test_training_tokens_follow_creation_order():
+    for comp in (True, False):
+        L = LayerView(P=3, C=4, Kp=2, quota=1, compress=comp)
+        kind, a, b = oracle.training_tokens(L, 10)
+        idx = [oracle.creation_index(L, int(k), int(x), int(y)) for k, x, y in zip(kind, a, b)]
+        assert idx == list(range(len(kind)))
+        assert len(kind) == 3 + 10 + (2 * 2 if comp else 0)
+
+
+def test_blockmask_prefill_fig2a_golden():
+    """Zero queries weigh every visible key equally; one-hot values then make
+    each output row the mask row of Fig. 2(a) divided by its count."""
+    lines = list(golden_lines("fig2a_mask.txt"))
+    want = np.array([[int(t) for t in ln.split()[1:15]] for ln in lines], np.float64)
+    L = LayerView(P=2, C=4, Kp=2, quota=2)
+    kind, a, b = oracle.training_tokens(L, 8)
+    T = len(kind)
+    assert T == 14
+    rng = np.random.default_rng(0)
+
+    def fetch(kk, ka, kb, which):
+        if which == "k":
+            return rng.standard_normal((len(kk), 1, 16))
+        out = np.zeros((len(kk), 1, 16))
+        for n, (x, y, z) in enumerate(zip(kk, ka, kb)):
+            out[n, 0, oracle.creation_index(L, int(x), int(y), int(z))] = 1.0
+        return out
+
+    out, lse = oracle.blockmask_prefill(L, 8, np.zeros((T, 1, 16)), fetch, oracle.F32, 1e6)
+    cnt = want.sum(1)
+    np.testing.assert_allclose(out[:, 0, :14] * cnt[:, None], want, atol=1e-12)
+    np.testing.assert_allclose(out[:, 0, 14:], 0.0)
+    np.testing.assert_allclose(lse[:, 0], np.log(cnt), atol=1e-12)
+
+
+def test_blockmask_prefill_compression_off_is_causal_sdpa():
+    L = LayerView(P=5, C=8, Kp=4, quota=2, compress=False)
+    G, Hq, Hkv, d = 19, 4, 2, 16
+    T = L.P + G
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((T, Hq, d))
+    k = rng.standard_normal((T, Hkv, d))
+    v = rng.standard_normal((T, Hkv, d))
+    kind, a, b = oracle.training_tokens(L, G)
+    idx = {(int(x), int(y), int(z)): i for i, (x, y, z) in enumerate(zip(kind, a, b))}
+
+    def fetch(kk, ka, kb, which):
+        src = k if which == "k" else v
+        return src[[idx[(int(x), int(y), int(z))] for x, y, z in zip(kk, ka, kb)]]
+
+    out, lse = oracle.blockmask_prefill(L, G, q, fetch, oracle.F32, 1e6)
+    pos = np.arange(T)
+    qr = torch.from_numpy(oracle.rope_rows(q, pos, 1e6, oracle.F32)).transpose(0, 1)
+    kr = torch.from_numpy(oracle.rope_rows(k, pos, 1e6, oracle.F32)).transpose(0, 1)
+    vv = torch.from_numpy(v).transpose(0, 1)
+    kr = kr.repeat_interleave(Hq // Hkv, 0)
+    vv = vv.repeat_interleave(Hq // Hkv, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qr, kr, vv, is_causal=True)
+    np.testing.assert_allclose(out, ref.transpose(0, 1).numpy(), atol=1e-10)
+
+
+def test_blockmask_prefill_rows_equal_decode_and_compression():
+    """A text row is the decode of that token right after it is written; a
+    pause row is that pause token's query in the compression of its block."""
+    L = LayerView(P=3, C=8, Kp=4, quota=2)
+    G, Hq, Hkv, d = 21, 2, 1, 16
+    kind, a, b = oracle.training_tokens(L, G)
+    T = len(kind)
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((T, Hq, d))
+    kv = {w: rng.standard_normal((T, Hkv, d)) for w in ("k", "v")}
+    idx = {(int(x), int(y), int(z)): i for i, (x, y, z) in enumerate(zip(kind, a, b))}
+
+    def fetch(kk, ka, kb, which):
+        return kv[which][[idx[(int(x), int(y), int(z))] for x, y, z in zip(kk, ka, kb)]]
+
+    out, lse = oracle.blockmask_prefill(L, G, q, fetch, oracle.BF16, 1e6)
+    for r in range(T):
+        if kind[r] == oracle.TEXT:
+            g = int(a[r]) + 1
+            o2, l2, _ = oracle.decode(L, g, (g - 1) // L.C, q[r], fetch, oracle.BF16, 1e6)
+        elif kind[r] == oracle.PAUSE:
+            blk = int(a[r])
+            qb = q[[idx[(oracle.PAUSE, blk, j)] for j in range(L.Kp)]]
+            o2, l2, _ = oracle.compress(L, (blk + 1) * L.C, blk, blk, qb, fetch, oracle.BF16, 1e6,
+                                        queries=[int(b[r])])
+            o2, l2 = o2[0], l2[0]
+        else:
+            continue
+        np.testing.assert_allclose(out[r], o2, atol=1e-12)
+        np.testing.assert_allclose(lse[r], l2, atol=1e-12)
