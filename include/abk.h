@@ -173,6 +173,30 @@ abk_status abk_export_layout(const abk_pool* p, int32_t seq_id, int32_t layer, i
 abk_status abk_read_rows(const abk_pool* p, int32_t seq_id, int32_t layer, int32_t row0,
                          int32_t nrows, void* k_out, void* v_out);
 
+/* Block-mask prefill (the training-forward attention of arXiv 2610.20641,
+ * Fig. 2(a) of its figure captions), one layer of one sequence. The sequence
+ * is laid out in training order: prompt_len prompt rows, then for each block
+ * its C text rows followed, when the block is complete (text_tokens counts
+ * all text tokens; blocks b < text_tokens / C are complete), by the layer's
+ * Kp pause rows; T = prompt_len + text_tokens + (text_tokens / C) * Kp rows
+ * (no pause rows when compression is off). q [T, Hq, d], k/v [T, Hkv, d]:
+ * device, pool dtype, pre-RoPE; every row is rotated at its own position
+ * (prompt i; text j at prompt_len + j; pause k of block b at prompt_len + b C
+ * + bitrev(k) C/Kp, Fig. 2(b)), keys rounded once to the pool dtype like
+ * stored keys. Each row attends, with the layer's quota, to what the mask
+ * shows it: prompt rows causally to the prompt; text rows to the prompt, the
+ * kept code rows (pause k < quota) of earlier blocks and their own block's
+ * text causally; pause rows to the same plus their whole block and their
+ * block's pause rows up to their own. Compression off: plain causal
+ * attention. out [T, Hq, d] (pool dtype) and lse [T, Hq] fp32 (natural log),
+ * caller-owned. Uses the pool's stream, RoPE table and a library-owned
+ * staging buffer (grown on demand); reads and writes no sequence state.
+ * INVALID_ARG for a bad layer, negative lengths or prompt_len + text_tokens >
+ * max_position; UNSUPPORTED unless the pool is bf16 with d = 128 and four
+ * query heads per KV head. */
+abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_len, int32_t text_tokens,
+                                   const void* q, const void* k, const void* v, void* out, float* lse);
+
 /* Pool-wide counters. resident_bytes = K+V bytes of resident rows. */
 abk_status abk_pool_stats(const abk_pool* p, int64_t* pages_used, int64_t* pages_free,
                           int64_t* resident_bytes);

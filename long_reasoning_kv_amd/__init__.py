@@ -22,7 +22,7 @@ SYMBOLS = [
     "abk_write_prompt", "abk_append_kv", "abk_decode_attention", "abk_append_decode",
     "abk_compress_block",
     "abk_free_block", "abk_seq_query", "abk_export_layout", "abk_read_rows",
-    "abk_pool_stats", "abk_synth_fill", "abk_last_error",
+    "abk_pool_stats", "abk_synth_fill", "abk_blockmask_attention", "abk_last_error",
 ]
 
 
@@ -79,6 +79,7 @@ def lib():
             "abk_read_rows": [vp, i32, i32, i32, i32, vp, vp],
             "abk_pool_stats": [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)],
             "abk_synth_fill": [vp, i32, i32, u64],
+            "abk_blockmask_attention": [vp, i32, i32, i32, vp, vp, vp, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -198,6 +199,10 @@ class Pool:
         a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
         _check(lib().abk_pool_stats(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
         return {"pages_used": a.value, "pages_free": b.value, "resident_bytes": c.value}
+
+    def blockmask_attention(self, layer, prompt_len, text_tokens, q, k, v, out, lse):
+        _check(lib().abk_blockmask_attention(self._h, layer, prompt_len, text_tokens, _ptr(q), _ptr(k),
+                                             _ptr(v), _ptr(out), _ptr(lse)))
 
     def synth_fill(self, sid, generated, seed):
         _check(lib().abk_synth_fill(self._h, sid, generated, seed & 0xFFFFFFFFFFFFFFFF))

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libabk.so")
 SOURCES = ["csrc/abk_api.cpp", "csrc/pool.cpp", "csrc/pool_kernels.hip", "csrc/decode.hip",
-           "csrc/compress.hip"]
+           "csrc/compress.hip", "csrc/prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

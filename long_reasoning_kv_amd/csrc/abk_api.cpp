@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <climits>
 #include <cstring>
@@ -65,6 +66,8 @@ struct abk_pool {
   size_t part_bytes = 0;
   void* kp_rot = nullptr;
   size_t kp_rot_bytes = 0;
+  void* bm_stage = nullptr;  // block-mask prefill: staged keys/values, persistent rows
+  size_t bm_stage_bytes = 0;
   void* desc = nullptr;
   size_t desc_bytes = 0;
   int32_t* export_d = nullptr;
@@ -251,7 +254,7 @@ abk_status abk_pool_destroy(abk_pool* p) {
     abk::DevPool& d = p->dev;
     for (void* b : {(void*)d.kpool, (void*)d.vpool, (void*)d.pos, (void*)d.ptab, (void*)d.meta,
                     (void*)d.rope, (void*)p->quota_d, (void*)p->pause_d, (void*)p->part,
-                    p->kp_rot, p->desc, (void*)p->export_d})
+                    p->kp_rot, p->bm_stage, p->desc, (void*)p->export_d})
       if (b) (void)hipFree(b);
     for (auto& s : p->ring) {
       if (s.host) (void)hipHostFree(s.host);
@@ -611,6 +614,112 @@ abk_status abk_free_block(abk_pool* p, int32_t n, const int32_t* seq_ids) {
     for (int32_t i = 0; i < a.n; ++i) a.slot[i] = seq_ids[c0 + i];
     ABK_HIP(abk::launch_free(a, p->stream));
   }
+  return ABK_OK;
+}
+
+abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_len, int32_t text_tokens,
+                                   const void* q, const void* k, const void* v, void* out, float* lse) {
+  if (abk_status st = check_pool(p)) return st;
+  if (p->host.check_layer(layer)) return set_err(ABK_ERR_INVALID_ARG, "bad layer");
+  const abk::Shape& s = p->shape;
+  if (prompt_len < 0 || text_tokens < 0) return set_err(ABK_ERR_INVALID_ARG, "negative length");
+  if ((int64_t)prompt_len + text_tokens > s.max_position)
+    return set_err(ABK_ERR_INVALID_ARG, "positions reach max_position");
+  const int32_t C = s.C, Kp = s.pause[layer], quota = s.quota[layer];
+  const bool comp = s.compress != 0;
+  const int32_t nb = comp ? text_tokens / C : 0;  // complete blocks: followed by their pause rows
+  const int64_t T64 = (int64_t)prompt_len + text_tokens + (int64_t)nb * Kp;
+  if (T64 > (1 << 30)) return set_err(ABK_ERR_INVALID_ARG, "sequence too long");
+  const int32_t T = (int32_t)T64;
+  if (!(s.dtype == 1 && s.D == 128 && s.Hq == 4 * s.Hkv))
+    return set_err(ABK_ERR_UNSUPPORTED, "block-mask prefill needs bf16, d = 128, four query heads per KV head");
+  if (T == 0) return ABK_OK;
+  if (!p->host_only && (!q || !k || !v || !out || !lse))
+    return set_err(ABK_ERR_INVALID_ARG, "q/k/v/out/lse is NULL");
+  if (p->host_only) return ABK_OK;
+
+  // query tiles of up to 32 tokens of one kind in one block, per KV head
+  struct Tile {
+    int32_t kind, row0, ntok, tok0, nA, bstart, nB, blk;
+    int64_t work;  // keys seen by its last query (a size for the schedule)
+  };
+  std::vector<Tile> tiles;
+  const int32_t P0 = comp ? prompt_len : T;  // rows attended causally from the start
+  for (int32_t t0 = 0; t0 < P0; t0 += 32) {
+    const int32_t n = std::min(32, P0 - t0);
+    tiles.push_back({0, t0, n, t0, 0, 0, 0, -1, t0 + n});
+  }
+  if (comp) {
+    const int32_t nblk = (text_tokens + C - 1) / C;
+    for (int32_t blk = 0; blk < nblk; ++blk) {
+      const int32_t bstart = prompt_len + blk * (C + Kp), ctext = std::min(C, text_tokens - blk * C);
+      const int32_t nA = prompt_len + blk * quota;
+      for (int32_t i0 = 0; i0 < ctext; i0 += 32) {
+        const int32_t n = std::min(32, ctext - i0);
+        tiles.push_back({1, bstart + i0, n, i0, nA, bstart, i0 + n, blk, (int64_t)nA + i0 + n});
+      }
+      if (blk < nb)
+        for (int32_t j0 = 0; j0 < Kp; j0 += 32) {
+          const int32_t n = std::min(32, Kp - j0);
+          tiles.push_back({2, bstart + C + j0, n, j0, nA, bstart, C + j0 + n, blk, (int64_t)nA + C + j0 + n});
+        }
+    }
+  }
+  // Workgroups of one (KV head, block) share blockIdx mod 8, i.e. one XCD and
+  // its L2, since they read the same keys; each XCD's list runs heaviest first.
+  const int32_t nblk_all = (comp ? (text_tokens + C - 1) / C : 0) + 1;
+  std::vector<std::vector<std::pair<int64_t, std::array<int32_t, abk::kBmRec>>>> lists(8);
+  for (int32_t h = 0; h < s.Hkv; ++h)
+    for (const Tile& t : tiles) {
+      const int32_t x = (h * nblk_all + (t.blk + 1)) % 8;
+      lists[x].push_back({t.work, {h, t.kind, t.row0, t.ntok, t.tok0, t.nA, t.bstart, t.nB, t.blk}});
+    }
+  size_t maxlen = 0;
+  for (auto& l : lists) {
+    std::stable_sort(l.begin(), l.end(), [](const auto& a, const auto& b) { return a.first > b.first; });
+    maxlen = std::max(maxlen, l.size());
+  }
+  std::vector<int32_t>& d = p->scratch;
+  d.assign(maxlen * 8 * abk::kBmRec, 0);
+  for (size_t j = 0; j < maxlen; ++j)
+    for (int32_t x = 0; x < 8; ++x) {
+      int32_t* r = &d[(j * 8 + x) * abk::kBmRec];
+      if (j < lists[x].size())
+        std::copy(lists[x][j].second.begin(), lists[x][j].second.end(), r);
+      else
+        r[0] = -1;  // no work
+    }
+  const int32_t nrec = (int32_t)(maxlen * 8);
+
+  const int32_t npers = comp ? prompt_len + nb * quota : T;
+  const size_t row_bytes = (size_t)s.Hkv * s.D * s.esize();
+  const size_t stage = 2 * (size_t)T * row_bytes, pers = comp ? 2 * (size_t)npers * row_bytes : 0;
+  if (abk_status st = grow(p, &p->bm_stage, &p->bm_stage_bytes, stage + pers)) return st;
+  if (abk_status st = upload_desc(p, d.data(), d.size() * sizeof(int32_t))) return st;
+  abk::BlockMaskArgs a;
+  a.P = p->dev;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.kst = p->bm_stage;
+  a.vst = (char*)p->bm_stage + (size_t)T * row_bytes;
+  a.kpers = comp ? (char*)p->bm_stage + stage : a.kst;
+  a.vpers = comp ? (char*)p->bm_stage + stage + (size_t)npers * row_bytes : a.vst;
+  a.desc = (const int32_t*)p->desc;
+  a.Hq = s.Hq;
+  a.T = T;
+  a.prompt = prompt_len;
+  a.C = C;
+  a.Kp = Kp;
+  int32_t lg = 0;
+  while ((1 << lg) < Kp) ++lg;
+  a.log2Kp = lg;
+  a.quota = quota;
+  a.npers = npers;
+  a.compress = comp ? 1 : 0;
+  ABK_HIP(abk::launch_blockmask(a, nrec, p->stream));
   return ABK_OK;
 }
 

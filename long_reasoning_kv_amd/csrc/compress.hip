@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_mfma.h"
 #include "common.h"
 
 namespace abk {
@@ -164,51 +165,14 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
 // ---- a5 on bf16 MFMA (d = 128, four query heads per KV head, 64-row pages) -------
 //
 // Workgroup = (sequence, KV head, tile of 128 query rows); query row r is pause
-// r/4, head 4h + r%4. Each of the 4 wavefronts owns 32 query rows (two 16-row
-// N-blocks). For every 64-key tile (a context page, then pause-key tiles):
-//   S^T = K Q^T   with v_mfma_f32_16x16x32_bf16: A = K rows from LDS, B = the
-//                 rotated query rounded once to bf16 (like stored keys; the
-//                 softmax scale goes on the fp32 scores), C lane l = keys
-//                 4(l/16)+i x query l%16;
-//   online softmax per query column, all lane-local plus permlane swaps; the
-//                 running maximum is only moved (and O^T rescaled) when a
-//                 tile's maximum exceeds it by more than 2^8, which keeps the
-//                 result exact and makes rescales rare;
-//   O^T += V^T P^T: B = P^T straight from the S^T registers (bf16), A = V^T
-//                 read from the row-major V tile with ds_read_b64_tr_b16.
-// The M-blocks of S^T take keys 32(mb/2) + 8(m/4) + 4(mb%2) + m%4 so that for
-// each 32-key step a lane's 8 probabilities are 8 consecutive keys, which is
-// what two transposing reads of V deliver. K and V rows in LDS have their
-// 16-byte chunks XOR-swizzled by row (K: bits 0, 1, 3, 4; V: bits 0, 1 and 3 of the
-// row) so that an A-operand read of either touches every bank evenly. The next
-// tile is loaded into registers while the current one is computed; LDS is
-// double-buffered (64 KB). Masks are applied only to partial and pause tiles.
-
-// V^T operand of O^T += V^T P^T for dims 16db + l%16 and keys k0 + 8(l/16) + 0..7
-// of a row-major, swizzled 64-key V tile: two ds_read_b64_tr_b16. Within each
-// 16-lane group, lane s supplies row k0 + 8g + 4hh + s/4 at dims 16db + 4(s%4)
-// and receives 4 keys of dim 16db + s.
-__device__ __forceinline__ int vt_swz(int row) { return 2 * ((row & 3) | ((row >> 1) & 4)); }
-__device__ __forceinline__ uint4 vt_operand(const uint4* __restrict__ tile, int db, int k0, int lane) {
-  const int g = lane >> 4, s = lane & 15;
-  uint32_t w[4];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int row = k0 + 8 * g + 4 * hh + (s >> 2);
-    const int dim = 16 * db + 4 * (s & 3);
-    const int chunk = (dim >> 3) ^ vt_swz(row);
-    const char* addr = (const char*)(tile + row * 16 + chunk) + 2 * (dim & 7);
-    const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4_t*)(addr));
-    const uint2 u = __builtin_bit_cast(uint2, r);
-    w[2 * hh] = u.x;
-    w[2 * hh + 1] = u.y;
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
+// r/4, head 4h + r%4. Each of the 4 wavefronts owns 32 query rows and runs the
+// per-tile math of attn_mfma.h over the 64-key tiles: the context pages
+// (persistent, then open), then the pause-key tiles. The next tile streams
+// straight into LDS while the current one is computed (double-buffered, 64 KB).
+// Masks are applied only to partial and pause tiles.
 
 __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs a) {
-  constexpr int D = 128, G = 4, TK = 64, RB = D * 2;
+  constexpr int D = 128, G = 4, TK = kTileKeys, RB = D * 2;
   // K rows (chunks swizzled by kswz) and V rows (swizzled by vt_swz), two
   // buffers each; separate arrays so that the compiler can tell them apart
   __shared__ uint4 lk0[TK * RB / 16], lk1[TK * RB / 16];
@@ -246,38 +210,20 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   // ---- the wavefront's query rows: rotated at the bitrev position, rounded
   // once to bf16 (like stored keys); the softmax scale goes on the fp32 scores
   const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
-  uint4 qh[2][4];  // [N-block][k-step]: dims 32ks + 8 g4 + 0..7
+  WaveAttn wa;
   int qpause[2];
-  {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      int r = q0 + wave * 32 + nb * 16 + l16;
-      const bool rv = r < q0 + nq;
-      r = rv ? r : q0;
-      const int pz = r >> 2, hh = r & 3;
-      qpause[nb] = rv ? pz : -1;
-      const int pos = prompt + blk * P.C + bitrev_dev(pz, a.log2Kp) * (P.C / a.Kp);
-      const bf16_t* qrow = (const bf16_t*)a.qp + (((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh) * D;
-      float x[4][8];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) unpack16(*(const uint4*)(qrow + 32 * ks + 8 * g4), x[ks], bf16_t());
-      const double2* rope = P.rope + (size_t)pos * (D / 2);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        double y0[8], y1[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const double2 cs = rope[32 * ks + 8 * g4 + j];
-          y0[j] = rot_first(x[ks][j], x[ks + 2][j], cs);
-          y1[j] = rot_second(x[ks][j], x[ks + 2][j], cs);
-        }
-        qh[nb][ks] = make_uint4(pack_bf16x2_f64(y0[0], y0[1]), pack_bf16x2_f64(y0[2], y0[3]),
-                                pack_bf16x2_f64(y0[4], y0[5]), pack_bf16x2_f64(y0[6], y0[7]));
-        qh[nb][ks + 2] = make_uint4(pack_bf16x2_f64(y1[0], y1[1]), pack_bf16x2_f64(y1[2], y1[3]),
-                                    pack_bf16x2_f64(y1[4], y1[5]), pack_bf16x2_f64(y1[6], y1[7]));
-      }
-    }
+  for (int nb = 0; nb < 2; ++nb) {
+    int r = q0 + wave * 32 + nb * 16 + l16;
+    const bool rv = r < q0 + nq;
+    r = rv ? r : q0;
+    const int pz = r >> 2, hh = r & 3;
+    qpause[nb] = rv ? pz : -1;
+    const int pos = prompt + blk * P.C + bitrev_dev(pz, a.log2Kp) * (P.C / a.Kp);
+    const bf16_t* qrow = (const bf16_t*)a.qp + (((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh) * D;
+    query_operand(qrow, P.rope + (size_t)pos * (D / 2), g4, wa.qh[nb]);
   }
+  wa.init();
 
   // ---- tile t: 64 K rows and 64 V rows (a context page, or pause keys). The
   // page table is read through the constant address space (scalar loads: it
@@ -355,18 +301,6 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
     }
   };
 
-  // key of S^T M-block mb, row m (see above)
-  auto keyof = [](int mb, int m) { return 32 * (mb >> 1) + 8 * (m >> 2) + 4 * (mb & 1) + (m & 3); };
-
-  f32x4_t acc_o[2][8];  // [N-block][dim block]
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int db = 0; db < 8; ++db) acc_o[nb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // running maximum (log2 units) and sum per query column; the finite start
-  // keeps exp2(s - m) well defined while a column has seen only masked keys
-  float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
-
   // One tile: start loading tile t+1 into (nk, nv), compute tile t from
   // (ck, cv). The restrict qualifiers tell the compiler that the loads in
   // flight do not write the buffers being read, so it waits for them only at
@@ -379,94 +313,16 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
     const int t = gt(u);
     issue(gt(min(u + 1, ntiles - 1)), page_next, nk, nv);
     page_next = page_of(gt(min(u + 2, ntiles - 1)));
+    // mask: partial context pages and pause tiles (a uniform test); in a
+    // pause tile a query sees pause keys up to its own
     const bool ctx = t < ntc;
     const int nval = ctx ? (t == npp - 1 ? n_pers - t * TK : TK) : min(TK, a.Kp - (t - ntc) * TK);
     const int kbase = ctx ? 0 : (t - ntc) * TK;  // pause index of key 0 of a pause tile
-    f32x4_t s[4][2];
+    auto limits = [&](int (&lim)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int kr = keyof(mb, l16);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 ka = ck[kr * 16 + ((4 * ks + g4) ^ kswz(kr))];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma_bf16(ka, qh[nb][ks], s[mb][nb]);
-      }
-    }
-    // mask (partial context pages and pause tiles only; the test is uniform).
-    // Key keyof(mb, 4 g4 + e) = 8 g4 + (32(mb/2) + 4(mb%2) + e) is kept when it
-    // is a valid row and, in a pause tile, not after the query's own pause
-    // token: one limit per query column, one compare per element
-    if (!ctx || nval < TK) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int lim = (ctx ? nval : min(nval, qpause[nb] - kbase + 1)) - 8 * g4;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            s[mb][nb][e] = 32 * (mb >> 1) + 4 * (mb & 1) + e < lim ? s[mb][nb][e] : -INFINITY;
-      }
-    }
-    // online softmax per query column (lane-local after the row swaps)
-    float mn[2], alpha[2];
-    bool moved = false;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[mb][nb][e]);
-      mx = rows4_max(mx) * qs;  // log2 units
-      const bool up = mx > m_run[nb] + 8.f;
-      mn[nb] = up ? mx : m_run[nb];
-      alpha[nb] = fast_exp2(m_run[nb] - mn[nb]);
-      moved = moved || up;
-      m_run[nb] = mn[nb];
-    }
-    if (__builtin_amdgcn_ballot_w64(moved)) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        l_run[nb] *= alpha[nb];
-#pragma unroll
-        for (int db = 0; db < 8; ++db) acc_o[nb][db] *= alpha[nb];
-      }
-    }
-    uint4 pb[2][2];  // [N-block][32-key step]: bf16 probabilities, 8 keys
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float ps = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = fast_exp2(fmaf(s[mb][nb][e], qs, -mn[nb]));
-          s[mb][nb][e] = p;  // the score register now holds its probability
-          ps += p;
-        }
-      l_run[nb] += ps;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // keys 32kk + 8 g4 + j: j < 4 from M-block 2kk, j >= 4 from 2kk+1
-        const f32x4_t u0 = s[2 * kk][nb], u1 = s[2 * kk + 1][nb];
-        pb[nb][kk] = make_uint4(pack_bf16x2(u0[0], u0[1]), pack_bf16x2(u0[2], u0[3]),
-                                pack_bf16x2(u1[0], u1[1]), pack_bf16x2(u1[2], u1[3]));
-      }
-    }
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint4 va = vt_operand(cv, db, 32 * kk, lane);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc_o[nb][db] = mfma_bf16(va, pb[nb][kk], acc_o[nb][db]);
-      }
-    }
+      for (int nb = 0; nb < 2; ++nb) lim[nb] = (ctx ? nval : min(nval, qpause[nb] - kbase + 1)) - 8 * g4;
+    };
+    wa.tile(ck, cv, !ctx || nval < TK, limits, qs, lane);
   };
 
   if (ntiles > 0) {
@@ -486,14 +342,14 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   if (ns > 1) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const float L = rows4_sum(l_run[nb]);
+      const float L = rows4_sum(wa.l[nb]);
       const int rl = wave * 32 + nb * 16 + l16;
       if (rl >= nq) continue;
       float* pp = a.part + (((((size_t)i * P.Hkv + hk) * ntq + qt) * ns + sp) * 128 + rl) * (D + 2);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) *(f32x4_t*)(pp + 16 * db + 4 * g4) = acc_o[nb][db];
+      for (int db = 0; db < 8; ++db) *(f32x4_t*)(pp + 16 * db + 4 * g4) = wa.acc[nb][db];
       if (g4 == 0) {
-        pp[D] = m_run[nb];
+        pp[D] = wa.m[nb];
         pp[D + 1] = L;
       }
     }
@@ -501,20 +357,11 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const float L = rows4_sum(l_run[nb]);
     const int r = q0 + wave * 32 + nb * 16 + l16;
     if (r >= q0 + nq) continue;
     const int pz = r >> 2, hh = r & 3;
-    bf16_t* dst = (bf16_t*)a.out + (((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh) * D;
-    const float inv = 1.f / L;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const uint32_t lo = bf16_bits(acc_o[nb][db][0] * inv) | (bf16_bits(acc_o[nb][db][1] * inv) << 16);
-      const uint32_t hi = bf16_bits(acc_o[nb][db][2] * inv) | (bf16_bits(acc_o[nb][db][3] * inv) << 16);
-      *(uint2*)(dst + 16 * db + 4 * g4) = make_uint2(lo, hi);
-    }
-    if (g4 == 0)
-      a.lse[((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh] = (m_run[nb] + __log2f(L)) * 0.6931471805599453f;
+    const size_t row = ((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh;
+    wa.store(nb, (bf16_t*)a.out + row * D, a.lse + row, lane);
   }
 }
 

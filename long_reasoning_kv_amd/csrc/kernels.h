@@ -104,6 +104,32 @@ struct CompressArgs {
   int32_t nsplit;        // MFMA path: context splits per query tile (1 = none)
 };
 
+// Block-mask prefill of one sequence in training order (T rows: the prompt,
+// then per block C text rows and, for complete blocks, Kp pause rows), one
+// layer. The staging pass rotates every key once into kst [Hkv][T][D] (values
+// into vst) and gathers the prompt and the kept code rows (pause k < quota of
+// every complete block) into kpers/vpers [Hkv][npers][D]: the layer's
+// persistent rows. The attention pass takes one workgroup per record of desc
+// (kBmRec ints): {KV head (-1: none), kind (0 prompt, 1 text, 2 pause), first
+// query row, query tokens (<= 32), index of the first query in its range
+// (prompt, text-in-block or pause index), persistent rows it sees, first row
+// of its block in kst, rows of the block it sees, block}.
+constexpr int kBmRec = 9;
+struct BlockMaskArgs {
+  DevPool P;
+  const void* q;   // [T][Hq][D] pre-RoPE
+  const void* k;   // [T][Hkv][D] pre-RoPE
+  const void* v;   // [T][Hkv][D]
+  void* out;       // [T][Hq][D]
+  float* lse;      // [T][Hq]
+  void* kst;       // [Hkv][T][D]
+  void* vst;       // [Hkv][T][D]
+  void* kpers;     // [Hkv][npers][D] (the staging buffers themselves when compression is off)
+  void* vpers;
+  const int32_t* desc;
+  int32_t Hq, T, prompt, C, Kp, log2Kp, quota, npers, compress;
+};
+
 // Fill: desc holds per layer {pers_off, npers_pages, open_off, nopen_pages}
 // then the page lists.
 struct FillArgs {
@@ -138,7 +164,7 @@ bool decode_stream_supported(const DevPool& P, int32_t G);
 int32_t decode_stream_blocks_per_cu(const DevPool& P);
 hipError_t launch_decode_stream(const StreamArgs& a, int32_t nwg, hipStream_t s);
 // bf16, d = 128, four query heads per KV head, 64-row pages: MFMA decode with
-// wavefront-level stream-K over 16-row tiles (U, T, useg in tiles; T per wavefront)
+// wavefront-level stream-K over 32-row tiles (U, T, useg in tiles; T per wavefront)
 bool decode_mfma_supported(const DevPool& P, int32_t G);
 int32_t decode_mfma_waves_per_cu();
 hipError_t launch_decode_mfma(const StreamArgs& a, int32_t nwaves, hipStream_t s);  // + merge (always when fused)
@@ -147,6 +173,10 @@ hipError_t launch_prompt(const PromptArgs& a, hipStream_t s);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 bool compress_mfma_supported(const DevPool& P, int32_t G);
 hipError_t launch_fill(const FillArgs& a, int32_t max_rows, hipStream_t s);
+// block-mask prefill (bf16, d = 128, four query heads per KV head): staging pass
+// then one attention workgroup per descriptor record
+bool blockmask_supported(const DevPool& P, int32_t G);
+hipError_t launch_blockmask(const BlockMaskArgs& a, int32_t nrec, hipStream_t s);
 hipError_t launch_read(const ReadArgs& a, hipStream_t s);
 hipError_t launch_export(const ExportArgs& a, hipStream_t s);
 

@@ -1,0 +1,232 @@
+// Block-mask prefill: attention of every token of a sequence laid out in
+// training order (the prompt, then per block its C text tokens followed, once
+// the block is complete, by its K pause tokens) under the block mask of
+// Fig. 2(a) of arXiv 2610.20641, one layer. A prompt token sees the prompt
+// causally; a text token sees the prompt, the kept code rows (pause k < quota)
+// of earlier blocks and its own block's text causally; a pause token sees the
+// same plus its whole block and its block's pause keys up to its own. Every
+// token is rotated at its own position (pause k of block b at P + bC +
+// bitrev(k) C/K, Fig. 2(b)). With compression off the mask is plain causal.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_mfma.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace abk {
+
+// ---- staging: every key rotated once, values copied, persistent rows gathered ----
+//
+// Workgroup = one row of the sequence; thread (head, j) rotates the dimension
+// pair (j, j + D/2) in fp64 and rounds once to bf16, like every stored key.
+__global__ void __launch_bounds__(512) blockmask_stage_kernel(BlockMaskArgs a) {
+  constexpr int D = 128;
+  const DevPool& P = a.P;
+  const int row = blockIdx.x;
+  int pos, pidx = -1;
+  if (!a.compress || row < a.prompt) {
+    pos = row;  // prompt rows (all rows when compression is off) sit at their index
+    pidx = a.compress ? row : -1;
+  } else {
+    const int rel = row - a.prompt, blk = rel / (a.C + a.Kp), off = rel % (a.C + a.Kp);
+    if (off < a.C) {
+      pos = a.prompt + blk * a.C + off;
+    } else {
+      const int k = off - a.C;
+      pos = a.prompt + blk * a.C + bitrev_dev(k, a.log2Kp) * (a.C / a.Kp);
+      if (k < a.quota) pidx = a.prompt + blk * a.quota + k;  // a kept code row
+    }
+  }
+  const double2* rope = P.rope + (size_t)pos * (D / 2);
+  const bf16_t* kin = (const bf16_t*)a.k + (size_t)row * P.Hkv * D;
+  const bf16_t* vin = (const bf16_t*)a.v + (size_t)row * P.Hkv * D;
+  for (int t = threadIdx.x; t < P.Hkv * (D / 2); t += blockDim.x) {
+    const int hh = t / (D / 2), j = t % (D / 2);
+    const double x1 = to_f32(kin[hh * D + j]), x2 = to_f32(kin[hh * D + j + D / 2]);
+    const double2 cs = rope[j];
+    const bf16_t y1 = from_f64<bf16_t>(rot_first(x1, x2, cs));
+    const bf16_t y2 = from_f64<bf16_t>(rot_second(x1, x2, cs));
+    const bf16_t v1 = vin[hh * D + j], v2 = vin[hh * D + j + D / 2];
+    bf16_t* ks = (bf16_t*)a.kst + ((size_t)hh * a.T + row) * D;
+    bf16_t* vs = (bf16_t*)a.vst + ((size_t)hh * a.T + row) * D;
+    ks[j] = y1;
+    ks[j + D / 2] = y2;
+    vs[j] = v1;
+    vs[j + D / 2] = v2;
+    if (pidx >= 0) {
+      bf16_t* kp = (bf16_t*)a.kpers + ((size_t)hh * a.npers + pidx) * D;
+      bf16_t* vp = (bf16_t*)a.vpers + ((size_t)hh * a.npers + pidx) * D;
+      kp[j] = y1;
+      kp[j + D / 2] = y2;
+      vp[j] = v1;
+      vp[j + D / 2] = v2;
+    }
+  }
+}
+
+// ---- attention on bf16 MFMA ---------------------------------------------------
+//
+// Workgroup = one descriptor record: a KV head and up to 32 query tokens of one
+// kind inside one block (query row r is token r/4, head 4h + r%4; each of the 4
+// wavefronts owns 32 rows). Its keys are two contiguous ranges: A, the layer's
+// persistent rows (kpers: the prompt, then the kept code rows in block order),
+// of which it sees the first nA (prompt tokens: causally); and B, its own
+// block in training order (kst from the block's first text row), of which it
+// sees the first nB rows, text causally and, for pause queries, pause keys up
+// to their own. Each range streams through LDS in 64-key tiles with the
+// per-tile math of attn_mfma.h, the next tile loading while the current one is
+// computed; a tile is masked only when one of its keys lies past the smallest
+// limit of the workgroup's queries.
+__global__ void __launch_bounds__(256, 2) blockmask_attn_mfma_kernel(BlockMaskArgs a) {
+  constexpr int D = 128, G = 4, TK = kTileKeys, RB = D * 2;
+  __shared__ uint4 lk0[TK * RB / 16], lk1[TK * RB / 16];
+  __shared__ uint4 lv0[TK * RB / 16], lv1[TK * RB / 16];
+  const DevPool& P = a.P;
+  const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int32_t* rec = a.desc + (size_t)blockIdx.x * kBmRec;
+  const int hk = rec[0];
+  if (hk < 0) return;
+  const int kind = rec[1], row0 = rec[2], ntok = rec[3], tok0 = rec[4], nA = rec[5];
+  const int bstart = rec[6], nB = rec[7], blk = rec[8];
+  const int rowsA = kind == 0 ? tok0 + ntok : nA;  // range A rows the workgroup reads
+  const int ntA = (rowsA + TK - 1) / TK, ntB = (nB + TK - 1) / TK, ntiles = ntA + ntB;
+  // smallest visibility limit of the workgroup's queries in each range
+  const int minA = kind == 0 ? tok0 + 1 : nA;
+  const int minB = kind == 1 ? tok0 + 1 : a.C + tok0 + 1;
+
+  // ---- the wavefront's query rows (rotated at their positions, rounded once
+  // to bf16) and their limits in both ranges; rows past the tile's tokens
+  // repeat its last token and are not written
+  const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
+  WaveAttn wa;
+  int limA[2], limB[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r = wave * 32 + nb * 16 + l16;
+    const int tok = min(r >> 2, ntok - 1), hh = r & 3;
+    const int qi = tok0 + tok;  // the query's index in its range
+    int pos;
+    if (kind == 0) pos = row0 + tok;
+    else if (kind == 1) pos = a.prompt + blk * a.C + qi;
+    else pos = a.prompt + blk * a.C + bitrev_dev(qi, a.log2Kp) * (a.C / a.Kp);
+    const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)(row0 + tok) * a.Hq + hk * G + hh) * D;
+    query_operand(qrow, P.rope + (size_t)pos * (D / 2), g4, wa.qh[nb]);
+    limA[nb] = kind == 0 ? qi + 1 : nA;
+    limB[nb] = kind == 1 ? qi + 1 : (kind == 2 ? a.C + qi + 1 : 0);
+  }
+  wa.init();
+
+  // ---- tile t: range A tile t (t < ntA), else range B tile t - ntA
+  struct TileSrc {
+    const char* kb;
+    const char* vb;
+    int nval, r0;
+    bool in_a;
+  };
+  auto tile_src = [&](int t) __attribute__((always_inline)) {
+    TileSrc ts;
+    ts.in_a = t < ntA;
+    if (ts.in_a) {
+      ts.r0 = t * TK;
+      const size_t off = ((size_t)hk * a.npers + ts.r0) * RB;
+      ts.kb = (const char*)a.kpers + off;
+      ts.vb = (const char*)a.vpers + off;
+      ts.nval = min(TK, rowsA - ts.r0);
+    } else {
+      ts.r0 = (t - ntA) * TK;
+      const size_t off = ((size_t)hk * a.T + bstart + ts.r0) * RB;
+      ts.kb = (const char*)a.kst + off;
+      ts.vb = (const char*)a.vst + off;
+      ts.nval = min(TK, nB - ts.r0);
+    }
+    return ts;
+  };
+  // loads as in the compression kernel: in load j of wavefront w, lane l fills
+  // LDS chunk 256j + 64w + l (row 16j + 4w + l/16 at swizzled position l%16);
+  // rows past the tile's valid count repeat its last row
+  const int r_in = 4 * wave + (lane >> 4);
+  const int vchunk = (lane & 15) ^ vt_swz(r_in);
+  uint32_t kof_full[4], vof_full[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    kof_full[j] = (16 * j + r_in) * RB + 16 * ((lane & 15) ^ kswz(16 * j + r_in));
+    vof_full[j] = (16 * j + r_in) * RB + 16 * vchunk;
+  }
+  auto issue = [&](int t, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
+    const TileSrc ts = tile_src(t);
+    uint32_t kof[4], vof[4];
+    if (ts.nval == TK) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kof[j] = kof_full[j];
+        vof[j] = vof_full[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = min(16 * j + r_in, ts.nval - 1);
+        kof[j] = row * RB + 16 * ((lane & 15) ^ kswz(16 * j + r_in));
+        vof[j] = row * RB + 16 * vchunk;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_global_load_lds((const void*)(ts.kb + kof[j]),
+                                       (__attribute__((address_space(3))) void*)(dk + 256 * j + 64 * wave),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(ts.vb + vof[j]),
+                                       (__attribute__((address_space(3))) void*)(dv + 256 * j + 64 * wave),
+                                       16, 0, 0);
+    }
+  };
+
+  // one tile from (ck, cv) while the next loads into (nk, nv); the load is
+  // unconditional (past the end it repeats the last tile into the spare buffer)
+  auto step = [&](int u, const uint4* __restrict__ ck, const uint4* __restrict__ cv,
+                  uint4* __restrict__ nk, uint4* __restrict__ nv) __attribute__((always_inline)) {
+    issue(min(u + 1, ntiles - 1), nk, nv);
+    const bool in_a = u < ntA;
+    const int r0 = in_a ? u * TK : (u - ntA) * TK;
+    const int rows = in_a ? rowsA : nB;
+    auto limits = [&](int (&lim)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) lim[nb] = min(in_a ? limA[nb] : limB[nb], rows) - r0 - 8 * g4;
+    };
+    wa.tile(ck, cv, r0 + TK > (in_a ? minA : minB), limits, qs, lane);
+  };
+
+  if (ntiles > 0) {
+    issue(0, lk0, lv0);
+    __syncthreads();
+    for (int u = 0; u < ntiles; u += 2) {
+      step(u, lk0, lv0, lk1, lv1);
+      __syncthreads();
+      if (u + 1 >= ntiles) break;
+      step(u + 1, lk1, lv1, lk0, lv0);
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r = wave * 32 + nb * 16 + l16;
+    if ((r >> 2) >= ntok) continue;
+    const size_t row = (size_t)(row0 + (r >> 2)) * a.Hq + hk * G + (r & 3);
+    wa.store(nb, (bf16_t*)a.out + row * D, a.lse + row, lane);
+  }
+}
+
+// ---- launcher ----------------------------------------------------------------------
+
+bool blockmask_supported(const DevPool& P, int32_t G) { return P.dtype == 1 && P.D == 128 && G == 4; }
+
+hipError_t launch_blockmask(const BlockMaskArgs& a, int32_t nrec, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(blockmask_stage_kernel, dim3(a.T), dim3(512), 0, s, a);
+  if (nrec > 0) hipLaunchKernelGGL(blockmask_attn_mfma_kernel, dim3(nrec), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace abk

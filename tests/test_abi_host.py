@@ -183,3 +183,20 @@ def test_null_and_range_arguments():
     assert L.abk_pool_destroy(None) == abk.OK
     assert L.abk_pool_stats(None, None, None, None) == abk.INVALID_ARG
     pool.close()
+
+
+def test_blockmask_attention_argument_checks():
+    """Checks before any launch: bad layer, negative or too long sequences,
+    unsupported shapes; an empty sequence is a no-op."""
+    pool = _pool()  # fp32, d = 16: no block-mask prefill kernel
+    L = abk.lib()
+    assert L.abk_blockmask_attention(pool._h, 5, 0, 8, None, None, None, None, None) == abk.INVALID_ARG
+    assert L.abk_blockmask_attention(pool._h, 0, -1, 8, None, None, None, None, None) == abk.INVALID_ARG
+    assert L.abk_blockmask_attention(pool._h, 0, 0, 5000, None, None, None, None, None) == abk.INVALID_ARG
+    assert L.abk_blockmask_attention(pool._h, 0, 2, 8, None, None, None, None, None) == abk.UNSUPPORTED
+    pool.close()
+    bf = _pool(dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128, page_rows=4,
+               pool_bytes=2 * 2 * 4 * 128 * 2 * 40)
+    assert L.abk_blockmask_attention(bf._h, 0, 0, 0, None, None, None, None, None) == abk.OK
+    assert L.abk_blockmask_attention(bf._h, 0, 3, 17, None, None, None, None, None) == abk.OK  # host-only
+    bf.close()
