@@ -479,6 +479,78 @@ def run_compress(args, torch, abk):
     }
 
 
+def blockmask_visible_keys(P: int, G: int, C: int, Kp: int, q: int, compress: bool = True):
+    """Keys each token of a training-order sequence attends to under the block
+    mask, summed over the sequence (compression off: causal, T(T+1)/2)."""
+    if not compress:
+        T = P + G
+        return T * (T + 1) // 2
+    tot = P * (P + 1) // 2
+    nb = G // C
+    for blk in range((G + C - 1) // C):
+        n = min(C, G - blk * C)
+        base = P + blk * q
+        tot += n * base + n * (n + 1) // 2           # text: prefix + causal in block
+        if blk < nb:
+            tot += Kp * (base + C) + Kp * (Kp + 1) // 2  # pause: prefix + block + causal
+    return tot
+
+
+def run_prefill(args, torch, abk):
+    """Block-mask prefill at the Fig. 9 shape: one sequence of 16,384 text
+    tokens after a 256-token prompt, C = 512, K = 256 pause tokens per block,
+    every one of the 36 layers (its own quota); the same kernel with
+    compression off (plain causal attention over the same text) beside it."""
+    P, G, Kp = 256, 16384, 256
+    quotas = layer_quotas(2)
+    bf = torch.bfloat16
+    res = {}
+    for comp in (True, False):
+        pool = abk.Pool(num_layers=L, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_tokens=C,
+                        num_pause=Kp, layer_quota=quotas.tolist(), page_rows=PR, max_seqs=1,
+                        pool_bytes=2 * HKV * PR * D * 2 * 16, max_position=P + G, dtype="bf16",
+                        rope_base=1e6, compress=comp)
+        T = P + G + ((G // C) * Kp if comp else 0)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(5)
+        q = torch.randn((T, HQ, D), device="cuda", dtype=bf, generator=gen)
+        k = torch.randn((T, HKV, D), device="cuda", dtype=bf, generator=gen)
+        v = torch.randn((T, HKV, D), device="cuda", dtype=bf, generator=gen)
+        out = torch.empty((T, HQ, D), device="cuda", dtype=bf)
+        lse = torch.empty((T, HQ), device="cuda", dtype=torch.float32)
+        times = []
+        for rep in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for l in range(L):
+                pool.blockmask_attention(l, P, G, q, k, v, out, lse)
+            e1.record()
+            torch.cuda.synchronize()
+            if rep > 0:
+                times.append(e0.elapsed_time(e1))
+        pool.close()
+        del q, k, v, out, lse
+        keys = sum(blockmask_visible_keys(P, G, C, Kp, int(qq), comp) for qq in quotas)
+        flops = 4.0 * D * HQ * keys
+        ms = float(np.mean(times))
+        res[comp] = (ms, flops, T)
+    ms, flops, T = res[True]
+    ms_c, flops_c, _ = res[False]
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": "block-mask prefill (training-forward attention), 36 layers of one sequence",
+        "ms_per_forward": ms, "rows": T, "tflop_per_forward": flops / 1e12,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None},
+        "causal_ms_per_forward": ms_c, "causal_tflop_per_forward": flops_c / 1e12,
+        "causal_tflops": flops_c / (ms_c * 1e-3) / 1e12, "time_vs_causal": ms / ms_c,
+        "config": {"workload": "Fig. 9 shape: 256-token prompt + 16,384 text tokens, C = 512, "
+                               "K = 256 pause tokens per block (4:1 mean quota), 36 layers with "
+                               "quotas 6x256/12x64/18x128; causal: the same kernel with "
+                               "compression off over the 16,640 prompt + text tokens"},
+    }
+
+
 def serving_mix_admit(quotas, steps: int, compress: bool, pool_pages: int, seed: int = 4):
     """Admit sequences (P ~ U[128, 512], G ~ U[1024, 32768], seeded) while the
     pool holds each one's largest footprint over the run: its persistent rows
@@ -656,6 +728,7 @@ def main():
                     help="append and decode as two calls per layer (default: abk_append_decode)")
     ap.add_argument("--compress-reps", type=int, default=2)
     ap.add_argument("--no-compress", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-single-sequence", action="store_true",
                     help="skip the single-sequence compression latency (profiled runs of the event)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -712,6 +785,10 @@ def main():
     if not args.no_compress:
         print("[bench] compression event: 64 sequences x 36 layers", file=sys.stderr, flush=True)
         comp = run_compress(args, torch, abk)
+    pre = None
+    if not args.no_prefill:
+        print("[bench] block-mask prefill: 16K text tokens, 36 layers", file=sys.stderr, flush=True)
+        pre = run_prefill(args, torch, abk)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline (bounded sample)", file=sys.stderr, flush=True)
@@ -723,7 +800,7 @@ def main():
         "data": "synthetic", "config": res["config"], "hbm_gbps": res["hbm_gbps"],
         "decode_ms_per_step": res["decode_ms_per_step"],
         "compress_ms_in_timed_steps": res["compress_ms_in_timed_steps"],
-        "roofline": res["roofline"], "cpu_baseline": cpu, "compress": comp,
+        "roofline": res["roofline"], "cpu_baseline": cpu, "compress": comp, "prefill": pre,
     }
     print(json.dumps(line), flush=True)
 

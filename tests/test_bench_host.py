@@ -1,0 +1,45 @@
+"""CPU checks of bench.py's accounting: the workload sizes and algorithmic
+counts its roofline figures divide by, against the oracle's own enumeration."""
+import numpy as np
+import pytest
+
+import bench
+import oracle
+from oracle import LayerView
+
+
+@pytest.mark.parametrize("P,G,C,Kp,q,comp", [(3, 21, 8, 4, 2, True), (0, 16, 8, 4, 4, True),
+                                             (5, 7, 4, 2, 1, True), (4, 9, 8, 4, 2, False)])
+def test_prefill_key_count_matches_oracle(P, G, C, Kp, q, comp):
+    """The prefill's algorithmic flops are 4 d Hq times the keys every token
+    sees under the block mask."""
+    L = LayerView(P, C, Kp, q, comp)
+    kind, a, b = oracle.training_tokens(L, G)
+    nb = G // C if comp else 0
+    tot = sum(len(oracle.visible_keys(L, G, nb, (int(x), int(y), int(z)))[0])
+              for x, y, z in zip(kind, a, b))
+    assert bench.blockmask_visible_keys(P, G, C, Kp, q, comp) == tot
+
+
+def test_decode_resident_rows_match_oracle():
+    """Rows a decode step reads per (sequence, layer), as bench.py counts them
+    (C = 512), equal the size of the oracle's visible set."""
+    rng = np.random.default_rng(0)
+    for _ in range(12):
+        P = int(rng.integers(0, 600))
+        q = int(rng.choice([64, 128, 256]))
+        G = int(rng.integers(1, 3000))
+        L = LayerView(P, bench.C, 256, q)
+        keys = oracle.visible_keys(L, G, (G - 1) // bench.C, (oracle.TEXT, G - 1, 0))[0]
+        assert int(bench.resident_rows(np.array([P]), np.array([G]), q)[0]) == len(keys)
+        L0 = LayerView(P, bench.C, 256, q, compress=False)
+        keys0 = oracle.visible_keys(L0, G, 0, (oracle.TEXT, G - 1, 0))[0]
+        assert int(bench.resident_rows(np.array([P]), np.array([G]), q, compress=False)[0]) == len(keys0)
+
+
+def test_serving_mix_admission_fits_the_pool():
+    quotas = bench.layer_quotas(2)
+    pages = 50_000
+    for comp in (True, False):
+        P, G, used = bench.serving_mix_admit(quotas, 64, comp, pages)
+        assert len(P) > 0 and used <= pages
