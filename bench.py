@@ -63,7 +63,8 @@ def resident_rows(P, G, q, compress=True):
 
 KERNEL_SOURCES = {
     "decode_mfma": ("decode.hip", "common.h", "kernels.h"),
-    "compress_attn_mfma": ("compress.hip", "common.h", "kernels.h"),
+    "compress_attn_mfma": ("compress.hip", "attn_mfma.h", "common.h", "kernels.h"),
+    "blockmask_attn_mfma": ("prefill.hip", "attn_mfma.h", "common.h", "kernels.h"),
 }
 
 
@@ -170,7 +171,11 @@ def profile_summary(d):
             ("compress_attn_mfma", "compress_attn_mfma_64seq_36L", "cmp_trace", "cmp",
              "compress_attn_mfma",
              "block compression event: 64 sequences x 36 layers, K = 256 pause tokens, bf16, "
-             "d = 128, 32 q / 8 KV heads (bench.py compression event)")):
+             "d = 128, 32 q / 8 KV heads (bench.py compression event)"),
+            ("blockmask_attn_mfma", "blockmask_attn_mfma_fig9_36L", "pre_trace", "pre",
+             "blockmask_",
+             "block-mask prefill at the Fig. 9 shape: 256-token prompt + 16,384 text tokens, "
+             "C = 512, K = 256, 36 layers, bf16, d = 128, 32 q / 8 KV heads (bench.py prefill)")):
         if not os.path.isdir(os.path.join(d, prefix + "_fetch")):
             continue
         table, _ = _stats_table(d, trace, [match, "append_kernel", "pause_rope"])
@@ -204,6 +209,11 @@ def profile_summary(d):
                      f"{rf['achieved']:.0f} GB/s = {100 * rf['frac']:.1f}% of 8 TB/s",
                      f"counted HBM bytes / algorithmic bytes: "
                      f"{per_call / rf['algorithmic_bytes_per_launch']:.3f}"]
+        if fam == "blockmask_attn_mfma" and bj and bj.get("prefill"):
+            pf = bj["prefill"]
+            extra = [f"bench.py in the traced run: {pf['ms_per_forward']:.1f} ms per 36-layer forward, "
+                     f"{pf['roofline']['achieved']:.0f} TFLOP/s algorithmic = "
+                     f"{100 * pf['roofline']['frac']:.1f}% of 2.5 PFLOP/s bf16"]
         if fam == "compress_attn_mfma":
             sq = {}
             for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_MFMA",
@@ -251,6 +261,45 @@ def profile_summary(d):
         with open(os.path.join(prof, fam + "_traffic.json"), "w") as f:
             json.dump(rec, f, indent=1)
         print(f"wrote profiles/{tag}.txt and profiles/{fam}_traffic.json")
+    if os.path.isdir(os.path.join(d, "mix_trace")):
+        mix_summary(d, prof)
+
+
+def mix_summary(d, prof):
+    """profiles/serving_mix_200GiB.txt: the kernel table of a traced serving-mix
+    run beside the bench lines of that run and of an untraced full run."""
+    table, _ = _stats_table(d, "mix_trace", ["decode_", "compress", "pause_rope", "free_kernel"])
+    lines = ["serving mix -- 200 GiB paged pool, 36 layers, quotas 6x256/12x64/18x128, "
+             "P ~ U[128,512], G ~ U[1024,32768]; AbridgeKV, then full KV through the same kernels", "",
+             "Commands (run from the repository root with TMPDIR=/tmp; the library built in-tree beforehand):",
+             f"  trace pass: {_cmd(d, 'mix_trace')}", "",
+             "rocprofv3 --kernel-trace --stats of the traced run (durations in us; both modes):"] + table
+    for name, what in (("mix_trace", "traced run"), ("mix_full", "untraced run")):
+        path = os.path.join(d, name + ".json")
+        if not os.path.exists(path):
+            continue
+        j = json.load(open(path))
+        lines += ["", f"bench.py line of the {what}" + (f" ({_cmd(d, name)})" if name == "mix_full" else "") + ":"]
+        for mode in ("abridgekv", "full_kv"):
+            m = j[mode]
+            lines.append(f"  {mode:9s}: {m['sequences_resident']} sequences, {m['steps']} steps, "
+                         f"{m['tokens_per_s']:.0f} tokens/s, {m['ms_per_step']:.2f} ms/step, "
+                         f"{m['compressions_in_timed_steps']} compressions, "
+                         f"{m['kv_gbps_incl_compression']:.0f} GB/s of K/V read")
+        lines.append(f"  ratios: sequences x{j['sequences_ratio']:.2f}, tokens/s x{j['tokens_per_s_ratio']:.2f}")
+        if name == "mix_full":
+            tr = j["abridgekv"]["occupancy_trace"]
+            kv = tr["seq0_kv_mb"]
+            lines += ["", "occupancy (untraced run, AbridgeKV): first sequence's resident K/V in MB, "
+                          "every 16th step, with its generated count:",
+                      "  " + ", ".join(f"{g}:{x:.0f}" for g, x in
+                                       list(zip(tr["seq0_generated"], kv))[::16]),
+                      "pool pages by layer budget (rows kept per block) every 32 steps:"]
+            for q, v in tr["pages_by_quota"].items():
+                lines.append(f"  {q:>3s}-row layers: " + ", ".join(str(x) for x in v))
+    with open(os.path.join(prof, "serving_mix_200GiB.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote profiles/serving_mix_200GiB.txt")
 
 
 # ---------------------------------------------------------------------------------
@@ -505,7 +554,7 @@ def run_prefill(args, torch, abk):
     quotas = layer_quotas(2)
     bf = torch.bfloat16
     res = {}
-    for comp in (True, False):
+    for comp in ((True,) if args.no_prefill_causal else (True, False)):
         pool = abk.Pool(num_layers=L, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_tokens=C,
                         num_pause=Kp, layer_quota=quotas.tolist(), page_rows=PR, max_seqs=1,
                         pool_bytes=2 * HKV * PR * D * 2 * 16, max_position=P + G, dtype="bf16",
@@ -535,13 +584,18 @@ def run_prefill(args, torch, abk):
         ms = float(np.mean(times))
         res[comp] = (ms, flops, T)
     ms, flops, T = res[True]
-    ms_c, flops_c, _ = res[False]
+    ms_c, flops_c, _ = res.get(False, (float("nan"), float("nan"), 0))
     tflops = flops / (ms * 1e-3) / 1e12
+    # algorithmic bytes per launch (one layer): q, out and lse of every row, k
+    # and v of every row once
+    nbytes = T * (2 * HQ * D * 2 + HQ * 4 + 2 * HKV * D * 2)
     return {
         "metric": "block-mask prefill (training-forward attention), 36 layers of one sequence",
         "ms_per_forward": ms, "rows": T, "tflop_per_forward": flops / 1e12,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None},
+                     "frac": tflops / BF16_PEAK_TFLOPS,
+                     # HBM bytes per launch (one layer), from the counters
+                     "traffic": traffic_from_profiles("blockmask_attn_mfma", nbytes)},
         "causal_ms_per_forward": ms_c, "causal_tflop_per_forward": flops_c / 1e12,
         "causal_tflops": flops_c / (ms_c * 1e-3) / 1e12, "time_vs_causal": ms / ms_c,
         "config": {"workload": "Fig. 9 shape: 256-token prompt + 16,384 text tokens, C = 512, "
@@ -623,6 +677,27 @@ def run_serving_mix(args, torch, abk, compress: bool):
     lse = torch.empty((B, HQ), device="cuda", dtype=torch.float32)
     views = [[(q_in[t, l], k_in[t, l], v_in[t, l]) for l in range(L)] for t in range(nsets)]
     stats = {"compressions": 0, "rows": 0}
+    # occupancy trace (host bookkeeping only, no GPU synchronisation): the first
+    # sequence's resident K/V summed over layers every step, and the pool's
+    # pages by budget class (layers keeping 64 / 128 / 256 rows per block)
+    # every 32 steps
+    row_bytes = 2 * HKV * D * 2
+    trace = {"seq0_kv_mb": [], "seq0_generated": [], "budget_steps": [],
+             "pages_by_quota": {str(q): [] for q in sorted(set(quotas.tolist()))}, "pages_used": []}
+
+    def record(t):
+        rows = sum(pool.seq_query(sids[0], l)["resident_rows"] for l in range(L))
+        trace["seq0_kv_mb"].append(round(rows * row_bytes / 1e6, 3))
+        trace["seq0_generated"].append(int(g[0]))
+        if t % 32 == 0:
+            by = {q: 0 for q in trace["pages_by_quota"]}
+            for s in sids:
+                for l in range(L):
+                    by[str(int(quotas[l]))] += pool.seq_query(s, l)["n_pages"]
+            trace["budget_steps"].append(t)
+            for q in by:
+                trace["pages_by_quota"][q].append(by[q])
+            trace["pages_used"].append(pool.stats()["pages_used"])
 
     def step(t, count):
         if compress:
@@ -651,18 +726,19 @@ def run_serving_mix(args, torch, abk, compress: bool):
     t0 = time.perf_counter()
     for t in range(steps):
         step(warm + t, True)
+        record(t)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     st = pool.stats()
     pool.close()
     del q_in, k_in, v_in
     torch.cuda.empty_cache()
-    row_bytes = 2 * HKV * D * 2
     return {"sequences_resident": B, "tokens_per_s": B * steps / dt, "ms_per_step": 1e3 * dt / steps,
             "steps": steps, "compressions_in_timed_steps": stats["compressions"],
             "decode_kv_gb_per_step": stats["rows"] * row_bytes / steps / 1e9,
             "kv_gbps_incl_compression": stats["rows"] * row_bytes / dt / 1e9,
-            "pool_pages_used_at_end": st["pages_used"], "pool_pages": int(pool_pages)}
+            "pool_pages_used_at_end": st["pages_used"], "pool_pages": int(pool_pages),
+            "occupancy_trace": trace}
 
 
 def cpu_baseline(workload, budget_s: float):
@@ -729,6 +805,8 @@ def main():
     ap.add_argument("--compress-reps", type=int, default=2)
     ap.add_argument("--no-compress", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-prefill-causal", action="store_true",
+                    help="skip the plain-causal comparison of the prefill (profiled runs)")
     ap.add_argument("--no-single-sequence", action="store_true",
                     help="skip the single-sequence compression latency (profiled runs of the event)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

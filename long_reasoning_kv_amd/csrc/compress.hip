@@ -367,33 +367,53 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
 
 // ---- context splits: merge the partials of one (sequence, KV head, query tile) -------
 //
-// Workgroup = (pair, query tile); 8 rows x 32 threads at a time, each thread 4
-// dims: out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s.
+// Workgroup = (pair, query tile, group of 8 query rows); 32 threads per row, 4
+// dims each. Each thread fetches the maximum, sum and its 4 output elements of
+// eight partials in one round of independent loads and combines them online:
+// out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s.
 __global__ void __launch_bounds__(256) compress_merge_kernel(CompressArgs a) {
-  constexpr int D = 128, G = 4;
+  constexpr int D = 128, G = 4, K = 8;
   const int ntq = (4 * a.Kp + 127) / 128, ns = a.nsplit;
-  const int pair = blockIdx.x / ntq, qt = blockIdx.x % ntq;
+  const int rg = blockIdx.x % 16, pq = blockIdx.x / 16;
+  const int pair = pq / ntq, qt = pq % ntq;
   const int i = pair / a.P.Hkv, hk = pair % a.P.Hkv;
   const int q0 = qt * 128, nq = min(128, 4 * a.Kp - q0);
-  const float* base = a.part + (((size_t)i * a.P.Hkv + hk) * ntq + qt) * ns * 128 * (D + 2);
+  const int rl = rg * 8 + (threadIdx.x >> 5);
+  if (rl >= nq) return;
+  const size_t stride = (size_t)128 * (D + 2);  // one split's partials
+  const float* base = a.part + ((((size_t)i * a.P.Hkv + hk) * ntq + qt) * ns * 128 + rl) * (D + 2);
   const int d = 4 * (threadIdx.x & 31);
-  for (int rl = threadIdx.x >> 5; rl < nq; rl += 8) {
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, base[((size_t)s2 * 128 + rl) * (D + 2) + D]);
-    float Ls = 0.f;
-    f32x4_t O = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < ns; ++s2) {
-      const float* pp = base + ((size_t)s2 * 128 + rl) * (D + 2);
-      const float wgt = fast_exp2(pp[D] - M);
-      Ls += wgt * pp[D + 1];
-      O += wgt * *(const f32x4_t*)(pp + d);
+  float M = -INFINITY, Ls = 0.f;
+  f32x4_t O = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < ns; s0 += K) {
+    float mv[K], lv[K];
+    f32x4_t ov[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const float* pp = base + (size_t)min(s0 + k, ns - 1) * stride;
+      mv[k] = pp[D];
+      lv[k] = pp[D + 1];
+      ov[k] = *(const f32x4_t*)(pp + d);
     }
-    const int r = q0 + rl, pz = r >> 2, hh = r & 3;
-    const float inv = 1.f / Ls;
-    bf16_t* dst = (bf16_t*)a.out + (((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh) * D + d;
-    *(uint2*)dst = make_uint2(pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv));
-    if (d == 0) a.lse[((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh] = (M + __log2f(Ls)) * 0.6931471805599453f;
+    float cm = M;
+#pragma unroll
+    for (int k = 0; k < K; ++k) cm = s0 + k < ns ? fmaxf(cm, mv[k]) : cm;
+    const float r = fast_exp2(M - cm);  // first round: M = -inf, r = 0
+    Ls *= r;
+    O *= r;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const float wgt = s0 + k < ns ? fast_exp2(mv[k] - cm) : 0.f;
+      Ls += wgt * lv[k];
+      O += wgt * ov[k];
+    }
+    M = cm;
   }
+  const int r = q0 + rl, pz = r >> 2, hh = r & 3;
+  const float inv = 1.f / Ls;
+  bf16_t* dst = (bf16_t*)a.out + (((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh) * D + d;
+  *(uint2*)dst = make_uint2(pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv));
+  if (d == 0) a.lse[((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh] = (M + __log2f(Ls)) * 0.6931471805599453f;
 }
 
 // ---- launcher ----------------------------------------------------------------------
@@ -419,7 +439,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
     const int nwg = ((npair + 7) / 8) * 8 * ntq * a.nsplit;
     hipLaunchKernelGGL(compress_attn_mfma_kernel, dim3(nwg), dim3(256), 0, s, a);
     if (a.nsplit > 1)
-      hipLaunchKernelGGL(compress_merge_kernel, dim3(npair * ntq), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(compress_merge_kernel, dim3(npair * ntq * 16), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
