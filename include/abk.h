@@ -197,6 +197,17 @@ abk_status abk_read_rows(const abk_pool* p, int32_t seq_id, int32_t layer, int32
 abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_len, int32_t text_tokens,
                                    const void* q, const void* k, const void* v, void* out, float* lse);
 
+/* Prompt prefill into the pool, one layer: abk_write_prompt(seq_id, layer, k,
+ * v) followed by the prompt's causal attention (abk_blockmask_attention of the
+ * sequence's P prompt rows and no text). q [P, Hq, d] pre-RoPE, k/v [P, Hkv,
+ * d] as for abk_write_prompt; out [P, Hq, d] (pool dtype), lse [P, Hq] fp32,
+ * caller-owned, device. Errors as for the two calls, all checked before
+ * anything is written: INVALID_ARG (unknown sequence, bad layer, NULL
+ * pointers with P > 0), UNSUPPORTED (the block-mask prefill's shapes),
+ * BAD_STATE (generation has started at that layer). */
+abk_status abk_prefill_prompt(abk_pool* p, int32_t seq_id, int32_t layer, const void* q, const void* k,
+                              const void* v, void* out, float* lse);
+
 /* Pool-wide counters. resident_bytes = K+V bytes of resident rows. */
 abk_status abk_pool_stats(const abk_pool* p, int64_t* pages_used, int64_t* pages_free,
                           int64_t* resident_bytes);

@@ -22,7 +22,8 @@ SYMBOLS = [
     "abk_write_prompt", "abk_append_kv", "abk_decode_attention", "abk_append_decode",
     "abk_compress_block",
     "abk_free_block", "abk_seq_query", "abk_export_layout", "abk_read_rows",
-    "abk_pool_stats", "abk_synth_fill", "abk_blockmask_attention", "abk_last_error",
+    "abk_pool_stats", "abk_synth_fill", "abk_blockmask_attention", "abk_prefill_prompt",
+    "abk_last_error",
 ]
 
 
@@ -80,6 +81,7 @@ def lib():
             "abk_pool_stats": [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)],
             "abk_synth_fill": [vp, i32, i32, u64],
             "abk_blockmask_attention": [vp, i32, i32, i32, vp, vp, vp, vp, vp],
+            "abk_prefill_prompt": [vp, i32, i32, vp, vp, vp, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -203,6 +205,10 @@ class Pool:
     def blockmask_attention(self, layer, prompt_len, text_tokens, q, k, v, out, lse):
         _check(lib().abk_blockmask_attention(self._h, layer, prompt_len, text_tokens, _ptr(q), _ptr(k),
                                              _ptr(v), _ptr(out), _ptr(lse)))
+
+    def prefill_prompt(self, sid, layer, q, k, v, out, lse):
+        _check(lib().abk_prefill_prompt(self._h, sid, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                        _ptr(lse)))
 
     def synth_fill(self, sid, generated, seed):
         _check(lib().abk_synth_fill(self._h, sid, generated, seed & 0xFFFFFFFFFFFFFFFF))

@@ -723,6 +723,23 @@ abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_le
   return ABK_OK;
 }
 
+abk_status abk_prefill_prompt(abk_pool* p, int32_t seq_id, int32_t layer, const void* q, const void* k,
+                              const void* v, void* out, float* lse) {
+  if (abk_status st = check_pool(p)) return st;
+  if (p->host.check_seq(seq_id)) return set_err(ABK_ERR_INVALID_ARG, "unknown sequence id");
+  if (p->host.check_layer(layer)) return set_err(ABK_ERR_INVALID_ARG, "bad layer");
+  const abk::Shape& s = p->shape;
+  if (!(s.dtype == 1 && s.D == 128 && s.Hq == 4 * s.Hkv))
+    return set_err(ABK_ERR_UNSUPPORTED, "prompt prefill needs bf16, d = 128, four query heads per KV head");
+  const int32_t P = p->host.seq(seq_id).P;
+  if (!p->host_only && P > 0 && (!q || !out || !lse))
+    return set_err(ABK_ERR_INVALID_ARG, "q/out/lse is NULL");
+  // the rows into the pool (every check before anything changes), then the
+  // prompt's causal attention from the same inputs
+  if (abk_status st = abk_write_prompt(p, seq_id, layer, k, v)) return st;
+  return abk_blockmask_attention(p, layer, P, 0, q, k, v, out, lse);
+}
+
 abk_status abk_seq_query(const abk_pool* p, int32_t seq_id, int32_t layer, abk_seq_info* out) {
   if (abk_status st = check_pool(p)) return st;
   if (!out) return set_err(ABK_ERR_INVALID_ARG, "out is NULL");

@@ -200,3 +200,26 @@ def test_blockmask_attention_argument_checks():
     assert L.abk_blockmask_attention(bf._h, 0, 0, 0, None, None, None, None, None) == abk.OK
     assert L.abk_blockmask_attention(bf._h, 0, 3, 17, None, None, None, None, None) == abk.OK  # host-only
     bf.close()
+
+
+def test_prefill_prompt_checks_before_writing():
+    L = abk.lib()
+    pool = _pool()  # fp32: no prompt prefill kernel
+    s = pool.seq_create(3)
+    assert L.abk_prefill_prompt(pool._h, 7, 0, None, None, None, None, None) == abk.INVALID_ARG
+    assert L.abk_prefill_prompt(pool._h, s, 9, None, None, None, None, None) == abk.INVALID_ARG
+    assert L.abk_prefill_prompt(pool._h, s, 0, None, None, None, None, None) == abk.UNSUPPORTED
+    # nothing was written: appending is still refused for want of a prompt
+    with pytest.raises(abk.AbkError) as e:
+        pool.append_kv(0, [s], None, None)
+    assert e.value.status == abk.BAD_STATE
+    pool.close()
+    bf = _pool(dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128, page_rows=4,
+               pool_bytes=2 * 2 * 4 * 128 * 2 * 40)
+    s = bf.seq_create(3)
+    bf.prefill_prompt(s, 0, None, None, None, None, None)  # host-only: bookkeeping only
+    bf.append_kv(0, [s], None, None)                       # the prompt counts as written
+    with pytest.raises(abk.AbkError) as e:
+        bf.prefill_prompt(s, 0, None, None, None, None, None)
+    assert e.value.status == abk.BAD_STATE                 # generation has started
+    bf.close()

@@ -111,3 +111,44 @@ def test_blockmask_prefill_fig9_shape_sampled():
         _close(f"fig9 prefill lse L{layer} q{quotas[layer]}", host(lse[rows]), l_ref, 1e-3)
         assert np.isfinite(host(out)).all() and np.isfinite(host(lse)).all()
     pool.close()
+
+
+def test_prefill_prompt_writes_the_rows_and_attends():
+    """abk_prefill_prompt: the prompt's causal attention against the oracle, the
+    pool rows bit-equal to abk_write_prompt's, and a later decode over them
+    against the oracle."""
+    from tests.harness import Run
+    C, Kp, quotas = 64, 16, [16, 8]
+    runs = [Run(L=2, Hq=HQ, Hkv=HKV, D=D, C=C, Kp=Kp, quota=quotas, pr=16, dtype="bf16", max_seqs=4,
+                seed=21) for _ in range(2)]
+    for P in (37, 1, 0):
+        sids = [r.new_seq(P, P) for r in runs]
+        for l in range(2):
+            L = LayerView(P, C, Kp, quotas[l])
+            # the harness regenerates prompt rows from the sequence's seed at each layer
+            kind, a, b, q, k, v = _synth_inputs(L, 0, l, seed=runs[0].seeds[sids[0]])
+            kd, vd = dev(k, "bf16"), dev(v, "bf16")
+            out = torch.empty((P, HQ, D), device="cuda", dtype=torch.bfloat16)
+            lse = torch.empty((P, HQ), device="cuda", dtype=torch.float32)
+            runs[0].pool.prefill_prompt(sids[0], l, dev(q, "bf16"), kd, vd, out, lse)
+            runs[1].pool.write_prompt(sids[1], l, kd, vd)
+            torch.cuda.synchronize()
+            if P:
+                o_ref, l_ref = oracle.blockmask_prefill(L, 0, q, _fetcher(L, 0, k, v), oracle.BF16, 1e6)
+                _close(f"prompt prefill out P{P} L{l}", host(out), o_ref, 2e-2)
+                _close(f"prompt prefill lse P{P} L{l}", host(lse), l_ref, 1e-3)
+                kk = [torch.empty((P, HKV, D), device="cuda", dtype=torch.bfloat16) for _ in range(4)]
+                runs[0].pool.read_rows(sids[0], l, 0, P, kk[0], kk[1])
+                runs[1].pool.read_rows(sids[1], l, 0, P, kk[2], kk[3])
+                torch.cuda.synchronize()
+                assert torch.equal(kk[0], kk[2]) and torch.equal(kk[1], kk[3])
+        # a few tokens later the decode sees the prompt rows as written
+        runs[0].G[sids[0]] = 0
+        runs[0].grow({sids[0]: 5})
+        for l in range(2):
+            out, lse, q = runs[0].decode([sids[0]], l)
+            o_ref, l_ref, _ = runs[0].oracle_decode(sids[0], l, q[0])
+            _close(f"decode after prompt prefill P{P} L{l}", out[0], o_ref, 2e-2)
+            _close(f"decode lse after prompt prefill P{P} L{l}", lse[0], l_ref, 1e-3)
+    for r in runs:
+        r.pool.close()
