@@ -332,8 +332,9 @@ namespace {
 // flattened (sequence, head, tile) work; a sequence's tiles cover its
 // persistent rows, then its open rows. `before_append`: counts exclude the
 // token a fused call is about to append (which the kernel handles itself), and
-// a sequence with no rows yet gets one empty tile. Fails (UNSUPPORTED) before
-// anything changes if a head would need more than kMaxSplits partials.
+// a sequence with no rows yet gets one empty tile. Runs are lengthened where a
+// head would otherwise span more than kMaxSplits of them (one long sequence
+// among few heads).
 abk_status mfma_schedule(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
                          bool before_append, std::vector<abk::StreamArgs>* chunks) {
   const abk::Shape& s = p->shape;
@@ -356,7 +357,10 @@ abk_status mfma_schedule(abk_pool* p, int32_t layer, int32_t n, const int32_t* s
     const int32_t U = a.useg[m];
     const int32_t kMinUnits = 4;  // per wavefront, to amortise its set-up
     int32_t W = std::max(1, std::min(p->mfma_waves, (U + kMinUnits - 1) / kMinUnits));
-    const int32_t T = (U + W - 1) / W;
+    int32_t umax = 0;  // the longest head's tiles
+    for (int32_t i = 0; i < m; ++i) umax = std::max(umax, (a.useg[i + 1] - a.useg[i]) / s.Hkv);
+    // a head of u tiles spans at most ceil(u / T) + 1 runs
+    const int32_t T = std::max((U + W - 1) / W, (umax + abk::kMaxSplits - 3) / (abk::kMaxSplits - 2));
     int32_t maxp = 1;
     for (int32_t i = 0; i < m; ++i) {
       const int32_t units = (a.useg[i + 1] - a.useg[i]) / s.Hkv;
@@ -444,7 +448,9 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
       const int32_t U = a.useg[m];
       const int32_t kMinUnits = 8;  // per workgroup, to amortise its set-up
       int32_t W = std::max(1, std::min(p->stream_wgs, (U + kMinUnits - 1) / kMinUnits));
-      const int32_t T = (U + W - 1) / W;
+      int32_t umax = 0;  // the longest head's units; it spans at most ceil(u / T) + 1 runs
+      for (int32_t i = 0; i < m; ++i) umax = std::max(umax, (a.useg[i + 1] - a.useg[i]) / s.Hkv);
+      const int32_t T = std::max((U + W - 1) / W, (umax + abk::kMaxSplits - 3) / (abk::kMaxSplits - 2));
       W = (U + T - 1) / T;
       int32_t maxp = 1;
       for (int32_t i = 0; i < m; ++i) {

@@ -340,3 +340,33 @@ def test_fused_append_decode_equals_two_calls(compress):
                 twins[1].pool.read_rows(sb, l, 0, n, kb, vb)
                 torch.cuda.synchronize()
                 assert torch.equal(ka, kb) and torch.equal(va, vb), (l,)
+
+
+@pytest.mark.parametrize("Hq,Hkv,pr,compress,fused", [(32, 8, 64, True, False), (32, 8, 64, True, True),
+                                                      (4, 1, 64, False, False), (4, 1, 64, False, True),
+                                                      (4, 1, 32, False, False)])
+def test_one_long_sequence_many_partials_per_head(Hq, Hkv, pr, compress, fused):
+    """A single long sequence: each head's rows span many stream-K runs (more
+    partials than one merge round takes; with one KV head, more than the split
+    limit unless the runs are lengthened). 64-row pages: MFMA decode; 32-row
+    pages: the SIMT stream kernel."""
+    C, Kp, P = 512, 256, 300
+    G = 24000 if compress else 33000  # open block of 448 rows when compressed
+    rows = P + (((G - 1) // C) * 256 + (G - ((G - 1) // C) * C) if compress else G) + 2
+    pool_bytes = 2 * Hkv * pr * 128 * 2 * (rows // pr + 16)
+    run = Run(L=1, Hq=Hq, Hkv=Hkv, D=128, C=C, Kp=Kp, quota=[256], pr=pr, dtype="bf16",
+              compress=compress, max_seqs=1, pool_bytes=pool_bytes, max_position=33792, seed=8)
+    s = run.new_seq(P, 0)
+    run.fill(s, G)
+    if fused:
+        out, lse, q = run.step_fused([s])[0]
+    else:
+        run.grow({s: G + 1})
+        out, lse, q = run.decode([s], 0)
+    o_ref, l_ref, _ = run.oracle_decode(s, 0, q[0])
+    tag = f"long seq Hkv{Hkv} pr{pr} c{int(compress)} f{int(fused)}"
+    err_o = float(np.abs(out[0] - o_ref).max())
+    err_l = float(np.abs(lse[0] - l_ref).max())
+    print(f"[parity] {tag}: out {err_o:.3e} lse {err_l:.3e}", flush=True)
+    assert err_o <= 2e-2 and err_l <= 1e-3
+    run.pool.close()
