@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import long_reasoning_kv_amd as abk
 import oracle
 import synth
 from oracle import PAUSE, PROMPT, TEXT
@@ -131,7 +132,7 @@ def test_bf16_ragged_history_decode_and_layout(pr, split):
 # (page rows, C, K, quotas): 16-row pages take the SIMT kernel; 64-row pages the
 # MFMA kernel with 1, 2 and 4 query tiles and partial causal pause tiles
 COMPRESS_CASES = [(16, 64, 16, [16, 4]), (64, 128, 32, [32, 8]), (64, 128, 64, [64, 16]),
-                  (64, 256, 128, [128, 32])]
+                  (64, 256, 128, [128, 32]), (64, 64, 64, [64, 1])]  # last: as many pause rows as block rows, quota 1
 
 
 @pytest.mark.parametrize("pr,C,Kp,quota", COMPRESS_CASES)
@@ -370,3 +371,26 @@ def test_one_long_sequence_many_partials_per_head(Hq, Hkv, pr, compress, fused):
     print(f"[parity] {tag}: out {err_o:.3e} lse {err_l:.3e}", flush=True)
     assert err_o <= 2e-2 and err_l <= 1e-3
     run.pool.close()
+
+
+def test_positions_up_to_max_position():
+    """A history whose last token sits at the last row of the RoPE table
+    (position max_position - 1) decodes against the oracle; the next append
+    is refused before anything changes."""
+    run = _bf16_run(pr=64, split_rows=0, max_position=200)
+    s = run.new_seq(8, 0)
+    run.write_prompts(s)
+    run.grow({s: 192})
+    for l in range(2):
+        out, lse, q = run.decode([s], l)
+        o_ref, l_ref, keys = run.oracle_decode(s, l, q[0])
+        assert int(keys[3].max()) == 199
+        err = float(np.abs(out[0] - o_ref).max())
+        print(f"[parity] max_position L{l}: out {err:.3e}", flush=True)
+        assert err <= 2e-2 and float(np.abs(lse[0] - l_ref).max()) <= 1e-3
+    before = run.pool.seq_query(s, 0)
+    k = torch.zeros((1, 8, 128), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(abk.AbkError) as e:
+        run.pool.append_kv(0, [s], k, k)
+    assert e.value.status == abk.INVALID_ARG
+    assert run.pool.seq_query(s, 0) == before
