@@ -6,15 +6,19 @@ layers of a Qwen3-4B-shaped cache (32 query / 8 KV heads, d = 128, bf16) for 22
 sequences with prompts U[128, 512] and U[4096, 32768] generated tokens, blocks
 of C = 512 compressed to per-layer quotas (6 layers keep 256 rows per block, 12
 keep 64, 18 keep 128; which layers is a seeded permutation). A step is, per
-layer: append the current token (RoPE + write), then split-KV decode attention
-over the resident rows; any sequence whose block completes is compressed at
-every layer and its raw pages freed inside the step, as in serving. Inputs are
-synthetic and already resident in HBM when timing starts.
+layer, one call that appends the current token (RoPE + write) and runs the
+split-KV decode attention over the resident rows (abk_append_decode); any
+sequence whose block completes is compressed at every layer and its raw pages
+freed inside the step, as in serving. Inputs are synthetic and already
+resident in HBM when timing starts.
 
-Prints one JSON line: tokens/s, achieved HBM GB/s of the decode kernel against
-MI355X's 8 TB/s (HIP events around every decode launch in the timed region),
-the CPU oracle on a bounded sample, and the block-compression event (64
-sequences x 36 layers) with its MFMA-rate figures.
+Prints one JSON line: tokens/s, achieved HBM GB/s of the decode call against
+MI355X's 8 TB/s (HIP events around every call in the timed region), the CPU
+oracle on a bounded sample, the block-compression event (64 sequences x 36
+layers) and the block-mask prefill at the Fig. 9 shape, each with its MFMA
+rate. `--serving-mix` instead runs the saturated serving mix (200 GiB pool,
+AbridgeKV against full KV); `--profile-summary DIR` writes profiles/ from
+rocprofv3 runs.
 """
 from __future__ import annotations
 

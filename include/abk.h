@@ -20,9 +20,10 @@
  *  - Device buffers (q/k/v/out/lse and the pages) are plain device pointers;
  *    the caller owns its buffers, the pool owns pages, tables and workspace.
  *  - Row layouts are contiguous, row-major, in the pool's dtype unless stated.
- *    Keys are given before RoPE; the library rotates them (rotate-half, angle
- *    pos * rope_base^(-2i/d)) and stores the rotated row. Values are stored
- *    as given. Queries are rotated in fp32 and never rounded.
+ *    Keys and queries are given before RoPE; the library rotates them
+ *    (rotate-half, angle pos * rope_base^(-2i/d)) in fp64 from an fp64
+ *    cos/sin table and rounds the result once to the pool dtype: the stored
+ *    key row, and the query the scores take. Values are stored as given.
  *  - All device work is enqueued on the stream given at creation; calls
  *    return without synchronising unless stated. Host bookkeeping updates
  *    synchronously.
@@ -30,8 +31,9 @@
  *    error has enqueued nothing and changed no state. abk_last_error() gives
  *    the reason (thread-local text).
  *  - One host thread per pool.
- *  - Scores are q.k/sqrt(d); softmax runs in fp32; lse is the natural log of
- *    the sum of exp(score) (so out = sum exp(score - lse) v).
+ *  - Scores are q.k/sqrt(d), accumulated in fp32 from the rounded operands;
+ *    softmax runs in fp32; lse is the natural log of the sum of exp(score)
+ *    (so out = sum exp(score - lse) v).
  */
 #ifndef ABK_H
 #define ABK_H
