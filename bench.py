@@ -745,56 +745,78 @@ def run_serving_mix(args, torch, abk, compress: bool):
             "occupancy_trace": trace}
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(workload, budget_s: float):
     """The CPU oracle as it stands, on a bounded sample of the decode step:
     (sequence, layer) pairs until the time budget is spent; cost scales with
-    resident rows, so the whole step's time is extrapolated by rows."""
+    resident rows, so the whole step's time is extrapolated by rows. Timed
+    with every host thread, then on one thread for a third of the budget."""
     import oracle
     import synth
     from oracle import TEXT, LayerView
     quotas, P, G = workload
     B = len(P)
-    sampled_rows = 0
-    secs = 0.0
-    npairs = 0
     # (sequence, layer) pairs in a seeded order: the oracle decodes them one by
-    # one until it has spent budget_s seconds
+    # one until it has spent the budget
     pairs = [(si, l) for si in range(B) for l in range(L)]
     order = np.random.default_rng(12345).permutation(len(pairs))
     pairs = [pairs[k] for k in order]
-    for si, l in pairs:
-        Lv = LayerView(int(P[si]), C, int(quotas.max()), int(quotas[l]))
-        g, nb = int(G[si]), (int(G[si]) - 1) // C
-        seed = 2 * 1000003 + si * 7919 + 17
-        # inputs of the rows the mask shows (generation is not timed)
-        kind, ka, kb, _ = oracle.visible_keys(Lv, g, nb, (TEXT, g - 1, 0))
-        rows = {}
-        for which, w in (("k", synth.WHICH_K), ("v", synth.WHICH_V)):
-            out = np.empty((len(kind), HKV, D))
-            for kd in (0, 1, 2):
-                m = kind == kd
-                if m.any():
-                    out[m] = synth.rows(seed, l, kd, ka[m], kb[m], w, HKV, D, "bf16")
-            rows[which] = out
 
-        def fetch(kind_, a_, b_, which, rows=rows):
-            return rows[which]
+    def sample(budget):
+        sampled_rows, secs, npairs = 0, 0.0, 0
+        for si, l in pairs:
+            Lv = LayerView(int(P[si]), C, int(quotas.max()), int(quotas[l]))
+            g, nb = int(G[si]), (int(G[si]) - 1) // C
+            seed = 2 * 1000003 + si * 7919 + 17
+            # inputs of the rows the mask shows (generation is not timed)
+            kind, ka, kb, _ = oracle.visible_keys(Lv, g, nb, (TEXT, g - 1, 0))
+            rows = {}
+            for which, w in (("k", synth.WHICH_K), ("v", synth.WHICH_V)):
+                out = np.empty((len(kind), HKV, D))
+                for kd in (0, 1, 2):
+                    m = kind == kd
+                    if m.any():
+                        out[m] = synth.rows(seed, l, kd, ka[m], kb[m], w, HKV, D, "bf16")
+                rows[which] = out
 
-        q = synth.rows(seed, l, TEXT, [g - 1], 0, synth.WHICH_Q, HQ, D, "bf16")[0]
-        t0 = time.perf_counter()
-        _, _, keys = oracle.decode(Lv, g, nb, q, fetch, oracle.BF16, 1e6)
-        secs += time.perf_counter() - t0
-        sampled_rows += len(keys[0])
-        npairs += 1
-        if secs > budget_s:
-            break
+            def fetch(kind_, a_, b_, which, rows=rows):
+                return rows[which]
+
+            q = synth.rows(seed, l, TEXT, [g - 1], 0, synth.WHICH_Q, HQ, D, "bf16")[0]
+            t0 = time.perf_counter()
+            _, _, keys = oracle.decode(Lv, g, nb, q, fetch, oracle.BF16, 1e6)
+            secs += time.perf_counter() - t0
+            sampled_rows += len(keys[0])
+            npairs += 1
+            if secs > budget:
+                break
+        return sampled_rows, secs, npairs
+
     total_rows = sum(int(resident_rows(P, G, quotas[l]).sum()) for l in range(L))
-    step_s = secs * total_rows / sampled_rows
-    return {"value": B / step_s, "unit": "tokens/s", "cores": oracle.num_threads(),
+    threads = oracle.num_threads()
+    sampled_rows, secs, npairs = sample(budget_s)
+    oracle.set_num_threads(1)
+    rows1, secs1, npairs1 = sample(budget_s / 3)
+    oracle.set_num_threads(threads)
+    return {"value": B / (secs * total_rows / sampled_rows), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{npairs} (sequence, layer) pairs of the step in a seeded random order "
                       f"({sampled_rows} resident rows, {secs:.2f} s of oracle time); "
-                      f"extrapolated by rows to the 22-sequence 36-layer step ({total_rows} rows)"}
+                      f"extrapolated by rows to the 22-sequence 36-layer step ({total_rows} rows)",
+            "single_core_value": B / (secs1 * total_rows / rows1),
+            "single_core_sample": f"the first {npairs1} pairs of the same order on one thread "
+                                  f"({rows1} rows, {secs1:.2f} s)",
+            "cpu_model": _cpu_model()}
 
 
 def main():

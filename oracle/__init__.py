@@ -77,6 +77,7 @@ def lib():
         L.orc_attention.argtypes = [vp, i32, i32, i32, i64, vp, vp, vp, vp]
         L.orc_attention_batch.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_num_threads.restype = i32
+        L.orc_set_num_threads.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -175,6 +176,10 @@ def attention_batch(q: np.ndarray, off: np.ndarray, k: np.ndarray, v: np.ndarray
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().orc_set_num_threads(int(n))
 
 
 # ---- composed steps ----------------------------------------------------------

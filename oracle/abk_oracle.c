@@ -247,6 +247,15 @@ void orc_attention_batch(const double* q, int64_t nq, int Hq, int Hkv, int d,
   }
 }
 
+/* Threads the oracle's parallel loops use from now on (timing on one core). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
