@@ -394,3 +394,25 @@ def test_positions_up_to_max_position():
         run.pool.append_kv(0, [s], k, k)
     assert e.value.status == abk.INVALID_ARG
     assert run.pool.seq_query(s, 0) == before
+
+
+def test_empty_calls_change_nothing():
+    """Every hot-path call with no sequences (or no rows) is a no-op on the
+    device path too; the state and a later decode are as before."""
+    run = _bf16_run(pr=64, split_rows=0)
+    s = run.new_seq(5, 0)
+    run.write_prompts(s)
+    run.grow({s: 70})
+    before = [run.pool.seq_query(s, l) for l in range(2)]
+    e = torch.empty(0, device="cuda", dtype=torch.bfloat16)
+    f = torch.empty(0, device="cuda", dtype=torch.float32)
+    for l in range(2):
+        run.pool.append_kv(l, [], e, e)
+        run.pool.decode_attention(l, [], e, e, f)
+        run.pool.append_decode(l, [], e, e, e, e, f)
+        run.pool.compress_block(l, [], e, e, e, e, f)
+        run.pool.blockmask_attention(l, 0, 0, e, e, e, e, f)
+    run.pool.free_block([])
+    torch.cuda.synchronize()
+    assert [run.pool.seq_query(s, l) for l in range(2)] == before
+    _check_decode(run, [s], 0)
