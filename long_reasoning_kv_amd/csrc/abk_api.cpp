@@ -589,18 +589,19 @@ abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32
   a.nsplit = 1;
   if (abk::compress_mfma_supported(p->dev, a.G)) {
     // few sequences: split each query tile's context over several workgroups so
-    // that about two per CU run, keeping at least 4 context tiles per split
-    const int32_t ntq = (4 * Kp + 127) / 128;
+    // that about one per CU runs, keeping at least 4 context tiles per split
+    const int32_t ntq = (4 * Kp + abk::kCompressRows - 1) / abk::kCompressRows;
     const int32_t wgs = (n * s.Hkv + 7) / 8 * 8 * ntq;
     int32_t min_ntc = INT32_MAX;
     for (int32_t i = 0; i < n; ++i)
       min_ntc = std::min(min_ntc, (plan[i].pers_before + 63) / 64 + s.C / 64);
-    const int32_t target = 2 * std::max(1, p->cus);
+    const int32_t target = std::max(1, p->cus);
     if (wgs < target)
       a.nsplit = std::max(1, std::min({(target + wgs - 1) / wgs, min_ntc / 4, 16}));
     if (a.nsplit > 1) {
       if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
-                               (size_t)n * s.Hkv * ntq * a.nsplit * 128 * (s.D + 2) * sizeof(float)))
+                               (size_t)n * s.Hkv * ntq * a.nsplit * abk::kCompressRows * (s.D + 2) *
+                                   sizeof(float)))
         return st;
       a.part = p->part;
     }

@@ -50,6 +50,16 @@ __device__ __forceinline__ uint4 vt_operand(const uint4* __restrict__ tile, int 
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Two ds_read_b64_tr_b16 four rows apart (halves hh = 0, 1 of a V^T operand),
+// joined as one 128-bit operand without moving registers.
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ uint4 vt_pair(const char* addr) {
+  const s16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(addr));
+  const s16x4_t r1 =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(addr + 4 * 256));
+  return __builtin_bit_cast(uint4, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // key of S^T M-block mb, row m (see above)
 __device__ __forceinline__ int tile_key(int mb, int m) {
   return 32 * (mb >> 1) + 8 * (m >> 2) + 4 * (mb & 1) + (m & 3);
@@ -81,6 +91,31 @@ __device__ __forceinline__ void query_operand(const bf16_t* qrow, const double2*
   (void)D;
 }
 
+// Per-lane byte offsets of the operand reads of a 64-key tile. They depend on
+// the lane only (both swizzles of a row are functions of its low bits, which
+// are the lane's): K operand of M-block mb, k-step ks at k[ks] + kmb_off(mb);
+// V^T operand of dim block db, key step kk, half hh at v[db] + vkk_off(kk, hh).
+struct TileOffsets {
+  uint32_t k[4], v[8];
+};
+__device__ __forceinline__ TileOffsets tile_offsets(int lane) {
+  const int l16 = lane & 15, g4 = lane >> 4;
+  TileOffsets o;
+  const int kr0 = tile_key(0, l16);  // key row of M-block 0; kswz(tile_key(mb, l16)) = kswz(kr0)
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) o.k[ks] = kr0 * 256 + 16 * ((4 * ks + g4) ^ kswz(kr0));
+  const int g = lane >> 4, sl = lane & 15;
+  const int row0 = 8 * g + (sl >> 2);  // vt_swz(row0 + 32 kk + 4 hh) = vt_swz(row0)
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const int dim = 16 * db + 4 * (sl & 3);
+    o.v[db] = row0 * 256 + 16 * ((dim >> 3) ^ vt_swz(row0)) + 2 * (dim & 7);
+  }
+  return o;
+}
+__device__ __forceinline__ constexpr int kmb_off(int mb) { return (32 * (mb >> 1) + 4 * (mb & 1)) * 256; }
+__device__ __forceinline__ constexpr int vkk_off(int kk, int hh) { return (32 * kk + 4 * hh) * 256; }
+
 // The running state of a wavefront's 32 query rows.
 struct WaveAttn {
   uint4 qh[2][4];       // [N-block][k-step]: B operands of S^T
@@ -99,30 +134,49 @@ struct WaveAttn {
     }
   }
 
-  // One 64-key tile from its K and V buffers in LDS. When `masked`, key
-  // tile_key(mb, 4 g4 + e) = 8 g4 + (32(mb/2) + 4(mb%2) + e) of query column
-  // nb is kept only if 32(mb/2) + 4(mb%2) + e < lim[nb], the bound in this
-  // lane's key coordinates that limits(lim) fills (called only then): one
-  // compare per element. qs = log2(e)/sqrt(d).
+  // One 64-key tile from its K and V buffers in LDS: qk, softmax, pv.
   template <class Limits>
   __device__ __forceinline__ void tile(const uint4* __restrict__ ck, const uint4* __restrict__ cv,
                                        bool masked, Limits limits, float qs, int lane) {
-    const int l16 = lane & 15, g4 = lane >> 4;
     f32x4_t s[4][2];
+    uint4 pb[2][2];
+    const TileOffsets o = tile_offsets(lane);
+    qk(ck, o, s);
+    softmax(s, masked, limits, qs, lane, pb);
+    pv(cv, o, pb);
+  }
+
+  // S^T of a tile: s[mb][nb] lane l holds the unscaled scores of keys
+  // tile_key(mb, 4 g4 + e) against query column l%16 of N-block nb.
+  __device__ __forceinline__ void qk(const uint4* __restrict__ ck, const TileOffsets& o,
+                                     f32x4_t (&s)[4][2]) const {
+    const char* base = (const char*)ck;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) s[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const int kr = tile_key(mb, l16);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint4 ka = ck[kr * 16 + ((4 * ks + g4) ^ kswz(kr))];
+        const uint4 ka = *(const uint4*)(base + o.k[ks] + kmb_off(mb));
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma_bf16(ka, qh[nb][ks], s[mb][nb]);
       }
     }
+  }
+
+  // Online softmax of a tile's scores. When `masked`, key tile_key(mb, 4 g4 +
+  // e) = 8 g4 + (32(mb/2) + 4(mb%2) + e) of query column nb is kept only if
+  // 32(mb/2) + 4(mb%2) + e < lim[nb], the bound in this lane's key
+  // coordinates that limits(lim) fills (called only then): one compare per
+  // element. qs = log2(e)/sqrt(d). Moves the running maximum (rescaling O^T
+  // and the sum) when needed, adds the tile's probabilities to the sum and
+  // leaves them, as bf16, in pb[nb][kk] (keys 32 kk + 8 g4 + 0..7).
+  template <class Limits>
+  __device__ __forceinline__ void softmax(f32x4_t (&s)[4][2], bool masked, Limits limits, float qs, int lane,
+                                          uint4 (&pb)[2][2]) {
+    (void)lane;
     if (masked) {
       int lim[2];
       limits(lim);
@@ -134,7 +188,7 @@ struct WaveAttn {
           for (int e = 0; e < 4; ++e)
             s[mb][nb][e] = 32 * (mb >> 1) + 4 * (mb & 1) + e < lim[nb] ? s[mb][nb][e] : -INFINITY;
     }
-    // online softmax per query column (lane-local after the row swaps)
+    // per query column (lane-local after the row swaps)
     float mn[2], alpha[2];
     bool moved = false;
 #pragma unroll
@@ -159,7 +213,6 @@ struct WaveAttn {
         for (int db = 0; db < 8; ++db) acc[nb][db] *= alpha[nb];
       }
     }
-    uint4 pb[2][2];  // [N-block][32-key step]: bf16 probabilities, 8 keys
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       float ps = 0.f;
@@ -180,15 +233,64 @@ struct WaveAttn {
                                 pack_bf16x2(u1[0], u1[1]), pack_bf16x2(u1[2], u1[3]));
       }
     }
+  }
+
+  // O^T += V^T P^T for a tile's probabilities pb (V^T through two
+  // ds_read_b64_tr_b16 per operand, as in vt_operand).
+  __device__ __forceinline__ void pv(const uint4* __restrict__ cv, const TileOffsets& o,
+                                     const uint4 (&pb)[2][2]) {
+    const char* base = (const char*)cv;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint4 va = vt_operand(cv, db, 32 * kk, lane);
+        const uint4 va = vt_pair(base + o.v[db] + vkk_off(kk, 0));
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[nb][db] = mfma_bf16(va, pb[nb][kk], acc[nb][db]);
       }
     }
+  }
+
+  // The V^T operands of dim blocks db0..db0+3 of a tile, read into registers:
+  // va[db - db0][kk].
+  __device__ __forceinline__ static void v_operands(const uint4* __restrict__ cv, const TileOffsets& o, int db0,
+                                                    uint4 (&va)[4][2]) {
+    const char* base = (const char*)cv;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        va[d][kk] = vt_pair(base + o.v[db0 + d] + vkk_off(kk, 0));
+      }
+  }
+  // O^T += V^T P^T for dim blocks db0..db0+3 from operands in registers.
+  __device__ __forceinline__ void pv_regs(const uint4 (&va)[4][2], int db0, const uint4 (&pb)[2][2]) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[nb][db0 + d] = mfma_bf16(va[d][kk], pb[nb][kk], acc[nb][db0 + d]);
+  }
+  // The K operands of M-blocks mb0, mb0 + 1 of a tile: ka[m][ks].
+  __device__ __forceinline__ static void k_operands(const uint4* __restrict__ ck, const TileOffsets& o, int mb0,
+                                                    uint4 (&ka)[2][4]) {
+    const char* base = (const char*)ck;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) ka[m][ks] = *(const uint4*)(base + o.k[ks] + kmb_off(mb0 + m));
+  }
+  // S^T of M-blocks mb0, mb0 + 1 from their K operands.
+  __device__ __forceinline__ void qk_regs(const uint4 (&ka)[2][4], int mb0, f32x4_t (&s)[4][2]) const {
+    // four independent accumulation chains, interleaved
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          s[mb0 + m][nb] = mfma_bf16(ka[m][ks], qh[nb][ks], ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : s[mb0 + m][nb]);
   }
 
   // Write query column nb's normalised output (bf16, dims 16 db + 4 g4 + e) to

@@ -164,25 +164,44 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
 
 // ---- a5 on bf16 MFMA (d = 128, four query heads per KV head, 64-row pages) -------
 //
-// Workgroup = (sequence, KV head, tile of 128 query rows); query row r is pause
-// r/4, head 4h + r%4. Each of the 4 wavefronts owns 32 query rows and runs the
+// Workgroup = (sequence, KV head, tile of 256 query rows); query row r is pause
+// r/4, head 4h + r%4. Each of the 8 wavefronts owns 32 query rows and runs the
 // per-tile math of attn_mfma.h over the 64-key tiles: the context pages
-// (persistent, then open), then the pause-key tiles. The next tile streams
-// straight into LDS while the current one is computed (double-buffered, 64 KB).
-// Masks are applied only to partial and pause tiles.
+// (persistent, then open), then the pause-key tiles. Masks are applied only to
+// partial and pause tiles.
+//
+// The wavefronts form two groups, one wavefront of each on every SIMD, kept
+// one phase apart by a workgroup barrier between phases. In a matrix phase a
+// wavefront runs the previous tile's O^T += V^T P^T and then this tile's
+// S^T = K Q^T (64 MFMAs); in a vector phase it runs this tile's softmax. The
+// groups alternate, so each SIMD's matrix core works on one group's products
+// while its vector unit runs the other group's softmax:
+//   phase 2u:   group 0 matrix (PV u-1, QK u)   group 1 softmax u-1
+//   phase 2u+1: group 0 softmax u               group 1 matrix (PV u-1, QK u)
+// for u = 0..ntiles (absent tiles skipped). Tiles stream straight into a ring
+// of four LDS buffers (32 KB each: K rows swizzled by kswz, V rows by vt_swz):
+// at phase 2u every wavefront issues its share of tile u+2, and before the
+// barrier that ends phase 2u it waits for its share of tile u+1. Tile u's
+// buffer is read from phase 2u to 2u+3, and the load into it is issued at
+// phase 2u-4, after the barrier that ends its previous tile's last read.
 
-__global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs a) {
-  constexpr int D = 128, G = 4, TK = kTileKeys, RB = D * 2;
-  // K rows (chunks swizzled by kswz) and V rows (swizzled by vt_swz), two
-  // buffers each; separate arrays so that the compiler can tell them apart
-  __shared__ uint4 lk0[TK * RB / 16], lk1[TK * RB / 16];
-  __shared__ uint4 lv0[TK * RB / 16], lv1[TK * RB / 16];
+#ifndef ABK_PP_GROUP
+#define ABK_PP_GROUP(w) ((w) >> 2)  // wavefronts w and w + 4 share a SIMD
+#endif
+
+__global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs a) {
+  constexpr int D = 128, G = 4, TK = kTileKeys, RB = D * 2, QR = kCompressRows;
+  constexpr int TCH = TK * RB / 16;  // 16-byte chunks of a 64-row K (or V) tile
+  // the ring: separate arrays so that the compiler can tell them apart
+  __shared__ uint4 lk0[TCH], lk1[TCH], lk2[TCH], lk3[TCH];
+  __shared__ uint4 lv0[TCH], lv1[TCH], lv2[TCH], lv3[TCH];
   const DevPool& P = a.P;
   const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
+  const bool grp0 = ABK_PP_GROUP(wave) == 0;
   // workgroup -> (pair = sequence x KV head, query tile, context split); the
   // workgroups of one pair share blockIdx.x mod 8, i.e. one XCD and its L2
-  const int ntq = (4 * a.Kp + 127) / 128;
+  const int ntq = (4 * a.Kp + QR - 1) / QR;
   const int ns = a.nsplit;
   const int npair = a.n * P.Hkv;
   const int b = blockIdx.x, xcd = b & 7, jj = b >> 3;
@@ -194,8 +213,8 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   const int32_t* tab = ptab_of(P, slot, a.layer);
   const int npp = (n_pers + TK - 1) / TK, nop = P.C / TK;
   const int ntc = npp + nop;  // context tiles
-  const int q0 = qt * 128;    // first query row of the workgroup
-  const int nq = min(128, 4 * a.Kp - q0);
+  const int q0 = qt * QR;     // first query row of the workgroup
+  const int nq = min(QR, 4 * a.Kp - q0);
   const int last_pause = (q0 + nq - 1) >> 2;
   // this split's tiles: context tiles [tc0, tc1), then, in the last split, the
   // pause-key tiles; local tile u maps to tile index gt(u) (pause tiles follow
@@ -208,7 +227,8 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   auto gt = [&](int u) { return u < nct ? tc0 + u : ntc + (u - nct); };
 
   // ---- the wavefront's query rows: rotated at the bitrev position, rounded
-  // once to bf16 (like stored keys); the softmax scale goes on the fp32 scores
+  // once to bf16 (like stored keys); the softmax scale goes on the fp32 scores.
+  // Rows past the workgroup's last are computed on its first row, not stored.
   const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
   WaveAttn wa;
   int qpause[2];
@@ -227,7 +247,7 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
 
   // ---- tile t: 64 K rows and 64 V rows (a context page, or pause keys). The
   // page table is read through the constant address space (scalar loads: it
-  // does not change while the kernel runs), one tile ahead of its use.
+  // does not change while the kernel runs).
   const __attribute__((address_space(4))) int32_t* ctab =
       (const __attribute__((address_space(4))) int32_t*)tab;
   auto page_of = [&](int t) __attribute__((always_inline)) {
@@ -237,84 +257,121 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
   struct TileSrc {
     const char* kb;
     const char* vb;
-    int kstride, vstride, nval;
+    int vstride, nval;
   };
-  auto tile_src = [&](int t, int page) __attribute__((always_inline)) {
+  auto tile_src = [&](int t) __attribute__((always_inline)) {
     TileSrc ts;
     if (t < ntc) {
-      const size_t off = (((size_t)page * P.Hkv + hk) * TK) * RB;
+      const size_t off = (((size_t)page_of(t) * P.Hkv + hk) * TK) * RB;
       ts.kb = (const char*)P.kpool + off;
       ts.vb = (const char*)P.vpool + off;
-      ts.kstride = RB;
       ts.vstride = RB;
       ts.nval = (t == npp - 1) ? n_pers - t * TK : TK;
     } else {
       const int k0 = (t - ntc) * TK;
       ts.kb = (const char*)a.kp_rot + (((size_t)i * P.Hkv + hk) * a.Kp + k0) * RB;
       ts.vb = (const char*)a.vp + (((size_t)i * a.Kp + k0) * P.Hkv + hk) * RB;
-      ts.kstride = RB;
       ts.vstride = P.Hkv * RB;
       ts.nval = min(TK, a.Kp - k0);
     }
     return ts;
   };
   // Tile t straight from global memory into LDS (global_load_lds_dwordx4): in
-  // load j of wavefront w, lane l fills LDS chunk 256j + 64w + l, i.e. row
-  // 16j + 4w + l/16 at swizzled position l%16, so it fetches the source chunk
-  // that belongs there. Rows past the tile's valid count repeat its last row.
+  // load j of wavefront w, lane l fills LDS chunk 512j + 64w + l, i.e. row
+  // 32j + 4w + l/16 at swizzled position l%16, so it fetches the source chunk
+  // that belongs there (both swizzles ignore bit 5 of the row). Rows past the
+  // tile's valid count repeat its last row. Four loads per wavefront.
   const int r_in = 4 * wave + (lane >> 4);
-  const int vchunk = (lane & 15) ^ vt_swz(r_in);  // bits 0, 1, 3 of 16j + r_in are r_in's
-  // byte offsets of a whole context page's loads (rows 64 x 256 B): the same
-  // for every such tile, so computed once; 32-bit offsets from a uniform base
-  // let the loads take the scalar-base form
-  uint32_t kof_full[4], vof_full[4];
+  const int kchunk = (lane & 15) ^ kswz(r_in), vchunk = (lane & 15) ^ vt_swz(r_in);
+  // byte offsets of a whole context page's loads: the same for every such
+  // tile, so computed once; 32-bit offsets from a uniform base let the loads
+  // take the scalar-base form
+  uint32_t kof_full[2], vof_full[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    kof_full[j] = (16 * j + r_in) * RB + 16 * ((lane & 15) ^ kswz(16 * j + r_in));
-    vof_full[j] = (16 * j + r_in) * RB + 16 * vchunk;
+  for (int j = 0; j < 2; ++j) {
+    kof_full[j] = (32 * j + r_in) * RB + 16 * kchunk;
+    vof_full[j] = (32 * j + r_in) * RB + 16 * vchunk;
   }
-  auto issue = [&](int t, int page, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
-    const TileSrc ts = tile_src(t, page);
-    uint32_t kof[4], vof[4];
+  auto issue = [&](int u, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
+    const TileSrc ts = tile_src(gt(min(u, ntiles - 1)));
+    uint32_t kof[2], vof[2];
     if (ts.nval == TK && ts.vstride == RB) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         kof[j] = kof_full[j];
         vof[j] = vof_full[j];
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = min(16 * j + r_in, ts.nval - 1);
-        kof[j] = row * ts.kstride + 16 * ((lane & 15) ^ kswz(16 * j + r_in));
+      for (int j = 0; j < 2; ++j) {
+        const int row = min(32 * j + r_in, ts.nval - 1);
+        kof[j] = row * RB + 16 * kchunk;
         vof[j] = row * ts.vstride + 16 * vchunk;
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       __builtin_amdgcn_global_load_lds((const void*)(ts.kb + kof[j]),
-                                       (__attribute__((address_space(3))) void*)(dk + 256 * j + 64 * wave),
+                                       (__attribute__((address_space(3))) void*)(dk + 512 * j + 64 * wave),
                                        16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(ts.vb + vof[j]),
-                                       (__attribute__((address_space(3))) void*)(dv + 256 * j + 64 * wave),
+                                       (__attribute__((address_space(3))) void*)(dv + 512 * j + 64 * wave),
                                        16, 0, 0);
     }
   };
+  // the end of a phase: the wavefront's LDS reads have returned and, at the end
+  // of an even phase, its loads older than the last tile's four have landed;
+  // then every wavefront of the workgroup gets here (the loads of all of them
+  // are then in LDS). The signal fences keep the compiler from moving
+  // LDS accesses across the barrier.
+  auto end_phase = [&](bool wait_loads) __attribute__((always_inline)) {
+    if (wait_loads) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0): tile u+2 may fly
+    else __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): this phase's LDS reads are done
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
 
-  // One tile: start loading tile t+1 into (nk, nv), compute tile t from
-  // (ck, cv). The restrict qualifiers tell the compiler that the loads in
-  // flight do not write the buffers being read, so it waits for them only at
-  // the barrier that ends the step. The load is unconditional (the last one
-  // repeats the last tile into the spare buffer): a load issued on one path
-  // only makes the compiler wait for it before every later LDS read.
-  int page_next = page_of(gt(min(1, ntiles - 1)));
-  auto step = [&](int u, const uint4* __restrict__ ck, const uint4* __restrict__ cv,
-                  uint4* __restrict__ nk, uint4* __restrict__ nv) __attribute__((always_inline)) {
+  uint4 pb[2][2];  // a tile's probabilities between its softmax and the next matrix phase
+  uint4 va[4][2];  // its V^T operands of dims 0..63, read at the end of the softmax phase
+  TileOffsets to = tile_offsets(lane);
+  // The empty asm hides the lane offsets' values from the compiler, so that it
+  // adds them to each buffer's address at the read (an immediate offset)
+  // instead of keeping a register per buffer.
+  auto refresh = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(to.k[j]));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(to.v[j]));
+  };
+  // matrix phase of tile u: P V of tile u-1 (dims 0..63 from the operands in
+  // registers, dims 64..127 read from its V buffer vm1 first), then Q K^T of
+  // tile u from its K buffer k0; each group of operand reads is issued one
+  // group of products ahead of its use
+  auto matrix = [&](int u, const uint4* __restrict__ k0, const uint4* __restrict__ vm1, f32x4_t (&s)[4][2])
+      __attribute__((always_inline)) {
+    refresh();
+    const bool has_pv = u >= 1, has_qk = u < ntiles;
+    uint4 vb[4][2], ka[2][4], kb[2][4];
+    if (has_pv) {
+      WaveAttn::v_operands(vm1, to, 4, vb);
+      wa.pv_regs(va, 0, pb);
+    }
+    if (has_qk) WaveAttn::k_operands(k0, to, 0, ka);
+    if (has_pv) wa.pv_regs(vb, 4, pb);
+    if (has_qk) {
+      WaveAttn::k_operands(k0, to, 2, kb);
+      wa.qk_regs(ka, 0, s);
+      wa.qk_regs(kb, 2, s);
+    }
+  };
+  // softmax phase of tile u: masks for partial context pages and pause tiles (a
+  // uniform test; in a pause tile a query sees pause keys up to its own), then
+  // the tile's V operands of dims 0..63 from buffer v_buf into registers
+  auto vector = [&](int u, const uint4* __restrict__ v_buf, f32x4_t (&s)[4][2]) __attribute__((always_inline)) {
+    if (u < 0 || u >= ntiles) return;
+    refresh();
     const int t = gt(u);
-    issue(gt(min(u + 1, ntiles - 1)), page_next, nk, nv);
-    page_next = page_of(gt(min(u + 2, ntiles - 1)));
-    // mask: partial context pages and pause tiles (a uniform test); in a
-    // pause tile a query sees pause keys up to its own
     const bool ctx = t < ntc;
     const int nval = ctx ? (t == npp - 1 ? n_pers - t * TK : TK) : min(TK, a.Kp - (t - ntc) * TK);
     const int kbase = ctx ? 0 : (t - ntc) * TK;  // pause index of key 0 of a pause tile
@@ -322,19 +379,65 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) lim[nb] = (ctx ? nval : min(nval, qpause[nb] - kbase + 1)) - 8 * g4;
     };
-    wa.tile(ck, cv, !ctx || nval < TK, limits, qs, lane);
+    wa.softmax(s, !ctx || nval < TK, limits, qs, lane, pb);
+    WaveAttn::v_operands(v_buf, to, 0, va);
+  };
+  // Tile u: its matrix phase, then its softmax phase; group 0 runs them as
+  // phases 2u and 2u+1, group 1 one phase later. Tile u is in buffer (k0, v0);
+  // at every even phase 2u each wavefront issues its share of tile u+2 (past
+  // the end it repeats the last tile into the spare buffer) and at the end of
+  // it waits for its share of tile u+1. Each group runs its own copy of the
+  // loop; both pass the same number of barriers.
+  auto tile0 = [&](int u, const uint4* __restrict__ k0, const uint4* __restrict__ v0,
+                   const uint4* __restrict__ vm1, uint4* __restrict__ k2, uint4* __restrict__ v2)
+      __attribute__((always_inline)) {
+    f32x4_t s[4][2];
+    issue(u + 2, k2, v2);
+    matrix(u, k0, vm1, s);
+    end_phase(true);
+    vector(u, v0, s);
+    end_phase(false);
+  };
+  auto tile1 = [&](int u, const uint4* __restrict__ k0, const uint4* __restrict__ v0,
+                   const uint4* __restrict__ vm1, uint4* __restrict__ k3, uint4* __restrict__ v3)
+      __attribute__((always_inline)) {
+    f32x4_t s[4][2];
+    matrix(u, k0, vm1, s);
+    end_phase(false);
+    issue(u + 3, k3, v3);
+    vector(u, v0, s);
+    end_phase(true);
   };
 
   if (ntiles > 0) {
-    issue(gt(0), page_of(gt(0)), lk0, lv0);
-    __syncthreads();
-    for (int u = 0; u < ntiles; u += 2) {
-      step(u, lk0, lv0, lk1, lv1);
-      __syncthreads();
-      if (u + 1 >= ntiles) break;
-      step(u + 1, lk1, lv1, lk0, lv0);
-      __syncthreads();
+    issue(0, lk0, lv0);
+    issue(1, lk1, lv1);
+    end_phase(true);  // tile 0 is in
+    if (grp0) {
+      for (int u = 0; u <= ntiles; u += 4) {
+        tile0(u, lk0, lv0, lv3, lk2, lv2);
+        if (u + 1 > ntiles) break;
+        tile0(u + 1, lk1, lv1, lv0, lk3, lv3);
+        if (u + 2 > ntiles) break;
+        tile0(u + 2, lk2, lv2, lv1, lk0, lv0);
+        if (u + 3 > ntiles) break;
+        tile0(u + 3, lk3, lv3, lv2, lk1, lv1);
+      }
+      end_phase(false);  // group 1's last softmax phase
+    } else {
+      issue(2, lk2, lv2);  // phase 0: group 0's first matrix phase
+      end_phase(true);
+      for (int u = 0; u <= ntiles; u += 4) {
+        tile1(u, lk0, lv0, lv3, lk3, lv3);
+        if (u + 1 > ntiles) break;
+        tile1(u + 1, lk1, lv1, lv0, lk0, lv0);
+        if (u + 2 > ntiles) break;
+        tile1(u + 2, lk2, lv2, lv1, lk1, lv1);
+        if (u + 3 > ntiles) break;
+        tile1(u + 3, lk3, lv3, lv2, lk2, lv2);
+      }
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load may land in LDS after the end
   }
 
   // ---- output: O^T / l; lane holds dims 16 db + 4 g4 + e of query l16. With
@@ -345,7 +448,7 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
       const float L = rows4_sum(wa.l[nb]);
       const int rl = wave * 32 + nb * 16 + l16;
       if (rl >= nq) continue;
-      float* pp = a.part + (((((size_t)i * P.Hkv + hk) * ntq + qt) * ns + sp) * 128 + rl) * (D + 2);
+      float* pp = a.part + (((((size_t)i * P.Hkv + hk) * ntq + qt) * ns + sp) * QR + rl) * (D + 2);
 #pragma unroll
       for (int db = 0; db < 8; ++db) *(f32x4_t*)(pp + 16 * db + 4 * g4) = wa.acc[nb][db];
       if (g4 == 0) {
@@ -372,16 +475,16 @@ __global__ void __launch_bounds__(256, 2) compress_attn_mfma_kernel(CompressArgs
 // eight partials in one round of independent loads and combines them online:
 // out = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s.
 __global__ void __launch_bounds__(256) compress_merge_kernel(CompressArgs a) {
-  constexpr int D = 128, G = 4, K = 8;
-  const int ntq = (4 * a.Kp + 127) / 128, ns = a.nsplit;
-  const int rg = blockIdx.x % 16, pq = blockIdx.x / 16;
+  constexpr int D = 128, G = 4, K = 8, QR = kCompressRows, NRG = QR / 8;
+  const int ntq = (4 * a.Kp + QR - 1) / QR, ns = a.nsplit;
+  const int rg = blockIdx.x % NRG, pq = blockIdx.x / NRG;
   const int pair = pq / ntq, qt = pq % ntq;
   const int i = pair / a.P.Hkv, hk = pair % a.P.Hkv;
-  const int q0 = qt * 128, nq = min(128, 4 * a.Kp - q0);
+  const int q0 = qt * QR, nq = min(QR, 4 * a.Kp - q0);
   const int rl = rg * 8 + (threadIdx.x >> 5);
   if (rl >= nq) return;
-  const size_t stride = (size_t)128 * (D + 2);  // one split's partials
-  const float* base = a.part + ((((size_t)i * a.P.Hkv + hk) * ntq + qt) * ns * 128 + rl) * (D + 2);
+  const size_t stride = (size_t)QR * (D + 2);  // one split's partials
+  const float* base = a.part + ((((size_t)i * a.P.Hkv + hk) * ntq + qt) * ns * QR + rl) * (D + 2);
   const int d = 4 * (threadIdx.x & 31);
   float M = -INFINITY, Ls = 0.f;
   f32x4_t O = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -434,12 +537,13 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   });
   if (mfma) {
     // tiles of one (sequence, KV head) pair share blockIdx.x mod 8 (one XCD)
-    const int ntq = (4 * a.Kp + 127) / 128;
+    const int ntq = (4 * a.Kp + kCompressRows - 1) / kCompressRows;
     const int npair = a.n * a.P.Hkv;
     const int nwg = ((npair + 7) / 8) * 8 * ntq * a.nsplit;
-    hipLaunchKernelGGL(compress_attn_mfma_kernel, dim3(nwg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(compress_attn_mfma_kernel, dim3(nwg), dim3(512), 0, s, a);
     if (a.nsplit > 1)
-      hipLaunchKernelGGL(compress_merge_kernel, dim3(npair * ntq * 16), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(compress_merge_kernel, dim3(npair * ntq * (kCompressRows / 8)), dim3(256), 0, s,
+                         a);
   }
   return hipGetLastError();
 }

@@ -87,6 +87,10 @@ struct PromptArgs {
   int32_t slot, layer, prompt_len;
 };
 
+// Query rows (pause tokens x query heads of a KV head) per workgroup of the
+// MFMA compression kernel.
+constexpr int kCompressRows = 256;
+
 // One compression record per sequence in desc (ints):
 // {slot, block, pers_before, prompt_len, pages_off, npages, first_new, pad}
 constexpr int kCompRec = 8;
@@ -99,7 +103,7 @@ struct CompressArgs {
   float* lse;
   void* kp_rot;          // workspace [n][Hkv][Kp][D]: rotated pause keys
   const int32_t* desc;   // n records, then page lists
-  float* part;           // nsplit > 1: [n][Hkv][query tiles][nsplit][128][D + 2] partials
+  float* part;           // nsplit > 1: [n][Hkv][query tiles][nsplit][kCompressRows][D + 2] partials
   int32_t layer, n, Hq, G, Kp, quota, log2Kp;
   int32_t nsplit;        // MFMA path: context splits per query tile (1 = none)
 };
