@@ -51,6 +51,20 @@ def layer_quotas(seed: int):
     return q
 
 
+def head_quotas(quotas, seed: int = 2):
+    """Per-(layer, KV head) quotas with each layer's total kept: a layer of
+    quota q <= 128 gives its 8 KV heads a seeded permutation of {2q, q/2, q/2,
+    q, q, q, q, q} (one head doubled, two halved, as in Fig. 7's single-head
+    moves); a layer at the pause count (256) keeps 256 on every head."""
+    rng = np.random.default_rng(seed + 1000)
+    out = []
+    for q in quotas:
+        q = int(q)
+        row = [2 * q, q // 2, q // 2] + [q] * (HKV - 3) if 2 * q <= 256 else [q] * HKV
+        out.append([int(x) for x in rng.permutation(row)])
+    return out
+
+
 def decode_workload(seed: int = 2, batch: int = 22):
     rng = np.random.default_rng(seed)
     P = rng.integers(128, 512, batch, endpoint=True)
@@ -312,19 +326,22 @@ def run_decode(args, torch, abk):
     quotas, P, G = decode_workload(args.seed)
     B = len(P)
     Kp = int(quotas.max())
+    hq = head_quotas(quotas, args.seed) if args.per_head else [[int(q)] * HKV for q in quotas]
     # warmup, then the timed steps twice: alone (value, ms_per_step), then with
     # HIP events around every call (the roofline's per-call durations)
     total_steps = args.warmup + 2 * args.steps
     # pool: resident rows now plus growth over the run, in whole pages, with slack
     pages = 0
     for l in range(L):
-        R = resident_rows(P, G + total_steps, quotas[l])
-        pages += int(np.sum(np.ceil(R / PR) + 2 + C // PR))
-    page_bytes = HKV * PR * D * 2
+        for qh in (hq[l] if args.per_head else [quotas[l]]):
+            R = resident_rows(P, G + total_steps, qh)
+            pages += int(np.sum(np.ceil(R / PR) + 2 + C // PR))
+    page_bytes = (1 if args.per_head else HKV) * PR * D * 2
     pool = abk.Pool(num_layers=L, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_tokens=C,
                     num_pause=Kp, layer_quota=quotas.tolist(), page_rows=PR, max_seqs=B,
                     pool_bytes=2 * page_bytes * pages, max_position=33792, dtype="bf16",
-                    rope_base=1e6, decode_split_rows=args.split_rows)
+                    rope_base=1e6, decode_split_rows=args.split_rows,
+                    head_quota=hq if args.per_head else None)
     sids = []
     for i in range(B):
         s = pool.seq_create(int(P[i]))
@@ -387,7 +404,8 @@ def run_decode(args, torch, abk):
             if rec is not None:
                 rec[l][1].record()
         if rec is not None:
-            rows_log.append([int((P + nb * quotas[l] + (g + 1 - nb * C)).sum()) for l in range(L)])
+            # resident (row, KV head) pairs each call reads
+            rows_log.append([sum(int((P + nb * qh + (g + 1 - nb * C)).sum()) for qh in hq[l]) for l in range(L)])
         g[:] += 1
 
     rows_log = []
@@ -410,7 +428,7 @@ def run_decode(args, torch, abk):
     row_bytes = 2 * HKV * D * 2
     io_bytes = B * (2 * HQ * D * 2 + HQ * 4) + (0 if args.separate_append else B * 2 * row_bytes)
     dec_ms = [e0.elapsed_time(e1) for evs in ev for e0, e1 in evs]
-    dec_bytes = [rows * row_bytes + io_bytes for rl in rows_log for rows in rl]
+    dec_bytes = [rh * (2 * D * 2) + io_bytes for rl in rows_log for rh in rl]
     achieved = sum(dec_bytes) / (sum(dec_ms) * 1e-3) / 1e9
     comp_ms = sum(a.elapsed_time(b) for a, b in cev)
     tokens = B * args.steps
@@ -433,11 +451,15 @@ def run_decode(args, torch, abk):
             "avg_launch_us": float(np.mean(dec_ms)) * 1e3,
         },
         "config": {
-            "workload": "36-layer per-layer-quota decode step (append + split-KV decode per "
+            "workload": "36-layer " + ("per-(layer, KV head)" if args.per_head else "per-layer") +
+                        "-quota decode step (append + split-KV decode per "
                         "layer, " + ("two calls" if args.separate_append else "one fused call") +
                         " each; compress+free when a block completes), 22 sequences",
             "layers": L, "batch": B, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
-            "block_tokens": C, "pause_tokens": Kp, "quotas": "6x256/12x64/18x128 (seeded)",
+            "block_tokens": C, "pause_tokens": Kp,
+            "quotas": ("per (layer, KV head): each layer's 8 heads a seeded permutation of "
+                       "{2q, q/2, q/2, q x 5} of the layer quota q (6x256/12x64/18x128, seeded; 256: "
+                       "every head)" if args.per_head else "6x256/12x64/18x128 (seeded)"),
             "prompt": "U[128,512]", "generated": "U[4096,32768]", "page_rows": PR,
             "resident_kv_gb": resident / 1e9,
             "full_kv_equivalent_gb": full_kv_rows * row_bytes / 1e9,
@@ -833,6 +855,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--split-rows", type=int, default=0, help="rows per split-KV work item (0: library default)")
+    ap.add_argument("--per-head", action="store_true",
+                    help="decode step with quotas per (layer, KV head) of the same layer totals")
     ap.add_argument("--separate-append", action="store_true",
                     help="append and decode as two calls per layer (default: abk_append_decode)")
     ap.add_argument("--compress-reps", type=int, default=2)

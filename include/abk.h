@@ -80,6 +80,19 @@ typedef struct {
                                 workgroup where the shape allows, else 512-row splits);
                                 > 0 = fixed split-KV work items of this many rows (whole
                                 pages) */
+  const int32_t* head_quota; /* optional [L][Hkv] code rows kept per block by each (layer,
+                                KV head), 0 <= quota <= the layer's pause count (copied);
+                                NULL = layer_quota for every head. Per-head quotas vary
+                                the budget head by head (figure captions, Fig. 7: the cost
+                                of halving one (layer, KV head)'s quota; AI Radio
+                                transcript: a per-head schedule). With them, every (layer
+                                l, KV head h) has its own rows and page table: the pool's
+                                pages hold one KV head, and the `layer` argument of
+                                abk_seq_query, abk_export_layout and abk_read_rows names
+                                the pair as l * Hkv + h (rows [n][1][d]). The hot-path
+                                calls keep their model-layer arguments and tensor
+                                layouts. abk_blockmask_attention and abk_prefill_prompt
+                                return UNSUPPORTED on such a pool. */
 } abk_pool_config;
 
 typedef struct {

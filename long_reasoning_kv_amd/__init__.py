@@ -45,6 +45,7 @@ class PoolConfig(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_double),
         ("compress", ctypes.c_int32), ("host_only", ctypes.c_int32),
         ("decode_split_rows", ctypes.c_int32),
+        ("head_quota", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -113,12 +114,23 @@ class Pool:
     def __init__(self, *, num_layers, num_q_heads, num_kv_heads, head_dim, block_tokens,
                  num_pause, layer_quota, layer_pause=None, page_rows=64, max_seqs=64,
                  pool_bytes=1 << 30, max_position=40960, dtype="bf16", rope_base=1e6,
-                 compress=True, host_only=False, decode_split_rows=0, stream=None):
+                 compress=True, host_only=False, decode_split_rows=0, head_quota=None, stream=None):
+        """head_quota: optional per-(layer, KV head) quotas, [L][Hkv] nested or
+        flat; then per-(sequence, layer) queries and layouts name the pair
+        (l, h) as layer l * Hkv + h."""
         self.L = num_layers
         self.Hq, self.Hkv, self.D = num_q_heads, num_kv_heads, head_dim
         self.C, self.page_rows = block_tokens, page_rows
         self.dtype = dtype
         self.quota = list(layer_quota)
+        self.head_quota = None
+        self._head_quota = None
+        if head_quota is not None:
+            flat = [int(x) for row in head_quota for x in (row if hasattr(row, "__iter__") else [row])]
+            if len(flat) != num_layers * num_kv_heads:
+                raise ValueError("head_quota needs num_layers x num_kv_heads entries")
+            self.head_quota = [flat[l * num_kv_heads:(l + 1) * num_kv_heads] for l in range(num_layers)]
+            self._head_quota = (ctypes.c_int32 * len(flat))(*flat)
         self.pause = list(layer_pause) if layer_pause is not None else [num_pause] * num_layers
         self._quota = (ctypes.c_int32 * num_layers)(*self.quota)
         self._pause = (ctypes.c_int32 * num_layers)(*layer_pause) if layer_pause is not None else None
@@ -128,7 +140,8 @@ class Pool:
             ctypes.cast(self._pause, ctypes.POINTER(ctypes.c_int32)) if self._pause else None,
             page_rows, max_seqs, pool_bytes, max_position,
             {"f32": F32, "bf16": BF16}[dtype], rope_base, int(compress), int(host_only),
-            decode_split_rows)
+            decode_split_rows,
+            ctypes.cast(self._head_quota, ctypes.POINTER(ctypes.c_int32)) if self._head_quota else None)
         if stream is None and not host_only:
             import torch
             stream = torch.cuda.current_stream().cuda_stream

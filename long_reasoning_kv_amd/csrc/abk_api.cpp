@@ -52,7 +52,11 @@ struct PinnedSlot {
 
 struct abk_pool {
   abk::HostPool host;
-  abk::Shape shape;
+  abk::Shape shape;  // as the host pool and the kernels see it (per-head quotas: see hs)
+  // Per-head quotas: hs = the model's KV heads, and every (layer l, KV head h)
+  // is layer l * hs + h of the pool, with one KV head (pages of one head, g
+  // query heads). Otherwise hs = 1.
+  int32_t hs = 1;
   bool host_only = false;
   int32_t split_rows = 0;  // 0: automatic schedule; > 0: fixed split-KV work items of this many rows
   int32_t stream_wgs = 0;  // resident workgroups of the stream-K decode (0: not used)
@@ -122,6 +126,40 @@ abk_status check_pool(const abk_pool* p) {
 
 size_t row_elems(const abk::Shape& s) { return (size_t)s.Hkv * s.D; }
 
+// The model layer `layer` as pool layers [layer * hs, layer * hs + hs).
+abk_status check_model_layer(const abk_pool* p, int32_t layer) {
+  if (layer < 0 || layer >= p->shape.L / p->hs) return set_err(ABK_ERR_INVALID_ARG, "bad layer");
+  return ABK_OK;
+}
+
+// Entries of a hot-path call: (sequence i, head j) at index i * hs + j, each a
+// (sequence, pool layer) with its own page table. Kernels address an entry's
+// metadata and page table through one combined index sid * L + pool layer
+// with a device view whose layer count is 1 (flat_view).
+struct Entries {
+  std::vector<int32_t> sid, lay, cslot;
+};
+Entries entries(const abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids) {
+  Entries e;
+  const size_t m = (size_t)n * p->hs;
+  e.sid.resize(m);
+  e.lay.resize(m);
+  e.cslot.resize(m);
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t j = 0; j < p->hs; ++j) {
+      const size_t x = (size_t)i * p->hs + j;
+      e.sid[x] = seq_ids[i];
+      e.lay[x] = layer * p->hs + j;
+      e.cslot[x] = seq_ids[i] * p->shape.L + e.lay[x];
+    }
+  return e;
+}
+abk::DevPool flat_view(const abk_pool* p) {
+  abk::DevPool d = p->dev;
+  d.L = 1;
+  return d;
+}
+
 }  // namespace
 
 extern "C" {
@@ -150,6 +188,24 @@ abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_poo
   else s.pause.assign(s.L, cfg->num_pause);
   if (s.Hkv < 1 || s.D < 1 || s.pr < 1 || (s.dtype != 0 && s.dtype != 1))
     return set_err(ABK_ERR_INVALID_ARG, "bad shape or dtype");
+  int32_t hs = 1;
+  if (cfg->head_quota) {
+    // per-(layer, KV head) quotas: one pool layer per pair, one KV head each
+    if (s.Hq < 1 || s.Hq % s.Hkv) return set_err(ABK_ERR_INVALID_ARG, "bad head counts");
+    if ((int64_t)s.L * s.Hkv > 4096) return set_err(ABK_ERR_INVALID_ARG, "num_layers * num_kv_heads above 4096");
+    hs = s.Hkv;
+    std::vector<int32_t> q, k;
+    for (int32_t l = 0; l < s.L; ++l)
+      for (int32_t h = 0; h < hs; ++h) {
+        q.push_back(cfg->head_quota[(size_t)l * hs + h]);
+        k.push_back(s.pause[l]);
+      }
+    s.quota = q;
+    s.pause = k;
+    s.L *= hs;
+    s.Hq /= hs;
+    s.Hkv = 1;
+  }
   const int64_t page_bytes = (int64_t)s.Hkv * s.pr * s.D * s.esize();
   s.num_pages = cfg->pool_bytes / (2 * page_bytes);
   abk_pool* p = new abk_pool();
@@ -163,6 +219,7 @@ abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_poo
     return set_err(ABK_ERR_UNSUPPORTED, "num_kv_heads * head_dim above 2048");
   }
   p->shape = s;
+  p->hs = hs;
   p->host_only = cfg->host_only != 0;
   if (cfg->decode_split_rows < 0) {
     delete p;
@@ -281,44 +338,54 @@ abk_status abk_write_prompt(abk_pool* p, int32_t seq_id, int32_t layer, const vo
                             const void* v) {
   if (abk_status st = check_pool(p)) return st;
   if (p->host.check_seq(seq_id)) return set_err(ABK_ERR_INVALID_ARG, "unknown sequence id");
+  if (abk_status st = check_model_layer(p, layer)) return st;
   const int32_t P = p->host.seq(seq_id).P;
   if (!p->host_only && P > 0 && (!k || !v)) return set_err(ABK_ERR_INVALID_ARG, "k/v is NULL");
-  if (abk::Status st = p->host.write_prompt(seq_id, layer)) return from_host(st, p->host.err);
+  if (abk::Status st = p->host.write_prompt(seq_id, layer * p->hs, p->hs)) return from_host(st, p->host.err);
   if (p->host_only) return ABK_OK;
-  const auto& pages = p->host.seq(seq_id).layers[layer].pers_pages;
   const int32_t np = (P + p->shape.pr - 1) / p->shape.pr;
-  if (abk_status st = upload_desc(p, pages.data(), np * sizeof(int32_t))) return st;
-  abk::PromptArgs a;
-  a.P = p->dev;
-  a.k = k;
-  a.v = v;
-  a.pages = (const int32_t*)p->desc;
-  a.slot = seq_id;
-  a.layer = layer;
-  a.prompt_len = P;
-  ABK_HIP(abk::launch_prompt(a, p->stream));
+  const size_t hb = (size_t)p->shape.Hkv * p->shape.D * p->shape.esize();  // one pool layer's heads
+  for (int32_t j = 0; j < p->hs; ++j) {
+    const int32_t lv = layer * p->hs + j;
+    const auto& pages = p->host.seq(seq_id).layers[lv].pers_pages;
+    if (abk_status st = upload_desc(p, pages.data(), np * sizeof(int32_t))) return st;
+    abk::PromptArgs a;
+    a.P = flat_view(p);
+    a.k = (const char*)k + j * hb;
+    a.v = (const char*)v + j * hb;
+    a.kv_stride = p->hs * p->shape.Hkv * p->shape.D;  // elements between the caller's rows
+    a.pages = (const int32_t*)p->desc;
+    a.slot = seq_id * p->shape.L + lv;
+    a.layer = 0;
+    a.prompt_len = P;
+    ABK_HIP(abk::launch_prompt(a, p->stream));
+  }
   return ABK_OK;
 }
 
 abk_status abk_append_kv(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
                          const void* k, const void* v) {
   if (abk_status st = check_pool(p)) return st;
+  if (abk_status st = check_model_layer(p, layer)) return st;
   if (!p->host_only && n > 0 && (!k || !v)) return set_err(ABK_ERR_INVALID_ARG, "k/v is NULL");
   std::vector<int32_t> new_page;
-  if (abk::Status st = p->host.append(layer, n, seq_ids, &new_page)) return from_host(st, p->host.err);
+  if (abk::Status st = p->host.append(layer * p->hs, p->hs, n, seq_ids, &new_page))
+    return from_host(st, p->host.err);
   if (p->host_only) return ABK_OK;
-  const size_t rb = row_elems(p->shape) * p->shape.esize();
-  for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
-    const int32_t m = std::min(n - c0, abk::kMaxBatch);
+  const Entries e = entries(p, layer, n, seq_ids);
+  const int32_t ne = (int32_t)e.sid.size();
+  const size_t rb = row_elems(p->shape) * p->shape.esize();  // one entry's row
+  for (int32_t c0 = 0; c0 < ne; c0 += abk::kMaxBatch) {
+    const int32_t m = std::min(ne - c0, abk::kMaxBatch);
     abk::AppendArgs a;
-    a.P = p->dev;
+    a.P = flat_view(p);
     a.k = (const char*)k + c0 * rb;
     a.v = (const char*)v + c0 * rb;
-    a.layer = layer;
+    a.layer = 0;
     a.n = m;
     a.compress = p->shape.compress;
     for (int32_t i = 0; i < m; ++i) {
-      a.slot[i] = seq_ids[c0 + i];
+      a.slot[i] = e.cslot[c0 + i];
       a.new_page[i] = new_page[c0 + i];
     }
     ABK_HIP(abk::launch_append(a, p->stream));
@@ -335,10 +402,11 @@ namespace {
 // a sequence with no rows yet gets one empty tile. Runs are lengthened where a
 // head would otherwise span more than kMaxSplits of them (one long sequence
 // among few heads).
-abk_status mfma_schedule(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
-                         bool before_append, std::vector<abk::StreamArgs>* chunks) {
+abk_status mfma_schedule(abk_pool* p, const Entries& e, bool before_append,
+                         std::vector<abk::StreamArgs>* chunks) {
   const abk::Shape& s = p->shape;
   constexpr int32_t TK = 32;
+  const int32_t n = (int32_t)e.sid.size();
   chunks->clear();
   for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
     const int32_t m = std::min(n - c0, abk::kMaxBatch);
@@ -346,12 +414,12 @@ abk_status mfma_schedule(abk_pool* p, int32_t layer, int32_t n, const int32_t* s
     abk::StreamArgs& a = chunks->back();
     a.useg[0] = 0;
     for (int32_t i = 0; i < m; ++i) {
-      const int32_t id = seq_ids[c0 + i];
-      const int32_t pers = p->host.seq(id).layers[layer].pers_rows;
-      const int32_t open = p->host.open_rows(id, layer);
+      const int32_t id = e.sid[c0 + i], lv = e.lay[c0 + i];
+      const int32_t pers = p->host.seq(id).layers[lv].pers_rows;
+      const int32_t open = p->host.open_rows(id, lv);
       int32_t units = (pers + TK - 1) / TK + (open + TK - 1) / TK;
       if (before_append && units == 0) units = 1;
-      a.slot[i] = id;
+      a.slot[i] = e.cslot[c0 + i];
       a.useg[i + 1] = a.useg[i] + units * s.Hkv;
     }
     const int32_t U = a.useg[m];
@@ -380,8 +448,7 @@ abk_status mfma_schedule(abk_pool* p, int32_t layer, int32_t n, const int32_t* s
 
 // Launch the scheduled chunks; k/v/new_page non-null: fused append of the
 // current token.
-abk_status launch_mfma_chunks(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
-                              const void* q, void* out, float* lse, const void* k, const void* v,
+abk_status launch_mfma_chunks(abk_pool* p, const void* q, void* out, float* lse, const void* k, const void* v,
                               const int32_t* new_page, std::vector<abk::StreamArgs>* chunks) {
   const abk::Shape& s = p->shape;
   const int32_t G = s.Hq / s.Hkv;
@@ -395,18 +462,17 @@ abk_status launch_mfma_chunks(abk_pool* p, int32_t layer, int32_t n, const int32
     abk::StreamArgs& a = (*chunks)[c];
     const int32_t c0 = (int32_t)c * abk::kMaxBatch;
     const int32_t W = (a.U + a.T - 1) / a.T;
-    a.P = p->dev;
+    a.P = flat_view(p);
     a.q = (const char*)q + c0 * qb;
     a.out = (char*)out + c0 * qb;
     a.lse = lse + (size_t)c0 * s.Hq;
     a.part = p->part;
-    a.layer = layer;
+    a.layer = 0;
     a.compress = s.compress;
     a.fused = k != nullptr;
     a.k = k ? (const char*)k + c0 * kb : nullptr;
     a.v = v ? (const char*)v + c0 * kb : nullptr;
     for (int32_t i = 0; i < a.n; ++i) a.new_page[i] = new_page ? new_page[c0 + i] : -1;
-    (void)seq_ids;
     ABK_HIP(abk::launch_decode_mfma(a, W, p->stream));
   }
   return ABK_OK;
@@ -417,32 +483,35 @@ abk_status launch_mfma_chunks(abk_pool* p, int32_t layer, int32_t n, const int32
 abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
                                 const void* q, void* out, float* lse) {
   if (abk_status st = check_pool(p)) return st;
+  if (abk_status st = check_model_layer(p, layer)) return st;
   if (!p->host_only && n > 0 && (!q || !out || !lse))
     return set_err(ABK_ERR_INVALID_ARG, "q/out/lse is NULL");
-  if (abk::Status st = p->host.check_decode(layer, n, seq_ids)) return from_host(st, p->host.err);
+  if (abk::Status st = p->host.check_decode(layer * p->hs, p->hs, n, seq_ids)) return from_host(st, p->host.err);
   if (p->host_only || n == 0) return ABK_OK;
   const abk::Shape& s = p->shape;
   const int32_t G = s.Hq / s.Hkv;
-  const size_t qb = (size_t)s.Hq * s.D * s.esize();
+  const size_t qb = (size_t)s.Hq * s.D * s.esize();  // one entry's queries
+  const Entries e = entries(p, layer, n, seq_ids);
+  const int32_t ne = (int32_t)e.sid.size();
   if (p->mfma_waves > 0 && p->split_rows == 0) {
     std::vector<abk::StreamArgs> chunks;
-    if (abk_status st = mfma_schedule(p, layer, n, seq_ids, false, &chunks)) return st;
-    return launch_mfma_chunks(p, layer, n, seq_ids, q, out, lse, nullptr, nullptr, nullptr, &chunks);
+    if (abk_status st = mfma_schedule(p, e, false, &chunks)) return st;
+    return launch_mfma_chunks(p, q, out, lse, nullptr, nullptr, nullptr, &chunks);
   }
   if (p->stream_wgs > 0 && p->split_rows == 0) {
     // stream-K: equal runs of 32-row units over the flattened (sequence, head, unit) work
     const int32_t nq = s.pr / 32;
-    for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
-      const int32_t m = std::min(n - c0, abk::kMaxBatch);
+    for (int32_t c0 = 0; c0 < ne; c0 += abk::kMaxBatch) {
+      const int32_t m = std::min(ne - c0, abk::kMaxBatch);
       abk::StreamArgs a;
       a.fused = 0;
       a.compress = s.compress;
       a.k = a.v = nullptr;
       a.useg[0] = 0;
       for (int32_t i = 0; i < m; ++i) {
-        const auto& lay = p->host.seq(seq_ids[c0 + i]).layers[layer];
+        const auto& lay = p->host.seq(e.sid[c0 + i]).layers[e.lay[c0 + i]];
         const int32_t units = (int32_t)(lay.pers_pages.size() + lay.open_pages.size()) * nq;
-        a.slot[i] = seq_ids[c0 + i];
+        a.slot[i] = e.cslot[c0 + i];
         a.useg[i + 1] = a.useg[i] + units * s.Hkv;
       }
       const int32_t U = a.useg[m];
@@ -464,12 +533,12 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
       if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
                                (size_t)m * s.Hkv * maxp * G * (s.D + 2) * sizeof(float)))
         return st;
-      a.P = p->dev;
+      a.P = flat_view(p);
       a.q = (const char*)q + c0 * qb;
       a.out = (char*)out + c0 * qb;
       a.lse = lse + (size_t)c0 * s.Hq;
       a.part = p->part;
-      a.layer = layer;
+      a.layer = 0;
       a.n = m;
       a.T = T;
       a.U = U;
@@ -481,40 +550,40 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
   // pages per split-KV work item; widened when a sequence would need more
   // than kMaxSplits of them
   int32_t split_pages = std::max(1, (p->split_rows > 0 ? p->split_rows : 512) / s.pr);
-  std::vector<int32_t> splits(n);
+  std::vector<int32_t> splits(ne);
   int32_t max_nvp = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    const auto& lay = p->host.seq(seq_ids[i]).layers[layer];
+  for (int32_t i = 0; i < ne; ++i) {
+    const auto& lay = p->host.seq(e.sid[i]).layers[e.lay[i]];
     splits[i] = (int32_t)(lay.pers_pages.size() + lay.open_pages.size());
     max_nvp = std::max(max_nvp, splits[i]);
   }
   split_pages = std::max(split_pages, (max_nvp + abk::kMaxSplits - 1) / abk::kMaxSplits);
-  for (int32_t i = 0; i < n; ++i) splits[i] = (splits[i] + split_pages - 1) / split_pages;
+  for (int32_t i = 0; i < ne; ++i) splits[i] = (splits[i] + split_pages - 1) / split_pages;
   // size the partials for the whole call first (growing synchronises)
   size_t need = 0;
-  for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
+  for (int32_t c0 = 0; c0 < ne; c0 += abk::kMaxBatch) {
     size_t t = 0;
-    for (int32_t i = c0; i < std::min(n, c0 + abk::kMaxBatch); ++i) t += splits[i];
+    for (int32_t i = c0; i < std::min(ne, c0 + abk::kMaxBatch); ++i) t += splits[i];
     need = std::max(need, t);
   }
   if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
                            need * s.Hkv * G * (s.D + 2) * sizeof(float)))
     return st;
-  for (int32_t c0 = 0; c0 < n; c0 += abk::kMaxBatch) {
-    const int32_t m = std::min(n - c0, abk::kMaxBatch);
+  for (int32_t c0 = 0; c0 < ne; c0 += abk::kMaxBatch) {
+    const int32_t m = std::min(ne - c0, abk::kMaxBatch);
     abk::DecodeArgs a;
-    a.P = p->dev;
+    a.P = flat_view(p);
     a.q = (const char*)q + c0 * qb;
     a.out = (char*)out + c0 * qb;
     a.lse = lse + (size_t)c0 * s.Hq;
     a.part = p->part;
-    a.layer = layer;
+    a.layer = 0;
     a.n = m;
     a.G = G;
     a.split_pages = split_pages;
     a.prefix[0] = 0;
     for (int32_t i = 0; i < m; ++i) {
-      a.slot[i] = seq_ids[c0 + i];
+      a.slot[i] = e.cslot[c0 + i];
       a.prefix[i + 1] = a.prefix[i] + splits[c0 + i];
     }
     ABK_HIP(abk::launch_decode(a, a.prefix[m], p->stream));
@@ -532,45 +601,51 @@ abk_status abk_append_decode(abk_pool* p, int32_t layer, int32_t n, const int32_
     if (abk_status st = abk_append_kv(p, layer, n, seq_ids, k, v)) return st;
     return abk_decode_attention(p, layer, n, seq_ids, q, out, lse);
   }
-  if (p->host.check_layer(layer)) return set_err(ABK_ERR_INVALID_ARG, "bad layer");
+  if (abk_status st = check_model_layer(p, layer)) return st;
   if (abk::Status st = p->host.check_batch(n, seq_ids)) return from_host(st, p->host.err);
+  const Entries e = entries(p, layer, n, seq_ids);
   std::vector<abk::StreamArgs> chunks;
-  if (abk_status st = mfma_schedule(p, layer, n, seq_ids, true, &chunks)) return st;
+  if (abk_status st = mfma_schedule(p, e, true, &chunks)) return st;
   std::vector<int32_t> new_page;
-  if (abk::Status st = p->host.append(layer, n, seq_ids, &new_page)) return from_host(st, p->host.err);
-  return launch_mfma_chunks(p, layer, n, seq_ids, q, out, lse, k, v, new_page.data(), &chunks);
+  if (abk::Status st = p->host.append(layer * p->hs, p->hs, n, seq_ids, &new_page))
+    return from_host(st, p->host.err);
+  return launch_mfma_chunks(p, q, out, lse, k, v, new_page.data(), &chunks);
 }
 
 abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
                               const void* q_pause, const void* k_pause, const void* v_pause,
                               void* out, float* lse) {
   if (abk_status st = check_pool(p)) return st;
+  if (abk_status st = check_model_layer(p, layer)) return st;
   if (!p->host_only && n > 0 && (!q_pause || !k_pause || !v_pause || !out || !lse))
     return set_err(ABK_ERR_INVALID_ARG, "a pause/out/lse pointer is NULL");
-  std::vector<abk::CompressPlan> plan;
-  if (abk::Status st = p->host.compress(layer, n, seq_ids, &plan)) return from_host(st, p->host.err);
+  std::vector<abk::CompressPlan> plan;  // one per (sequence, head) entry
+  if (abk::Status st = p->host.compress(layer * p->hs, p->hs, n, seq_ids, &plan))
+    return from_host(st, p->host.err);
   if (p->host_only || n == 0) return ABK_OK;
   const abk::Shape& s = p->shape;
-  const int32_t Kp = s.pause[layer];
+  const int32_t Kp = s.pause[layer * p->hs];
+  const int32_t ne = (int32_t)plan.size();
   std::vector<int32_t>& d = p->scratch;
-  d.assign((size_t)n * abk::kCompRec, 0);
-  for (int32_t i = 0; i < n; ++i) {
+  d.assign((size_t)ne * abk::kCompRec, 0);
+  for (int32_t i = 0; i < ne; ++i) {
     int32_t* r = &d[(size_t)i * abk::kCompRec];
-    r[0] = plan[i].slot;
+    r[0] = plan[i].slot * s.L + plan[i].layer;  // combined index (flat device view)
     r[1] = plan[i].block;
     r[2] = plan[i].pers_before;
     r[3] = p->host.seq(plan[i].slot).P;
     r[4] = (int32_t)d.size();
     r[5] = (int32_t)plan[i].pages.size();
     r[6] = plan[i].first_new;
+    r[7] = plan[i].quota;
     d.insert(d.end(), plan[i].pages.begin(), plan[i].pages.end());
   }
   if (abk_status st = grow(p, &p->kp_rot, &p->kp_rot_bytes,
-                           (size_t)n * s.Hkv * Kp * s.D * s.esize()))
+                           (size_t)ne * s.Hkv * Kp * s.D * s.esize()))
     return st;
   if (abk_status st = upload_desc(p, d.data(), d.size() * sizeof(int32_t))) return st;
   abk::CompressArgs a;
-  a.P = p->dev;
+  a.P = flat_view(p);
   a.qp = q_pause;
   a.kp = k_pause;
   a.vp = v_pause;
@@ -578,12 +653,12 @@ abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32
   a.lse = lse;
   a.kp_rot = p->kp_rot;
   a.desc = (const int32_t*)p->desc;
-  a.layer = layer;
-  a.n = n;
-  a.Hq = s.Hq;
+  a.layer = 0;
+  a.n = ne;
+  a.hsplit = p->hs;
+  a.Hq = s.Hq * p->hs;  // the caller's query heads
   a.G = s.Hq / s.Hkv;
   a.Kp = Kp;
-  a.quota = s.quota[layer];
   a.log2Kp = abk::log2_exact(Kp);
   a.part = nullptr;
   a.nsplit = 1;
@@ -591,16 +666,16 @@ abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32
     // few sequences: split each query tile's context over several workgroups so
     // that about one per CU runs, keeping at least 4 context tiles per split
     const int32_t ntq = (4 * Kp + abk::kCompressRows - 1) / abk::kCompressRows;
-    const int32_t wgs = (n * s.Hkv + 7) / 8 * 8 * ntq;
+    const int32_t wgs = (ne * s.Hkv + 7) / 8 * 8 * ntq;
     int32_t min_ntc = INT32_MAX;
-    for (int32_t i = 0; i < n; ++i)
+    for (int32_t i = 0; i < ne; ++i)
       min_ntc = std::min(min_ntc, (plan[i].pers_before + 63) / 64 + s.C / 64);
     const int32_t target = std::max(1, p->cus);
     if (wgs < target)
       a.nsplit = std::max(1, std::min({(target + wgs - 1) / wgs, min_ntc / 4, 16}));
     if (a.nsplit > 1) {
       if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
-                               (size_t)n * s.Hkv * ntq * a.nsplit * abk::kCompressRows * (s.D + 2) *
+                               (size_t)ne * s.Hkv * ntq * a.nsplit * abk::kCompressRows * (s.D + 2) *
                                    sizeof(float)))
         return st;
       a.part = p->part;
@@ -627,6 +702,7 @@ abk_status abk_free_block(abk_pool* p, int32_t n, const int32_t* seq_ids) {
 abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_len, int32_t text_tokens,
                                    const void* q, const void* k, const void* v, void* out, float* lse) {
   if (abk_status st = check_pool(p)) return st;
+  if (p->hs != 1) return set_err(ABK_ERR_UNSUPPORTED, "block-mask prefill with per-head quotas");
   if (p->host.check_layer(layer)) return set_err(ABK_ERR_INVALID_ARG, "bad layer");
   const abk::Shape& s = p->shape;
   if (prompt_len < 0 || text_tokens < 0) return set_err(ABK_ERR_INVALID_ARG, "negative length");
@@ -735,6 +811,7 @@ abk_status abk_prefill_prompt(abk_pool* p, int32_t seq_id, int32_t layer, const 
   if (abk_status st = check_pool(p)) return st;
   if (p->host.check_seq(seq_id)) return set_err(ABK_ERR_INVALID_ARG, "unknown sequence id");
   if (p->host.check_layer(layer)) return set_err(ABK_ERR_INVALID_ARG, "bad layer");
+  if (p->hs != 1) return set_err(ABK_ERR_UNSUPPORTED, "prompt prefill with per-head quotas");
   const abk::Shape& s = p->shape;
   if (!(s.dtype == 1 && s.D == 128 && s.Hq == 4 * s.Hkv))
     return set_err(ABK_ERR_UNSUPPORTED, "prompt prefill needs bf16, d = 128, four query heads per KV head");
@@ -863,6 +940,7 @@ abk_status abk_synth_fill(abk_pool* p, int32_t seq_id, int32_t generated, uint64
   a.G = generated;
   a.nb = q.nb;
   a.compress = s.compress;
+  a.hsplit = p->hs;
   ABK_HIP(abk::launch_fill(a, max_rows, p->stream));
   return ABK_OK;
 }

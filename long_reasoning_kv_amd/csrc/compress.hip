@@ -20,12 +20,14 @@ __global__ void __launch_bounds__(1024) pause_rope_scatter_kernel(CompressArgs a
   const int k = blockIdx.x, i = blockIdx.y;
   const int32_t* rec = a.desc + i * kCompRec;
   const int slot = rec[0], blk = rec[1], pers_before = rec[2], prompt = rec[3];
-  const int pages_off = rec[4], npages = rec[5], first_new = rec[6];
+  const int pages_off = rec[4], npages = rec[5], first_new = rec[6], quota = rec[7];
   const int pos = prompt + blk * P.C + bitrev_dev(k, a.log2Kp) * (P.C / a.Kp);
-  const T* kin = (const T*)a.kp + ((size_t)i * a.Kp + k) * P.Hkv * D;
-  const T* vin = (const T*)a.vp + ((size_t)i * a.Kp + k) * P.Hkv * D;
+  // the caller's sequence and first KV head of this entry
+  const int ir = i / a.hsplit, H0 = (i % a.hsplit) * P.Hkv, HkvR = P.Hkv * a.hsplit;
+  const T* kin = (const T*)a.kp + (((size_t)ir * a.Kp + k) * HkvR + H0) * D;
+  const T* vin = (const T*)a.vp + (((size_t)ir * a.Kp + k) * HkvR + H0) * D;
   const double2* rope = P.rope + (size_t)pos * (D / 2);
-  const bool keep = k < a.quota;
+  const bool keep = k < quota;
   int page = 0, srow = 0;
   if (keep) {
     const int row = pers_before + k;
@@ -54,13 +56,13 @@ __global__ void __launch_bounds__(1024) pause_rope_scatter_kernel(CompressArgs a
     int32_t* tab = ptab_of(P, slot, a.layer);
     const int first_idx = pers_before / P.pr;
     for (int j = first_new; j < npages; ++j) tab[first_idx + j] = a.desc[pages_off + j];
-    P.meta[(slot * P.L + a.layer) * 4 + 0] = pers_before + a.quota;
+    P.meta[(slot * P.L + a.layer) * 4 + 0] = pers_before + quota;
   }
 }
 
 // ---- a5: pause-token attention under the block mask (SIMT form) -------------------
 //
-// One wavefront per (sequence, pause j, query head). Keys: the sequence's
+// One wavefront per (entry, pause j, query head of the entry). Keys: the sequence's
 // resident rows at this layer (prompt, earlier code rows, the whole block)
 // followed by the rotated pause keys 0..j. 64 keys per step: one lane per key
 // scores it, the wavefront takes the step's max, and each lane accumulates
@@ -71,7 +73,9 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
   const DevPool& P = a.P;
   const int j = blockIdx.x, hq = blockIdx.y, i = blockIdx.z;
   const int lane = threadIdx.x;
-  const int hk = hq / a.G;
+  const int hk = hq / a.G;  // the entry's KV head
+  // the caller's sequence, and the caller's index of this query head
+  const int ir = i / a.hsplit, HQ = (i % a.hsplit) * P.Hkv * a.G + hq, HkvR = P.Hkv * a.hsplit;
   const int32_t* rec = a.desc + i * kCompRec;
   const int slot = rec[0], blk = rec[1], n_pers = rec[2], prompt = rec[3];
   const int n_ctx = n_pers + P.C;
@@ -83,7 +87,7 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
   __shared__ float ps[64];
   {
     const double2* rope = P.rope + (size_t)pos * (D / 2);
-    const T* qh = (const T*)a.qp + (((size_t)i * a.Kp + j) * a.Hq + hq) * D;
+    const T* qh = (const T*)a.qp + (((size_t)ir * a.Kp + j) * a.Hq + HQ) * D;
     const float sc = 1.4426950408889634f / sqrtf((float)D);
     for (int d = lane; d < D; d += 64)
       qs[d] = sc * round_to<T>(rope_elem<D>([&](int e) { return (double)to_f32(qh[e]); }, d, rope));
@@ -107,7 +111,7 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
     } else {
       const int kk = r - n_ctx;
       *kr = (const T*)a.kp_rot + (((size_t)i * P.Hkv + hk) * a.Kp + kk) * D;
-      *vr = (const T*)a.vp + (((size_t)i * a.Kp + kk) * P.Hkv + hk) * D;
+      *vr = (const T*)a.vp + (((size_t)ir * a.Kp + kk) * HkvR + (i % a.hsplit) * P.Hkv + hk) * D;
     }
   };
 
@@ -153,13 +157,13 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
       }
     }
   }
-  T* out = (T*)a.out + (((size_t)i * a.Kp + j) * a.Hq + hq) * D;
+  T* out = (T*)a.out + (((size_t)ir * a.Kp + j) * a.Hq + HQ) * D;
 #pragma unroll
   for (int t = 0; t < DPL; ++t) {
     const int d = lane + 64 * t;
     if (d < D) out[d] = from_f32<T>(o[t] / l);
   }
-  if (lane == 0) a.lse[((size_t)i * a.Kp + j) * a.Hq + hq] = (m + __log2f(l)) * 0.6931471805599453f;
+  if (lane == 0) a.lse[((size_t)ir * a.Kp + j) * a.Hq + HQ] = (m + __log2f(l)) * 0.6931471805599453f;
 }
 
 // ---- a5 on bf16 MFMA (d = 128, four query heads per KV head, 64-row pages) -------
@@ -208,6 +212,8 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
   const int pair = (jj / (ntq * ns)) * 8 + xcd, qt = (jj % (ntq * ns)) / ns, sp = jj % ns;
   if (pair >= npair) return;
   const int i = pair / P.Hkv, hk = pair % P.Hkv;
+  // the caller's sequence and KV head of this pair
+  const int ir = i / a.hsplit, H = (i % a.hsplit) * P.Hkv + hk, HkvR = P.Hkv * a.hsplit;
   const int32_t* rec = a.desc + i * kCompRec;
   const int slot = rec[0], blk = rec[1], n_pers = rec[2], prompt = rec[3];
   const int32_t* tab = ptab_of(P, slot, a.layer);
@@ -240,7 +246,7 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
     const int pz = r >> 2, hh = r & 3;
     qpause[nb] = rv ? pz : -1;
     const int pos = prompt + blk * P.C + bitrev_dev(pz, a.log2Kp) * (P.C / a.Kp);
-    const bf16_t* qrow = (const bf16_t*)a.qp + (((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh) * D;
+    const bf16_t* qrow = (const bf16_t*)a.qp + (((size_t)ir * a.Kp + pz) * a.Hq + H * G + hh) * D;
     query_operand(qrow, P.rope + (size_t)pos * (D / 2), g4, wa.qh[nb]);
   }
   wa.init();
@@ -270,8 +276,8 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
     } else {
       const int k0 = (t - ntc) * TK;
       ts.kb = (const char*)a.kp_rot + (((size_t)i * P.Hkv + hk) * a.Kp + k0) * RB;
-      ts.vb = (const char*)a.vp + (((size_t)i * a.Kp + k0) * P.Hkv + hk) * RB;
-      ts.vstride = P.Hkv * RB;
+      ts.vb = (const char*)a.vp + (((size_t)ir * a.Kp + k0) * HkvR + H) * RB;
+      ts.vstride = HkvR * RB;
       ts.nval = min(TK, a.Kp - k0);
     }
     return ts;
@@ -463,7 +469,7 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
     const int r = q0 + wave * 32 + nb * 16 + l16;
     if (r >= q0 + nq) continue;
     const int pz = r >> 2, hh = r & 3;
-    const size_t row = ((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh;
+    const size_t row = ((size_t)ir * a.Kp + pz) * a.Hq + H * G + hh;
     wa.store(nb, (bf16_t*)a.out + row * D, a.lse + row, lane);
   }
 }
@@ -480,6 +486,7 @@ __global__ void __launch_bounds__(256) compress_merge_kernel(CompressArgs a) {
   const int rg = blockIdx.x % NRG, pq = blockIdx.x / NRG;
   const int pair = pq / ntq, qt = pq % ntq;
   const int i = pair / a.P.Hkv, hk = pair % a.P.Hkv;
+  const int ir = i / a.hsplit, H = (i % a.hsplit) * a.P.Hkv + hk;  // the caller's sequence, KV head
   const int q0 = qt * QR, nq = min(QR, 4 * a.Kp - q0);
   const int rl = rg * 8 + (threadIdx.x >> 5);
   if (rl >= nq) return;
@@ -514,9 +521,9 @@ __global__ void __launch_bounds__(256) compress_merge_kernel(CompressArgs a) {
   }
   const int r = q0 + rl, pz = r >> 2, hh = r & 3;
   const float inv = 1.f / Ls;
-  bf16_t* dst = (bf16_t*)a.out + (((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh) * D + d;
+  bf16_t* dst = (bf16_t*)a.out + (((size_t)ir * a.Kp + pz) * a.Hq + H * G + hh) * D + d;
   *(uint2*)dst = make_uint2(pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv));
-  if (d == 0) a.lse[((size_t)i * a.Kp + pz) * a.Hq + hk * G + hh] = (M + __log2f(Ls)) * 0.6931471805599453f;
+  if (d == 0) a.lse[((size_t)ir * a.Kp + pz) * a.Hq + H * G + hh] = (M + __log2f(Ls)) * 0.6931471805599453f;
 }
 
 // ---- launcher ----------------------------------------------------------------------
@@ -532,7 +539,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   ABK_DISPATCH_TD(a.P.dtype, a.P.D, {
     hipLaunchKernelGGL((pause_rope_scatter_kernel<T, DD>), dim3(a.Kp, a.n), dim3(th), 0, s, a);
     if (!mfma)
-      hipLaunchKernelGGL((compress_attn_simt_kernel<T, DD>), dim3(a.Kp, a.Hq, a.n), dim3(64), 0,
+      hipLaunchKernelGGL((compress_attn_simt_kernel<T, DD>), dim3(a.Kp, a.P.Hkv * a.G, a.n), dim3(64), 0,
                          s, a);
   });
   if (mfma) {

@@ -78,33 +78,38 @@ struct FreeArgs {
   int32_t slot[kMaxBatch];
 };
 
-// Prompt write: rows 0..P-1 of (slot, layer); pages from desc.
+// Prompt write: rows 0..P-1 of (slot, layer); pages from desc. Row r's P.Hkv
+// heads are read at k + r * kv_stride (elements).
 struct PromptArgs {
   DevPool P;
   const void* k;
   const void* v;
   const int32_t* pages;  // ceil(P/pr) ids (device)
-  int32_t slot, layer, prompt_len;
+  int32_t slot, layer, prompt_len, kv_stride;
 };
 
 // Query rows (pause tokens x query heads of a KV head) per workgroup of the
 // MFMA compression kernel.
 constexpr int kCompressRows = 256;
 
-// One compression record per sequence in desc (ints):
-// {slot, block, pers_before, prompt_len, pages_off, npages, first_new, pad}
+// One compression record per entry in desc (ints): {slot, block, pers_before,
+// prompt_len, pages_off, npages, first_new, quota}. An entry is a sequence
+// (hsplit = 1) or one (sequence, KV head) of a pool with per-head quotas
+// (hsplit = the caller's KV heads, the pool's P.Hkv = 1): entry i is then the
+// caller's sequence i / hsplit, KV heads (i % hsplit) * P.Hkv + 0..P.Hkv-1.
+// The caller's q/k/v/out/lse keep their [sequence][pause][head][D] layouts.
 constexpr int kCompRec = 8;
 struct CompressArgs {
   DevPool P;
-  const void* qp;
-  const void* kp;
+  const void* qp;        // [n / hsplit][Kp][Hq][D]
+  const void* kp;        // [n / hsplit][Kp][P.Hkv * hsplit][D]
   const void* vp;
   void* out;
   float* lse;
-  void* kp_rot;          // workspace [n][Hkv][Kp][D]: rotated pause keys
+  void* kp_rot;          // workspace [n][P.Hkv][Kp][D]: rotated pause keys
   const int32_t* desc;   // n records, then page lists
-  float* part;           // nsplit > 1: [n][Hkv][query tiles][nsplit][kCompressRows][D + 2] partials
-  int32_t layer, n, Hq, G, Kp, quota, log2Kp;
+  float* part;           // nsplit > 1: [n][P.Hkv][query tiles][nsplit][kCompressRows][D + 2] partials
+  int32_t layer, n, hsplit, Hq, G, Kp, log2Kp;  // Hq: the caller's query heads
   int32_t nsplit;        // MFMA path: context splits per query tile (1 = none)
 };
 
@@ -136,13 +141,15 @@ struct BlockMaskArgs {
 
 // Fill: desc holds per layer {pers_off, npers_pages, open_off, nopen_pages}
 // then the page lists.
+// Rows are keyed for the generator by the model's (layer, KV head): pool
+// layer l with hsplit > 1 (per-head quotas) is layer l / hsplit, head l % hsplit.
 struct FillArgs {
   DevPool P;
   const int32_t* desc;
   const int32_t* quota;  // [L] device
   const int32_t* pause;  // [L] device
   uint64_t seed;
-  int32_t slot, prompt_len, G, nb, compress;
+  int32_t slot, prompt_len, G, nb, compress, hsplit;
 };
 
 // Gather rows [row0, row0+nrows) of (slot, layer) through the device page

@@ -91,6 +91,9 @@ Status HostPool::check_seq(int32_t id) const {
 }
 
 Status HostPool::check_layer(int32_t l) const { return (l < 0 || l >= s_.L) ? kInvalidArg : kOk; }
+Status HostPool::check_layers(int32_t l0, int32_t nl) const {
+  return (nl < 1 || l0 < 0 || (int64_t)l0 + nl > s_.L) ? kInvalidArg : kOk;
+}
 
 Status HostPool::check_batch(int32_t n, const int32_t* ids) {
   if (n < 0) return fail(kInvalidArg, "negative batch size");
@@ -140,101 +143,115 @@ Status HostPool::seq_release(int32_t id) {
   return kOk;
 }
 
-Status HostPool::write_prompt(int32_t id, int32_t l) {
+Status HostPool::write_prompt(int32_t id, int32_t l0, int32_t nl) {
   if (check_seq(id)) return fail(kInvalidArg, "unknown sequence id");
-  if (check_layer(l)) return fail(kInvalidArg, "bad layer");
-  LayerState& lay = seqs_[id].layers[l];
-  if (lay.G != 0) return fail(kBadState, "prompt rewritten after generation began");
-  lay.prompt_written = true;
+  if (check_layers(l0, nl)) return fail(kInvalidArg, "bad layer");
+  for (int32_t j = 0; j < nl; ++j)
+    if (seqs_[id].layers[l0 + j].G != 0) return fail(kBadState, "prompt rewritten after generation began");
+  for (int32_t j = 0; j < nl; ++j) seqs_[id].layers[l0 + j].prompt_written = true;
   return kOk;
 }
 
-Status HostPool::append(int32_t l, int32_t n, const int32_t* ids, std::vector<int32_t>* new_page) {
-  if (check_layer(l)) return fail(kInvalidArg, "bad layer");
+Status HostPool::append(int32_t l0, int32_t nl, int32_t n, const int32_t* ids, std::vector<int32_t>* new_page) {
+  if (check_layers(l0, nl)) return fail(kInvalidArg, "bad layer");
   if (Status st = check_batch(n, ids)) return st;
   int64_t need = 0;
   for (int32_t i = 0; i < n; ++i) {
     const SeqState& q = seqs_[ids[i]];
-    const LayerState& lay = q.layers[l];
-    if (!lay.prompt_written) return fail(kBadState, "prompt not written at this layer");
-    if (lay.G != gmin(q)) return fail(kBadState, "layer is ahead of the current token");
-    if ((int64_t)q.P + lay.G >= s_.max_position) return fail(kInvalidArg, "position reaches max_position");
-    if (s_.compress) {
-      int32_t op = lay.G - q.nb * s_.C;
-      if (op >= s_.C) return fail(kBadState, "open block is full: compress and free it first");
-      need += (op % s_.pr == 0);
-    } else {
-      need += (lay.pers_rows % s_.pr == 0);
+    const int32_t g0 = gmin(q);
+    for (int32_t j = 0; j < nl; ++j) {
+      const LayerState& lay = q.layers[l0 + j];
+      if (!lay.prompt_written) return fail(kBadState, "prompt not written at this layer");
+      if (lay.G != g0) return fail(kBadState, "layer is ahead of the current token");
+      if ((int64_t)q.P + lay.G >= s_.max_position) return fail(kInvalidArg, "position reaches max_position");
+      if (s_.compress) {
+        int32_t op = lay.G - q.nb * s_.C;
+        if (op >= s_.C) return fail(kBadState, "open block is full: compress and free it first");
+        need += (op % s_.pr == 0);
+      } else {
+        need += (lay.pers_rows % s_.pr == 0);
+      }
     }
   }
   if (need > pages_free()) return fail(kOutOfPages, "not enough free pages to append");
-  new_page->assign(n, -1);
+  new_page->assign((size_t)n * nl, -1);
   for (int32_t i = 0; i < n; ++i) {
     SeqState& q = seqs_[ids[i]];
-    LayerState& lay = q.layers[l];
-    if (s_.compress) {
-      if ((lay.G - q.nb * s_.C) % s_.pr == 0) {
-        (*new_page)[i] = take_page();
-        lay.open_pages.push_back((*new_page)[i]);
+    for (int32_t j = 0; j < nl; ++j) {
+      LayerState& lay = q.layers[l0 + j];
+      int32_t& np = (*new_page)[(size_t)i * nl + j];
+      if (s_.compress) {
+        if ((lay.G - q.nb * s_.C) % s_.pr == 0) {
+          np = take_page();
+          lay.open_pages.push_back(np);
+        }
+      } else {
+        if (lay.pers_rows % s_.pr == 0) {
+          np = take_page();
+          lay.pers_pages.push_back(np);
+        }
+        lay.pers_rows += 1;
       }
-    } else {
-      if (lay.pers_rows % s_.pr == 0) {
-        (*new_page)[i] = take_page();
-        lay.pers_pages.push_back((*new_page)[i]);
-      }
-      lay.pers_rows += 1;
+      lay.G += 1;
     }
-    lay.G += 1;
   }
   return kOk;
 }
 
-Status HostPool::check_decode(int32_t l, int32_t n, const int32_t* ids) {
-  if (check_layer(l)) return fail(kInvalidArg, "bad layer");
+Status HostPool::check_decode(int32_t l0, int32_t nl, int32_t n, const int32_t* ids) {
+  if (check_layers(l0, nl)) return fail(kInvalidArg, "bad layer");
   if (Status st = check_batch(n, ids)) return st;
   for (int32_t i = 0; i < n; ++i) {
     const SeqState& q = seqs_[ids[i]];
-    const LayerState& lay = q.layers[l];
-    if (!lay.prompt_written || lay.G == 0 || lay.G != gmax(q))
-      return fail(kBadState, "current token not appended at this layer");
-    if (lay.compressed) return fail(kBadState, "block compressed at this layer but not freed");
+    for (int32_t j = 0; j < nl; ++j) {
+      const LayerState& lay = q.layers[l0 + j];
+      if (!lay.prompt_written || lay.G == 0 || lay.G != gmax(q))
+        return fail(kBadState, "current token not appended at this layer");
+      if (lay.compressed) return fail(kBadState, "block compressed at this layer but not freed");
+    }
   }
   return kOk;
 }
 
-Status HostPool::compress(int32_t l, int32_t n, const int32_t* ids, std::vector<CompressPlan>* plan) {
-  if (check_layer(l)) return fail(kInvalidArg, "bad layer");
+Status HostPool::compress(int32_t l0, int32_t nl, int32_t n, const int32_t* ids, std::vector<CompressPlan>* plan) {
+  if (check_layers(l0, nl)) return fail(kInvalidArg, "bad layer");
   if (!s_.compress) return fail(kBadState, "compression is off (full-KV pool)");
   if (Status st = check_batch(n, ids)) return st;
-  const int32_t qn = s_.quota[l];
   int64_t need = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    const LayerState& lay = seqs_[ids[i]].layers[l];
-    if (open_rows(ids[i], l) != s_.C) return fail(kBadState, "open block is not complete");
-    if (lay.compressed) return fail(kBadState, "block already compressed at this layer");
-    need += cdiv(lay.pers_rows + qn, s_.pr) - cdiv(lay.pers_rows, s_.pr);
-  }
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t j = 0; j < nl; ++j) {
+      const int32_t l = l0 + j;
+      const LayerState& lay = seqs_[ids[i]].layers[l];
+      if (open_rows(ids[i], l) != s_.C) return fail(kBadState, "open block is not complete");
+      if (lay.compressed) return fail(kBadState, "block already compressed at this layer");
+      need += cdiv(lay.pers_rows + s_.quota[l], s_.pr) - cdiv(lay.pers_rows, s_.pr);
+    }
   if (need > pages_free()) return fail(kOutOfPages, "not enough free pages for code rows");
   plan->clear();
   for (int32_t i = 0; i < n; ++i) {
     SeqState& q = seqs_[ids[i]];
-    LayerState& lay = q.layers[l];
-    CompressPlan cp;
-    cp.slot = ids[i];
-    cp.block = q.nb;
-    cp.pers_before = lay.pers_rows;
-    cp.first_new = 0;
-    int32_t have = cdiv(lay.pers_rows, s_.pr);
-    int32_t want = cdiv(lay.pers_rows + qn, s_.pr);
-    for (int32_t k = have; k < want; ++k) lay.pers_pages.push_back(take_page());
-    if (qn > 0) {
-      int32_t first = lay.pers_rows / s_.pr, last = (lay.pers_rows + qn - 1) / s_.pr;
-      cp.pages.assign(lay.pers_pages.begin() + first, lay.pers_pages.begin() + last + 1);
-      cp.first_new = have - first;
+    for (int32_t j = 0; j < nl; ++j) {
+      const int32_t l = l0 + j, qn = s_.quota[l];
+      LayerState& lay = q.layers[l];
+      CompressPlan cp;
+      cp.slot = ids[i];
+      cp.layer = l;
+      cp.quota = qn;
+      cp.block = q.nb;
+      cp.pers_before = lay.pers_rows;
+      cp.first_new = 0;
+      int32_t have = cdiv(lay.pers_rows, s_.pr);
+      int32_t want = cdiv(lay.pers_rows + qn, s_.pr);
+      for (int32_t k = have; k < want; ++k) lay.pers_pages.push_back(take_page());
+      if (qn > 0) {
+        int32_t first = lay.pers_rows / s_.pr, last = (lay.pers_rows + qn - 1) / s_.pr;
+        cp.pages.assign(lay.pers_pages.begin() + first, lay.pers_pages.begin() + last + 1);
+        cp.first_new = have - first;
+      }
+      lay.pers_rows += qn;
+      lay.compressed = true;
+      plan->push_back(std::move(cp));
     }
-    lay.pers_rows += qn;
-    lay.compressed = true;
-    plan->push_back(std::move(cp));
   }
   return kOk;
 }

@@ -55,9 +55,9 @@ struct SeqState {
   std::vector<LayerState> layers;
 };
 
-// What one sequence of a compress call needs on the device.
+// What one (sequence, layer) of a compress call needs on the device.
 struct CompressPlan {
-  int32_t slot, block, pers_before;
+  int32_t slot, layer, quota, block, pers_before;
   std::vector<int32_t> pages;  // pages covering rows [pers_before, pers_before + quota)
   int32_t first_new;           // index in `pages` of the first newly taken page
 };
@@ -76,15 +76,20 @@ class HostPool {
   // Checks shared by the ABI.
   Status check_seq(int32_t id) const;
   Status check_layer(int32_t l) const;
+  Status check_layers(int32_t l0, int32_t nl) const;
   Status check_batch(int32_t n, const int32_t* ids);
 
+  // The calls below act on the layers [l0, l0 + nl) together (one layer, or
+  // the per-head layers of one model layer): every check passes for all of
+  // them before anything changes. Per-(sequence, layer) outputs are ordered
+  // sequence-major: entry i * nl + j is sequence ids[i] at layer l0 + j.
   Status seq_create(int32_t P, int32_t* id);
   Status seq_release(int32_t id);
-  Status write_prompt(int32_t id, int32_t l);
-  // new_page[i] = page taken for sequence i's row, or -1.
-  Status append(int32_t l, int32_t n, const int32_t* ids, std::vector<int32_t>* new_page);
-  Status check_decode(int32_t l, int32_t n, const int32_t* ids);
-  Status compress(int32_t l, int32_t n, const int32_t* ids, std::vector<CompressPlan>* plan);
+  Status write_prompt(int32_t id, int32_t l0, int32_t nl = 1);
+  // new_page[e] = page taken for entry e's row, or -1.
+  Status append(int32_t l0, int32_t nl, int32_t n, const int32_t* ids, std::vector<int32_t>* new_page);
+  Status check_decode(int32_t l0, int32_t nl, int32_t n, const int32_t* ids);
+  Status compress(int32_t l0, int32_t nl, int32_t n, const int32_t* ids, std::vector<CompressPlan>* plan);
   Status free_block(int32_t n, const int32_t* ids);
   Status fill(int32_t id, int32_t G);
 

@@ -83,8 +83,8 @@ __global__ void __launch_bounds__(1024) prompt_kernel(PromptArgs a) {
   }
   if (r >= a.prompt_len) return;
   const int page = a.pages[r / P.pr], srow = r % P.pr;
-  const T* k = (const T*)a.k + (size_t)r * P.Hkv * D;
-  const T* v = (const T*)a.v + (size_t)r * P.Hkv * D;
+  const T* k = (const T*)a.k + (size_t)r * a.kv_stride;
+  const T* v = (const T*)a.v + (size_t)r * a.kv_stride;
   const double2* rope = P.rope + (size_t)r * (D / 2);
   for (int t = threadIdx.x; t < P.Hkv * (D / 2); t += blockDim.x) {
     const int hh = t / (D / 2), j = t % (D / 2);
@@ -145,16 +145,18 @@ __global__ void __launch_bounds__(512) fill_kernel(FillArgs a) {
     page = a.desc[open_off + (r - pers_rows) / P.pr];
     srow = (r - pers_rows) % P.pr;
   }
-  // generate the raw row (stored type) into LDS, then rotate the key
+  // generate the raw row (stored type) into LDS, then rotate the key; keyed by
+  // the model's layer and KV head
   __shared__ float kraw[1024 * 2];  // up to Hkv*D = 1024 elements
   const int n = P.Hkv * D;
+  const int ml = l / a.hsplit, mh0 = (l % a.hsplit) * P.Hkv;
   for (int t = threadIdx.x; t < n / 2; t += blockDim.x) {
     const int hh = t / (D / 2), e = t % (D / 2);
     double z0, z1;
-    synth_pair(synth_row_key(a.seed, l, kind, ia, ib, 0, hh), e, &z0, &z1);
+    synth_pair(synth_row_key(a.seed, ml, kind, ia, ib, 0, mh0 + hh), e, &z0, &z1);
     kraw[hh * D + 2 * e] = to_f32(from_f32<T>((float)z0));
     kraw[hh * D + 2 * e + 1] = to_f32(from_f32<T>((float)z1));
-    synth_pair(synth_row_key(a.seed, l, kind, ia, ib, 1, hh), e, &z0, &z1);
+    synth_pair(synth_row_key(a.seed, ml, kind, ia, ib, 1, mh0 + hh), e, &z0, &z1);
     const size_t o = (((size_t)page * P.Hkv + hh) * P.pr + srow) * D;
     ((T*)P.vpool)[o + 2 * e] = from_f32<T>((float)z0);
     ((T*)P.vpool)[o + 2 * e + 1] = from_f32<T>((float)z1);

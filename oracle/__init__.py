@@ -16,6 +16,8 @@ states them:
 * compression of block b: every pause query PAUSE(b, j) with its own visible
   key set (prompt, retained code rows, the whole block, pause keys k <= j),
   then the code rows k < quota are what the layer keeps;
+* per-head quotas: the same two steps for each KV head with its own quota,
+  its query heads seeing that head only;
 * block-mask prefill (training-forward attention): every token of a sequence
   laid out in training order (prompt, then each block's text followed by its
   pause tokens once the block is complete) as a query with its own visible set.
@@ -232,6 +234,46 @@ def compress(L: LayerView, G: int, nb: int, block: int, q_raw: np.ndarray, fetch
     code_k = rope_rows(fetch(ckind, cb, ck, "k"), cpos, base, dtype)
     code_v = fetch(ckind, cb, ck, "v")
     return out, lse, (ckind, cb, ck, cpos, code_k, code_v)
+
+
+def _head_fetch(fetch, h: int):
+    """fetch restricted to KV head h: rows [n, 1, d]."""
+    return lambda kind, a, b, which: fetch(kind, a, b, which)[:, h:h + 1]
+
+
+def decode_heads(Ls, G: int, nb: int, q_raw: np.ndarray, fetch, dtype: int, base: float):
+    """Decode with a quota per (layer, KV head) (figure captions, Fig. 7: one
+    head's quota halved or doubled; AI Radio transcript: a per-head schedule).
+    Ls[h] is KV head h's view of the layer, with its own quota; the query heads
+    of group h see KV head h only, with the visible set that quota gives.
+    q_raw [Hq, d]. Returns (out [Hq, d], lse [Hq], keys per KV head)."""
+    Hkv = len(Ls)
+    g = q_raw.shape[0] // Hkv
+    outs, lses, keys = [], [], []
+    for h in range(Hkv):
+        o, l, k = decode(Ls[h], G, nb, q_raw[h * g:(h + 1) * g], _head_fetch(fetch, h), dtype, base)
+        outs.append(o)
+        lses.append(l)
+        keys.append(k)
+    return np.concatenate(outs), np.concatenate(lses), keys
+
+
+def compress_heads(Ls, G: int, nb: int, block: int, q_raw: np.ndarray, fetch, dtype: int, base: float,
+                   queries=None):
+    """Compression of ``block`` with a quota per (layer, KV head): every KV head
+    h attends under its own view Ls[h] and keeps its own prefix k < quota.
+    q_raw [Kp, Hq, d]. Returns (out [Kp, Hq, d], lse [Kp, Hq], code per KV
+    head)."""
+    Hkv = len(Ls)
+    g = q_raw.shape[1] // Hkv
+    outs, lses, codes = [], [], []
+    for h in range(Hkv):
+        o, l, c = compress(Ls[h], G, nb, block, q_raw[:, h * g:(h + 1) * g], _head_fetch(fetch, h), dtype,
+                           base, queries)
+        outs.append(o)
+        lses.append(l)
+        codes.append(c)
+    return np.concatenate(outs, axis=1), np.concatenate(lses, axis=1), codes
 
 
 def training_tokens(L: LayerView, G: int):

@@ -205,6 +205,77 @@ class PageModel:
             lay.pers_ids += [(PAUSE, s.nb, k) for k in range(q)]
             lay.compressed = True
 
+    # -- per-head quotas: the layers of one model layer's KV heads together ----
+    # With a quota per (layer, KV head) (figure captions, Fig. 7), the model's
+    # layer l is this model's layers l*hs .. l*hs + hs - 1 (one per KV head).
+    # A call checks every (sequence, head) first; then allocation runs
+    # sequence by sequence, heads in ascending order within a sequence.
+    def append_heads(self, l: int, hs: int, sids):
+        lays = [l * hs + j for j in range(hs)]
+        for lv in lays:
+            self._check_layer(lv)
+        self._check_ids(sids)
+        need = 0
+        for sid in sids:
+            s = self.seqs[sid]
+            g0 = min(x.G for x in s.layers)
+            for lv in lays:
+                lay = s.layers[lv]
+                if not lay.prompt_written:
+                    raise PoolError(BAD_STATE, "prompt not written")
+                if lay.G != g0:
+                    raise PoolError(BAD_STATE, "layer ahead of the current token")
+                if self.compress_on:
+                    op = self.open_rows(sid, lv)
+                    if op >= self.C:
+                        raise PoolError(BAD_STATE, "open block full: compress and free it first")
+                    need += op % self.pr == 0
+                else:
+                    need += len(lay.pers_ids) % self.pr == 0
+        self._need(need)
+        for sid in sids:
+            s = self.seqs[sid]
+            for lv in lays:
+                lay = s.layers[lv]
+                if self.compress_on:
+                    if self.open_rows(sid, lv) % self.pr == 0:
+                        lay.open_pages += self._alloc(1)
+                else:
+                    if len(lay.pers_ids) % self.pr == 0:
+                        lay.pers_pages += self._alloc(1)
+                    lay.pers_ids.append((TEXT, lay.G, 0))
+                lay.G += 1
+
+    def check_decode_heads(self, l: int, hs: int, sids):
+        for j in range(hs):
+            self.check_decode(l * hs + j, sids)
+
+    def compress_heads(self, l: int, hs: int, sids):
+        lays = [l * hs + j for j in range(hs)]
+        for lv in lays:
+            self._check_layer(lv)
+        self._check_ids(sids)
+        if not self.compress_on:
+            raise PoolError(BAD_STATE, "compression is off")
+        need = 0
+        for sid in sids:
+            for lv in lays:
+                lay = self.seqs[sid].layers[lv]
+                if self.open_rows(sid, lv) != self.C or lay.compressed:
+                    raise PoolError(BAD_STATE, "block not complete or already compressed")
+                r = len(lay.pers_ids)
+                need += _cdiv(r + self.quota[lv], self.pr) - _cdiv(r, self.pr)
+        self._need(need)
+        for sid in sids:
+            s = self.seqs[sid]
+            for lv in lays:
+                lay = s.layers[lv]
+                q = self.quota[lv]
+                r = len(lay.pers_ids)
+                lay.pers_pages += self._alloc(_cdiv(r + q, self.pr) - _cdiv(r, self.pr))
+                lay.pers_ids += [(PAUSE, s.nb, k) for k in range(q)]
+                lay.compressed = True
+
     def free_block(self, sids):
         self._check_ids(sids)
         if not self.compress_on:

@@ -33,9 +33,10 @@ class Run:
 
     def __init__(self, *, L, Hq, Hkv, D, C, Kp, quota, pause=None, pr, dtype="bf16",
                  compress=True, max_seqs=64, pool_bytes=None, max_position=40960,
-                 split_rows=0, base=1e6, seed=0):
+                 split_rows=0, base=1e6, seed=0, head_quota=None):
         self.L, self.Hq, self.Hkv, self.D, self.C = L, Hq, Hkv, D, C
         self.quota = list(quota)
+        self.head_quota = [list(r) for r in head_quota] if head_quota is not None else None
         self.pause = list(pause) if pause is not None else [Kp] * L
         self.pr, self.dtype, self.compress, self.base = pr, dtype, compress, base
         esize = 4 if dtype == "f32" else 2
@@ -45,8 +46,8 @@ class Run:
                              block_tokens=C, num_pause=Kp, layer_quota=quota, layer_pause=pause,
                              page_rows=pr, max_seqs=max_seqs, pool_bytes=pool_bytes,
                              max_position=max_position, dtype=dtype, rope_base=base,
-                             compress=compress, decode_split_rows=split_rows)
-        self.page_bytes = Hkv * pr * D * esize
+                             compress=compress, decode_split_rows=split_rows, head_quota=head_quota)
+        self.page_bytes = (1 if head_quota is not None else Hkv) * pr * D * esize
         self.seed = seed
         self.seeds = {}   # sid -> synth seed
         self.P = {}       # sid -> prompt length
@@ -71,6 +72,11 @@ class Run:
 
     def view(self, sid, layer) -> LayerView:
         return LayerView(self.P[sid], self.C, self.pause[layer], self.quota[layer], self.compress)
+
+    def views(self, sid, layer):
+        """Per-KV-head views of a pool with per-head quotas."""
+        return [LayerView(self.P[sid], self.C, self.pause[layer], q, self.compress)
+                for q in self.head_quota[layer]]
 
     # -- histories through the ABI --------------------------------------------
     def new_seq(self, P, idx):
@@ -180,6 +186,10 @@ class Run:
             self.nb[s] += 1
 
     def oracle_decode(self, sid, layer, q):
+        if self.head_quota is not None:
+            out, lse, keys = oracle.decode_heads(self.views(sid, layer), self.G[sid], self.nb[sid], q,
+                                                 self.fetch(sid, layer), ORC_DT[self.dtype], self.base)
+            return out, lse, keys
         return oracle.decode(self.view(sid, layer), self.G[sid], self.nb[sid], q, self.fetch(sid, layer),
                              ORC_DT[self.dtype], self.base)
 
@@ -188,6 +198,9 @@ class Run:
         b = self.nb[sid]
         Kp = self.pause[layer]
         q = self.rows(sid, layer, PAUSE, np.full(Kp, b), np.arange(Kp), synth.WHICH_Q)
+        if self.head_quota is not None:
+            return oracle.compress_heads(self.views(sid, layer), self.G[sid], b, b, q, self.fetch(sid, layer),
+                                         ORC_DT[self.dtype], self.base)
         return oracle.compress(self.view(sid, layer), self.G[sid], b, b, q, self.fetch(sid, layer),
                                ORC_DT[self.dtype], self.base)
 

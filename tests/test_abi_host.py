@@ -223,3 +223,73 @@ def test_prefill_prompt_checks_before_writing():
         bf.prefill_prompt(s, 0, None, None, None, None, None)
     assert e.value.status == abk.BAD_STATE                 # generation has started
     bf.close()
+
+
+# ---- per-head quotas (figure captions, Fig. 7: a quota per (layer, KV head)) ----
+
+HEAD_Q = [[4, 1], [2, 0], [1, 4]]  # [layer][KV head]
+
+
+def test_per_head_host_pool_matches_page_model():
+    # the pool keeps one row set per (layer, KV head): the page model with one
+    # layer per pair, a model layer's heads handled together in each call
+    hs = 2
+    pool = _pool(head_quota=HEAD_Q, _pages=400)
+    pm = PageModel(num_pages=400 * 2, page_rows=4, num_layers=3 * hs, C=8,
+                   quotas=[q for row in HEAD_Q for q in row], pauses=[4] * 6, max_seqs=4)
+    assert pool.stats()["pages_free"] == 800  # pages of one KV head: twice as many
+    sids = [_both(pool, pm, lambda P=P: pool.seq_create(P), lambda P=P: pm.seq_create(P))
+            for P in (2, 5, 0)]
+    for s in sids:
+        for l in range(3):
+            _both(pool, pm, lambda s=s, l=l: pool.write_prompt(s, l, None, None),
+                  lambda s=s, l=l: [pm.write_prompt(s, l * hs + j) for j in range(hs)] and None)
+    for t in range(27):
+        for l in range(3):
+            _both(pool, pm, lambda l=l: pool.append_kv(l, sids, None, None),
+                  lambda l=l: pm.append_heads(l, hs, sids))
+            _both(pool, pm, lambda l=l: pool.decode_attention(l, sids, None, None, None),
+                  lambda l=l: pm.check_decode_heads(l, hs, sids))
+        done = [s for s in sids if pm.open_rows(s, 0) == 8]
+        if done:
+            _both(pool, pm, lambda: pool.free_block(done), lambda: pm.free_block(done))
+            for l in range(3):
+                _both(pool, pm, lambda l=l: pool.compress_block(l, done, None, None, None, None, None),
+                      lambda l=l: pm.compress_heads(l, hs, done))
+            _both(pool, pm, lambda: pool.free_block(done), lambda: pm.free_block(done))
+        for s in sids:
+            for lv in range(3 * hs):
+                info = pool.seq_query(s, lv)
+                assert info["resident_rows"] == pm.resident_rows(s, lv), (s, lv)
+                pages, pos = pool.export_layout(s, lv)
+                mp, mpos, _ = pm.layout(s, lv)
+                assert pages == mp and pos == mpos, (s, lv)
+    # every (layer, head) kept its own quota per finished block
+    s = sids[0]
+    for l in range(3):
+        for h in range(hs):
+            info = pool.seq_query(s, l * hs + h)
+            assert info["resident_rows"] == 2 + info["blocks_done"] * HEAD_Q[l][h] + info["open_rows"]
+    assert pool.stats()["pages_free"] == pm.pages_free()
+    pool.close()
+
+
+def test_per_head_config_and_call_checks():
+    with pytest.raises(abk.AbkError) as e:
+        _pool(head_quota=[[4, 8], [2, 0], [1, 4]])  # above the pause count
+    assert e.value.status == 1
+    with pytest.raises(ValueError):
+        _pool(head_quota=[[4, 1], [2, 0]])  # not L x Hkv
+    pool = _pool(head_quota=HEAD_Q)
+    s = pool.seq_create(3)
+    with pytest.raises(abk.AbkError) as e:
+        pool.append_kv(3, [s], None, None)  # model layers are 0..2
+    assert e.value.status == 1
+    # the pool's (layer, head) pairs are 0..5 for inspection
+    assert pool.seq_query(s, 5)["prompt_len"] == 3
+    with pytest.raises(abk.AbkError):
+        pool.seq_query(s, 6)
+    with pytest.raises(abk.AbkError) as e:
+        pool.blockmask_attention(0, 4, 8, None, None, None, None, None)
+    assert e.value.status == 5
+    pool.close()

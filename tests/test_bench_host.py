@@ -43,3 +43,16 @@ def test_serving_mix_admission_fits_the_pool():
     for comp in (True, False):
         P, G, used = bench.serving_mix_admit(quotas, 64, comp, pages)
         assert len(P) > 0 and used <= pages
+
+
+def test_head_quotas_keep_layer_totals():
+    """The per-head decode workload keeps each layer's rows: its 8 head quotas
+    sum to 8 x the layer quota, are powers of two at most the pause count (256),
+    and vary within every layer below 256."""
+    quotas = bench.layer_quotas(2)
+    hq = bench.head_quotas(quotas, 2)
+    assert len(hq) == bench.L
+    for q, row in zip(quotas, hq):
+        assert len(row) == bench.HKV and sum(row) == bench.HKV * int(q)
+        assert all(x > 0 and (x & (x - 1)) == 0 and x <= 256 for x in row)
+        assert (len(set(row)) > 1) == (int(q) < 256)

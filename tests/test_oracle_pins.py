@@ -439,3 +439,73 @@ def test_blockmask_prefill_rows_equal_decode_and_compression():
             continue
         np.testing.assert_allclose(out[r], o2, atol=1e-12)
         np.testing.assert_allclose(lse[r], l2, atol=1e-12)
+
+
+# ---- per-head quotas (figure captions, Fig. 7: a quota per (layer, KV head)) ----
+
+def _keyed_rows(Hkv, d, seed):
+    data = {}
+    rng = np.random.default_rng(seed)
+
+    def row(t, which):
+        key = (t, which)
+        if key not in data:
+            data[key] = rng.standard_normal((Hkv, d))
+        return data[key]
+
+    def fetch(kind, a, b, which):
+        return np.stack([row((int(x), int(y), int(z)), which) for x, y, z in zip(kind, a, b)])
+
+    return row, fetch
+
+
+@pytest.mark.parametrize("quotas", [(4, 1), (2, 0), (4, 4)])
+def test_decode_per_head_equals_attention_over_each_heads_rows(quotas):
+    # KV head h keeps the pause prefix k < quotas[h] of every finished block;
+    # its two query heads attend over exactly the prompt, those code rows and
+    # the open block, and see no other KV head
+    P, C, K, g, d, base = 3, 8, 4, 2, 16, 1e6
+    Hkv = len(quotas)
+    G = 29
+    nb = (G - 1) // C
+    row, fetch = _keyed_rows(Hkv, d, 11)
+    qraw = RNG.standard_normal((g * Hkv, d))
+    Ls = [LayerView(P=P, C=C, Kp=K, quota=q) for q in quotas]
+    out, lse, keys = oracle.decode_heads(Ls, G, nb, qraw, fetch, dtype=-1, base=base)
+    for h, q in enumerate(quotas):
+        res = [(PROMPT, i, 0) for i in range(P)]
+        res += [(PAUSE, bb, k) for bb in range(nb) for k in range(q)]
+        res += [(TEXT, j, 0) for j in range(nb * C, G)]
+        kk = np.stack([row(t, "k")[h:h + 1] for t in res])
+        vv = np.stack([row(t, "v")[h:h + 1] for t in res])
+        pos = np.array([P + bb * C + [0, 4, 2, 6][k] for bb in range(nb) for k in range(q)], dtype=np.int64)
+        pos = np.concatenate([np.arange(P), pos, P + np.arange(nb * C, G)])
+        kr = oracle.rope_rows(kk, pos, base)
+        qr = oracle.rope_rows(qraw[None, h * g:(h + 1) * g], np.array([P + G - 1]), base)[0]
+        o2, l2 = oracle.attention(qr, kr, vv)
+        np.testing.assert_allclose(out[h * g:(h + 1) * g], o2, atol=1e-14)
+        np.testing.assert_allclose(lse[h * g:(h + 1) * g], l2, atol=1e-14)
+        assert len(keys[h][0]) == P + nb * q + (G - nb * C)
+
+
+def test_per_head_with_equal_quotas_equals_per_layer():
+    # one quota for every head is the per-layer case: decode and compression
+    # of all heads at once (the attention routine's GQA path) give the same
+    P, C, K, q, g, Hkv, d = 5, 8, 4, 2, 2, 3, 16
+    G = 24
+    nb = 2
+    _, fetch = _keyed_rows(Hkv, d, 12)
+    L = LayerView(P=P, C=C, Kp=K, quota=q)
+    qd = RNG.standard_normal((g * Hkv, d))
+    o1, l1, _ = oracle.decode(L, G + 1, nb, qd, fetch, oracle.F32, 1e6)
+    o2, l2, _ = oracle.decode_heads([L] * Hkv, G + 1, nb, qd, fetch, oracle.F32, 1e6)
+    np.testing.assert_allclose(o2, o1, atol=1e-14)
+    np.testing.assert_allclose(l2, l1, atol=1e-14)
+    qc = RNG.standard_normal((K, g * Hkv, d))
+    c1 = oracle.compress(L, G, nb, nb, qc, fetch, oracle.F32, 1e6)
+    c2 = oracle.compress_heads([L] * Hkv, G, nb, nb, qc, fetch, oracle.F32, 1e6)
+    np.testing.assert_allclose(c2[0], c1[0], atol=1e-14)
+    np.testing.assert_allclose(c2[1], c1[1], atol=1e-14)
+    for h in range(Hkv):
+        np.testing.assert_array_equal(c2[2][h][5], c1[2][5][:, h:h + 1])
+        np.testing.assert_array_equal(c2[2][h][4], c1[2][4][:, h:h + 1])
