@@ -638,12 +638,13 @@ def run_prefill(args, torch, abk):
     }
 
 
-def serving_mix_admit(quotas, steps: int, compress: bool, pool_pages: int, seed: int = 4):
+def serving_mix_admit(quotas, steps: int, compress: bool, pool_pages: int, seed: int = 4, by_quota=None):
     """Admit sequences (P ~ U[128, 512], G ~ U[1024, 32768], seeded) while the
     pool holds each one's largest footprint over the run: its persistent rows
     after the blocks it completes during the run, plus a whole open block per
     layer (compressed before its pages are freed), or in full-KV mode all its
-    rows at the end. Both modes draw the same sequence stream."""
+    rows at the end. Both modes draw the same sequence stream. by_quota (a
+    dict, optional) receives the admitted footprint's pages per quota value."""
     rng = np.random.default_rng(seed)
     Ps, Gs, used = [], [], 0
     while True:
@@ -659,7 +660,20 @@ def serving_mix_admit(quotas, steps: int, compress: bool, pool_pages: int, seed:
         Ps.append(P)
         Gs.append(G)
         used += need
+        if by_quota is not None and compress:
+            for q in quotas:
+                by_quota[int(q)] = by_quota.get(int(q), 0) + -(-(P + ((G + steps - 1) // C) * int(q)) // PR) + C // PR
     return np.array(Ps, dtype=np.int64), np.array(Gs, dtype=np.int64), used
+
+
+def budget_pool_split(by_quota: dict, pool_pages: int):
+    """Pages of one pool per budget level (quota value, ascending): each level's
+    admitted footprint plus the free rest shared in proportion to it."""
+    qs = sorted(by_quota)
+    used = sum(by_quota.values())
+    rest = pool_pages - used
+    pages = [by_quota[q] + rest * by_quota[q] // used for q in qs]
+    return qs, pages
 
 
 def run_serving_mix(args, torch, abk, compress: bool):
@@ -667,19 +681,22 @@ def run_serving_mix(args, torch, abk, compress: bool):
     as fit, then `steps` decode steps of all of them (one fused append + decode
     call per layer); a sequence whose block completes is compressed at every
     layer and freed inside the step. Full-KV mode runs the same kernels with
-    compression off."""
+    compression off. With args.budget_pools (AbridgeKV mode), the pages form one
+    pool per budget level, sized by the admitted sequences' needs."""
     steps, warm = args.serving_mix_steps, 2
     quotas = layer_quotas(2)
     Kp = int(quotas.max())
     page_bytes = HKV * PR * D * 2
     pool_bytes = 200 << 30
     pool_pages = pool_bytes // (2 * page_bytes)
-    P, G, used = serving_mix_admit(quotas, steps + warm, compress, pool_pages)
+    by_quota = {}
+    P, G, used = serving_mix_admit(quotas, steps + warm, compress, pool_pages, by_quota=by_quota)
     B = len(P)
+    split = budget_pool_split(by_quota, pool_pages) if (compress and args.budget_pools) else None
     pool = abk.Pool(num_layers=L, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_tokens=C,
                     num_pause=Kp, layer_quota=quotas.tolist(), page_rows=PR, max_seqs=B,
                     pool_bytes=pool_bytes, max_position=33792, dtype="bf16", rope_base=1e6,
-                    compress=compress)
+                    compress=compress, budget_pool_pages=split[1] if split else None)
     sids = []
     for i in range(B):
         s = pool.seq_create(int(P[i]))
@@ -724,9 +741,14 @@ def run_serving_mix(args, torch, abk, compress: bool):
         trace["seq0_generated"].append(int(g[0]))
         if t % 32 == 0:
             by = {q: 0 for q in trace["pages_by_quota"]}
-            for s in sids:
-                for l in range(L):
-                    by[str(int(quotas[l]))] += pool.seq_query(s, l)["n_pages"]
+            if split:
+                # each budget pool's own count
+                for x in pool.budget_stats():
+                    by[str(x["quota"])] = x["pages_used"]
+            else:
+                for s in sids:
+                    for l in range(L):
+                        by[str(int(quotas[l]))] += pool.seq_query(s, l)["n_pages"]
             trace["budget_steps"].append(t)
             for q in by:
                 trace["pages_by_quota"][q].append(by[q])
@@ -763,10 +785,15 @@ def run_serving_mix(args, torch, abk, compress: bool):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     st = pool.stats()
+    budget = pool.budget_stats() if split else None
     pool.close()
     del q_in, k_in, v_in
     torch.cuda.empty_cache()
+    if budget:
+        for x, n in zip(budget, split[1]):
+            x["pages"] = n
     return {"sequences_resident": B, "tokens_per_s": B * steps / dt, "ms_per_step": 1e3 * dt / steps,
+            "budget_pools": budget,
             "steps": steps, "compressions_in_timed_steps": stats["compressions"],
             "decode_kv_gb_per_step": stats["rows"] * row_bytes / steps / 1e9,
             "kv_gbps_incl_compression": stats["rows"] * row_bytes / dt / 1e9,
@@ -873,6 +900,8 @@ def main():
     ap.add_argument("--serving-mix", action="store_true",
                     help="only run the saturated serving mix (200 GiB pool, AbridgeKV and full KV)")
     ap.add_argument("--serving-mix-steps", type=int, default=512)
+    ap.add_argument("--budget-pools", action="store_true",
+                    help="serving mix: one page pool per budget level (AbridgeKV mode)")
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 runs under DIR (no GPU needed)")
     args = ap.parse_args()

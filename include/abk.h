@@ -93,6 +93,17 @@ typedef struct {
                                 calls keep their model-layer arguments and tensor
                                 layouts. abk_blockmask_attention and abk_prefill_prompt
                                 return UNSUPPORTED on such a pool. */
+  const int64_t* budget_pool_pages; /* optional: a separate page pool per budget level (AI
+                                Radio transcript: the serving engine keeps one page pool
+                                per budget level). A level is one distinct quota value
+                                (of layer_quota, or of head_quota when given), in
+                                ascending order; entry k is the page count of level k's
+                                pool, which holds page ids [sum of the earlier counts,
+                                + entry k). Every (sequence, layer) takes its pages from
+                                its level's pool only, lowest free id first, and a call
+                                fails with OUT_OF_PAGES when any level it needs is short.
+                                The counts must sum to at most the pages pool_bytes gives
+                                (the rest stay unused). NULL = one pool for all levels. */
 } abk_pool_config;
 
 typedef struct {
@@ -224,6 +235,12 @@ abk_status abk_prefill_prompt(abk_pool* p, int32_t seq_id, int32_t layer, const 
                               const void* v, void* out, float* lse);
 
 /* Pool-wide counters. resident_bytes = K+V bytes of resident rows. */
+/* Pages of budget level `level` (0 .. levels-1; with no separate pools, level
+ * 0 is the one pool and *quota is -1): its quota value, pages in use and
+ * pages free. *levels (optional) receives the number of levels. Errors:
+ * INVALID_ARG (level out of range). */
+abk_status abk_budget_pool_stats(const abk_pool* p, int32_t level, int32_t* levels, int32_t* quota,
+                                 int64_t* pages_used, int64_t* pages_free);
 abk_status abk_pool_stats(const abk_pool* p, int64_t* pages_used, int64_t* pages_free,
                           int64_t* resident_bytes);
 

@@ -22,7 +22,8 @@ SYMBOLS = [
     "abk_write_prompt", "abk_append_kv", "abk_decode_attention", "abk_append_decode",
     "abk_compress_block",
     "abk_free_block", "abk_seq_query", "abk_export_layout", "abk_read_rows",
-    "abk_pool_stats", "abk_synth_fill", "abk_blockmask_attention", "abk_prefill_prompt",
+    "abk_pool_stats", "abk_budget_pool_stats", "abk_synth_fill", "abk_blockmask_attention",
+    "abk_prefill_prompt",
     "abk_last_error",
 ]
 
@@ -46,6 +47,7 @@ class PoolConfig(ctypes.Structure):
         ("compress", ctypes.c_int32), ("host_only", ctypes.c_int32),
         ("decode_split_rows", ctypes.c_int32),
         ("head_quota", ctypes.POINTER(ctypes.c_int32)),
+        ("budget_pool_pages", ctypes.POINTER(ctypes.c_int64)),
     ]
 
 
@@ -114,10 +116,12 @@ class Pool:
     def __init__(self, *, num_layers, num_q_heads, num_kv_heads, head_dim, block_tokens,
                  num_pause, layer_quota, layer_pause=None, page_rows=64, max_seqs=64,
                  pool_bytes=1 << 30, max_position=40960, dtype="bf16", rope_base=1e6,
-                 compress=True, host_only=False, decode_split_rows=0, head_quota=None, stream=None):
+                 compress=True, host_only=False, decode_split_rows=0, head_quota=None,
+                 budget_pool_pages=None, stream=None):
         """head_quota: optional per-(layer, KV head) quotas, [L][Hkv] nested or
         flat; then per-(sequence, layer) queries and layouts name the pair
-        (l, h) as layer l * Hkv + h."""
+        (l, h) as layer l * Hkv + h. budget_pool_pages: optional page counts
+        of one pool per distinct quota value (ascending)."""
         self.L = num_layers
         self.Hq, self.Hkv, self.D = num_q_heads, num_kv_heads, head_dim
         self.C, self.page_rows = block_tokens, page_rows
@@ -125,6 +129,8 @@ class Pool:
         self.quota = list(layer_quota)
         self.head_quota = None
         self._head_quota = None
+        self._budget = (ctypes.c_int64 * len(budget_pool_pages))(*budget_pool_pages) \
+            if budget_pool_pages is not None else None
         if head_quota is not None:
             flat = [int(x) for row in head_quota for x in (row if hasattr(row, "__iter__") else [row])]
             if len(flat) != num_layers * num_kv_heads:
@@ -141,7 +147,8 @@ class Pool:
             page_rows, max_seqs, pool_bytes, max_position,
             {"f32": F32, "bf16": BF16}[dtype], rope_base, int(compress), int(host_only),
             decode_split_rows,
-            ctypes.cast(self._head_quota, ctypes.POINTER(ctypes.c_int32)) if self._head_quota else None)
+            ctypes.cast(self._head_quota, ctypes.POINTER(ctypes.c_int32)) if self._head_quota else None,
+            ctypes.cast(self._budget, ctypes.POINTER(ctypes.c_int64)) if self._budget else None)
         if stream is None and not host_only:
             import torch
             stream = torch.cuda.current_stream().cuda_stream
@@ -209,6 +216,19 @@ class Pool:
 
     def read_rows(self, sid, layer, row0, nrows, k_out, v_out):
         _check(lib().abk_read_rows(self._h, sid, layer, row0, nrows, _ptr(k_out), _ptr(v_out)))
+
+    def budget_stats(self) -> list:
+        """Per budget level: {quota, pages_used, pages_free} (one entry with
+        quota -1 when the pool is shared)."""
+        out, k, n = [], 0, 1
+        while k < n:
+            lv, q, u, f = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+            _check(lib().abk_budget_pool_stats(self._h, k, ctypes.byref(lv), ctypes.byref(q), ctypes.byref(u),
+                                               ctypes.byref(f)))
+            n = lv.value
+            out.append({"quota": q.value, "pages_used": u.value, "pages_free": f.value})
+            k += 1
+        return out
 
     def stats(self) -> dict:
         a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()

@@ -206,6 +206,12 @@ abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_poo
     s.Hq /= hs;
     s.Hkv = 1;
   }
+  if (cfg->budget_pool_pages) {
+    std::vector<int32_t> lq = s.quota;
+    std::sort(lq.begin(), lq.end());
+    lq.erase(std::unique(lq.begin(), lq.end()), lq.end());
+    s.level_pages.assign(cfg->budget_pool_pages, cfg->budget_pool_pages + lq.size());
+  }
   const int64_t page_bytes = (int64_t)s.Hkv * s.pr * s.D * s.esize();
   s.num_pages = cfg->pool_bytes / (2 * page_bytes);
   abk_pool* p = new abk_pool();
@@ -895,6 +901,18 @@ abk_status abk_read_rows(const abk_pool* cp, int32_t seq_id, int32_t layer, int3
   a.row0 = row0;
   a.nrows = nrows;
   ABK_HIP(abk::launch_read(a, p->stream));
+  return ABK_OK;
+}
+
+abk_status abk_budget_pool_stats(const abk_pool* p, int32_t level, int32_t* levels, int32_t* quota,
+                                 int64_t* pages_used, int64_t* pages_free) {
+  if (abk_status st = check_pool(p)) return st;
+  if (levels) *levels = p->host.levels();
+  if (level < 0 || level >= p->host.levels()) return set_err(ABK_ERR_INVALID_ARG, "budget level out of range");
+  const int64_t fr = p->host.level_free(level);
+  if (quota) *quota = p->host.level_quota(level);
+  if (pages_used) *pages_used = p->host.level_pages(level) - fr;
+  if (pages_free) *pages_free = fr;
   return ABK_OK;
 }
 

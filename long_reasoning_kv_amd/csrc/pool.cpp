@@ -42,18 +42,64 @@ Status HostPool::init(const Shape& s, std::string* e) {
   if (s.num_pages < 1 || s.num_pages > INT32_MAX) return bad("pool_bytes gives no pages (or too many)");
   if (!(s.rope_base > 0.0)) return bad("rope_base must be positive");
   if (s.dtype != 0 && s.dtype != 1) return bad("dtype must be ABK_F32 or ABK_BF16");
+  // budget levels: one per distinct quota value when separate pools are asked for
+  std::vector<int32_t> lq;
+  if (!s.level_pages.empty()) {
+    lq = s.quota;
+    std::sort(lq.begin(), lq.end());
+    lq.erase(std::unique(lq.begin(), lq.end()), lq.end());
+    if (s.level_pages.size() != lq.size()) return bad("budget_pool_pages needs one count per distinct quota");
+    int64_t tot = 0;
+    for (int64_t n : s.level_pages) {
+      if (n < 0) return bad("negative budget pool size");
+      tot += n;
+    }
+    if (tot > s.num_pages) return bad("budget pools hold more pages than pool_bytes gives");
+  } else {
+    lq.assign(1, -1);
+  }
   s_ = s;
+  level_quota_ = lq;
+  free_.assign(lq.size(), MinHeap());
+  level_start_.assign(lq.size() + 1, 0);
+  for (size_t k = 0; k < lq.size(); ++k)
+    level_start_[k + 1] = level_start_[k] + (s.level_pages.empty() ? s.num_pages : s.level_pages[k]);
+  for (size_t k = 0; k < lq.size(); ++k)
+    for (int64_t p = level_start_[k]; p < level_start_[k + 1]; ++p) free_[k].push((int32_t)p);
+  level_of_.assign(s.L, 0);
+  if (!s.level_pages.empty())
+    for (int32_t l = 0; l < s.L; ++l)
+      level_of_[l] = (int32_t)(std::lower_bound(lq.begin(), lq.end(), s.quota[l]) - lq.begin());
   seqs_.assign(s.max_seqs, SeqState());
-  for (int32_t p = 0; p < (int32_t)s.num_pages; ++p) free_pages_.push(p);
   for (int32_t i = 0; i < s.max_seqs; ++i) free_slots_.push(i);
   mark_.assign(s.max_seqs, 0);
   return kOk;
 }
 
-int32_t HostPool::take_page() {
-  int32_t p = free_pages_.top();
-  free_pages_.pop();
+int32_t HostPool::take_page(int32_t l) {
+  MinHeap& h = free_[level_of_[l]];
+  int32_t p = h.top();
+  h.pop();
   return p;
+}
+
+void HostPool::give_page(int32_t p) {
+  const size_t k = std::upper_bound(level_start_.begin(), level_start_.end(), (int64_t)p) - level_start_.begin() - 1;
+  free_[k].push(p);
+}
+
+int64_t HostPool::pages_free() const {
+  int64_t t = 0;
+  for (const auto& h : free_) t += (int64_t)h.size();
+  return t;
+}
+
+Status HostPool::check_need(const std::vector<int64_t>& need, const char* what) {
+  for (size_t k = 0; k < need.size(); ++k)
+    if (need[k] > (int64_t)free_[k].size())
+      return fail(kOutOfPages, std::string("not enough free pages ") + what +
+                                   (free_.size() > 1 ? " in budget pool " + std::to_string(k) : std::string()));
+  return kOk;
 }
 
 int32_t HostPool::gmin(const SeqState& q) const {
@@ -114,8 +160,9 @@ Status HostPool::seq_create(int32_t P, int32_t* id) {
   if (!id) return fail(kInvalidArg, "seq_id is NULL");
   if (P < 0 || P > s_.max_position) return fail(kInvalidArg, "prompt length out of range");
   if (free_slots_.empty()) return fail(kOutOfPages, "no free sequence slot");
-  int64_t need = (int64_t)s_.L * cdiv(P, s_.pr);
-  if (need > pages_free()) return fail(kOutOfPages, "not enough free pages for the prompt");
+  std::vector<int64_t> need(levels(), 0);
+  for (int32_t l = 0; l < s_.L; ++l) need[level_of_[l]] += cdiv(P, s_.pr);
+  if (Status st = check_need(need, "for the prompt")) return st;
   int32_t sid = free_slots_.top();
   free_slots_.pop();
   SeqState& q = seqs_[sid];
@@ -123,8 +170,9 @@ Status HostPool::seq_create(int32_t P, int32_t* id) {
   q.live = true;
   q.P = P;
   q.layers.assign(s_.L, LayerState());
-  for (auto& lay : q.layers) {
-    for (int32_t i = 0; i < cdiv(P, s_.pr); ++i) lay.pers_pages.push_back(take_page());
+  for (int32_t l = 0; l < s_.L; ++l) {
+    LayerState& lay = q.layers[l];
+    for (int32_t i = 0; i < cdiv(P, s_.pr); ++i) lay.pers_pages.push_back(take_page(l));
     lay.pers_rows = P;
   }
   *id = sid;
@@ -155,7 +203,7 @@ Status HostPool::write_prompt(int32_t id, int32_t l0, int32_t nl) {
 Status HostPool::append(int32_t l0, int32_t nl, int32_t n, const int32_t* ids, std::vector<int32_t>* new_page) {
   if (check_layers(l0, nl)) return fail(kInvalidArg, "bad layer");
   if (Status st = check_batch(n, ids)) return st;
-  int64_t need = 0;
+  std::vector<int64_t> need(levels(), 0);
   for (int32_t i = 0; i < n; ++i) {
     const SeqState& q = seqs_[ids[i]];
     const int32_t g0 = gmin(q);
@@ -167,13 +215,13 @@ Status HostPool::append(int32_t l0, int32_t nl, int32_t n, const int32_t* ids, s
       if (s_.compress) {
         int32_t op = lay.G - q.nb * s_.C;
         if (op >= s_.C) return fail(kBadState, "open block is full: compress and free it first");
-        need += (op % s_.pr == 0);
+        need[level_of_[l0 + j]] += (op % s_.pr == 0);
       } else {
-        need += (lay.pers_rows % s_.pr == 0);
+        need[level_of_[l0 + j]] += (lay.pers_rows % s_.pr == 0);
       }
     }
   }
-  if (need > pages_free()) return fail(kOutOfPages, "not enough free pages to append");
+  if (Status st = check_need(need, "to append")) return st;
   new_page->assign((size_t)n * nl, -1);
   for (int32_t i = 0; i < n; ++i) {
     SeqState& q = seqs_[ids[i]];
@@ -182,12 +230,12 @@ Status HostPool::append(int32_t l0, int32_t nl, int32_t n, const int32_t* ids, s
       int32_t& np = (*new_page)[(size_t)i * nl + j];
       if (s_.compress) {
         if ((lay.G - q.nb * s_.C) % s_.pr == 0) {
-          np = take_page();
+          np = take_page(l0 + j);
           lay.open_pages.push_back(np);
         }
       } else {
         if (lay.pers_rows % s_.pr == 0) {
-          np = take_page();
+          np = take_page(l0 + j);
           lay.pers_pages.push_back(np);
         }
         lay.pers_rows += 1;
@@ -217,16 +265,16 @@ Status HostPool::compress(int32_t l0, int32_t nl, int32_t n, const int32_t* ids,
   if (check_layers(l0, nl)) return fail(kInvalidArg, "bad layer");
   if (!s_.compress) return fail(kBadState, "compression is off (full-KV pool)");
   if (Status st = check_batch(n, ids)) return st;
-  int64_t need = 0;
+  std::vector<int64_t> need(levels(), 0);
   for (int32_t i = 0; i < n; ++i)
     for (int32_t j = 0; j < nl; ++j) {
       const int32_t l = l0 + j;
       const LayerState& lay = seqs_[ids[i]].layers[l];
       if (open_rows(ids[i], l) != s_.C) return fail(kBadState, "open block is not complete");
       if (lay.compressed) return fail(kBadState, "block already compressed at this layer");
-      need += cdiv(lay.pers_rows + s_.quota[l], s_.pr) - cdiv(lay.pers_rows, s_.pr);
+      need[level_of_[l]] += cdiv(lay.pers_rows + s_.quota[l], s_.pr) - cdiv(lay.pers_rows, s_.pr);
     }
-  if (need > pages_free()) return fail(kOutOfPages, "not enough free pages for code rows");
+  if (Status st = check_need(need, "for code rows")) return st;
   plan->clear();
   for (int32_t i = 0; i < n; ++i) {
     SeqState& q = seqs_[ids[i]];
@@ -242,7 +290,7 @@ Status HostPool::compress(int32_t l0, int32_t nl, int32_t n, const int32_t* ids,
       cp.first_new = 0;
       int32_t have = cdiv(lay.pers_rows, s_.pr);
       int32_t want = cdiv(lay.pers_rows + qn, s_.pr);
-      for (int32_t k = have; k < want; ++k) lay.pers_pages.push_back(take_page());
+      for (int32_t k = have; k < want; ++k) lay.pers_pages.push_back(take_page(l));
       if (qn > 0) {
         int32_t first = lay.pers_rows / s_.pr, last = (lay.pers_rows + qn - 1) / s_.pr;
         cp.pages.assign(lay.pers_pages.begin() + first, lay.pers_pages.begin() + last + 1);
@@ -284,17 +332,17 @@ Status HostPool::fill(int32_t id, int32_t G) {
     return fail(kInvalidArg, "position reaches max_position");
   int32_t nb = (s_.compress && G > 0) ? (G - 1) / s_.C : 0;
   int32_t opn = s_.compress ? G - nb * s_.C : 0;
-  int64_t need = 0;
+  std::vector<int64_t> need(levels(), 0);
   for (int32_t l = 0; l < s_.L; ++l) {
     int64_t r1 = q.P + (s_.compress ? (int64_t)nb * s_.quota[l] : G);
-    need += cdiv(r1, s_.pr) - cdiv(q.P, s_.pr) + cdiv(opn, s_.pr);
+    need[level_of_[l]] += cdiv(r1, s_.pr) - cdiv(q.P, s_.pr) + cdiv(opn, s_.pr);
   }
-  if (need > pages_free()) return fail(kOutOfPages, "not enough free pages for the fill");
+  if (Status st = check_need(need, "for the fill")) return st;
   for (int32_t l = 0; l < s_.L; ++l) {
     LayerState& lay = q.layers[l];
     int32_t r1 = q.P + (s_.compress ? nb * s_.quota[l] : G);
-    for (int32_t k = cdiv(q.P, s_.pr); k < cdiv(r1, s_.pr); ++k) lay.pers_pages.push_back(take_page());
-    for (int32_t k = 0; k < cdiv(opn, s_.pr); ++k) lay.open_pages.push_back(take_page());
+    for (int32_t k = cdiv(q.P, s_.pr); k < cdiv(r1, s_.pr); ++k) lay.pers_pages.push_back(take_page(l));
+    for (int32_t k = 0; k < cdiv(opn, s_.pr); ++k) lay.open_pages.push_back(take_page(l));
     lay.pers_rows = r1;
     lay.G = G;
     lay.prompt_written = true;

@@ -34,6 +34,10 @@ struct Shape {
   int64_t num_pages = 0;
   double rope_base = 0.0;
   std::vector<int32_t> quota, pause;  // per layer
+  // Optional separate page pools per budget level (a level = one distinct
+  // quota value, ascending): pages of level k are ids [sum of earlier counts,
+  // + level_pages[k]). Empty: one pool for every layer.
+  std::vector<int64_t> level_pages;
   int32_t esize() const { return dtype == 0 ? 4 : 2; }
   int32_t max_pers_pages() const { return (max_position + pr - 1) / pr; }
   int32_t max_open_pages() const { return compress ? C / pr : 0; }
@@ -68,7 +72,13 @@ class HostPool {
 
   const Shape& shape() const { return s_; }
   const SeqState& seq(int32_t id) const { return seqs_[id]; }
-  int64_t pages_free() const { return (int64_t)free_pages_.size(); }
+  int64_t pages_free() const;
+  // budget levels: count, the level of a layer, a level's quota and pages
+  int32_t levels() const { return (int32_t)free_.size(); }
+  int32_t level_of(int32_t l) const { return level_of_[l]; }
+  int32_t level_quota(int32_t k) const { return level_quota_[k]; }
+  int64_t level_pages(int32_t k) const { return level_start_[k + 1] - level_start_[k]; }
+  int64_t level_free(int32_t k) const { return (int64_t)free_[k].size(); }
   int32_t open_rows(int32_t id, int32_t l) const;
   int32_t resident_rows(int32_t id, int32_t l) const;
   int64_t resident_rows_total() const;
@@ -103,14 +113,20 @@ class HostPool {
     err = msg;
     return st;
   }
-  int32_t take_page();
-  void give_page(int32_t p) { free_pages_.push(p); }
+  int32_t take_page(int32_t l);  // from layer l's budget pool
+  void give_page(int32_t p);
+  // pages a call needs per budget level; fails unless every level has them
+  Status check_need(const std::vector<int64_t>& need, const char* what);
   int32_t gmin(const SeqState& q) const;
   int32_t gmax(const SeqState& q) const;
 
   Shape s_;
   std::vector<SeqState> seqs_;
-  std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_pages_;
+  using MinHeap = std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>>;
+  std::vector<MinHeap> free_;         // per budget level
+  std::vector<int64_t> level_start_;  // first page id of each level, then the end
+  std::vector<int32_t> level_of_;     // per layer
+  std::vector<int32_t> level_quota_;  // per level (-1: one pool for all quotas)
   std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_slots_;
   std::vector<uint32_t> mark_;  // duplicate detection, stamped per call
   uint32_t stamp_ = 0;

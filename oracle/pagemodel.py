@@ -64,7 +64,7 @@ class _Seq:
 
 class PageModel:
     def __init__(self, num_pages: int, page_rows: int, num_layers: int, C: int, quotas,
-                 pauses=None, max_seqs: int = 64, compress: bool = True):
+                 pauses=None, max_seqs: int = 64, compress: bool = True, budget_pages=None):
         self.num_pages = num_pages
         self.pr = page_rows
         self.L = num_layers
@@ -73,8 +73,24 @@ class PageModel:
         self.Kp = list(pauses) if pauses is not None else [max(self.quota)] * num_layers
         self.max_seqs = max_seqs
         self.compress_on = compress
-        self._free = list(range(num_pages))
-        heapq.heapify(self._free)
+        # separate pools per budget level (the AI Radio transcript: one page
+        # pool per budget level): level k = k-th smallest distinct quota, its
+        # pages the k-th consecutive id range; otherwise one pool
+        if budget_pages is None:
+            self.level_quota = [-1]
+            bounds = [0, num_pages]
+            self.level_of = [0] * num_layers
+        else:
+            self.level_quota = sorted(set(self.quota))
+            assert len(budget_pages) == len(self.level_quota) and sum(budget_pages) <= num_pages
+            bounds = [0]
+            for n in budget_pages:
+                bounds.append(bounds[-1] + n)
+            self.level_of = [self.level_quota.index(q) for q in self.quota]
+        self._bounds = bounds
+        self._free = [list(range(bounds[k], bounds[k + 1])) for k in range(len(bounds) - 1)]
+        for h in self._free:
+            heapq.heapify(h)
         self._slots = list(range(max_seqs))
         heapq.heapify(self._slots)
         self.seqs = {}
@@ -83,16 +99,26 @@ class PageModel:
     def view(self, sid: int, l: int) -> LayerView:
         return LayerView(self.seqs[sid].P, self.C, self.Kp[l], self.quota[l], self.compress_on)
 
-    def _alloc(self, n: int):
-        return [heapq.heappop(self._free) for _ in range(n)]
+    def _alloc(self, n: int, l: int):
+        h = self._free[self.level_of[l]]
+        return [heapq.heappop(h) for _ in range(n)]
 
     def _release(self, pages):
         for p in pages:
-            heapq.heappush(self._free, p)
+            k = max(i for i in range(len(self._free)) if self._bounds[i] <= p)
+            heapq.heappush(self._free[k], p)
 
-    def _need(self, n: int):
-        if n > len(self._free):
-            raise PoolError(OUT_OF_PAGES, f"need {n} pages, {len(self._free)} free")
+    def _need(self, need: dict):
+        """need: layer -> pages; every budget level must hold its layers' sum."""
+        per = {}
+        for l, n in need.items():
+            per[self.level_of[l]] = per.get(self.level_of[l], 0) + n
+        for k, n in per.items():
+            if n > len(self._free[k]):
+                raise PoolError(OUT_OF_PAGES, f"need {n} pages in level {k}, {len(self._free[k])} free")
+
+    def level_free(self, k: int) -> int:
+        return len(self._free[k])
 
     def _check_ids(self, sids):
         if len(set(sids)) != len(sids):
@@ -116,7 +142,7 @@ class PageModel:
         return self.pers_rows(sid, l) + self.open_rows(sid, l)
 
     def pages_free(self) -> int:
-        return len(self._free)
+        return sum(len(h) for h in self._free)
 
     # -- operations -----------------------------------------------------------
     def seq_create(self, P: int) -> int:
@@ -124,11 +150,11 @@ class PageModel:
             raise PoolError(INVALID_ARG, "negative prompt")
         if not self._slots:
             raise PoolError(OUT_OF_PAGES, "no free sequence slot")
-        self._need(self.L * _cdiv(P, self.pr))
+        self._need({l: _cdiv(P, self.pr) for l in range(self.L)})
         sid = heapq.heappop(self._slots)
         s = _Seq(P, self.L)
-        for lay in s.layers:
-            lay.pers_pages = self._alloc(_cdiv(P, self.pr))
+        for l, lay in enumerate(s.layers):
+            lay.pers_pages = self._alloc(_cdiv(P, self.pr), l)
             lay.pers_ids = [(PROMPT, i, 0) for i in range(P)]
         self.seqs[sid] = s
         return sid
@@ -159,16 +185,16 @@ class PageModel:
                 need += op % self.pr == 0
             else:
                 need += len(lay.pers_ids) % self.pr == 0
-        self._need(need)
+        self._need({l: need})
         for sid in sids:
             s = self.seqs[sid]
             lay = s.layers[l]
             if self.compress_on:
                 if self.open_rows(sid, l) % self.pr == 0:
-                    lay.open_pages += self._alloc(1)
+                    lay.open_pages += self._alloc(1, l)
             else:
                 if len(lay.pers_ids) % self.pr == 0:
-                    lay.pers_pages += self._alloc(1)
+                    lay.pers_pages += self._alloc(1, l)
                 lay.pers_ids.append((TEXT, lay.G, 0))
             lay.G += 1
 
@@ -196,12 +222,12 @@ class PageModel:
                 raise PoolError(BAD_STATE, "block not complete or already compressed")
             r = len(lay.pers_ids)
             need += _cdiv(r + q, self.pr) - _cdiv(r, self.pr)
-        self._need(need)
+        self._need({l: need})
         for sid in sids:
             s = self.seqs[sid]
             lay = s.layers[l]
             r = len(lay.pers_ids)
-            lay.pers_pages += self._alloc(_cdiv(r + q, self.pr) - _cdiv(r, self.pr))
+            lay.pers_pages += self._alloc(_cdiv(r + q, self.pr) - _cdiv(r, self.pr), l)
             lay.pers_ids += [(PAUSE, s.nb, k) for k in range(q)]
             lay.compressed = True
 
@@ -215,7 +241,7 @@ class PageModel:
         for lv in lays:
             self._check_layer(lv)
         self._check_ids(sids)
-        need = 0
+        need = {lv: 0 for lv in lays}
         for sid in sids:
             s = self.seqs[sid]
             g0 = min(x.G for x in s.layers)
@@ -229,9 +255,9 @@ class PageModel:
                     op = self.open_rows(sid, lv)
                     if op >= self.C:
                         raise PoolError(BAD_STATE, "open block full: compress and free it first")
-                    need += op % self.pr == 0
+                    need[lv] += op % self.pr == 0
                 else:
-                    need += len(lay.pers_ids) % self.pr == 0
+                    need[lv] += len(lay.pers_ids) % self.pr == 0
         self._need(need)
         for sid in sids:
             s = self.seqs[sid]
@@ -239,10 +265,10 @@ class PageModel:
                 lay = s.layers[lv]
                 if self.compress_on:
                     if self.open_rows(sid, lv) % self.pr == 0:
-                        lay.open_pages += self._alloc(1)
+                        lay.open_pages += self._alloc(1, lv)
                 else:
                     if len(lay.pers_ids) % self.pr == 0:
-                        lay.pers_pages += self._alloc(1)
+                        lay.pers_pages += self._alloc(1, lv)
                     lay.pers_ids.append((TEXT, lay.G, 0))
                 lay.G += 1
 
@@ -257,14 +283,14 @@ class PageModel:
         self._check_ids(sids)
         if not self.compress_on:
             raise PoolError(BAD_STATE, "compression is off")
-        need = 0
+        need = {lv: 0 for lv in lays}
         for sid in sids:
             for lv in lays:
                 lay = self.seqs[sid].layers[lv]
                 if self.open_rows(sid, lv) != self.C or lay.compressed:
                     raise PoolError(BAD_STATE, "block not complete or already compressed")
                 r = len(lay.pers_ids)
-                need += _cdiv(r + self.quota[lv], self.pr) - _cdiv(r, self.pr)
+                need[lv] += _cdiv(r + self.quota[lv], self.pr) - _cdiv(r, self.pr)
         self._need(need)
         for sid in sids:
             s = self.seqs[sid]
@@ -272,7 +298,7 @@ class PageModel:
                 lay = s.layers[lv]
                 q = self.quota[lv]
                 r = len(lay.pers_ids)
-                lay.pers_pages += self._alloc(_cdiv(r + q, self.pr) - _cdiv(r, self.pr))
+                lay.pers_pages += self._alloc(_cdiv(r + q, self.pr) - _cdiv(r, self.pr), lv)
                 lay.pers_ids += [(PAUSE, s.nb, k) for k in range(q)]
                 lay.compressed = True
 
@@ -315,10 +341,10 @@ class PageModel:
             r0 = s.P
             r1 = s.P + (nb * self.quota[l] if self.compress_on else G)
             plan.append((_cdiv(r1, self.pr) - _cdiv(r0, self.pr), _cdiv(opn, self.pr)))
-        self._need(sum(a + b for a, b in plan))
+        self._need({l: a + b for l, (a, b) in enumerate(plan)})
         for l, lay in enumerate(s.layers):
-            lay.pers_pages += self._alloc(plan[l][0])
-            lay.open_pages += self._alloc(plan[l][1])
+            lay.pers_pages += self._alloc(plan[l][0], l)
+            lay.open_pages += self._alloc(plan[l][1], l)
             if self.compress_on:
                 lay.pers_ids += [(PAUSE, b, k) for b in range(nb) for k in range(self.quota[l])]
             else:
@@ -334,7 +360,7 @@ class PageModel:
                                    tuple(x.open_pages), x.compressed, x.prompt_written)
                                   for x in s.layers])
                 for sid, s in self.seqs.items()}
-        return sorted(self._free), sorted(self._slots), seqs
+        return sorted(p for h in self._free for p in h), sorted(self._slots), seqs
 
     def layout(self, sid: int, l: int):
         """(page ids: persistent then open, positions of resident rows,

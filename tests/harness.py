@@ -33,7 +33,7 @@ class Run:
 
     def __init__(self, *, L, Hq, Hkv, D, C, Kp, quota, pause=None, pr, dtype="bf16",
                  compress=True, max_seqs=64, pool_bytes=None, max_position=40960,
-                 split_rows=0, base=1e6, seed=0, head_quota=None):
+                 split_rows=0, base=1e6, seed=0, head_quota=None, budget_pool_pages=None):
         self.L, self.Hq, self.Hkv, self.D, self.C = L, Hq, Hkv, D, C
         self.quota = list(quota)
         self.head_quota = [list(r) for r in head_quota] if head_quota is not None else None
@@ -46,7 +46,8 @@ class Run:
                              block_tokens=C, num_pause=Kp, layer_quota=quota, layer_pause=pause,
                              page_rows=pr, max_seqs=max_seqs, pool_bytes=pool_bytes,
                              max_position=max_position, dtype=dtype, rope_base=base,
-                             compress=compress, decode_split_rows=split_rows, head_quota=head_quota)
+                             compress=compress, decode_split_rows=split_rows, head_quota=head_quota,
+                             budget_pool_pages=budget_pool_pages)
         self.page_bytes = (1 if head_quota is not None else Hkv) * pr * D * esize
         self.seed = seed
         self.seeds = {}   # sid -> synth seed

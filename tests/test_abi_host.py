@@ -293,3 +293,74 @@ def test_per_head_config_and_call_checks():
         pool.blockmask_attention(0, 4, 8, None, None, None, None, None)
     assert e.value.status == 5
     pool.close()
+
+
+# ---- separate page pools per budget level (AI Radio transcript) ----------------
+
+def _drive(pool, pm, sids, steps, hs=1):
+    for t in range(steps):
+        for l in range(3):
+            if hs == 1:
+                _both(pool, pm, lambda l=l: pool.append_kv(l, sids, None, None), lambda l=l: pm.append(l, sids))
+            else:
+                _both(pool, pm, lambda l=l: pool.append_kv(l, sids, None, None),
+                      lambda l=l: pm.append_heads(l, hs, sids))
+        done = [s for s in sids if pm.open_rows(s, 0) == 8]
+        if done:
+            for l in range(3):
+                if hs == 1:
+                    _both(pool, pm, lambda l=l: pool.compress_block(l, done, None, None, None, None, None),
+                          lambda l=l: pm.compress(l, done))
+                else:
+                    _both(pool, pm, lambda l=l: pool.compress_block(l, done, None, None, None, None, None),
+                          lambda l=l: pm.compress_heads(l, hs, done))
+            _both(pool, pm, lambda: pool.free_block(done), lambda: pm.free_block(done))
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_budget_pools_match_page_model(per_head):
+    # one pool per distinct quota (levels ascending), each with its own page id
+    # range; every (sequence, layer) allocates from its level only
+    hs = 2 if per_head else 1
+    quotas = [q for row in HEAD_Q for q in row] if per_head else [4, 2, 1]
+    levels = sorted(set(quotas))
+    budget = [12 + 2 * k for k in range(len(levels))]
+    kw = dict(head_quota=HEAD_Q) if per_head else {}
+    pool = _pool(budget_pool_pages=budget, _pages=400, **kw)
+    pm = PageModel(num_pages=400 * hs, page_rows=4, num_layers=3 * hs, C=8, quotas=quotas,
+                   pauses=[4] * (3 * hs), max_seqs=4, budget_pages=budget)
+    st = pool.budget_stats()
+    assert [x["quota"] for x in st] == levels
+    assert [x["pages_free"] for x in st] == budget
+    sids = [_both(pool, pm, lambda P=P: pool.seq_create(P), lambda P=P: pm.seq_create(P)) for P in (2, 5)]
+    for s in sids:
+        for l in range(3):
+            _both(pool, pm, lambda s=s, l=l: pool.write_prompt(s, l, None, None),
+                  lambda s=s, l=l: [pm.write_prompt(s, l * hs + j) for j in range(hs)] and None)
+    # grow until some level runs out; both refuse the same call
+    _drive(pool, pm, sids, 60, hs)
+    for s in sids:
+        for lv in range(3 * hs):
+            pages, pos = pool.export_layout(s, lv)
+            mp, mpos, _ = pm.layout(s, lv)
+            assert pages == mp and pos == mpos, (s, lv)
+            k = levels.index(quotas[lv])
+            lo = sum(budget[:k])
+            assert all(lo <= pg < lo + budget[k] for pg in pages), (s, lv)
+    st = pool.budget_stats()
+    assert [x["pages_free"] for x in st] == [pm.level_free(k) for k in range(len(levels))]
+    assert any(x["pages_free"] < 4 for x in st)  # some level was driven to its end
+    pool.close()
+
+
+def test_budget_pool_config_checks():
+    with pytest.raises(abk.AbkError) as e:
+        _pool(budget_pool_pages=[10, 10, 10 ** 6])  # more pages than pool_bytes gives
+    assert e.value.status == 1
+    with pytest.raises(abk.AbkError) as e:
+        _pool(budget_pool_pages=[10, -1, 10])
+    assert e.value.status == 1
+    pool = _pool()
+    st = pool.budget_stats()
+    assert len(st) == 1 and st[0]["quota"] == -1 and st[0]["pages_free"] == 300
+    pool.close()

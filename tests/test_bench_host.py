@@ -56,3 +56,16 @@ def test_head_quotas_keep_layer_totals():
         assert len(row) == bench.HKV and sum(row) == bench.HKV * int(q)
         assert all(x > 0 and (x & (x - 1)) == 0 and x <= 256 for x in row)
         assert (len(set(row)) > 1) == (int(q) < 256)
+
+
+def test_budget_pool_split_covers_the_admitted_needs():
+    """The serving mix's per-level pools hold every admitted sequence's largest
+    footprint at its level and together no more than the pool."""
+    quotas = bench.layer_quotas(2)
+    pages = 200 * 2 ** 30 // (2 * bench.HKV * bench.PR * bench.D * 2)
+    by = {}
+    P, G, used = bench.serving_mix_admit(quotas, 64, True, pages, by_quota=by)
+    assert sum(by.values()) == used
+    qs, split = bench.budget_pool_split(by, pages)
+    assert qs == sorted(set(int(q) for q in quotas))
+    assert all(n >= by[q] for q, n in zip(qs, split)) and sum(split) <= pages

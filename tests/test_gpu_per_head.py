@@ -122,3 +122,41 @@ def test_per_head_quotas_fp32_generic_kernels():
     for l in range(run.L):
         out, lse, q = run.decode(sids, l)
         _check_decode(run, sids, l, out, lse, q)
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_budget_pools_compress_then_decode(per_head):
+    # one page pool per budget level (AI Radio transcript): results as with one
+    # pool; every (sequence, layer) holds pages of its level's id range only
+    kw = dict(head_quota=HQ_BF16) if per_head else dict(head_quota=None, quota=[64, 16])
+    quotas = [q for row in HQ_BF16 for q in row] if per_head else [64, 16]
+    levels = sorted(set(quotas))
+    budget = [400] * len(levels)
+    run = _run(seed=34, budget_pool_pages=budget, **kw)
+    sids = [run.new_seq(P, i) for i, P in enumerate([5, 64, 30])]
+    for s in sids:
+        run.write_prompts(s)
+    run.grow({s: 2 * run.C for s in sids})
+    outs = [run.compress_layer(sids, l) for l in range(run.L)]
+    torch.cuda.synchronize()
+    if per_head:
+        for l, (out, lse) in enumerate(outs):
+            _check_compress(run, sids, l, out, lse)
+    run.pool.free_block(sids)
+    for s in sids:
+        run.nb[s] += 1
+    res = run.step_fused(sids)
+    to, tl = TOL[run.dtype]
+    for l, (out, lse, q) in enumerate(res):
+        if per_head:
+            _check_decode(run, sids, l, out, lse, q)
+        else:
+            for i, s in enumerate(sids):
+                o_ref, l_ref, _ = run.oracle_decode(s, l, q[i])
+                _close(f"decode out seq{s} L{l}", out[i], o_ref, to)
+                _close(f"decode lse seq{s} L{l}", lse[i], l_ref, tl)
+    for s in sids:
+        for lv in range(len(quotas)):
+            pages, _ = run.pool.export_layout(s, lv)
+            k = levels.index(quotas[lv])
+            assert all(sum(budget[:k]) <= p < sum(budget[:k + 1]) for p in pages), (s, lv)
