@@ -91,8 +91,8 @@ typedef struct {
                                 abk_seq_query, abk_export_layout and abk_read_rows names
                                 the pair as l * Hkv + h (rows [n][1][d]). The hot-path
                                 calls keep their model-layer arguments and tensor
-                                layouts. abk_blockmask_attention and abk_prefill_prompt
-                                return UNSUPPORTED on such a pool. */
+                                layouts; abk_blockmask_attention gives each KV head's
+                                queries that head's own kept code rows. */
   const int64_t* budget_pool_pages; /* optional: a separate page pool per budget level (AI
                                 Radio transcript: the serving engine keeps one page pool
                                 per budget level). A level is one distinct quota value

@@ -708,13 +708,18 @@ abk_status abk_free_block(abk_pool* p, int32_t n, const int32_t* seq_ids) {
 abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_len, int32_t text_tokens,
                                    const void* q, const void* k, const void* v, void* out, float* lse) {
   if (abk_status st = check_pool(p)) return st;
-  if (p->hs != 1) return set_err(ABK_ERR_UNSUPPORTED, "block-mask prefill with per-head quotas");
-  if (p->host.check_layer(layer)) return set_err(ABK_ERR_INVALID_ARG, "bad layer");
+  if (abk_status st = check_model_layer(p, layer)) return st;
   const abk::Shape& s = p->shape;
   if (prompt_len < 0 || text_tokens < 0) return set_err(ABK_ERR_INVALID_ARG, "negative length");
   if ((int64_t)prompt_len + text_tokens > s.max_position)
     return set_err(ABK_ERR_INVALID_ARG, "positions reach max_position");
-  const int32_t C = s.C, Kp = s.pause[layer], quota = s.quota[layer];
+  // the model's KV heads and each one's quota (per-head quotas: pool layers
+  // layer * hs + h)
+  const int32_t Hkv = s.Hkv * p->hs, Hq = s.Hq * p->hs;
+  if (Hkv > abk::kMaxPrefillHeads) return set_err(ABK_ERR_UNSUPPORTED, "block-mask prefill above 16 KV heads");
+  std::vector<int32_t> qh(Hkv);
+  for (int32_t h = 0; h < Hkv; ++h) qh[h] = s.quota[layer * p->hs + (p->hs > 1 ? h : 0)];
+  const int32_t C = s.C, Kp = s.pause[layer * p->hs], qmax = *std::max_element(qh.begin(), qh.end());
   const bool comp = s.compress != 0;
   const int32_t nb = comp ? text_tokens / C : 0;  // complete blocks: followed by their pause rows
   const int64_t T64 = (int64_t)prompt_len + text_tokens + (int64_t)nb * Kp;
@@ -727,30 +732,30 @@ abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_le
     return set_err(ABK_ERR_INVALID_ARG, "q/k/v/out/lse is NULL");
   if (p->host_only) return ABK_OK;
 
-  // query tiles of up to 32 tokens of one kind in one block, per KV head
+  // query tiles of up to 32 tokens of one kind in one block; per KV head, a
+  // text or pause tile sees nA = prompt + blk * that head's quota persistent rows
   struct Tile {
-    int32_t kind, row0, ntok, tok0, nA, bstart, nB, blk;
-    int64_t work;  // keys seen by its last query (a size for the schedule)
+    int32_t kind, row0, ntok, tok0, bstart, nB, blk;
+    int64_t work;  // keys seen by its last query beyond the persistent rows
   };
   std::vector<Tile> tiles;
   const int32_t P0 = comp ? prompt_len : T;  // rows attended causally from the start
   for (int32_t t0 = 0; t0 < P0; t0 += 32) {
     const int32_t n = std::min(32, P0 - t0);
-    tiles.push_back({0, t0, n, t0, 0, 0, 0, -1, t0 + n});
+    tiles.push_back({0, t0, n, t0, 0, 0, -1, t0 + n});
   }
   if (comp) {
     const int32_t nblk = (text_tokens + C - 1) / C;
     for (int32_t blk = 0; blk < nblk; ++blk) {
       const int32_t bstart = prompt_len + blk * (C + Kp), ctext = std::min(C, text_tokens - blk * C);
-      const int32_t nA = prompt_len + blk * quota;
       for (int32_t i0 = 0; i0 < ctext; i0 += 32) {
         const int32_t n = std::min(32, ctext - i0);
-        tiles.push_back({1, bstart + i0, n, i0, nA, bstart, i0 + n, blk, (int64_t)nA + i0 + n});
+        tiles.push_back({1, bstart + i0, n, i0, bstart, i0 + n, blk, (int64_t)i0 + n});
       }
       if (blk < nb)
         for (int32_t j0 = 0; j0 < Kp; j0 += 32) {
           const int32_t n = std::min(32, Kp - j0);
-          tiles.push_back({2, bstart + C + j0, n, j0, nA, bstart, C + j0 + n, blk, (int64_t)nA + C + j0 + n});
+          tiles.push_back({2, bstart + C + j0, n, j0, bstart, C + j0 + n, blk, (int64_t)C + j0 + n});
         }
     }
   }
@@ -758,10 +763,11 @@ abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_le
   // its L2, since they read the same keys; each XCD's list runs heaviest first.
   const int32_t nblk_all = (comp ? (text_tokens + C - 1) / C : 0) + 1;
   std::vector<std::vector<std::pair<int64_t, std::array<int32_t, abk::kBmRec>>>> lists(8);
-  for (int32_t h = 0; h < s.Hkv; ++h)
+  for (int32_t h = 0; h < Hkv; ++h)
     for (const Tile& t : tiles) {
       const int32_t x = (h * nblk_all + (t.blk + 1)) % 8;
-      lists[x].push_back({t.work, {h, t.kind, t.row0, t.ntok, t.tok0, t.nA, t.bstart, t.nB, t.blk}});
+      const int32_t nA = t.kind == 0 ? 0 : prompt_len + t.blk * qh[h];
+      lists[x].push_back({t.work + nA, {h, t.kind, t.row0, t.ntok, t.tok0, nA, t.bstart, t.nB, t.blk}});
     }
   size_t maxlen = 0;
   for (auto& l : lists) {
@@ -780,8 +786,8 @@ abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_le
     }
   const int32_t nrec = (int32_t)(maxlen * 8);
 
-  const int32_t npers = comp ? prompt_len + nb * quota : T;
-  const size_t row_bytes = (size_t)s.Hkv * s.D * s.esize();
+  const int32_t npers = comp ? prompt_len + nb * qmax : T;
+  const size_t row_bytes = (size_t)Hkv * s.D * s.esize();
   const size_t stage = 2 * (size_t)T * row_bytes, pers = comp ? 2 * (size_t)npers * row_bytes : 0;
   if (abk_status st = grow(p, &p->bm_stage, &p->bm_stage_bytes, stage + pers)) return st;
   if (abk_status st = upload_desc(p, d.data(), d.size() * sizeof(int32_t))) return st;
@@ -797,7 +803,8 @@ abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_le
   a.kpers = comp ? (char*)p->bm_stage + stage : a.kst;
   a.vpers = comp ? (char*)p->bm_stage + stage + (size_t)npers * row_bytes : a.vst;
   a.desc = (const int32_t*)p->desc;
-  a.Hq = s.Hq;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
   a.T = T;
   a.prompt = prompt_len;
   a.C = C;
@@ -805,7 +812,7 @@ abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_le
   int32_t lg = 0;
   while ((1 << lg) < Kp) ++lg;
   a.log2Kp = lg;
-  a.quota = quota;
+  for (int32_t h = 0; h < abk::kMaxPrefillHeads; ++h) a.quota_h[h] = h < Hkv ? qh[h] : 0;
   a.npers = npers;
   a.compress = comp ? 1 : 0;
   ABK_HIP(abk::launch_blockmask(a, nrec, p->stream));
@@ -816,8 +823,7 @@ abk_status abk_prefill_prompt(abk_pool* p, int32_t seq_id, int32_t layer, const 
                               const void* v, void* out, float* lse) {
   if (abk_status st = check_pool(p)) return st;
   if (p->host.check_seq(seq_id)) return set_err(ABK_ERR_INVALID_ARG, "unknown sequence id");
-  if (p->host.check_layer(layer)) return set_err(ABK_ERR_INVALID_ARG, "bad layer");
-  if (p->hs != 1) return set_err(ABK_ERR_UNSUPPORTED, "prompt prefill with per-head quotas");
+  if (abk_status st = check_model_layer(p, layer)) return st;
   const abk::Shape& s = p->shape;
   if (!(s.dtype == 1 && s.D == 128 && s.Hq == 4 * s.Hkv))
     return set_err(ABK_ERR_UNSUPPORTED, "prompt prefill needs bf16, d = 128, four query heads per KV head");

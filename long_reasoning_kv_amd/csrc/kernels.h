@@ -118,12 +118,15 @@ struct CompressArgs {
 // layer. The staging pass rotates every key once into kst [Hkv][T][D] (values
 // into vst) and gathers the prompt and the kept code rows (pause k < quota of
 // every complete block) into kpers/vpers [Hkv][npers][D]: the layer's
-// persistent rows. The attention pass takes one workgroup per record of desc
+// persistent rows. With a quota per KV head, head h keeps pause k < quota_h[h]
+// at rows [prompt + blk * quota_h[h] + k] of its [npers] slab (npers sized for
+// the largest). The attention pass takes one workgroup per record of desc
 // (kBmRec ints): {KV head (-1: none), kind (0 prompt, 1 text, 2 pause), first
 // query row, query tokens (<= 32), index of the first query in its range
 // (prompt, text-in-block or pause index), persistent rows it sees, first row
 // of its block in kst, rows of the block it sees, block}.
 constexpr int kBmRec = 9;
+constexpr int kMaxPrefillHeads = 16;
 struct BlockMaskArgs {
   DevPool P;
   const void* q;   // [T][Hq][D] pre-RoPE
@@ -136,7 +139,8 @@ struct BlockMaskArgs {
   void* kpers;     // [Hkv][npers][D] (the staging buffers themselves when compression is off)
   void* vpers;
   const int32_t* desc;
-  int32_t Hq, T, prompt, C, Kp, log2Kp, quota, npers, compress;
+  int32_t Hq, Hkv, T, prompt, C, Kp, log2Kp, npers, compress;
+  int32_t quota_h[kMaxPrefillHeads];  // code rows each KV head keeps per block
 };
 
 // Fill: desc holds per layer {pers_off, npers_pages, open_off, nopen_pages}

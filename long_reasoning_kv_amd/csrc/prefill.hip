@@ -24,25 +24,31 @@ __global__ void __launch_bounds__(512) blockmask_stage_kernel(BlockMaskArgs a) {
   constexpr int D = 128;
   const DevPool& P = a.P;
   const int row = blockIdx.x;
-  int pos, pidx = -1;
+  // a prompt row, and a pause row k < its head's quota (a kept code row), is
+  // also one of the head's persistent rows, at index pidx
+  int pos, blk = 0, k = 0;
+  bool pers = false, pause = false;
   if (!a.compress || row < a.prompt) {
     pos = row;  // prompt rows (all rows when compression is off) sit at their index
-    pidx = a.compress ? row : -1;
+    pers = a.compress;
   } else {
-    const int rel = row - a.prompt, blk = rel / (a.C + a.Kp), off = rel % (a.C + a.Kp);
+    const int rel = row - a.prompt, off = rel % (a.C + a.Kp);
+    blk = rel / (a.C + a.Kp);
     if (off < a.C) {
       pos = a.prompt + blk * a.C + off;
     } else {
-      const int k = off - a.C;
+      k = off - a.C;
+      pause = true;
       pos = a.prompt + blk * a.C + bitrev_dev(k, a.log2Kp) * (a.C / a.Kp);
-      if (k < a.quota) pidx = a.prompt + blk * a.quota + k;  // a kept code row
     }
   }
   const double2* rope = P.rope + (size_t)pos * (D / 2);
-  const bf16_t* kin = (const bf16_t*)a.k + (size_t)row * P.Hkv * D;
-  const bf16_t* vin = (const bf16_t*)a.v + (size_t)row * P.Hkv * D;
-  for (int t = threadIdx.x; t < P.Hkv * (D / 2); t += blockDim.x) {
+  const bf16_t* kin = (const bf16_t*)a.k + (size_t)row * a.Hkv * D;
+  const bf16_t* vin = (const bf16_t*)a.v + (size_t)row * a.Hkv * D;
+  for (int t = threadIdx.x; t < a.Hkv * (D / 2); t += blockDim.x) {
     const int hh = t / (D / 2), j = t % (D / 2);
+    const int q = a.quota_h[hh];
+    const int pidx = pers ? row : (pause && k < q ? a.prompt + blk * q + k : -1);
     const double x1 = to_f32(kin[hh * D + j]), x2 = to_f32(kin[hh * D + j + D / 2]);
     const double2 cs = rope[j];
     const bf16_t y1 = from_f64<bf16_t>(rot_first(x1, x2, cs));

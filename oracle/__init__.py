@@ -276,6 +276,21 @@ def compress_heads(Ls, G: int, nb: int, block: int, q_raw: np.ndarray, fetch, dt
     return np.concatenate(outs, axis=1), np.concatenate(lses, axis=1), codes
 
 
+def blockmask_prefill_heads(Ls, G: int, q_raw: np.ndarray, fetch, dtype: int, base: float, rows=None):
+    """The block-mask prefill with a quota per (layer, KV head): KV head h's
+    query heads under the mask of Ls[h] (its own kept code rows), seeing KV
+    head h only. q_raw [T, Hq, d]. Returns (out [n, Hq, d], lse [n, Hq])."""
+    Hkv = len(Ls)
+    g = q_raw.shape[1] // Hkv
+    outs, lses = [], []
+    for h in range(Hkv):
+        o, l = blockmask_prefill(Ls[h], G, np.asarray(q_raw)[:, h * g:(h + 1) * g], _head_fetch(fetch, h), dtype,
+                                 base, rows)
+        outs.append(o)
+        lses.append(l)
+    return np.concatenate(outs, axis=1), np.concatenate(lses, axis=1)
+
+
 def training_tokens(L: LayerView, G: int):
     """Token identities (kind, a, b) of a sequence with G text tokens in
     training order (the creation order of Fig. 2(a) in the figure captions):

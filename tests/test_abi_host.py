@@ -290,7 +290,10 @@ def test_per_head_config_and_call_checks():
     with pytest.raises(abk.AbkError):
         pool.seq_query(s, 6)
     with pytest.raises(abk.AbkError) as e:
-        pool.blockmask_attention(0, 4, 8, None, None, None, None, None)
+        pool.blockmask_attention(3, 4, 8, None, None, None, None, None)  # model layers only
+    assert e.value.status == 1
+    with pytest.raises(abk.AbkError) as e:
+        pool.blockmask_attention(0, 4, 8, None, None, None, None, None)  # f32, d = 16: no MFMA prefill
     assert e.value.status == 5
     pool.close()
 

@@ -152,3 +152,27 @@ def test_prefill_prompt_writes_the_rows_and_attends():
             _close(f"decode lse after prompt prefill P{P} L{l}", lse[0], l_ref, 1e-3)
     for r in runs:
         r.pool.close()
+
+
+@pytest.mark.parametrize("P,G", [(37, 3 * 64 + 45), (0, 2 * 64)])
+def test_blockmask_prefill_per_head_quotas(P, G):
+    # a quota per (layer, KV head) (figure captions, Fig. 7): each KV head's
+    # query heads see that head's own kept code rows of earlier blocks
+    C, Kp = 64, 16
+    hq = [[16, 0, 4, 8, 1, 16, 2, 8], [8, 8, 1, 2, 16, 0, 4, 16]]
+    pool = abk.Pool(num_layers=2, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_tokens=C,
+                    num_pause=Kp, layer_quota=[16, 16], page_rows=16, max_seqs=2,
+                    pool_bytes=2 * 16 * D * 2 * 1024, max_position=4096, dtype="bf16", rope_base=1e6,
+                    head_quota=hq)
+    for layer in range(2):
+        Ls = [LayerView(P, C, Kp, q) for q in hq[layer]]
+        kind, a, b, q, k, v = _synth_inputs(Ls[0], G, layer, seed=21 + layer)
+        T = len(kind)
+        out = torch.empty((T, HQ, D), device="cuda", dtype=torch.bfloat16)
+        lse = torch.empty((T, HQ), device="cuda", dtype=torch.float32)
+        pool.blockmask_attention(layer, P, G, dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), out, lse)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.blockmask_prefill_heads(Ls, G, q, _fetcher(Ls[0], G, k, v), oracle.BF16, 1e6)
+        _close(f"per-head prefill out P{P} G{G} L{layer} ({T} rows)", host(out), o_ref, 2e-2)
+        _close(f"per-head prefill lse P{P} G{G} L{layer}", host(lse), l_ref, 1e-3)
+    pool.close()
