@@ -46,7 +46,9 @@ __global__ void __launch_bounds__(512) blockmask_stage_kernel(BlockMaskArgs a) {
   const bf16_t* kin = (const bf16_t*)a.k + (size_t)row * a.Hkv * D;
   const bf16_t* vin = (const bf16_t*)a.v + (size_t)row * a.Hkv * D;
   for (int t = threadIdx.x; t < a.Hkv * (D / 2); t += blockDim.x) {
-    const int hh = t / (D / 2), j = t % (D / 2);
+    // D / 2 = 64 threads per head: a wavefront's head is uniform, so its quota
+    // is one scalar load
+    const int hh = sgpr(t / (D / 2)), j = t % (D / 2);
     const int q = a.quota_h[hh];
     const int pidx = pers ? row : (pause && k < q ? a.prompt + blk * q + k : -1);
     const double x1 = to_f32(kin[hh * D + j]), x2 = to_f32(kin[hh * D + j + D / 2]);
