@@ -884,6 +884,8 @@ def main():
     ap.add_argument("--split-rows", type=int, default=0, help="rows per split-KV work item (0: library default)")
     ap.add_argument("--per-head", action="store_true",
                     help="decode step with quotas per (layer, KV head) of the same layer totals")
+    ap.add_argument("--no-per-head", action="store_true",
+                    help="skip the per-head decode step reported beside the main line")
     ap.add_argument("--separate-append", action="store_true",
                     help="append and decode as two calls per layer (default: abk_append_decode)")
     ap.add_argument("--compress-reps", type=int, default=2)
@@ -945,6 +947,18 @@ def main():
     print(f"[bench] decode workload: 36 layers, 22 sequences, {args.warmup}+{args.steps} steps",
           file=sys.stderr, flush=True)
     res, workload = run_decode(args, torch, abk)
+    per_head = None
+    if not args.per_head and not args.no_per_head:
+        # the same step with quotas per (layer, KV head) of the same layer totals
+        print("[bench] decode step with per-head quotas", file=sys.stderr, flush=True)
+        ph, _ = run_decode(argparse.Namespace(**{**vars(args), "per_head": True}), torch, abk)
+        per_head = {"metric": "decode tokens/s with quotas per (layer, KV head)", "value": ph["value"],
+                    "unit": "tokens/s", "ms_per_step": ph["ms_per_step"],
+                    "vs_per_layer": ph["value"] / res["value"],
+                    "avg_launch_us": ph["roofline"]["avg_launch_us"],
+                    "hbm_gbps": ph["roofline"]["achieved"],
+                    "config": {"workload": ph["config"]["workload"], "quotas": ph["config"]["quotas"],
+                               "resident_kv_gb": ph["config"]["resident_kv_gb"]}}
     comp = None
     if not args.no_compress:
         print("[bench] compression event: 64 sequences x 36 layers", file=sys.stderr, flush=True)
@@ -966,6 +980,7 @@ def main():
         "decode_ms_per_step": res["decode_ms_per_step"],
         "compress_ms_in_timed_steps": res["compress_ms_in_timed_steps"],
         "roofline": res["roofline"], "cpu_baseline": cpu, "compress": comp, "prefill": pre,
+        "per_head": per_head,
     }
     print(json.dumps(line), flush=True)
 
