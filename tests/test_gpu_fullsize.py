@@ -226,3 +226,39 @@ def test_serving_mix_more_sequences_than_one_launch(compress):
             _close(f"mix out seq{i} L{l}", out[i], o_ref, 2e-2)
             _close(f"mix lse seq{i} L{l}", lse[i], l_ref, 1e-3)
     run.pool.close()
+
+
+def test_36_layer_per_head_decode_step_sampled():
+    # the bench's per-head step (quotas per (layer, KV head), bench.head_quotas):
+    # one fused call per layer over the 22 filled sequences, sampled against
+    # the oracle's per-head composition
+    quotas, P, G = bench.decode_workload(2)
+    hq = bench.head_quotas(quotas, 2)
+    B = len(P)
+    pool_bytes = 0
+    for l in range(L):
+        for q in hq[l]:
+            R = P + ((G + 1 - 1) // C) * q + C
+            pool_bytes += int(np.sum(np.ceil(R / PR) + 2 + C // PR)) * 2 * PR * D * 2
+    run = Run(L=L, Hq=HQ, Hkv=HKV, D=D, C=C, Kp=KP, quota=quotas.tolist(), pr=PR, dtype="bf16",
+              max_seqs=B, pool_bytes=pool_bytes, max_position=33792, seed=2, head_quota=hq)
+    sids = [run.new_seq(int(P[i]), i) for i in range(B)]
+    for s, g in zip(sids, G):
+        run.fill(s, int(g))
+    full = [s for s in sids if run.G[s] - run.nb[s] * C == C]
+    if full:
+        run.compress_and_free(full)
+    results = run.step_fused(sids)
+    print(f"[fullsize] 36-layer per-head step: {B} sequences", flush=True)
+    layers = _sample_layers(quotas)
+    for l in range(L):
+        out, lse, q = results[l]
+        assert np.isfinite(out).all() and np.isfinite(lse).all(), l
+        if l in layers:
+            for i in (0, 11, 21):
+                s = sids[i]
+                o_ref, l_ref, keys = run.oracle_decode(s, l, q[i])
+                _close(f"36L per-head decode out seq{i} L{l}", out[i], o_ref, 2e-2)
+                _close(f"36L per-head decode lse seq{i} L{l}", lse[i], l_ref, 1e-3)
+                for h in range(HKV):
+                    assert run.pool.seq_query(s, l * HKV + h)["resident_rows"] == len(keys[h][0]), (i, l, h)
