@@ -160,3 +160,31 @@ def test_budget_pools_compress_then_decode(per_head):
             pages, _ = run.pool.export_layout(s, lv)
             k = levels.index(quotas[lv])
             assert all(sum(budget[:k]) <= p < sum(budget[:k + 1]) for p in pages), (s, lv)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype,pr", [(16, 2, 64, "bf16", 16), (8, 8, 64, "bf16", 32),
+                                               (16, 2, 128, "bf16", 32), (2, 1, 16, "f32", 4)])
+def test_per_head_quotas_other_shapes(Hq, Hkv, D, dtype, pr):
+    # group sizes 8 and 1, d = 64 and 16, 16- and 32-row pages, fp32: the
+    # generic decode and compression kernels over per-head pools
+    C, Kp = 64, 16
+    rng = np.random.default_rng(Hq * 100 + Hkv)
+    hq = [[int(x) for x in rng.choice([0, 1, 2, 4, 8, 16], Hkv)] for _ in range(2)]
+    run = Run(L=2, Hq=Hq, Hkv=Hkv, D=D, C=C, Kp=Kp, quota=[Kp, Kp], pr=pr, dtype=dtype, head_quota=hq,
+              seed=35, max_position=4096, pool_bytes=64 << 20)
+    sids = [run.new_seq(P, i) for i, P in enumerate([3, 0, 20])]
+    for s in sids:
+        run.write_prompts(s)
+    for blk in range(2):
+        run.grow({s: (blk + 1) * C for s in sids})
+        outs = [run.compress_layer(sids, l) for l in range(run.L)]
+        torch.cuda.synchronize()
+        for l, (out, lse) in enumerate(outs):
+            _check_compress(run, sids, l, out, lse)
+        run.pool.free_block(sids)
+        for s in sids:
+            run.nb[s] += 1
+    run.grow({s: 2 * C + 7 for s in sids})
+    for l in range(run.L):
+        out, lse, q = run.decode(sids, l)
+        _check_decode(run, sids, l, out, lse, q)
