@@ -968,8 +968,8 @@ def main():
         profile_summary(args.profile_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
