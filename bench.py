@@ -527,10 +527,11 @@ def run_decode_1layer(args, torch, abk, reps: int = 50):
                                    "64-row pages; 1 GiB read before each timed call", "reps": reps}}
 
 
-def run_compress(args, torch, abk):
+def compress_event(args, torch, abk, layer_pause=None, single_sequence=True):
     """One block-compression event: 64 sequences complete a 512-token block at
     once; pause-token attention + code-row scatter at all 36 layers, then the
-    raw pages are freed."""
+    raw pages are freed. layer_pause None: every layer runs 256 pause tokens
+    and keeps its quota's prefix; else layer l runs layer_pause[l]."""
     rng = np.random.default_rng(3)
     quotas = layer_quotas(2)
     B = 64
@@ -538,21 +539,21 @@ def run_compress(args, torch, abk):
     b = rng.integers(0, 62, B, endpoint=True)
     G = (b + 1) * C
     Kp = 256
+    kps = [Kp] * L if layer_pause is None else [int(x) for x in layer_pause]
     pages = 0
     for l in range(L):
-        R = P + b * quotas[l] + C
         pages += int(np.sum(np.ceil((P + (b + 1) * quotas[l]) / PR) + 1 + C // PR))
     page_bytes = HKV * PR * D * 2
     pool = abk.Pool(num_layers=L, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_tokens=C,
-                    num_pause=Kp, layer_quota=quotas.tolist(), page_rows=PR, max_seqs=B,
-                    pool_bytes=2 * page_bytes * pages, max_position=33792, dtype="bf16",
+                    num_pause=Kp, layer_quota=quotas.tolist(), layer_pause=layer_pause, page_rows=PR,
+                    max_seqs=B, pool_bytes=2 * page_bytes * pages, max_position=33792, dtype="bf16",
                     rope_base=1e6)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(3)
     bf = torch.bfloat16
-    qp = torch.randn((L, B, Kp, HQ, D), device="cuda", dtype=bf, generator=gen)
-    kp = torch.randn((L, B, Kp, HKV, D), device="cuda", dtype=bf, generator=gen)
-    vp = torch.randn((L, B, Kp, HKV, D), device="cuda", dtype=bf, generator=gen)
+    qp = [torch.randn((B, kps[l], HQ, D), device="cuda", dtype=bf, generator=gen) for l in range(L)]
+    kp = [torch.randn((B, kps[l], HKV, D), device="cuda", dtype=bf, generator=gen) for l in range(L)]
+    vp = [torch.randn((B, kps[l], HKV, D), device="cuda", dtype=bf, generator=gen) for l in range(L)]
     out = torch.empty((B, Kp, HQ, D), device="cuda", dtype=bf)
     lse = torch.empty((B, Kp, HQ), device="cuda", dtype=torch.float32)
     times = []
@@ -577,7 +578,7 @@ def run_compress(args, torch, abk):
     # one sequence completing its last block alone (the common serving case):
     # the context of each query tile is split over several workgroups
     single = []
-    for rep in range(0 if args.no_single_sequence else args.compress_reps + 1):
+    for rep in range(args.compress_reps + 1 if single_sequence else 0):
         s = pool.seq_create(int(P[0]))
         pool.synth_fill(s, 63 * C, 3 * 1000003 + 999)
         torch.cuda.synchronize()
@@ -592,16 +593,26 @@ def run_compress(args, torch, abk):
             single.append(e0.elapsed_time(e1))
         pool.seq_release(s)
     pool.close()
-    ms = np.mean([sum(t) for t in times])
+    ms = float(np.mean([sum(t) for t in times]))
     # algorithmic flops: QK^T and PV over context N_l plus the causal pause part
     flops = 0.0
     nbytes = 0.0
     for l in range(L):
         N = P + b * quotas[l] + C
-        flops += float(np.sum(4.0 * HQ * Kp * D * (N + (Kp + 1) / 2.0)))
-        nbytes += float(np.sum(N)) * 2 * HKV * D * 2 + B * Kp * (2 * HQ + 2 * HKV) * D * 2
+        flops += float(np.sum(4.0 * HQ * kps[l] * D * (N + (kps[l] + 1) / 2.0)))
+        nbytes += float(np.sum(N)) * 2 * HKV * D * 2 + B * kps[l] * (2 * HQ + 2 * HKV) * D * 2
+    return {"ms": ms, "flops": flops, "nbytes": nbytes, "B": B, "P0": int(P[0]),
+            "single_ms": float(np.mean(single)) if single else None}
+
+
+def run_compress(args, torch, abk):
+    """The compression event under the default pause reading (256 pause tokens
+    at every layer, each layer keeping its quota's prefix), then the same event
+    with as many pause tokens per layer as its quota."""
+    ev = compress_event(args, torch, abk, single_sequence=not args.no_single_sequence)
+    ms, flops, nbytes, B = ev["ms"], ev["flops"], ev["nbytes"], ev["B"]
     tflops = flops / (ms * 1e-3) / 1e12
-    return {
+    res = {
         "metric": "block compressions/s (64 sequences x 36 layers per event)",
         "events_per_s": 1e3 / ms, "ms_per_event": ms,
         "blocks_per_s": B * 1e3 / ms,
@@ -613,9 +624,18 @@ def run_compress(args, torch, abk):
         "config": {"workload": "block compression, 64 sequences, 36 layers, K=256 pause tokens "
                                "(layer keeps quota prefix)", "prompt": "U[128,512]",
                    "block_index": "U{0..62}"},
-        "single_sequence_ms": float(np.mean(single)) if single else None,
-        "single_sequence": f"one sequence (prompt {int(P[0])}) compressing block 62 alone, 36 layers",
+        "single_sequence_ms": ev["single_ms"],
+        "single_sequence": f"one sequence (prompt {ev['P0']}) compressing block 62 alone, 36 layers",
     }
+    if not args.no_pause_per_layer:
+        a = compress_event(args, torch, abk, layer_pause=layer_quotas(2).tolist(), single_sequence=False)
+        ta = a["flops"] / (a["ms"] * 1e-3) / 1e12
+        res["pause_per_layer"] = {
+            "workload": "the same event with K_l = the layer's quota pause tokens (64/128/256)",
+            "ms_per_event": a["ms"], "blocks_per_s": a["B"] * 1e3 / a["ms"],
+            "tflop_per_event": a["flops"] / 1e12, "achieved_tflops": ta,
+            "frac": ta / BF16_PEAK_TFLOPS}
+    return res
 
 
 def blockmask_visible_keys(P: int, G: int, C: int, Kp: int, q: int, compress: bool = True):
@@ -946,6 +966,8 @@ def main():
     ap.add_argument("--separate-append", action="store_true",
                     help="append and decode as two calls per layer (default: abk_append_decode)")
     ap.add_argument("--compress-reps", type=int, default=2)
+    ap.add_argument("--no-pause-per-layer", action="store_true",
+                    help="skip the compression event with K_l = quota pause tokens per layer")
     ap.add_argument("--no-compress", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-prefill-causal", action="store_true",

@@ -169,6 +169,41 @@ def test_bf16_compress_then_decode_uses_code_rows(pr, C, Kp, quota):
     _check_decode(run, sids, 1)
 
 
+@pytest.mark.parametrize("pr,C,Kp,quota", [COMPRESS_CASES[0], COMPRESS_CASES[2]])
+def test_first_block_compression_with_empty_and_one_row_prompts(pr, C, Kp, quota):
+    """Block 0 compressed with no prompt (the context is the block alone and the
+    pause keys sit at bitrev(k)·C/K) and with a one-row prompt, on the SIMT
+    (16-row pages) and MFMA (64-row pages) paths; then decode over the code rows
+    and the next block's first row."""
+    run = _bf16_run(seed=12, pr=pr, C=C, Kp=Kp, quota=quota, split_rows=0)
+    sids = [run.new_seq(P, i) for i, P in enumerate([0, 1, 0])]
+    for s in sids:
+        run.write_prompts(s)
+    run.grow({s: C for s in sids})
+    outs = [run.compress_layer(sids, l) for l in range(run.L)]
+    torch.cuda.synchronize()
+    for l, (out, lse) in enumerate(outs):
+        out, lse = host(out), host(lse)
+        for i, s in enumerate(sids):
+            o_ref, l_ref, code = run.oracle_compress(s, l)
+            _close(f"compress out seq{s} L{l}", out[i], o_ref, 2e-2)
+            _close(f"compress lse seq{s} L{l}", lse[i], l_ref, 1e-3)
+            q = run.quota[l]
+            assert run.pool.seq_query(s, l)["resident_rows"] == run.P[s] + q + C
+            k = torch.empty((q, run.Hkv, run.D), device="cuda", dtype=torch.bfloat16)
+            v = torch.empty_like(k)
+            run.pool.read_rows(s, l, run.P[s], q, k, v)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(host(v), code[5])
+            np.testing.assert_array_equal(host(k), code[4])
+    run.pool.free_block(sids)
+    for s in sids:
+        run.nb[s] += 1
+    run.grow({s: C + 1 for s in sids})
+    _check_decode(run, sids, 0)
+    _check_decode(run, sids, 1)
+
+
 def test_fill_equals_history_built_through_the_abi():
     run = _bf16_run(seed=3)
     a = run.new_seq(21, 0)
