@@ -633,7 +633,21 @@ abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32
   const int32_t Kp = s.pause[layer * p->hs];
   const int32_t ne = (int32_t)plan.size();
   std::vector<int32_t>& d = p->scratch;
-  d.assign((size_t)ne * abk::kCompRec, 0);
+  // records, then the (entry, KV head) pairs in launch order: longest context
+  // first, so that the short ones fill in behind the long ones at the end of
+  // the launch; then the page lists
+  const int32_t npair = ne * s.Hkv;
+  d.assign((size_t)ne * abk::kCompRec + npair, 0);
+  {
+    std::vector<int32_t> ord(ne);
+    for (int32_t i = 0; i < ne; ++i) ord[i] = i;
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) {
+      return plan[x].pers_before > plan[y].pers_before;
+    });
+    int32_t* o = &d[(size_t)ne * abk::kCompRec];
+    for (int32_t r = 0; r < ne; ++r)
+      for (int32_t h = 0; h < s.Hkv; ++h) o[r * s.Hkv + h] = ord[r] * s.Hkv + h;
+  }
   for (int32_t i = 0; i < ne; ++i) {
     int32_t* r = &d[(size_t)i * abk::kCompRec];
     r[0] = plan[i].slot * s.L + plan[i].layer;  // combined index (flat device view)

@@ -203,14 +203,16 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
   const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
   const bool grp0 = ABK_PP_GROUP(wave) == 0;
-  // workgroup -> (pair = sequence x KV head, query tile, context split); the
-  // workgroups of one pair share blockIdx.x mod 8, i.e. one XCD and its L2
+  // workgroup -> (rank of its pair = sequence x KV head in the launch order,
+  // query tile, context split); the workgroups of one pair share blockIdx.x
+  // mod 8, i.e. one XCD and its L2
   const int ntq = (4 * a.Kp + QR - 1) / QR;
   const int ns = a.nsplit;
   const int npair = a.n * P.Hkv;
   const int b = blockIdx.x, xcd = b & 7, jj = b >> 3;
-  const int pair = (jj / (ntq * ns)) * 8 + xcd, qt = (jj % (ntq * ns)) / ns, sp = jj % ns;
-  if (pair >= npair) return;
+  const int rank = (jj / (ntq * ns)) * 8 + xcd, qt = (jj % (ntq * ns)) / ns, sp = jj % ns;
+  if (rank >= npair) return;
+  const int pair = sgpr(a.desc[a.n * kCompRec + rank]);  // pairs in launch order
   const int i = pair / P.Hkv, hk = pair % P.Hkv;
   // the caller's sequence and KV head of this pair
   const int ir = i / a.hsplit, H = (i % a.hsplit) * P.Hkv + hk, HkvR = P.Hkv * a.hsplit;

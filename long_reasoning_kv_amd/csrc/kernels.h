@@ -98,6 +98,8 @@ constexpr int kCompressRows = 256;
 // (hsplit = the caller's KV heads, the pool's P.Hkv = 1): entry i is then the
 // caller's sequence i / hsplit, KV heads (i % hsplit) * P.Hkv + 0..P.Hkv-1.
 // The caller's q/k/v/out/lse keep their [sequence][pause][head][D] layouts.
+// The records are followed by the n * P.Hkv pairs (entry * P.Hkv + KV head) in
+// the order the MFMA kernel launches them, then by the page lists.
 constexpr int kCompRec = 8;
 struct CompressArgs {
   DevPool P;
@@ -107,7 +109,7 @@ struct CompressArgs {
   void* out;
   float* lse;
   void* kp_rot;          // workspace [n][P.Hkv][Kp][D]: rotated pause keys
-  const int32_t* desc;   // n records, then page lists
+  const int32_t* desc;   // n records, the pairs in launch order, then page lists
   float* part;           // nsplit > 1: [n][P.Hkv][query tiles][nsplit][kCompressRows][D + 2] partials
   int32_t layer, n, hsplit, Hq, G, Kp, log2Kp;  // Hq: the caller's query heads
   int32_t nsplit;        // MFMA path: context splits per query tile (1 = none)
