@@ -234,13 +234,20 @@ abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_le
 abk_status abk_prefill_prompt(abk_pool* p, int32_t seq_id, int32_t layer, const void* q, const void* k,
                               const void* v, void* out, float* lse);
 
-/* Pool-wide counters. resident_bytes = K+V bytes of resident rows. */
-/* Pages of budget level `level` (0 .. levels-1; with no separate pools, level
- * 0 is the one pool and *quota is -1): its quota value, pages in use and
- * pages free. *levels (optional) receives the number of levels. Errors:
- * INVALID_ARG (level out of range). */
+/* Occupancy of one budget level's page pool (the AI Radio episode on
+ * AbridgeKV: the serving engine keeps a separate pool of pages for each
+ * budget level; pools are configured by abk_pool_config.budget_pool_pages).
+ * Level `level` is 0 .. levels-1 in ascending quota order; with no separate
+ * pools, level 0 is the one pool and *quota is -1. Writes its quota value,
+ * pages in use and pages free (host counters, no stream work); *levels
+ * receives the number of levels, also when `level` is out of range. Any
+ * output pointer may be NULL. Errors: INVALID_ARG (NULL pool, level out of
+ * range). */
 abk_status abk_budget_pool_stats(const abk_pool* p, int32_t level, int32_t* levels, int32_t* quota,
                                  int64_t* pages_used, int64_t* pages_free);
+
+/* Pool-wide counters (host, no stream work): pages in use and free over all
+ * levels; resident_bytes = K+V bytes of resident rows. */
 abk_status abk_pool_stats(const abk_pool* p, int64_t* pages_used, int64_t* pages_free,
                           int64_t* resident_bytes);
 
