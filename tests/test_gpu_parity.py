@@ -204,6 +204,57 @@ def test_first_block_compression_with_empty_and_one_row_prompts(pr, C, Kp, quota
     _check_decode(run, sids, 1)
 
 
+@pytest.mark.parametrize("pr", [16, 64])
+def test_pause_count_per_layer_matches_oracle_and_max_count_reading(pr):
+    """Layer l runs as many pause tokens as its quota (K_l = 64, 16, 32), on the
+    SIMT (16-row pages) and MFMA (64-row pages) paths: out, lse and code rows
+    against the oracle. A twin pool runs every layer with K = 64 and keeps the
+    quota prefix: pause k < q_l sits at the same position either way (the bit
+    reversal of a power-of-two prefix) and sees the same keys, so the code rows
+    and positions are bit-identical and the kept tokens' outputs agree."""
+    quota = [64, 16, 32]
+    kw = dict(seed=13, L=3, pr=pr, C=128, Kp=64, quota=quota, split_rows=0)
+    runs = [_bf16_run(pause=quota, **kw), _bf16_run(**kw)]
+    res = []
+    for run in runs:
+        sids = [run.new_seq(P, i) for i, P in enumerate([9, 0, 70])]
+        for s in sids:
+            run.write_prompts(s)
+        run.grow({s: 2 * 128 for s in sids})
+        res.append((sids, [run.compress_layer(sids, l) for l in range(run.L)]))
+    torch.cuda.synchronize()
+    (ra, rb), ((sa, oa), (sb, ob)) = runs, res
+    for l, q in enumerate(quota):
+        out_a, lse_a = host(oa[l][0]), host(oa[l][1])
+        out_b, lse_b = host(ob[l][0]), host(ob[l][1])
+        assert out_a.shape[1] == q and out_b.shape[1] == 64
+        for i, (s, t) in enumerate(zip(sa, sb)):
+            o_ref, l_ref, code = ra.oracle_compress(s, l)
+            _close(f"K_l out seq{s} L{l}", out_a[i], o_ref, 2e-2)
+            _close(f"K_l lse seq{s} L{l}", lse_a[i], l_ref, 1e-3)
+            _close(f"K_l vs K=64 out seq{s} L{l}", out_a[i], out_b[i][:q], 2e-2)
+            _close(f"K_l vs K=64 lse seq{s} L{l}", lse_a[i], lse_b[i][:q], 1e-3)
+            n = ra.pool.seq_query(s, l)["resident_rows"]
+            assert n == rb.pool.seq_query(t, l)["resident_rows"]
+            assert ra.pool.export_layout(s, l)[1] == rb.pool.export_layout(t, l)[1]
+            r0 = n - 128 - q
+            ka = torch.empty((q, ra.Hkv, ra.D), device="cuda", dtype=torch.bfloat16)
+            va, kb, vb = torch.empty_like(ka), torch.empty_like(ka), torch.empty_like(ka)
+            ra.pool.read_rows(s, l, r0, q, ka, va)
+            rb.pool.read_rows(t, l, r0, q, kb, vb)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(host(ka), code[4])
+            np.testing.assert_array_equal(host(va), code[5])
+            assert torch.equal(ka, kb) and torch.equal(va, vb)
+    for run, sids in ((ra, sa), (rb, sb)):
+        run.pool.free_block(sids)
+        for s in sids:
+            run.nb[s] += 1
+        run.grow({s: 2 * 128 + 1 for s in sids})
+    for l in range(3):
+        _check_decode(ra, sa, l)
+
+
 def test_fill_equals_history_built_through_the_abi():
     run = _bf16_run(seed=3)
     a = run.new_seq(21, 0)
