@@ -14,45 +14,61 @@ namespace abk {
 // ---- a4 + a6: pause RoPE at bit-reversed in-block positions, code-row scatter ----
 
 
+// One thread per (pause token, KV head, 16-byte group of each half row): it
+// rotates the group's pairs (d, d + D/2) in fp64 and writes them, rounded once,
+// to the workspace and, for a kept token, with its value to the code row.
+// kpb pause tokens per workgroup.
 template <typename T, int D>
-__global__ void __launch_bounds__(1024) pause_rope_scatter_kernel(CompressArgs a) {
+__global__ void __launch_bounds__(256) pause_rope_scatter_kernel(CompressArgs a, int kpb) {
+  constexpr int V = 16 / sizeof(T), NJ = D / 2 / V;
+  static_assert(NJ * V * 2 == D, "a half row is a whole number of 16-byte groups");
   const DevPool& P = a.P;
-  const int k = blockIdx.x, i = blockIdx.y;
+  const int i = blockIdx.y;
   const int32_t* rec = a.desc + i * kCompRec;
   const int slot = rec[0], blk = rec[1], pers_before = rec[2], prompt = rec[3];
   const int pages_off = rec[4], npages = rec[5], first_new = rec[6], quota = rec[7];
-  const int pos = prompt + blk * P.C + bitrev_dev(k, a.log2Kp) * (P.C / a.Kp);
   // the caller's sequence and first KV head of this entry
   const int ir = i / a.hsplit, H0 = (i % a.hsplit) * P.Hkv, HkvR = P.Hkv * a.hsplit;
-  const T* kin = (const T*)a.kp + (((size_t)ir * a.Kp + k) * HkvR + H0) * D;
-  const T* vin = (const T*)a.vp + (((size_t)ir * a.Kp + k) * HkvR + H0) * D;
-  const double2* rope = P.rope + (size_t)pos * (D / 2);
-  const bool keep = k < quota;
-  int page = 0, srow = 0;
-  if (keep) {
-    const int row = pers_before + k;
-    page = a.desc[pages_off + row / P.pr - pers_before / P.pr];
-    srow = row % P.pr;
-  }
-  for (int t = threadIdx.x; t < P.Hkv * (D / 2); t += blockDim.x) {
-    const int hh = t / (D / 2), j = t % (D / 2);
-    const double x1 = to_f32(kin[hh * D + j]), x2 = to_f32(kin[hh * D + j + D / 2]);
-    const double2 cs = rope[j];
-    const T y1 = from_f64<T>(rot_first(x1, x2, cs));
-    const T y2 = from_f64<T>(rot_second(x1, x2, cs));
+  const int per_k = P.Hkv * NJ;
+  for (int t = threadIdx.x; t < kpb * per_k; t += blockDim.x) {
+    const int k = blockIdx.x * kpb + t / per_k;
+    if (k >= a.Kp) break;
+    const int hh = (t % per_k) / NJ, j0 = (t % NJ) * V;
+    const int pos = prompt + blk * P.C + bitrev_dev(k, a.log2Kp) * (P.C / a.Kp);
+    const size_t in_row = (((size_t)ir * a.Kp + k) * HkvR + H0 + hh) * D;
+    const T* kin = (const T*)a.kp + in_row;
+    const double2* rope = P.rope + (size_t)pos * (D / 2) + j0;
+    T x1[V], x2[V], y1[V], y2[V];
+    const uint4 w1 = *(const uint4*)(kin + j0), w2 = *(const uint4*)(kin + D / 2 + j0);
+    __builtin_memcpy(x1, &w1, 16);
+    __builtin_memcpy(x2, &w2, 16);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const double2 cs = rope[e];
+      const double a1 = to_f32(x1[e]), a2 = to_f32(x2[e]);
+      y1[e] = from_f64<T>(rot_first(a1, a2, cs));
+      y2[e] = from_f64<T>(rot_second(a1, a2, cs));
+    }
+    uint4 o1, o2;
+    __builtin_memcpy(&o1, y1, 16);
+    __builtin_memcpy(&o2, y2, 16);
     T* kr = (T*)a.kp_rot + (((size_t)i * P.Hkv + hh) * a.Kp + k) * D;
-    kr[j] = y1;
-    kr[j + D / 2] = y2;
-    if (keep) {
+    *(uint4*)(kr + j0) = o1;
+    *(uint4*)(kr + D / 2 + j0) = o2;
+    if (k < quota) {
+      const int row = pers_before + k;
+      const int page = a.desc[pages_off + row / P.pr - pers_before / P.pr];
+      const int srow = row % P.pr;
       const size_t o = (((size_t)page * P.Hkv + hh) * P.pr + srow) * D;
-      ((T*)P.kpool)[o + j] = y1;
-      ((T*)P.kpool)[o + j + D / 2] = y2;
-      ((T*)P.vpool)[o + j] = vin[hh * D + j];
-      ((T*)P.vpool)[o + j + D / 2] = vin[hh * D + j + D / 2];
+      const T* vin = (const T*)a.vp + in_row;
+      *(uint4*)((T*)P.kpool + o + j0) = o1;
+      *(uint4*)((T*)P.kpool + o + D / 2 + j0) = o2;
+      *(uint4*)((T*)P.vpool + o + j0) = *(const uint4*)(vin + j0);
+      *(uint4*)((T*)P.vpool + o + D / 2 + j0) = *(const uint4*)(vin + D / 2 + j0);
+      if (hh == 0 && j0 == 0) P.pos[(size_t)page * P.pr + srow] = pos;
     }
   }
-  if (keep && threadIdx.x == 0) P.pos[(size_t)page * P.pr + srow] = pos;
-  if (k == 0 && threadIdx.x == 0) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
     int32_t* tab = ptab_of(P, slot, a.layer);
     const int first_idx = pers_before / P.pr;
     for (int j = first_new; j < npages; ++j) tab[first_idx + j] = a.desc[pages_off + j];
@@ -536,10 +552,14 @@ bool compress_mfma_supported(const DevPool& P, int32_t G) {
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
-  const int th = threads_for(a.P.Hkv, a.P.D);
   const bool mfma = a.P.dtype == 1 && a.P.D == 128 && a.G == 4 && a.P.pr == 64;
   ABK_DISPATCH_TD(a.P.dtype, a.P.D, {
-    hipLaunchKernelGGL((pause_rope_scatter_kernel<T, DD>), dim3(a.Kp, a.n), dim3(th), 0, s, a);
+    const int per_k = a.P.Hkv * (DD / 2) / (16 / (int)sizeof(T));
+    // fewer pause tokens per workgroup when the grid would be small
+    int kpb = per_k >= 256 ? 1 : 256 / per_k;
+    while (kpb > 1 && (int64_t)((a.Kp + kpb - 1) / kpb) * a.n < 1024) kpb >>= 1;
+    hipLaunchKernelGGL((pause_rope_scatter_kernel<T, DD>), dim3((a.Kp + kpb - 1) / kpb, a.n), dim3(256), 0,
+                       s, a, kpb);
     if (!mfma)
       hipLaunchKernelGGL((compress_attn_simt_kernel<T, DD>), dim3(a.Kp, a.P.Hkv * a.G, a.n), dim3(64), 0,
                          s, a);
