@@ -18,12 +18,18 @@ namespace abk {
 
 // ---- staging: every key rotated once, values copied, persistent rows gathered ----
 //
-// Workgroup = one row of the sequence; thread (head, j) rotates the dimension
-// pair (j, j + D/2) in fp64 and rounds once to bf16, like every stored key.
+// Workgroup = kStageRows rows of the sequence; wavefront w takes KV heads w,
+// w + 8, ... (so a head's quota is one scalar load), lane (row r, group g)
+// the 16-byte group g of each half of row r: it rotates the group's dimension
+// pairs (j, j + D/2) in fp64 and rounds once to bf16, like every stored key.
+constexpr int kStageRows = 8;
 __global__ void __launch_bounds__(512) blockmask_stage_kernel(BlockMaskArgs a) {
-  constexpr int D = 128;
+  constexpr int D = 128, V = 8, NJ = D / 2 / V;
+  static_assert(kStageRows * NJ == 64, "one wavefront covers the workgroup's rows of one head");
   const DevPool& P = a.P;
-  const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
+  const int row = blockIdx.x * kStageRows + lane / NJ, j0 = (lane % NJ) * V;
+  if (row >= a.T) return;
   // a prompt row, and a pause row k < its head's quota (a kept code row), is
   // also one of the head's persistent rows, at index pidx
   int pos, blk = 0, k = 0;
@@ -42,33 +48,39 @@ __global__ void __launch_bounds__(512) blockmask_stage_kernel(BlockMaskArgs a) {
       pos = a.prompt + blk * a.C + bitrev_dev(k, a.log2Kp) * (a.C / a.Kp);
     }
   }
-  const double2* rope = P.rope + (size_t)pos * (D / 2);
-  const bf16_t* kin = (const bf16_t*)a.k + (size_t)row * a.Hkv * D;
-  const bf16_t* vin = (const bf16_t*)a.v + (size_t)row * a.Hkv * D;
-  for (int t = threadIdx.x; t < a.Hkv * (D / 2); t += blockDim.x) {
-    // D / 2 = 64 threads per head: a wavefront's head is uniform, so its quota
-    // is one scalar load
-    const int hh = sgpr(t / (D / 2)), j = t % (D / 2);
+  const double2* rope = P.rope + (size_t)pos * (D / 2) + j0;
+  for (int hh = wave; hh < a.Hkv; hh += blockDim.x / 64) {
     const int q = a.quota_h[hh];
     const int pidx = pers ? row : (pause && k < q ? a.prompt + blk * q + k : -1);
-    const double x1 = to_f32(kin[hh * D + j]), x2 = to_f32(kin[hh * D + j + D / 2]);
-    const double2 cs = rope[j];
-    const bf16_t y1 = from_f64<bf16_t>(rot_first(x1, x2, cs));
-    const bf16_t y2 = from_f64<bf16_t>(rot_second(x1, x2, cs));
-    const bf16_t v1 = vin[hh * D + j], v2 = vin[hh * D + j + D / 2];
-    bf16_t* ks = (bf16_t*)a.kst + ((size_t)hh * a.T + row) * D;
-    bf16_t* vs = (bf16_t*)a.vst + ((size_t)hh * a.T + row) * D;
-    ks[j] = y1;
-    ks[j + D / 2] = y2;
-    vs[j] = v1;
-    vs[j + D / 2] = v2;
+    const size_t in = ((size_t)row * a.Hkv + hh) * D;
+    const uint4 kw1 = *(const uint4*)((const bf16_t*)a.k + in + j0);
+    const uint4 kw2 = *(const uint4*)((const bf16_t*)a.k + in + D / 2 + j0);
+    const uint4 vw1 = *(const uint4*)((const bf16_t*)a.v + in + j0);
+    const uint4 vw2 = *(const uint4*)((const bf16_t*)a.v + in + D / 2 + j0);
+    bf16_t x1[V], x2[V], y1[V], y2[V];
+    __builtin_memcpy(x1, &kw1, 16);
+    __builtin_memcpy(x2, &kw2, 16);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const double2 cs = rope[e];
+      const double a1 = to_f32(x1[e]), a2 = to_f32(x2[e]);
+      y1[e] = from_f64<bf16_t>(rot_first(a1, a2, cs));
+      y2[e] = from_f64<bf16_t>(rot_second(a1, a2, cs));
+    }
+    uint4 kr1, kr2;
+    __builtin_memcpy(&kr1, y1, 16);
+    __builtin_memcpy(&kr2, y2, 16);
+    const size_t st = ((size_t)hh * a.T + row) * D;
+    *(uint4*)((bf16_t*)a.kst + st + j0) = kr1;
+    *(uint4*)((bf16_t*)a.kst + st + D / 2 + j0) = kr2;
+    *(uint4*)((bf16_t*)a.vst + st + j0) = vw1;
+    *(uint4*)((bf16_t*)a.vst + st + D / 2 + j0) = vw2;
     if (pidx >= 0) {
-      bf16_t* kp = (bf16_t*)a.kpers + ((size_t)hh * a.npers + pidx) * D;
-      bf16_t* vp = (bf16_t*)a.vpers + ((size_t)hh * a.npers + pidx) * D;
-      kp[j] = y1;
-      kp[j + D / 2] = y2;
-      vp[j] = v1;
-      vp[j + D / 2] = v2;
+      const size_t pp = ((size_t)hh * a.npers + pidx) * D;
+      *(uint4*)((bf16_t*)a.kpers + pp + j0) = kr1;
+      *(uint4*)((bf16_t*)a.kpers + pp + D / 2 + j0) = kr2;
+      *(uint4*)((bf16_t*)a.vpers + pp + j0) = vw1;
+      *(uint4*)((bf16_t*)a.vpers + pp + D / 2 + j0) = vw2;
     }
   }
 }
@@ -232,7 +244,7 @@ bool blockmask_supported(const DevPool& P, int32_t G) { return P.dtype == 1 && P
 
 hipError_t launch_blockmask(const BlockMaskArgs& a, int32_t nrec, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(blockmask_stage_kernel, dim3(a.T), dim3(512), 0, s, a);
+  hipLaunchKernelGGL(blockmask_stage_kernel, dim3((a.T + kStageRows - 1) / kStageRows), dim3(512), 0, s, a);
   if (nrec > 0) hipLaunchKernelGGL(blockmask_attn_mfma_kernel, dim3(nrec), dim3(256), 0, s, a);
   return hipGetLastError();
 }
