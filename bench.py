@@ -968,7 +968,9 @@ def main():
     ap.add_argument("--compress-reps", type=int, default=2)
     ap.add_argument("--no-pause-per-layer", action="store_true",
                     help="skip the compression event with K_l = quota pause tokens per layer")
-    ap.add_argument("--no-compress", action="store_true")
+    ap.add_argument("--no-compress", action="store_true",
+                    help="skip the compression event and the one-layer decode call (the decode "
+                         "step alone, as the decode profile runs it)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-prefill-causal", action="store_true",
                     help="skip the plain-causal comparison of the prefill (profiled runs)")
