@@ -255,6 +255,36 @@ def test_pause_count_per_layer_matches_oracle_and_max_count_reading(pr):
         _check_decode(ra, sa, l)
 
 
+def test_pause_count_equal_to_block_at_c512():
+    """The largest pause count the pool accepts at the bench's block size: K = C
+    = 512 pause tokens (eight 256-row query tiles, eight pause-key tiles, every
+    pause at its own text position), quota 512, on the MFMA path; then decode
+    over the 512 code rows and the next block's first row."""
+    run = _bf16_run(seed=14, L=1, pr=64, C=512, Kp=512, quota=[512], split_rows=0)
+    sids = [run.new_seq(P, i) for i, P in enumerate([3, 0])]
+    for s in sids:
+        run.write_prompts(s)
+    run.grow({s: 512 for s in sids})
+    out, lse = run.compress_layer(sids, 0)
+    torch.cuda.synchronize()
+    out, lse = host(out), host(lse)
+    for i, s in enumerate(sids):
+        o_ref, l_ref, code = run.oracle_compress(s, 0)
+        _close(f"K=C=512 out seq{s}", out[i], o_ref, 2e-2)
+        _close(f"K=C=512 lse seq{s}", lse[i], l_ref, 1e-3)
+        k = torch.empty((512, run.Hkv, run.D), device="cuda", dtype=torch.bfloat16)
+        v = torch.empty_like(k)
+        run.pool.read_rows(s, 0, run.P[s], 512, k, v)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(k), code[4])
+        np.testing.assert_array_equal(host(v), code[5])
+    run.pool.free_block(sids)
+    for s in sids:
+        run.nb[s] += 1
+    run.grow({s: 513 for s in sids})
+    _check_decode(run, sids, 0)
+
+
 def test_fill_equals_history_built_through_the_abi():
     run = _bf16_run(seed=3)
     a = run.new_seq(21, 0)
