@@ -35,6 +35,8 @@ PROMPT, TEXT, PAUSE = 0, 1, 2
 F32, BF16 = 0, 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liborc.so")
+# a build of the same source with other flags (the sanitizer test's) may stand in
+_LOAD_PATH = os.environ.get("ABK_ORACLE_LIB") or _LIB_PATH
 _lib = None
 
 
@@ -57,9 +59,9 @@ class _Layer(ctypes.Structure):
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        if _LOAD_PATH == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build()
-        L = ctypes.CDLL(_LIB_PATH)
+        L = ctypes.CDLL(_LOAD_PATH)
         i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
         lp = ctypes.POINTER(_Layer)
         L.orc_bitrev.argtypes = [i32, i32]
