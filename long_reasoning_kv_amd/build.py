@@ -22,9 +22,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+def build(verbose: bool = False, out: str = LIB) -> str:
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-o", tmp] + \
+    cmd = [HIPCC, *FLAGS, "-o", tmp] + \
         [os.path.join(HERE, s) for s in SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)

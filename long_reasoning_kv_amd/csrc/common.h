@@ -155,7 +155,7 @@ __device__ __forceinline__ double rope_elem(F x, int d, const double2* rope_row)
 
 __device__ __forceinline__ int sgpr(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// a3: merge the split partials of one (sequence, KV head): weights
+// Merge the split partials of one (sequence, KV head): weights
 // exp2(m_s - M) / L per (split, query head) in LDS, then every output element
 // is one weighted sum over the splits.
 template <typename T, int D, int G>

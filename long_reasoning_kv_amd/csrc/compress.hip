@@ -1,4 +1,4 @@
-// Block compression of the AbridgeKV hot path (steps a4-a6): pause queries
+// Block compression of the AbridgeKV hot path: pause queries
 // and keys are rotated at their in-block bit-reversed positions (Fig. 2(b) of
 // arXiv 2610.20641), attend under the block mask (Fig. 2(a)) to the prompt,
 // retained code rows, the whole block and earlier pause keys, and the kept
@@ -11,7 +11,7 @@
 
 namespace abk {
 
-// ---- a4 + a6: pause RoPE at bit-reversed in-block positions, code-row scatter ----
+// ---- pause RoPE at bit-reversed in-block positions, code-row scatter -----------
 
 
 // One thread per (pause token, KV head, 16-byte group of each half row): it
@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(256) pause_rope_scatter_kernel(CompressArgs a,
   }
 }
 
-// ---- a5: pause-token attention under the block mask (SIMT form) -------------------
+// ---- pause-token attention under the block mask (SIMT form) -----------------------
 //
 // One wavefront per (entry, pause j, query head of the entry). Keys: the sequence's
 // resident rows at this layer (prompt, earlier code rows, the whole block)
@@ -182,7 +182,8 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
   if (lane == 0) a.lse[((size_t)ir * a.Kp + j) * a.Hq + HQ] = (m + __log2f(l)) * 0.6931471805599453f;
 }
 
-// ---- a5 on bf16 MFMA (d = 128, four query heads per KV head, 64-row pages) -------
+// ---- pause-token attention on bf16 MFMA (d = 128, four query heads per KV head,
+// 64-row pages) ------------------------------------------------------------------
 //
 // Workgroup = (sequence, KV head, tile of 256 query rows); query row r is pause
 // r/4, head 4h + r%4. Each of the 8 wavefronts owns 32 query rows and runs the
@@ -205,10 +206,6 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
 // buffer is read from phase 2u to 2u+3, and the load into it is issued at
 // phase 2u-4, after the barrier that ends its previous tile's last read.
 
-#ifndef ABK_PP_GROUP
-#define ABK_PP_GROUP(w) ((w) >> 2)  // wavefronts w and w + 4 share a SIMD
-#endif
-
 __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs a) {
   constexpr int D = 128, G = 4, TK = kTileKeys, RB = D * 2, QR = kCompressRows;
   constexpr int TCH = TK * RB / 16;  // 16-byte chunks of a 64-row K (or V) tile
@@ -218,7 +215,7 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
   const DevPool& P = a.P;
   const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  const bool grp0 = ABK_PP_GROUP(wave) == 0;
+  const bool grp0 = wave < 4;  // wavefronts w and w + 4 share a SIMD
   // workgroup -> (rank of its pair = sequence x KV head in the launch order,
   // query tile, context split); the workgroups of one pair share blockIdx.x
   // mod 8, i.e. one XCD and its L2

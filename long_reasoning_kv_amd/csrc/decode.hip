@@ -1,7 +1,7 @@
-// Decode attention of the AbridgeKV hot path (steps a2 and a3): the current
-// token of each sequence attends to its resident rows (prompt, code rows of
-// finished blocks, the open block) through the per-(sequence, layer) page
-// table. See the pages on AbridgeKV (arXiv 2610.20641): the abstract and
+// Decode attention of the AbridgeKV hot path (split-KV partials and their
+// combine): the current token of each sequence attends to its resident rows
+// (prompt, code rows of finished blocks, the open block) through the
+// per-(sequence, layer) page table. See the pages on AbridgeKV (arXiv 2610.20641): the abstract and
 // Fig. 1 captions (what stays resident), Fig. 2(a) (text tokens see the
 // prompt, earlier code rows and their own block).
 #include <hip/hip_runtime.h>
@@ -11,7 +11,7 @@
 
 namespace abk {
 
-// ---- a2 + a3: split-KV decode ----------------------------------------------------
+// ---- split-KV decode and merge --------------------------------------------------
 //
 // Work item (sequence i, split s) x KV head h. A split is a run of pages; a page
 // is cut into units of RW rows and wavefront w takes units w, w+4, ... so all
@@ -24,16 +24,12 @@ namespace abk {
 // and wavefronts at the end; a sequence with several splits leaves partials
 // (o, m, l) for the merge kernel.
 
-#ifndef ABK_UNIT_ROWS
-#define ABK_UNIT_ROWS 16  // rows of a page a wavefront reads per step
-#endif
-#ifndef ABK_PREFETCH_UNITS
-#define ABK_PREFETCH_UNITS 1  // units a wavefront keeps in flight while computing one
-#endif
+constexpr int kUnitRows = 16;      // rows of a page a wavefront reads per step
+constexpr int kPrefetchUnits = 1;  // units a wavefront keeps in flight while computing one
 template <typename T, int D>
 struct UnitCfg {
   using R = RowCfg<T, D>;
-  static constexpr int CW = R::RPL >= ABK_UNIT_ROWS ? 1 : ABK_UNIT_ROWS / R::RPL;  // loads/lane
+  static constexpr int CW = R::RPL >= kUnitRows ? 1 : kUnitRows / R::RPL;  // loads/lane
   static constexpr int RW = CW * R::RPL;                                            // rows/unit
 };
 
@@ -173,7 +169,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   };
 
   // ring of NB unit buffers: NB-1 units are in flight while one is computed
-  constexpr int NB = ABK_PREFETCH_UNITS + 1;
+  constexpr int NB = kPrefetchUnits + 1;
   uint4 kb[NB][CW], vb[NB][CW];
   size_t offb[NB];
   int nvb[NB];
@@ -254,7 +250,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// ---- a2, bf16 and d = 128: the streaming kernel -------------------------------------
+// ---- bf16 and d = 128: the streaming kernel ------------------------------------------
 //
 // Same work items and output as decode_split_kernel, shaped for CDNA4's VALU:
 //  - 8 lanes per row; lane c holds dims [8c, 8c+8) and [64+8c, 64+8c+8), i.e.
@@ -496,7 +492,7 @@ __global__ void __launch_bounds__(256) decode_bf16_d128_kernel(DecodeArgs a) {
   }
 }
 
-// ---- a2, bf16, d = 128, four query heads per KV head: LDS-staged streaming -------
+// ---- bf16, d = 128, four query heads per KV head: LDS-staged streaming -----------
 //
 // The workgroup streams a split's pages in units of 32 rows: every thread loads
 // its 16-byte pieces of a later unit's K and V into registers (two stages in
@@ -733,7 +729,7 @@ __global__ void __launch_bounds__(256) decode_bf16_d128_g4_kernel(DecodeArgs a) 
   }
 }
 
-// ---- a2 + a3, persistent stream-K form of the kernel above ------------------------
+// ---- persistent stream-K form of the kernel above ----------------------------------
 //
 // One resident wave of workgroups; workgroup w walks flattened units
 // [w*T, (w+1)*T), which cover one or a few (sequence, KV head) segments. Per
@@ -1019,7 +1015,7 @@ __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) 
   }
 }
 
-// ---- a2 + a3 on bf16 MFMA: wavefront-level stream-K over 32-row tiles ------------
+// ---- decode on bf16 MFMA: wavefront-level stream-K over 32-row tiles -------------
 //
 // Every wavefront is an independent stream over an equal run of the flattened
 // (sequence, KV head, 32-row tile) work, so no barrier is needed anywhere. A
@@ -1384,7 +1380,6 @@ static void decode_bf16_d128(const DecodeArgs& a, int32_t total, hipStream_t s) 
 
 hipError_t launch_decode(const DecodeArgs& a, int32_t total_work, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
-#ifndef ABK_DECODE_GENERIC_ONLY
   if (a.P.dtype == 1 && a.P.D == 128 && a.G == 4 && (a.P.pr == 32 || a.P.pr == 64)) {
     const dim3 grid(total_work, a.P.Hkv);
     if (a.P.pr == 64)
@@ -1406,7 +1401,6 @@ hipError_t launch_decode(const DecodeArgs& a, int32_t total_work, hipStream_t s)
     }
     return hipGetLastError();
   }
-#endif
   ABK_DISPATCH_TD(a.P.dtype, a.P.D, return decode_g<T, DD>(a, total_work, s));
   return hipSuccess;
 }

@@ -1,12 +1,13 @@
 // HIP kernels of the AbridgeKV cache bookkeeping on the device: the append
-// of the current token (step a1), the device view of a freed block (a7),
+// of the current token, the device view of a freed block,
 // prompt rows, synthetic bulk fills and inspection.
 //
 // What is computed follows the pages on AbridgeKV (arXiv 2610.20641): the
 // abstract and Fig. 1(a) (code rows written by pause tokens, raw block rows
 // freed), Fig. 2(a) (the block mask) and Fig. 2(b) (pause token k of block b
 // at position P + b*C + bitrev(k)*C/K). RoPE is rotate-half; stored keys are
-// rotated once, in fp32, and rounded to the pool dtype.
+// rotated in fp64 from the fp64 cos/sin table and rounded once to the pool
+// dtype.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,7 +16,7 @@
 
 namespace abk {
 
-// ---- a1: append the current token (RoPE k at its position, write k and v) ----
+// ---- append the current token (RoPE k at its position, write k and v) ----------
 
 template <typename T, int D>
 __global__ void __launch_bounds__(1024) append_kernel(AppendArgs a) {
@@ -56,7 +57,7 @@ __global__ void __launch_bounds__(1024) append_kernel(AppendArgs a) {
   }
 }
 
-// ---- a7: the open block's rows leave the device view -----------------------------
+// ---- free: the open block's rows leave the device view ---------------------------
 
 __global__ void free_kernel(FreeArgs a) {
   const int i = blockIdx.x;
