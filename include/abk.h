@@ -116,9 +116,16 @@ typedef struct {
 } abk_seq_info;
 
 /* Create a pool: page storage, per-(sequence, layer) page tables, RoPE table.
- * Page layout: K pages [page][kv_head][page_rows][d] and V pages likewise,
- * plus an int32 position per (page, row). hip_stream: a hipStream_t (NULL =
- * default stream). Errors: INVALID_ARG (config), HIP (allocation). */
+ * Each layer has its own budget of code rows per finished block, layer_quota
+ * (news write-up, the second of its three details, and figure captions,
+ * Fig. 6(b): the six most valuable layers keep 256 rows, the twelve least
+ * valuable 64, the rest 128, a mean of 128). A (sequence, layer) holds the
+ * prompt, its code rows and the open block's raw rows (AI Radio transcript:
+ * the resident cache, and a fixed budget per layer whose unkept rows are
+ * never allocated), in two page lists: persistent (prompt, then code rows)
+ * and open. Page layout: K pages [page][kv_head][page_rows][d] and V pages
+ * likewise, plus an int32 position per (page, row). hip_stream: a hipStream_t
+ * (NULL = default stream). Errors: INVALID_ARG (config), HIP (allocation). */
 abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_pool** out);
 /* Synchronises the stream, then frees everything the pool owns. */
 abk_status abk_pool_destroy(abk_pool* p);
@@ -135,7 +142,7 @@ abk_status abk_seq_release(abk_pool* p, int32_t seq_id);
 abk_status abk_write_prompt(abk_pool* p, int32_t seq_id, int32_t layer, const void* k,
                             const void* v);
 
-/* Step a1: append the current token of each sequence at one layer. k, v
+/* Append the current token of each sequence at one layer. k, v
  * [n, Hkv, d] device (k pre-RoPE); the row lands at position P + G (G counted
  * before the call) in the open block (compress) or after the persistent rows
  * (full-KV); a new page is taken when the row starts one. seq_ids: host array
@@ -144,8 +151,13 @@ abk_status abk_write_prompt(abk_pool* p, int32_t seq_id, int32_t layer, const vo
 abk_status abk_append_kv(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
                          const void* k, const void* v);
 
-/* Steps a2+a3: GQA decode attention of the current token of each sequence at
- * one layer, over its resident rows (prompt, code rows, open block).
+/* GQA decode attention of the current token of each sequence at one layer,
+ * over its resident rows: the prompt, the code rows that stand in for freed
+ * blocks, and the open block (arXiv abstract: later tokens attend to the pause
+ * tokens' entries in place of the freed block; figure captions, Fig. 2(a)).
+ * Long chain-of-thought decoding is bound by reading this cache (arXiv
+ * abstract), so the call streams each resident row once, split over the
+ * device, and merges the splits (the split-KV partials and their combine).
  * q [n, Hq, d] device, pre-RoPE, rotated at position P + G - 1; query head h
  * reads KV head h / (Hq/Hkv). out [n, Hq, d] (pool dtype), lse [n, Hq] fp32.
  * BAD_STATE unless the current token is appended at this layer and the layer
@@ -153,7 +165,7 @@ abk_status abk_append_kv(abk_pool* p, int32_t layer, int32_t n, const int32_t* s
 abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
                                 const void* q, void* out, float* lse);
 
-/* Steps a1 + a2 + a3 in one call: append the current token (k, v as for
+/* The append and the decode in one call: append the current token (k, v as for
  * abk_append_kv) and decode with q (as for abk_decode_attention) at one layer.
  * The result equals the two calls in sequence. For bf16 pools with d = 128,
  * four query heads per KV head, 64-row pages and the automatic schedule it is
@@ -164,8 +176,11 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
 abk_status abk_append_decode(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
                              const void* k, const void* v, const void* q, void* out, float* lse);
 
-/* Steps a4-a6: compress the completed open block b of each sequence at one
- * layer. q_pause [n, Kp, Hq, d], k_pause and v_pause [n, Kp, Hkv, d] device,
+/* Compress the completed open block b of each sequence at one layer: the
+ * pause tokens attend to the block and their entries become its code rows
+ * (figure captions, Fig. 1(a)), under the block mask of Fig. 2(a), at the
+ * in-block positions of Fig. 2(b); the layer keeps the first quota[layer] of
+ * them (news write-up, second detail). q_pause [n, Kp, Hq, d], k_pause and v_pause [n, Kp, Hkv, d] device,
  * pre-RoPE (Kp = the layer's pause count). Pause k is rotated at
  * P + b*C + bitrev(k)*C/Kp and attends to the prompt, the retained code rows of
  * earlier blocks, all C rows of block b, and pause keys j <= k. out [n, Kp, Hq,
@@ -177,9 +192,10 @@ abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32
                               const void* q_pause, const void* k_pause, const void* v_pause,
                               void* out, float* lse);
 
-/* Step a7: after every layer is compressed, return the open block's pages of
- * every layer to the free list and start the next block (its raw rows are no
- * longer resident). BAD_STATE unless every layer of every sequence is
+/* After every layer is compressed, return the open block's pages of every
+ * layer to the free list and start the next block: once the pause tokens have
+ * encoded a block, its raw cache is freed (arXiv abstract; figure captions,
+ * Fig. 1(a)), so a sequence's cache falls at each compression (Fig. 1(b)). BAD_STATE unless every layer of every sequence is
  * compressed; BAD_STATE in full-KV mode. */
 abk_status abk_free_block(abk_pool* p, int32_t n, const int32_t* seq_ids);
 
@@ -259,6 +275,14 @@ abk_status abk_pool_stats(const abk_pool* p, int64_t* pages_used, int64_t* pages
  * layer ascending, persistent before open. BAD_STATE unless the sequence is
  * fresh (no prompt written, nothing appended). */
 abk_status abk_synth_fill(abk_pool* p, int32_t seq_id, int32_t generated, uint64_t seed);
+
+/* Test support: make a later workspace allocation of the pool fail with
+ * ABK_ERR_HIP, as a failed hipMalloc or hipHostMalloc would. The call that
+ * needs to grow a workspace after `after` more successful growths gets the
+ * error; -1 turns the hook off. It checks that a call which fails there has
+ * changed no state (the workspace is sized before any bookkeeping). Errors:
+ * INVALID_ARG (NULL pool, after < -1). */
+abk_status abk_debug_fail_allocs(abk_pool* p, int32_t after);
 
 /* Thread-local text for the last non-OK status of this thread. */
 const char* abk_last_error(void);

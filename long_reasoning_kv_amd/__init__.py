@@ -23,7 +23,7 @@ SYMBOLS = [
     "abk_compress_block",
     "abk_free_block", "abk_seq_query", "abk_export_layout", "abk_read_rows",
     "abk_pool_stats", "abk_budget_pool_stats", "abk_synth_fill", "abk_blockmask_attention",
-    "abk_prefill_prompt",
+    "abk_prefill_prompt", "abk_debug_fail_allocs",
     "abk_last_error",
 ]
 
@@ -85,6 +85,7 @@ def lib():
             "abk_synth_fill": [vp, i32, i32, u64],
             "abk_blockmask_attention": [vp, i32, i32, i32, vp, vp, vp, vp, vp],
             "abk_prefill_prompt": [vp, i32, i32, vp, vp, vp, vp, vp],
+            "abk_debug_fail_allocs": [vp, i32],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -242,6 +243,11 @@ class Pool:
     def prefill_prompt(self, sid, layer, q, k, v, out, lse):
         _check(lib().abk_prefill_prompt(self._h, sid, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                         _ptr(lse)))
+
+    def debug_fail_allocs(self, after: int):
+        """Test support: the workspace growth after `after` more successful
+        ones fails (-1: off)."""
+        _check(lib().abk_debug_fail_allocs(self._h, after))
 
     def synth_fill(self, sid, generated, seed):
         _check(lib().abk_synth_fill(self._h, sid, generated, seed & 0xFFFFFFFFFFFFFFFF))

@@ -79,12 +79,23 @@ struct abk_pool {
   PinnedSlot ring[kRing];
   int ring_next = 0;
   std::vector<int32_t> scratch;  // host staging for descriptors
+  int32_t fail_allocs = -1;      // test hook: workspace allocations left before one fails (-1: off)
 };
 
 namespace {
 
+// The test hook's count-down: true when this workspace allocation is the one
+// made to fail.
+bool injected_failure(abk_pool* p) {
+  if (p->fail_allocs < 0) return false;
+  if (p->fail_allocs-- > 0) return false;
+  p->fail_allocs = -1;
+  return true;
+}
+
 abk_status grow(abk_pool* p, void** buf, size_t* have, size_t need) {
   if (need <= *have) return ABK_OK;
+  if (injected_failure(p)) return set_err(ABK_ERR_HIP, "workspace allocation failed (injected)");
   ABK_HIP(hipStreamSynchronize(p->stream));
   if (*buf) ABK_HIP(hipFree(*buf));
   *buf = nullptr;
@@ -95,16 +106,18 @@ abk_status grow(abk_pool* p, void** buf, size_t* have, size_t need) {
   return ABK_OK;
 }
 
-// Copy `bytes` of host data to the pool's device descriptor buffer, in stream
-// order, through a pinned slot that is reused only after its copy finished.
-abk_status upload_desc(abk_pool* p, const void* src, size_t bytes) {
+// Make the next descriptor upload of up to `bytes` allocation-free: the device
+// buffer and the next pinned slot of the ring are grown (the slot once its
+// previous copy has finished). Calls that change host state reserve first, so
+// that a failed allocation leaves the state as it was.
+abk_status reserve_desc(abk_pool* p, size_t bytes) {
   if (bytes == 0) return ABK_OK;
   if (abk_status st = grow(p, &p->desc, &p->desc_bytes, bytes)) return st;
   PinnedSlot& s = p->ring[p->ring_next];
-  p->ring_next = (p->ring_next + 1) % kRing;
   if (s.pending) ABK_HIP(hipEventSynchronize(s.ev));
   s.pending = false;
   if (s.cap < bytes) {
+    if (injected_failure(p)) return set_err(ABK_ERR_HIP, "pinned staging allocation failed (injected)");
     if (s.host) ABK_HIP(hipHostFree(s.host));
     s.host = nullptr;
     s.cap = 0;
@@ -113,6 +126,16 @@ abk_status upload_desc(abk_pool* p, const void* src, size_t bytes) {
     s.cap = cap;
   }
   if (!s.ev) ABK_HIP(hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
+  return ABK_OK;
+}
+
+// Copy `bytes` of host data to the pool's device descriptor buffer, in stream
+// order, through a pinned slot that is reused only after its copy finished.
+abk_status upload_desc(abk_pool* p, const void* src, size_t bytes) {
+  if (bytes == 0) return ABK_OK;
+  if (abk_status st = reserve_desc(p, bytes)) return st;
+  PinnedSlot& s = p->ring[p->ring_next];
+  p->ring_next = (p->ring_next + 1) % kRing;
   std::memcpy(s.host, src, bytes);
   ABK_HIP(hipMemcpyAsync(p->desc, s.host, bytes, hipMemcpyHostToDevice, p->stream));
   ABK_HIP(hipEventRecord(s.ev, p->stream));
@@ -452,18 +475,25 @@ abk_status mfma_schedule(abk_pool* p, const Entries& e, bool before_append,
   return ABK_OK;
 }
 
-// Launch the scheduled chunks; k/v/new_page non-null: fused append of the
-// current token.
-abk_status launch_mfma_chunks(abk_pool* p, const void* q, void* out, float* lse, const void* k, const void* v,
-                              const int32_t* new_page, std::vector<abk::StreamArgs>* chunks) {
+// Bytes of split partials the scheduled chunks need (the chunks run one after
+// another on the stream and share the buffer); `fused`: a fused call's
+// partial of the current token per head.
+size_t mfma_part_bytes(const abk_pool* p, const std::vector<abk::StreamArgs>& chunks, bool fused) {
   const abk::Shape& s = p->shape;
   const int32_t G = s.Hq / s.Hkv;
+  size_t need = 0;
+  for (const auto& a : chunks)
+    need = std::max(need, (size_t)a.n * s.Hkv * (a.maxp + (fused ? 1 : 0)) * G * (s.D + 2));
+  return need * sizeof(float);
+}
+
+// Launch the scheduled chunks with partials in `part` (at least
+// mfma_part_bytes); k/v/new_page non-null: fused append of the current token.
+abk_status launch_mfma_chunks(abk_pool* p, const void* q, void* out, float* lse, const void* k, const void* v,
+                              const int32_t* new_page, float* part, std::vector<abk::StreamArgs>* chunks) {
+  const abk::Shape& s = p->shape;
   const size_t qb = (size_t)s.Hq * s.D * s.esize();
   const size_t kb = (size_t)s.Hkv * s.D * s.esize();
-  size_t need = 0;
-  const size_t extra = k != nullptr;  // a fused call's partial of the current token
-  for (const auto& a : *chunks) need = std::max(need, (size_t)a.n * s.Hkv * (a.maxp + extra) * G * (s.D + 2));
-  if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes, need * sizeof(float))) return st;
   for (size_t c = 0; c < chunks->size(); ++c) {
     abk::StreamArgs& a = (*chunks)[c];
     const int32_t c0 = (int32_t)c * abk::kMaxBatch;
@@ -472,7 +502,7 @@ abk_status launch_mfma_chunks(abk_pool* p, const void* q, void* out, float* lse,
     a.q = (const char*)q + c0 * qb;
     a.out = (char*)out + c0 * qb;
     a.lse = lse + (size_t)c0 * s.Hq;
-    a.part = p->part;
+    a.part = part;
     a.layer = 0;
     a.compress = s.compress;
     a.fused = k != nullptr;
@@ -502,7 +532,8 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
   if (p->mfma_waves > 0 && p->split_rows == 0) {
     std::vector<abk::StreamArgs> chunks;
     if (abk_status st = mfma_schedule(p, e, false, &chunks)) return st;
-    return launch_mfma_chunks(p, q, out, lse, nullptr, nullptr, nullptr, &chunks);
+    if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes, mfma_part_bytes(p, chunks, false))) return st;
+    return launch_mfma_chunks(p, q, out, lse, nullptr, nullptr, nullptr, p->part, &chunks);
   }
   if (p->stream_wgs > 0 && p->split_rows == 0) {
     // stream-K: equal runs of 32-row units over the flattened (sequence, head, unit) work
@@ -612,10 +643,12 @@ abk_status abk_append_decode(abk_pool* p, int32_t layer, int32_t n, const int32_
   const Entries e = entries(p, layer, n, seq_ids);
   std::vector<abk::StreamArgs> chunks;
   if (abk_status st = mfma_schedule(p, e, true, &chunks)) return st;
+  // the workspace before the append changes any state
+  if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes, mfma_part_bytes(p, chunks, true))) return st;
   std::vector<int32_t> new_page;
   if (abk::Status st = p->host.append(layer * p->hs, p->hs, n, seq_ids, &new_page))
     return from_host(st, p->host.err);
-  return launch_mfma_chunks(p, q, out, lse, k, v, new_page.data(), &chunks);
+  return launch_mfma_chunks(p, q, out, lse, k, v, new_page.data(), p->part, &chunks);
 }
 
 abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
@@ -625,18 +658,49 @@ abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32
   if (abk_status st = check_model_layer(p, layer)) return st;
   if (!p->host_only && n > 0 && (!q_pause || !k_pause || !v_pause || !out || !lse))
     return set_err(ABK_ERR_INVALID_ARG, "a pause/out/lse pointer is NULL");
-  std::vector<abk::CompressPlan> plan;  // one per (sequence, head) entry
-  if (abk::Status st = p->host.compress(layer * p->hs, p->hs, n, seq_ids, &plan))
-    return from_host(st, p->host.err);
-  if (p->host_only || n == 0) return ABK_OK;
   const abk::Shape& s = p->shape;
-  const int32_t Kp = s.pause[layer * p->hs];
-  const int32_t ne = (int32_t)plan.size();
+  const int32_t l0 = layer * p->hs;
+  if (abk::Status st = p->host.check_compress(l0, p->hs, n, seq_ids)) return from_host(st, p->host.err);
+  const int32_t Kp = s.pause[l0];
+  const int32_t ne = n * p->hs;
+  const int32_t npair = ne * s.Hkv;
+  const int32_t G = s.Hq / s.Hkv;
+  // Workspace sizes from the counts before the call (the descriptor: records,
+  // launch order, then each entry's pages of its new code rows), grown before
+  // the host pool changes so that a failed allocation changes nothing.
+  size_t desc_ints = (size_t)ne * abk::kCompRec + npair;
+  int32_t min_ntc = INT32_MAX;
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t j = 0; j < p->hs; ++j) {
+      const int32_t pers = p->host.seq(seq_ids[i]).layers[l0 + j].pers_rows, qn = s.quota[l0 + j];
+      if (qn > 0) desc_ints += (pers + qn - 1) / s.pr - pers / s.pr + 1;
+      min_ntc = std::min(min_ntc, (pers + 63) / 64 + s.C / 64);
+    }
+  int32_t nsplit = 1, ntq = 0;
+  const bool mfma = !p->host_only && abk::compress_mfma_supported(p->dev, G);
+  if (mfma && n > 0) {
+    // few sequences: split each query tile's context over several workgroups so
+    // that about one per CU runs, keeping at least 4 context tiles per split
+    ntq = (4 * Kp + abk::kCompressRows - 1) / abk::kCompressRows;
+    const int32_t wgs = (npair + 7) / 8 * 8 * ntq;
+    const int32_t target = std::max(1, p->cus);
+    if (wgs < target) nsplit = std::max(1, std::min({(target + wgs - 1) / wgs, min_ntc / 4, 16}));
+  }
+  if (!p->host_only && n > 0) {
+    if (abk_status st = grow(p, &p->kp_rot, &p->kp_rot_bytes, (size_t)npair * Kp * s.D * s.esize())) return st;
+    if (nsplit > 1)
+      if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
+                               (size_t)npair * ntq * nsplit * abk::kCompressRows * (s.D + 2) * sizeof(float)))
+        return st;
+    if (abk_status st = reserve_desc(p, desc_ints * sizeof(int32_t))) return st;
+  }
+  std::vector<abk::CompressPlan> plan;  // one per (sequence, head) entry
+  if (abk::Status st = p->host.compress(l0, p->hs, n, seq_ids, &plan)) return from_host(st, p->host.err);
+  if (p->host_only || n == 0) return ABK_OK;
   std::vector<int32_t>& d = p->scratch;
   // records, then the (entry, KV head) pairs in launch order: longest context
   // first, so that the short ones fill in behind the long ones at the end of
   // the launch; then the page lists
-  const int32_t npair = ne * s.Hkv;
   d.assign((size_t)ne * abk::kCompRec + npair, 0);
   {
     std::vector<int32_t> ord(ne);
@@ -660,9 +724,6 @@ abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32
     r[7] = plan[i].quota;
     d.insert(d.end(), plan[i].pages.begin(), plan[i].pages.end());
   }
-  if (abk_status st = grow(p, &p->kp_rot, &p->kp_rot_bytes,
-                           (size_t)ne * s.Hkv * Kp * s.D * s.esize()))
-    return st;
   if (abk_status st = upload_desc(p, d.data(), d.size() * sizeof(int32_t))) return st;
   abk::CompressArgs a;
   a.P = flat_view(p);
@@ -677,30 +738,11 @@ abk_status abk_compress_block(abk_pool* p, int32_t layer, int32_t n, const int32
   a.n = ne;
   a.hsplit = p->hs;
   a.Hq = s.Hq * p->hs;  // the caller's query heads
-  a.G = s.Hq / s.Hkv;
+  a.G = G;
   a.Kp = Kp;
   a.log2Kp = abk::log2_exact(Kp);
-  a.part = nullptr;
-  a.nsplit = 1;
-  if (abk::compress_mfma_supported(p->dev, a.G)) {
-    // few sequences: split each query tile's context over several workgroups so
-    // that about one per CU runs, keeping at least 4 context tiles per split
-    const int32_t ntq = (4 * Kp + abk::kCompressRows - 1) / abk::kCompressRows;
-    const int32_t wgs = (ne * s.Hkv + 7) / 8 * 8 * ntq;
-    int32_t min_ntc = INT32_MAX;
-    for (int32_t i = 0; i < ne; ++i)
-      min_ntc = std::min(min_ntc, (plan[i].pers_before + 63) / 64 + s.C / 64);
-    const int32_t target = std::max(1, p->cus);
-    if (wgs < target)
-      a.nsplit = std::max(1, std::min({(target + wgs - 1) / wgs, min_ntc / 4, 16}));
-    if (a.nsplit > 1) {
-      if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
-                               (size_t)ne * s.Hkv * ntq * a.nsplit * abk::kCompressRows * (s.D + 2) *
-                                   sizeof(float)))
-        return st;
-      a.part = p->part;
-    }
-  }
+  a.nsplit = nsplit;
+  a.part = nsplit > 1 ? p->part : nullptr;
   ABK_HIP(abk::launch_compress(a, p->stream));
   return ABK_OK;
 }
@@ -841,6 +883,9 @@ abk_status abk_prefill_prompt(abk_pool* p, int32_t seq_id, int32_t layer, const 
   const abk::Shape& s = p->shape;
   if (!(s.dtype == 1 && s.D == 128 && s.Hq == 4 * s.Hkv))
     return set_err(ABK_ERR_UNSUPPORTED, "prompt prefill needs bf16, d = 128, four query heads per KV head");
+  // the block-mask prefill's own checks, before the prompt is written
+  if (s.Hkv * p->hs > abk::kMaxPrefillHeads)
+    return set_err(ABK_ERR_UNSUPPORTED, "block-mask prefill above 16 KV heads");
   const int32_t P = p->host.seq(seq_id).P;
   if (!p->host_only && P > 0 && (!q || !out || !lse))
     return set_err(ABK_ERR_INVALID_ARG, "q/out/lse is NULL");
@@ -933,6 +978,13 @@ abk_status abk_budget_pool_stats(const abk_pool* p, int32_t level, int32_t* leve
   if (quota) *quota = p->host.level_quota(level);
   if (pages_used) *pages_used = p->host.level_pages(level) - fr;
   if (pages_free) *pages_free = fr;
+  return ABK_OK;
+}
+
+abk_status abk_debug_fail_allocs(abk_pool* p, int32_t after) {
+  if (abk_status st = check_pool(p)) return st;
+  if (after < -1) return set_err(ABK_ERR_INVALID_ARG, "after must be >= -1");
+  p->fail_allocs = after;
   return ABK_OK;
 }
 

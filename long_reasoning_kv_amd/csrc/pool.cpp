@@ -261,7 +261,7 @@ Status HostPool::check_decode(int32_t l0, int32_t nl, int32_t n, const int32_t* 
   return kOk;
 }
 
-Status HostPool::compress(int32_t l0, int32_t nl, int32_t n, const int32_t* ids, std::vector<CompressPlan>* plan) {
+Status HostPool::check_compress(int32_t l0, int32_t nl, int32_t n, const int32_t* ids) {
   if (check_layers(l0, nl)) return fail(kInvalidArg, "bad layer");
   if (!s_.compress) return fail(kBadState, "compression is off (full-KV pool)");
   if (Status st = check_batch(n, ids)) return st;
@@ -274,7 +274,11 @@ Status HostPool::compress(int32_t l0, int32_t nl, int32_t n, const int32_t* ids,
       if (lay.compressed) return fail(kBadState, "block already compressed at this layer");
       need[level_of_[l]] += cdiv(lay.pers_rows + s_.quota[l], s_.pr) - cdiv(lay.pers_rows, s_.pr);
     }
-  if (Status st = check_need(need, "for code rows")) return st;
+  return check_need(need, "for code rows");
+}
+
+Status HostPool::compress(int32_t l0, int32_t nl, int32_t n, const int32_t* ids, std::vector<CompressPlan>* plan) {
+  if (Status st = check_compress(l0, nl, n, ids)) return st;
   plan->clear();
   for (int32_t i = 0; i < n; ++i) {
     SeqState& q = seqs_[ids[i]];

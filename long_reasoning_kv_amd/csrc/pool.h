@@ -99,6 +99,8 @@ class HostPool {
   // new_page[e] = page taken for entry e's row, or -1.
   Status append(int32_t l0, int32_t nl, int32_t n, const int32_t* ids, std::vector<int32_t>* new_page);
   Status check_decode(int32_t l0, int32_t nl, int32_t n, const int32_t* ids);
+  // the checks of compress alone (nothing changes)
+  Status check_compress(int32_t l0, int32_t nl, int32_t n, const int32_t* ids);
   Status compress(int32_t l0, int32_t nl, int32_t n, const int32_t* ids, std::vector<CompressPlan>* plan);
   Status free_block(int32_t n, const int32_t* ids);
   Status fill(int32_t id, int32_t G);

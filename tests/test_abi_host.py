@@ -223,6 +223,18 @@ def test_prefill_prompt_checks_before_writing():
         bf.prefill_prompt(s, 0, None, None, None, None, None)
     assert e.value.status == abk.BAD_STATE                 # generation has started
     bf.close()
+    # 32 KV heads (one pool layer per head): above the block-mask prefill's 16,
+    # refused before the prompt is written
+    wide = _pool(dtype="bf16", num_layers=1, num_q_heads=128, num_kv_heads=32, head_dim=128,
+                 page_rows=4, layer_quota=[4], head_quota=[[4] * 32], pool_bytes=2 * 4 * 128 * 2 * 400)
+    s = wide.seq_create(3)
+    with pytest.raises(abk.AbkError) as e:
+        wide.prefill_prompt(s, 0, None, None, None, None, None)
+    assert e.value.status == abk.UNSUPPORTED
+    with pytest.raises(abk.AbkError) as e:
+        wide.append_kv(0, [s], None, None)
+    assert e.value.status == abk.BAD_STATE                 # no prompt was written
+    wide.close()
 
 
 # ---- per-head quotas (figure captions, Fig. 7: a quota per (layer, KV head)) ----

@@ -111,7 +111,7 @@ def test_block_compression_event_sampled():
     print("[fullsize] compression event: 64 sequences filled", flush=True)
     layers = _sample_layers(quotas)
     seqs = (0, 31, 63)
-    queries = [0, 1, 100, 255]
+    queries = [0, 1, 100, 150, 255]  # every 64-pause query tile
     kept = {}
     before = {(i, l): run.pool.seq_query(sids[i], l)["resident_rows"] for i in seqs for l in layers}
     for l in range(L):

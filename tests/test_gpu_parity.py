@@ -85,7 +85,7 @@ def test_tiny_fp32_decode_compress_free():
     run.pool.read_rows(s, 0, 14, 4, k, v)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(v), code[5])
-    _close("code rows k", host(k), code[4], 2e-6)
+    np.testing.assert_array_equal(host(k), code[4])  # one rounding of the same fp64 rotation
     run.pool.free_block([s])
     pm.free_block([s])
     run.nb[s] += 1
@@ -532,3 +532,72 @@ def test_empty_calls_change_nothing():
     torch.cuda.synchronize()
     assert [run.pool.seq_query(s, l) for l in range(2)] == before
     _check_decode(run, [s], 0)
+
+
+@pytest.mark.parametrize("after", [0, 1, 2])
+def test_failed_workspace_allocation_changes_nothing(after):
+    """A call whose workspace growth fails (forced through the test hook, as a
+    failed hipMalloc / hipHostMalloc would) returns ABK_ERR_HIP and leaves every
+    count, page list and free page as it was; the same call then succeeds and
+    matches the oracle. The fused append + decode grows its partials (growth
+    0); the compression its rotated-key workspace (0) and a pinned staging
+    slot (1); after = 2 fails nothing."""
+    run = _bf16_run(pr=64, C=128, Kp=32, quota=[32, 8], split_rows=0, seed=11, max_seqs=4)
+    dec = [run.new_seq(P, i) for i, P in enumerate([7, 70])]
+    full = [run.new_seq(P, i + 2) for i, P in enumerate([3, 90])]
+    for s in dec:
+        run.fill(s, 100)
+    for s in full:
+        run.fill(s, 128)  # the open block holds C rows: ready to compress
+
+    def state():
+        return [run.pool.seq_query(s, l) for s in dec + full for l in range(run.L)], run.pool.stats()
+
+    def attempt(call):
+        before = state()
+        run.pool.debug_fail_allocs(after)
+        try:
+            call()
+            failed = False
+        except abk.AbkError as e:
+            assert e.status == abk.HIP_ERROR, e
+            failed = True
+        run.pool.debug_fail_allocs(-1)
+        if failed:
+            assert state() == before
+            call()
+        return failed
+
+    # fused append + decode at layer 0
+    k = np.stack([run.rows(s, 0, TEXT, [run.G[s]], 0, synth.WHICH_K)[0] for s in dec])
+    v = np.stack([run.rows(s, 0, TEXT, [run.G[s]], 0, synth.WHICH_V)[0] for s in dec])
+    q = np.stack([run.rows(s, 0, TEXT, [run.G[s]], 0, synth.WHICH_Q)[0] for s in dec])
+    out = torch.empty((2, 32, 128), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((2, 32), device="cuda", dtype=torch.float32)
+    failed = attempt(lambda: run.pool.append_decode(0, dec, dev(k, "bf16"), dev(v, "bf16"), dev(q, "bf16"),
+                                                   out, lse))
+    assert failed == (after == 0)
+    torch.cuda.synchronize()
+    for i, s in enumerate(dec):
+        run.G[s] += 1  # layer 0 only; the oracle is asked about layer 0
+        o_ref, l_ref, _ = run.oracle_decode(s, 0, q[i])
+        _close(f"fused after failure {after} seq{i}", host(out)[i], o_ref, 2e-2)
+        _close(f"fused lse after failure {after} seq{i}", host(lse)[i], l_ref, 1e-3)
+    # block compression at layer 0: a failed call leaves the block uncompressed
+    res = {}
+
+    def comp():
+        res["r"] = run.compress_layer(full, 0)
+
+    failed = attempt(comp)
+    assert failed == (after < 2)
+    torch.cuda.synchronize()
+    cout, clse = host(res["r"][0]), host(res["r"][1])
+    for i, s in enumerate(full):
+        o_ref, l_ref, code = run.oracle_compress(s, 0)
+        _close(f"compress after failure {after} seq{i}", cout[i], o_ref, 2e-2)
+        _close(f"compress lse after failure {after} seq{i}", clse[i], l_ref, 1e-3)
+    with pytest.raises(abk.AbkError) as e:
+        run.pool.free_block(full)  # layer 1 is not compressed yet
+    assert e.value.status == abk.BAD_STATE
+    run.pool.close()
