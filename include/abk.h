@@ -165,6 +165,20 @@ abk_status abk_append_kv(abk_pool* p, int32_t layer, int32_t n, const int32_t* s
 abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
                                 const void* q, void* out, float* lse);
 
+/* abk_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same checks, schedule and kernels, with the split partials
+ * in a fixed device array of 32 MiB per GPU (kNoAllocScratchBytes) instead of
+ * the pool's workspace. It calls no hipMalloc, hipFree or stream
+ * synchronisation, and its results equal abk_decode_attention's. Every call on
+ * one GPU shares that array: calls that overlap on one GPU (other streams,
+ * other pools, other threads) race and must be ordered by the caller. A call
+ * whose partials would exceed the array is refused before anything is
+ * enqueued (UNSUPPORTED; the bench's 22-sequence, 36-layer step needs about
+ * 6 MB per call). Other errors as for abk_decode_attention. */
+abk_status abk_decode_attention_noalloc(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                                        const void* q, void* out, float* lse);
+
 /* The append and the decode in one call: append the current token (k, v as for
  * abk_append_kv) and decode with q (as for abk_decode_attention) at one layer.
  * The result equals the two calls in sequence. For bf16 pools with d = 128,

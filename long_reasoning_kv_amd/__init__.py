@@ -23,7 +23,7 @@ SYMBOLS = [
     "abk_compress_block",
     "abk_free_block", "abk_seq_query", "abk_export_layout", "abk_read_rows",
     "abk_pool_stats", "abk_budget_pool_stats", "abk_synth_fill", "abk_blockmask_attention",
-    "abk_prefill_prompt", "abk_debug_fail_allocs",
+    "abk_prefill_prompt", "abk_debug_fail_allocs", "abk_decode_attention_noalloc",
     "abk_last_error",
 ]
 
@@ -86,6 +86,7 @@ def lib():
             "abk_blockmask_attention": [vp, i32, i32, i32, vp, vp, vp, vp, vp],
             "abk_prefill_prompt": [vp, i32, i32, vp, vp, vp, vp, vp],
             "abk_debug_fail_allocs": [vp, i32],
+            "abk_decode_attention_noalloc": [vp, i32, i32, ip, vp, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -187,6 +188,13 @@ class Pool:
     def decode_attention(self, layer, seq_ids, q, out, lse):
         n, ids = _ids(seq_ids)
         _check(lib().abk_decode_attention(self._h, layer, n, ids, _ptr(q), _ptr(out), _ptr(lse)))
+
+    def decode_attention_noalloc(self, layer, seq_ids, q, out, lse):
+        """decode_attention with the split partials in the library's fixed
+        per-GPU workspace: no device allocation; overlapping calls on one GPU
+        race."""
+        n, ids = _ids(seq_ids)
+        _check(lib().abk_decode_attention_noalloc(self._h, layer, n, ids, _ptr(q), _ptr(out), _ptr(lse)))
 
     def append_decode(self, layer, seq_ids, k, v, q, out, lse):
         n, ids = _ids(seq_ids)

@@ -80,6 +80,7 @@ struct abk_pool {
   int ring_next = 0;
   std::vector<int32_t> scratch;  // host staging for descriptors
   int32_t fail_allocs = -1;      // test hook: workspace allocations left before one fails (-1: off)
+  float* noalloc_part = nullptr;  // the allocation-free decode's fixed workspace on this device
 };
 
 namespace {
@@ -306,6 +307,12 @@ abk_status abk_pool_create(const abk_pool_config* cfg, void* hip_stream, abk_poo
   if ((err = hipMemcpy(p->pause_d, s.pause.data(), s.L * sizeof(int32_t), hipMemcpyHostToDevice)))
     return fail(err, "pause upload");
   if ((err = hipDeviceSynchronize())) return fail(err, "init sync");
+  // the allocation-free decode's workspace: its address on this device
+  {
+    void* ws = nullptr;
+    if ((err = abk::noalloc_scratch(&ws))) return fail(err, "allocation-free workspace address");
+    p->noalloc_part = (float*)ws;
+  }
   {
     int dev = 0, cus = 0;
     if ((err = hipGetDevice(&dev))) return fail(err, "device");
@@ -516,8 +523,28 @@ abk_status launch_mfma_chunks(abk_pool* p, const void* q, void* out, float* lse,
 
 }  // namespace
 
-abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
-                                const void* q, void* out, float* lse) {
+namespace {
+
+// The split partials of a decode call: the pool's buffer, grown to `bytes`,
+// or, for the allocation-free entry point, the fixed device array `fixed` of
+// `cap` bytes (a call that needs more is refused before anything is enqueued).
+abk_status decode_part(abk_pool* p, size_t bytes, float* fixed, size_t cap, float** part) {
+  if (fixed) {
+    if (bytes > cap)
+      return set_err(ABK_ERR_UNSUPPORTED, "split partials need " + std::to_string(bytes) +
+                                              " bytes; the allocation-free decode holds " + std::to_string(cap));
+    *part = fixed;
+    return ABK_OK;
+  }
+  if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes, bytes)) return st;
+  *part = p->part;
+  return ABK_OK;
+}
+
+// Decode attention of one layer (checks, schedule, launches) with the split
+// partials as decode_part gives them.
+abk_status decode_into(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids, const void* q, void* out,
+                       float* lse, float* fixed, size_t cap) {
   if (abk_status st = check_pool(p)) return st;
   if (abk_status st = check_model_layer(p, layer)) return st;
   if (!p->host_only && n > 0 && (!q || !out || !lse))
@@ -529,18 +556,24 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
   const size_t qb = (size_t)s.Hq * s.D * s.esize();  // one entry's queries
   const Entries e = entries(p, layer, n, seq_ids);
   const int32_t ne = (int32_t)e.sid.size();
+  float* part = nullptr;
   if (p->mfma_waves > 0 && p->split_rows == 0) {
     std::vector<abk::StreamArgs> chunks;
     if (abk_status st = mfma_schedule(p, e, false, &chunks)) return st;
-    if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes, mfma_part_bytes(p, chunks, false))) return st;
-    return launch_mfma_chunks(p, q, out, lse, nullptr, nullptr, nullptr, p->part, &chunks);
+    if (abk_status st = decode_part(p, mfma_part_bytes(p, chunks, false), fixed, cap, &part)) return st;
+    return launch_mfma_chunks(p, q, out, lse, nullptr, nullptr, nullptr, part, &chunks);
   }
   if (p->stream_wgs > 0 && p->split_rows == 0) {
-    // stream-K: equal runs of 32-row units over the flattened (sequence, head, unit) work
+    // stream-K: equal runs of 32-row units over the flattened (sequence, head,
+    // unit) work; every chunk is scheduled, and the partials sized, first
     const int32_t nq = s.pr / 32;
+    std::vector<abk::StreamArgs> chunks;
+    std::vector<int32_t> waves;
+    size_t need = 0;
     for (int32_t c0 = 0; c0 < ne; c0 += abk::kMaxBatch) {
       const int32_t m = std::min(ne - c0, abk::kMaxBatch);
-      abk::StreamArgs a;
+      chunks.emplace_back();
+      abk::StreamArgs& a = chunks.back();
       a.fused = 0;
       a.compress = s.compress;
       a.k = a.v = nullptr;
@@ -567,20 +600,22 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
         }
       }
       if (maxp > abk::kMaxSplits) return set_err(ABK_ERR_UNSUPPORTED, "too many partials per head");
-      if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
-                               (size_t)m * s.Hkv * maxp * G * (s.D + 2) * sizeof(float)))
-        return st;
+      need = std::max(need, (size_t)m * s.Hkv * maxp * G * (s.D + 2) * sizeof(float));
       a.P = flat_view(p);
       a.q = (const char*)q + c0 * qb;
       a.out = (char*)out + c0 * qb;
       a.lse = lse + (size_t)c0 * s.Hq;
-      a.part = p->part;
       a.layer = 0;
       a.n = m;
       a.T = T;
       a.U = U;
       a.maxp = maxp;
-      ABK_HIP(abk::launch_decode_stream(a, W, p->stream));
+      waves.push_back(W);
+    }
+    if (abk_status st = decode_part(p, need, fixed, cap, &part)) return st;
+    for (size_t c = 0; c < chunks.size(); ++c) {
+      chunks[c].part = part;
+      ABK_HIP(abk::launch_decode_stream(chunks[c], waves[c], p->stream));
     }
     return ABK_OK;
   }
@@ -603,9 +638,7 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
     for (int32_t i = c0; i < std::min(ne, c0 + abk::kMaxBatch); ++i) t += splits[i];
     need = std::max(need, t);
   }
-  if (abk_status st = grow(p, (void**)&p->part, &p->part_bytes,
-                           need * s.Hkv * G * (s.D + 2) * sizeof(float)))
-    return st;
+  if (abk_status st = decode_part(p, need * s.Hkv * G * (s.D + 2) * sizeof(float), fixed, cap, &part)) return st;
   for (int32_t c0 = 0; c0 < ne; c0 += abk::kMaxBatch) {
     const int32_t m = std::min(ne - c0, abk::kMaxBatch);
     abk::DecodeArgs a;
@@ -613,7 +646,7 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
     a.q = (const char*)q + c0 * qb;
     a.out = (char*)out + c0 * qb;
     a.lse = lse + (size_t)c0 * s.Hq;
-    a.part = p->part;
+    a.part = part;
     a.layer = 0;
     a.n = m;
     a.G = G;
@@ -626,6 +659,21 @@ abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int
     ABK_HIP(abk::launch_decode(a, a.prefix[m], p->stream));
   }
   return ABK_OK;
+}
+
+}  // namespace
+
+abk_status abk_decode_attention(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                                const void* q, void* out, float* lse) {
+  return decode_into(p, layer, n, seq_ids, q, out, lse, nullptr, 0);
+}
+
+abk_status abk_decode_attention_noalloc(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,
+                                        const void* q, void* out, float* lse) {
+  if (abk_status st = check_pool(p)) return st;
+  if (!p->host_only && !p->noalloc_part)
+    return set_err(ABK_ERR_BAD_STATE, "the allocation-free workspace was not resolved at pool creation");
+  return decode_into(p, layer, n, seq_ids, q, out, lse, p->noalloc_part, abk::kNoAllocScratchBytes);
 }
 
 abk_status abk_append_decode(abk_pool* p, int32_t layer, int32_t n, const int32_t* seq_ids,

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace abk {
@@ -1444,5 +1446,31 @@ hipError_t launch_decode_stream(const StreamArgs& a, int32_t nwg, hipStream_t s)
   if (a.maxp > 1)
     hipLaunchKernelGGL(decode_stream_merge_kernel, dim3(a.n, a.P.Hkv), dim3(512), 0, s, a);
   return hipGetLastError();
+}
+
+// ---- the allocation-free decode's workspace ----------------------------------------
+// Split partials of abk_decode_attention_noalloc, for callers that cannot
+// allocate device memory. Each GPU holds its own copy for the life of the
+// process. On the host, the array's name is only a stand-in for it: the
+// address that kernels take comes from hipGetSymbolAddress on each device.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 }  // namespace abk

@@ -195,6 +195,13 @@ hipError_t launch_fill(const FillArgs& a, int32_t max_rows, hipStream_t s);
 bool blockmask_supported(const DevPool& P, int32_t G);
 hipError_t launch_blockmask(const BlockMaskArgs& a, int32_t nrec, hipStream_t s);
 hipError_t launch_read(const ReadArgs& a, hipStream_t s);
+// Fixed device workspace of the allocation-free decode entry point: the split
+// partials live in a file-scope device array of this many bytes, one per GPU,
+// shared by every such call on that GPU. noalloc_scratch gives its address on
+// the current device (resolved once per device; the address is what host code
+// passes to kernels, never the array's name).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_export(const ExportArgs& a, hipStream_t s);
 
 }  // namespace abk

@@ -23,5 +23,6 @@ bool blockmask_supported(const DevPool&, int32_t) { return false; }
 hipError_t launch_blockmask(const BlockMaskArgs&, int32_t, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_read(const ReadArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_export(const ExportArgs&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t noalloc_scratch(void**) { return hipErrorNotSupported; }
 
 }  // namespace abk
