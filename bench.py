@@ -16,9 +16,10 @@ Prints one JSON line: tokens/s, achieved HBM GB/s of the decode call against
 MI355X's 8 TB/s (HIP events around every call in the timed region), the CPU
 oracle on a bounded sample, the block-compression event (64 sequences x 36
 layers) and the block-mask prefill at the Fig. 9 shape, each with its MFMA
-rate. `--serving-mix` instead runs the saturated serving mix (200 GiB pool,
-AbridgeKV against full KV); `--profile-summary DIR` writes profiles/ from
-rocprofv3 runs.
+rate, and a bounded run of the saturated serving mix (200 GiB pool, AbridgeKV
+against full KV through the same kernels, `--mix-steps` steps each).
+`--serving-mix` runs only the serving mix, with its occupancy trace;
+`--profile-summary DIR` writes profiles/ from rocprofv3 runs.
 """
 from __future__ import annotations
 
@@ -891,6 +892,22 @@ def run_serving_mix(args, torch, abk, compress: bool):
             "occupancy_trace": trace}
 
 
+def serving_mix_leg(a: dict, f: dict) -> dict:
+    """The serving mix's two modes as the default bench line reports them
+    (without the occupancy traces)."""
+    keys = ("sequences_resident", "tokens_per_s", "ms_per_step", "steps", "compressions_in_timed_steps",
+            "decode_kv_gb_per_step", "kv_gbps_incl_compression", "pool_pages_used_at_end", "pool_pages")
+    return {"metric": "serving mix: decode tokens/s and sequences resident, AbridgeKV vs full KV",
+            "unit": "tokens/s",
+            "config": {"workload": "saturated serving mix: 200 GiB paged pool, 36 layers, quotas "
+                                   "6x256/12x64/18x128, P ~ U[128,512], G ~ U[1024,32768], one fused "
+                                   "append+decode call per layer per step, compress+free at block "
+                                   "boundaries inside the steps; full KV: the same kernels, compression off"},
+            "abridgekv": {k: a[k] for k in keys}, "full_kv": {k: f[k] for k in keys},
+            "tokens_per_s_ratio": a["tokens_per_s"] / f["tokens_per_s"],
+            "sequences_ratio": a["sequences_resident"] / f["sequences_resident"]}
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -996,6 +1013,8 @@ def main():
     ap.add_argument("--serving-mix", action="store_true",
                     help="only run the saturated serving mix (200 GiB pool, AbridgeKV and full KV)")
     ap.add_argument("--serving-mix-steps", type=int, default=512)
+    ap.add_argument("--mix-steps", type=int, default=64,
+                    help="steps of each mode of the serving-mix leg of the default run (0: skip it)")
     ap.add_argument("--budget-pools", action="store_true",
                     help="serving mix: one page pool per budget level (AbridgeKV mode)")
     ap.add_argument("--profile-summary", metavar="DIR",
@@ -1065,6 +1084,12 @@ def main():
     if not args.no_prefill:
         print("[bench] block-mask prefill: 16K text tokens, 36 layers", file=sys.stderr, flush=True)
         pre = run_prefill(args, torch, abk)
+    mix = None
+    if args.mix_steps > 0:
+        print(f"[bench] serving mix: 200 GiB pool, {args.mix_steps} steps per mode", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()  # the earlier legs' cached blocks: the pool takes 200 GiB
+        margs = argparse.Namespace(**{**vars(args), "serving_mix_steps": args.mix_steps})
+        mix = serving_mix_leg(run_serving_mix(margs, torch, abk, True), run_serving_mix(margs, torch, abk, False))
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline (bounded sample)", file=sys.stderr, flush=True)
@@ -1080,7 +1105,7 @@ def main():
         "blocks_compressed": res["blocks_compressed"],
         "with_compression_amortized": res["with_compression_amortized"],
         "roofline": res["roofline"], "cpu_baseline": cpu, "compress": comp, "prefill": pre,
-        "per_head": per_head, "decode_1layer": one,
+        "per_head": per_head, "decode_1layer": one, "serving_mix": mix,
     }
     print(json.dumps(line), flush=True)
 
