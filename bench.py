@@ -223,7 +223,7 @@ def profile_summary(d):
         if fam == "decode_mfma" and bj:
             rf = bj["roofline"]
             extra = [f"bench.py in the traced run: {rf['avg_launch_us']:.1f} us per decode call "
-                     f"(HIP events around decode + merge), algorithmic "
+                     f"(HIP events around each step's fused calls, per call), algorithmic "
                      f"{rf['algorithmic_bytes_per_launch'] / 1e6:.1f} MB per call, "
                      f"{rf['achieved']:.0f} GB/s = {100 * rf['frac']:.1f}% of 8 TB/s",
                      f"counted HBM bytes / algorithmic bytes: "
@@ -329,7 +329,9 @@ def run_decode(args, torch, abk):
     Kp = int(quotas.max())
     hq = head_quotas(quotas, args.seed) if args.per_head else [[int(q)] * HKV for q in quotas]
     # warmup, then the timed steps twice: alone (value, ms_per_step), then with
-    # HIP events around every call (the roofline's per-call durations)
+    # HIP events for the roofline's per-call durations: around each step's 36
+    # fused calls (after the step's compressions), or with --separate-append
+    # around every decode call (the appends between them excluded)
     total_steps = args.warmup + 2 * args.steps
     # pool: resident rows now plus growth over the run, in whole pages, with slack
     pages = 0
@@ -402,12 +404,14 @@ def run_decode(args, torch, abk):
                 if rec is not None:
                     rec[l][0].record()
                 pool.decode_attention(l, sids, q, out, lse)
-            else:
                 if rec is not None:
-                    rec[l][0].record()
+                    rec[l][1].record()
+            else:
+                if rec is not None and l == 0:
+                    rec[0][0].record()
                 pool.append_decode(l, sids, k, v, q, out, lse)
-            if rec is not None:
-                rec[l][1].record()
+                if rec is not None and l == L - 1:
+                    rec[0][1].record()
         if rec is not None:
             # resident (row, KV head) pairs each call reads
             rows_log.append([sum(int((P + nb * qh + (g + 1 - nb * C)).sum()) for qh in hq[l]) for l in range(L)])
@@ -432,7 +436,11 @@ def run_decode(args, torch, abk):
     # and writes them as the new row
     row_bytes = 2 * HKV * D * 2
     io_bytes = B * (2 * HQ * D * 2 + HQ * 4) + (0 if args.separate_append else B * 2 * row_bytes)
-    dec_ms = [e0.elapsed_time(e1) for evs in ev for e0, e1 in evs]
+    if args.separate_append:
+        dec_ms = [e0.elapsed_time(e1) for evs in ev for e0, e1 in evs]
+    else:
+        # one bracket per step: its calls' mean duration, once per call
+        dec_ms = [evs[0][0].elapsed_time(evs[0][1]) / L for evs in ev for _ in range(L)]
     dec_bytes = [rh * (2 * D * 2) + io_bytes for rl in rows_log for rh in rl]
     achieved = sum(dec_bytes) / (sum(dec_ms) * 1e-3) / 1e9
     comp_ms = sum(a.elapsed_time(b) for a, b in cev)
@@ -461,6 +469,8 @@ def run_decode(args, torch, abk):
             "traffic": traffic_from_profiles("decode_mfma", float(np.mean(dec_bytes))),
             "kernel": ("decode_mfma_kernel (+ decode_stream_merge_kernel)" if args.separate_append else
                        "decode_mfma_kernel with fused append (+ decode_stream_merge_kernel)"),
+            "timing": ("HIP events around every decode call" if args.separate_append else
+                       "HIP events around each step's 36 fused calls, divided by 36"),
             "algorithmic_bytes_per_launch": float(np.mean(dec_bytes)),
             "avg_launch_us": float(np.mean(dec_ms)) * 1e3,
         },

@@ -1073,8 +1073,14 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
   };
   auto cursor_at = [&](int F) __attribute__((always_inline)) {
     Cur c;
-    c.i = 0;
-    while (a.useg[c.i + 1] <= F) ++c.i;
+    // the sequence whose tiles hold F: useg[i] <= F < useg[i + 1] (binary search)
+    int lo = 0, hi = a.n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.useg[mid] <= F) lo = mid;
+      else hi = mid - 1;
+    }
+    c.i = lo;
     load_seq(c);
     const int rel = F - a.useg[c.i];
     c.h = rel / c.units;
@@ -1091,12 +1097,15 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
       }
     }
   };
-  // byte offset of the tile's first row in the pools, and its valid rows
+  // byte offset of the tile's first row in the pools, and its valid rows. The
+  // persistent candidate page is read whether or not the tile is persistent:
+  // its address does not depend on the row counts, so the two reads overlap.
   auto locate = [&](const Cur& c, size_t* off, int* nval) __attribute__((always_inline)) {
     cptr tab = (cptr)ptab_of(P, c.slot, a.layer);
+    const int ppage = tab[min(c.lu >> 1, P.max_pers - 1)];
     int page, r0;
     if (c.lu < c.ptiles) {
-      page = tab[c.lu >> 1];
+      page = ppage;
       r0 = (c.lu & 1) * TK;
       *nval = min(TK, c.n_pers - c.lu * TK);
     } else {
