@@ -169,6 +169,60 @@ def _stats_table(d, name, match):
     return [head] + lines, path
 
 
+SQ_PASSES = {
+    "sq": ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_WAVES"),
+    "stall": ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY",
+              "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_VALU_MFMA_COEXEC_CYCLES"),
+    "lds": ("SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT", "SQ_LDS_UNALIGNED_STALL",
+            "SQ_LDS_IDX_ACTIVE", "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL"),
+    "grbm": ("GRBM_GUI_ACTIVE",),
+}
+
+
+def sq_summary(d, prefix, match):
+    """Lines on where an MFMA kernel's time goes, from the SQ counter passes
+    <prefix>_sq, _stall, _lds and _grbm (means per dispatch)."""
+    v = {}
+    for pas, names in SQ_PASSES.items():
+        for c in names:
+            r = _counters(d, f"{prefix}_{pas}", c, match)
+            if r:
+                v[c] = float(np.mean([x for _, x in r]))
+    if "GRBM_GUI_ACTIVE" not in v or "SQ_VALU_MFMA_BUSY_CYCLES" not in v:
+        return []
+    gui = v["GRBM_GUI_ACTIVE"] / NUM_XCD
+    simd = gui * NUM_CU * SIMD_PER_CU
+    out = [f"SQ counters, mean per dispatch (GRBM_GUI_ACTIVE summed over {NUM_XCD} XCDs: "
+           f"{gui:.4g} cycles each):"]
+    for c in sorted(v):
+        out.append(f"  {c:28s} {v[c]:.4g}")
+    out.append(f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {NUM_CU} CUs x {SIMD_PER_CU} SIMDs) = "
+               f"{100 * v['SQ_VALU_MFMA_BUSY_CYCLES'] / simd:.1f}%")
+    if "SQ_BUSY_CU_CYCLES" in v:
+        out.append(f"CU busy = SQ_BUSY_CU_CYCLES / (cycles x {NUM_CU}) = "
+                   f"{100 * v['SQ_BUSY_CU_CYCLES'] / (gui * NUM_CU):.1f}%")
+    if "SQ_INSTS_VALU" in v and "SQ_INSTS_MFMA" in v:
+        out.append(f"VALU instructions (MFMA included) per MFMA: {v['SQ_INSTS_VALU'] / v['SQ_INSTS_MFMA']:.2f}")
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in v:
+        out.append(f"cycles with a VALU instruction issued while the MFMA unit is busy: "
+                   f"{100 * v['SQ_VALU_MFMA_COEXEC_CYCLES'] / v['SQ_VALU_MFMA_BUSY_CYCLES']:.1f}% of MFMA-busy cycles")
+    if "SQ_WAVE_CYCLES" in v:
+        w = v["SQ_WAVE_CYCLES"]
+        out.append(f"wave time: issuing {100 * v['SQ_ACTIVE_INST_ANY'] / w:.1f}%, waiting to issue "
+                   f"(dependency or busy unit) {100 * v['SQ_WAIT_INST_ANY'] / w:.1f}%, waiting on a counter "
+                   f"or barrier {100 * v['SQ_WAIT_ANY'] / w:.1f}%; VALU issue {100 * v['SQ_ACTIVE_INST_VALU'] / w:.1f}%, "
+                   f"LDS issue {100 * v['SQ_ACTIVE_INST_LDS'] / w:.1f}%, waiting for LDS issue "
+                   f"{100 * v['SQ_WAIT_INST_LDS'] / w:.1f}%")
+    if "SQ_LDS_IDX_ACTIVE" in v:
+        out.append(f"LDS: bank conflicts {v['SQ_LDS_BANK_CONFLICT']:.0f}, address conflicts "
+                   f"{v['SQ_LDS_ADDR_CONFLICT']:.0f}, unaligned stalls {v['SQ_LDS_UNALIGNED_STALL']:.0f}; "
+                   f"FIFO-full cycles summed over the counters' instances: data {v['SQ_LDS_DATA_FIFO_FULL']:.3g}, "
+                   f"command {v['SQ_LDS_CMD_FIFO_FULL']:.3g} (against {gui:.3g} cycles per XCD)")
+    for pas in SQ_PASSES:
+        out.append(f"  {pas} pass: {_cmd(d, f'{prefix}_{pas}')}")
+    return out
+
+
 def profile_summary(d):
     """Write profiles/*.txt and profiles/*_traffic.json from a directory of
     rocprofv3 runs (one sub-directory per pass, ``<pass>.cmd`` holding the
@@ -233,33 +287,13 @@ def profile_summary(d):
             extra = [f"bench.py in the traced run: {pf['ms_per_forward']:.1f} ms per 36-layer forward, "
                      f"{pf['roofline']['achieved']:.0f} TFLOP/s algorithmic = "
                      f"{100 * pf['roofline']['frac']:.1f}% of 2.5 PFLOP/s bf16"]
-        if fam == "compress_attn_mfma":
-            sq = {}
-            for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_MFMA",
-                      "SQ_INSTS_VALU", "SQ_WAVES"):
-                v = _counters(d, "cmp_sq", c, match)
-                if v:
-                    sq[c] = float(np.mean([x for _, x in v]))
-            g = _counters(d, "cmp_grbm", "GRBM_GUI_ACTIVE", match)
-            if g and sq:
-                gui = float(np.mean([x for _, x in g])) / NUM_XCD
-                extra.append(f"per dispatch: GRBM_GUI_ACTIVE {gui * NUM_XCD:.4g} (summed over "
-                             f"{NUM_XCD} XCDs: {gui:.4g} cycles each)")
-                for c, v in sq.items():
-                    extra.append(f"  {c} {v:.4g}")
-                extra.append(f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {NUM_CU} CUs x "
-                             f"{SIMD_PER_CU} SIMDs) = "
-                             f"{100 * sq['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * NUM_CU * SIMD_PER_CU):.1f}%")
-                extra.append(f"CU busy = SQ_BUSY_CU_CYCLES / (cycles x {NUM_CU}) = "
-                             f"{100 * sq['SQ_BUSY_CU_CYCLES'] / (gui * NUM_CU):.1f}%")
-                extra.append(f"VALU instructions per MFMA: {sq['SQ_INSTS_VALU'] / sq['SQ_INSTS_MFMA']:.2f}")
-                extra.append(f"  sq pass:   {_cmd(d, 'cmp_sq')}")
-                extra.append(f"  grbm pass: {_cmd(d, 'cmp_grbm')}")
-            if bj and bj.get("compress"):
-                c = bj["compress"]
-                extra.append(f"bench.py in the traced run: {c['ms_per_event']:.1f} ms per event, "
-                             f"{c['roofline']['achieved']:.0f} TFLOP/s algorithmic = "
-                             f"{100 * c['roofline']['frac']:.1f}% of 2.5 PFLOP/s bf16")
+        if fam in ("compress_attn_mfma", "blockmask_attn_mfma"):
+            extra += sq_summary(d, prefix, "compress_attn_mfma" if prefix == "cmp" else "blockmask_attn")
+        if fam == "compress_attn_mfma" and bj and bj.get("compress"):
+            c = bj["compress"]
+            extra.append(f"bench.py in the traced run: {c['ms_per_event']:.1f} ms per event, "
+                         f"{c['roofline']['achieved']:.0f} TFLOP/s algorithmic = "
+                         f"{100 * c['roofline']['frac']:.1f}% of 2.5 PFLOP/s bf16")
         text = [f"{fam} -- {what}", "",
                 "Commands (run from the repository root with TMPDIR=/tmp; "
                 "the library built in-tree beforehand):",

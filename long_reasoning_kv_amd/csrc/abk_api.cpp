@@ -836,29 +836,30 @@ abk_status abk_blockmask_attention(abk_pool* p, int32_t layer, int32_t prompt_le
     return set_err(ABK_ERR_INVALID_ARG, "q/k/v/out/lse is NULL");
   if (p->host_only) return ABK_OK;
 
-  // query tiles of up to 32 tokens of one kind in one block; per KV head, a
-  // text or pause tile sees nA = prompt + blk * that head's quota persistent rows
+  // query tiles of up to kBmTokens tokens of one kind in one block; per KV
+  // head, a text or pause tile sees nA = prompt + blk * that head's quota
+  // persistent rows
   struct Tile {
     int32_t kind, row0, ntok, tok0, bstart, nB, blk;
     int64_t work;  // keys seen by its last query beyond the persistent rows
   };
   std::vector<Tile> tiles;
   const int32_t P0 = comp ? prompt_len : T;  // rows attended causally from the start
-  for (int32_t t0 = 0; t0 < P0; t0 += 32) {
-    const int32_t n = std::min(32, P0 - t0);
+  for (int32_t t0 = 0; t0 < P0; t0 += abk::kBmTokens) {
+    const int32_t n = std::min(abk::kBmTokens, P0 - t0);
     tiles.push_back({0, t0, n, t0, 0, 0, -1, t0 + n});
   }
   if (comp) {
     const int32_t nblk = (text_tokens + C - 1) / C;
     for (int32_t blk = 0; blk < nblk; ++blk) {
       const int32_t bstart = prompt_len + blk * (C + Kp), ctext = std::min(C, text_tokens - blk * C);
-      for (int32_t i0 = 0; i0 < ctext; i0 += 32) {
-        const int32_t n = std::min(32, ctext - i0);
+      for (int32_t i0 = 0; i0 < ctext; i0 += abk::kBmTokens) {
+        const int32_t n = std::min(abk::kBmTokens, ctext - i0);
         tiles.push_back({1, bstart + i0, n, i0, bstart, i0 + n, blk, (int64_t)i0 + n});
       }
       if (blk < nb)
-        for (int32_t j0 = 0; j0 < Kp; j0 += 32) {
-          const int32_t n = std::min(32, Kp - j0);
+        for (int32_t j0 = 0; j0 < Kp; j0 += abk::kBmTokens) {
+          const int32_t n = std::min(abk::kBmTokens, Kp - j0);
           tiles.push_back({2, bstart + C + j0, n, j0, bstart, C + j0 + n, blk, (int64_t)C + j0 + n});
         }
     }

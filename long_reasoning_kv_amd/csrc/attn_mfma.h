@@ -93,24 +93,24 @@ __device__ __forceinline__ void query_operand(const bf16_t* qrow, const double2*
 
 // Per-lane byte offsets of the operand reads of a 64-key tile. They depend on
 // the lane only (both swizzles of a row are functions of its low bits, which
-// are the lane's): K operand of M-block mb, k-step ks at k[ks] + kmb_off(mb);
-// V^T operand of dim block db, key step kk, half hh at v[db] + vkk_off(kk, hh).
+// are the lane's). K operand of M-block mb, k-step ks at k(ks) + kmb_off(mb);
+// V^T operand of dim block db, key step kk, half hh at v(db) + vkk_off(kk, hh).
+// The k-step (dim block) moves only bits 6-7 (5-7) of the swizzled offset, so
+// one base per operand kind is kept and the step is XORed in.
 struct TileOffsets {
-  uint32_t k[4], v[8];
+  uint32_t kb, vb;  // offsets of k-step 0 and of dim block 0
+  __device__ __forceinline__ uint32_t k(int ks) const { return kb ^ (64u * ks); }
+  __device__ __forceinline__ uint32_t v(int db) const { return vb ^ (32u * db); }
 };
 __device__ __forceinline__ TileOffsets tile_offsets(int lane) {
   const int l16 = lane & 15, g4 = lane >> 4;
   TileOffsets o;
   const int kr0 = tile_key(0, l16);  // key row of M-block 0; kswz(tile_key(mb, l16)) = kswz(kr0)
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) o.k[ks] = kr0 * 256 + 16 * ((4 * ks + g4) ^ kswz(kr0));
-  const int g = lane >> 4, sl = lane & 15;
-  const int row0 = 8 * g + (sl >> 2);  // vt_swz(row0 + 32 kk + 4 hh) = vt_swz(row0)
-#pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    const int dim = 16 * db + 4 * (sl & 3);
-    o.v[db] = row0 * 256 + 16 * ((dim >> 3) ^ vt_swz(row0)) + 2 * (dim & 7);
-  }
+  o.kb = kr0 * 256 + 16 * (g4 ^ kswz(kr0));
+  const int sl = lane & 15;
+  const int row0 = 8 * g4 + (sl >> 2);  // vt_swz(row0 + 32 kk + 4 hh) = vt_swz(row0)
+  const int dim = 4 * (sl & 3);
+  o.vb = row0 * 256 + 16 * ((dim >> 3) ^ vt_swz(row0)) + 2 * (dim & 7);
   return o;
 }
 __device__ __forceinline__ constexpr int kmb_off(int mb) { return (32 * (mb >> 1) + 4 * (mb & 1)) * 256; }
@@ -134,36 +134,14 @@ struct WaveAttn {
     }
   }
 
-  // One 64-key tile from its K and V buffers in LDS: qk, softmax, pv.
-  template <class Limits>
-  __device__ __forceinline__ void tile(const uint4* __restrict__ ck, const uint4* __restrict__ cv,
-                                       bool masked, Limits limits, float qs, int lane) {
-    f32x4_t s[4][2];
-    uint4 pb[2][2];
-    const TileOffsets o = tile_offsets(lane);
-    qk(ck, o, s);
-    softmax(s, masked, limits, qs, lane, pb);
-    pv(cv, o, pb);
-  }
-
-  // S^T of a tile: s[mb][nb] lane l holds the unscaled scores of keys
-  // tile_key(mb, 4 g4 + e) against query column l%16 of N-block nb.
-  __device__ __forceinline__ void qk(const uint4* __restrict__ ck, const TileOffsets& o,
-                                     f32x4_t (&s)[4][2]) const {
-    const char* base = (const char*)ck;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 ka = *(const uint4*)(base + o.k[ks] + kmb_off(mb));
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma_bf16(ka, qh[nb][ks], s[mb][nb]);
-      }
-    }
+  // Maximum of query column nb's 16 scores in this lane, as a tree.
+  __device__ __forceinline__ static float col_max(const f32x4_t (&s)[4][2], int nb) {
+    const float a = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), s[0][nb][2]);
+    const float b = fmaxf(fmaxf(s[0][nb][3], s[1][nb][0]), s[1][nb][1]);
+    const float c = fmaxf(fmaxf(s[1][nb][2], s[1][nb][3]), s[2][nb][0]);
+    const float d = fmaxf(fmaxf(s[2][nb][1], s[2][nb][2]), s[2][nb][3]);
+    const float e = fmaxf(fmaxf(s[3][nb][0], s[3][nb][1]), s[3][nb][2]);
+    return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[3][nb][3]));
   }
 
   // Online softmax of a tile's scores. When `masked`, key tile_key(mb, 4 g4 +
@@ -188,19 +166,20 @@ struct WaveAttn {
           for (int e = 0; e < 4; ++e)
             s[mb][nb][e] = 32 * (mb >> 1) + 4 * (mb & 1) + e < lim[nb] ? s[mb][nb][e] : -INFINITY;
     }
-    // per query column (lane-local after the row swaps)
+    // per query column (lane-local after the row swaps). The phase runs on
+    // one wavefront per SIMD, which hides no latency, so the reductions are
+    // trees and the two columns' chains are independent.
+    float mx[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) mx[nb] = col_max(s, nb);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) mx[nb] = rows4_max(mx[nb]) * qs;  // log2 units
     float mn[2], alpha[2];
     bool moved = false;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[mb][nb][e]);
-      mx = rows4_max(mx) * qs;  // log2 units
-      const bool up = mx > m[nb] + 8.f;
-      mn[nb] = up ? mx : m[nb];
+      const bool up = mx[nb] > m[nb] + 8.f;
+      mn[nb] = up ? mx[nb] : m[nb];
       alpha[nb] = fast_exp2(m[nb] - mn[nb]);
       moved = moved || up;
       m[nb] = mn[nb];
@@ -214,17 +193,18 @@ struct WaveAttn {
       }
     }
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float ps = 0.f;
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = fast_exp2(fmaf(s[mb][nb][e], qs, -mn[nb]));
-          s[mb][nb][e] = p;  // the score register now holds its probability
-          ps += p;
-        }
-      l[nb] += ps;
+        for (int e = 0; e < 4; ++e)  // the score register now holds its probability
+          s[mb][nb][e] = fast_exp2(fmaf(s[mb][nb][e], qs, -mn[nb]));
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float q4[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) q4[mb] = (s[mb][nb][0] + s[mb][nb][1]) + (s[mb][nb][2] + s[mb][nb][3]);
+      l[nb] += (q4[0] + q4[1]) + (q4[2] + q4[3]);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         // keys 32kk + 8 g4 + j: j < 4 from M-block 2kk, j >= 4 from 2kk+1
@@ -235,51 +215,36 @@ struct WaveAttn {
     }
   }
 
-  // O^T += V^T P^T for a tile's probabilities pb (V^T through two
-  // ds_read_b64_tr_b16 per operand, as in vt_operand).
-  __device__ __forceinline__ void pv(const uint4* __restrict__ cv, const TileOffsets& o,
-                                     const uint4 (&pb)[2][2]) {
-    const char* base = (const char*)cv;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint4 va = vt_pair(base + o.v[db] + vkk_off(kk, 0));
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[nb][db] = mfma_bf16(va, pb[nb][kk], acc[nb][db]);
-      }
-    }
-  }
-
-  // The V^T operands of dim blocks db0..db0+3 of a tile, read into registers:
-  // va[db - db0][kk].
+  // The V^T operands of dim blocks db0..db0+3 of a tile, read into registers
+  // in the order pv_regs uses them: va[db - db0][kk].
   __device__ __forceinline__ static void v_operands(const uint4* __restrict__ cv, const TileOffsets& o, int db0,
                                                     uint4 (&va)[4][2]) {
     const char* base = (const char*)cv;
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        va[d][kk] = vt_pair(base + o.v[db0 + d] + vkk_off(kk, 0));
-      }
+      for (int d = 0; d < 4; ++d) va[d][kk] = vt_pair(base + o.v(db0 + d) + vkk_off(kk, 0));
   }
   // O^T += V^T P^T for dim blocks db0..db0+3 from operands in registers.
+  // Key step outermost, so that the two products into one accumulator are
+  // eight products apart.
   __device__ __forceinline__ void pv_regs(const uint4 (&va)[4][2], int db0, const uint4 (&pb)[2][2]) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[nb][db0 + d] = mfma_bf16(va[d][kk], pb[nb][kk], acc[nb][db0 + d]);
   }
-  // The K operands of M-blocks mb0, mb0 + 1 of a tile: ka[m][ks].
+  // The K operands of M-blocks mb0, mb0 + 1 of a tile: ka[m][ks], read in the
+  // order qk_regs uses them.
   __device__ __forceinline__ static void k_operands(const uint4* __restrict__ ck, const TileOffsets& o, int mb0,
                                                     uint4 (&ka)[2][4]) {
     const char* base = (const char*)ck;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) ka[m][ks] = *(const uint4*)(base + o.k[ks] + kmb_off(mb0 + m));
+      for (int m = 0; m < 2; ++m) ka[m][ks] = *(const uint4*)(base + o.k(ks) + kmb_off(mb0 + m));
   }
   // S^T of M-blocks mb0, mb0 + 1 from their K operands.
   __device__ __forceinline__ void qk_regs(const uint4 (&ka)[2][4], int mb0, f32x4_t (&s)[4][2]) const {
@@ -307,5 +272,251 @@ struct WaveAttn {
     if (g4 == 0) *lse_dst = (m[nb] + __log2f(L)) * 0.6931471805599453f;
   }
 };
+
+// Scheduling groups for the compiler's scheduler: the next n MFMAs, or the
+// next n LDS reads, of the region in program order.
+template <int n>
+__device__ __forceinline__ void sched_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x008, n, 0);
+}
+template <int n>
+__device__ __forceinline__ void sched_lds() {
+  __builtin_amdgcn_sched_group_barrier(0x100, n, 0);
+}
+
+// Where a 64-key tile lies: K row r at kb + 256 r, V row r at vb + vstride r;
+// rows past nval repeat row nval - 1 (their keys are masked).
+struct TileSrc {
+  const char* kb;
+  const char* vb;
+  int vstride, nval;
+};
+
+// Attention of a workgroup of eight wavefronts (256 query rows, the 32 rows of
+// each wavefront in wa) over ntiles 64-key tiles, on a ping-pong schedule. The
+// wavefronts form two groups, wavefronts w and w + 4 sharing a SIMD, kept one
+// phase apart by a workgroup barrier between phases. In a matrix phase a
+// wavefront runs the previous tile's O^T += V^T P^T and then this tile's S^T =
+// K Q^T (64 MFMAs); in a vector phase it runs this tile's softmax. The groups
+// alternate, so each SIMD's matrix core works on one group's products while its
+// vector unit runs the other group's softmax:
+//   phase 2u:   group 0 matrix (PV u-1, QK u)   group 1 softmax u-1
+//   phase 2u+1: group 0 softmax u               group 1 matrix (PV u-1, QK u)
+// for u = 0..ntiles (the matrix phase of u = 0 adds zeros, that of u = ntiles
+// runs on a repeated tile and its scores are dropped, and no softmax phase runs
+// for u = ntiles). Tiles stream straight into a ring
+// of four LDS buffers (32 KB each: K rows swizzled by kswz, V rows by vt_swz):
+// at phase 2u every wavefront issues its share of tile u+2, and before the
+// barrier that ends phase 2u it waits for its share of tile u+1. Tile u's
+// buffer is read from phase 2u to 2u+3, and the load into it is issued at
+// phase 2u-4, after the barrier that ends its previous tile's last read.
+// tile_src(u) gives tile u's place; each wavefront asks for u = 0, 1, 2, ...
+// in order, once each, then for ntiles - 1 again past the end (a tile source
+// may fetch ahead). soft(u, s, pb) runs tile u's
+// softmax (wa.softmax with the tile's masks). The ring buffers are separate
+// __shared__ arrays of the kernel, so that the compiler can tell them apart.
+template <class TileFn, class SoftFn>
+__device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int lane, int wave,
+                                                   uint4* __restrict__ lk0, uint4* __restrict__ lk1,
+                                                   uint4* __restrict__ lk2, uint4* __restrict__ lk3,
+                                                   uint4* __restrict__ lv0, uint4* __restrict__ lv1,
+                                                   uint4* __restrict__ lv2, uint4* __restrict__ lv3,
+                                                   TileFn tile_src, SoftFn soft) {
+  constexpr int RB = 256;  // bytes of a bf16 row of 128 dims
+  const bool grp0 = wave < 4;
+  // Tile t straight from global memory into LDS (buffer_load_dwordx4 ... lds,
+  // the MUBUF form: the compiler's wait counting treats a FLAT load into LDS as
+  // an LDS access of unknown order and then waits for every LDS read): in
+  // load j of wavefront w, lane l fills LDS chunk 512j + 64w + l, i.e. row
+  // 32j + 4w + l/16 at swizzled position l%16, so it fetches the source chunk
+  // that belongs there (both swizzles ignore bit 5 of the row). Rows past the
+  // tile's valid count repeat its last row. Four loads per wavefront.
+  const int r_in = 4 * wave + (lane >> 4);
+  const int kchunk = (lane & 15) ^ kswz(r_in), vchunk = (lane & 15) ^ vt_swz(r_in);
+  // byte offsets of a whole tile of 256-byte rows: the same for every such
+  // tile, so computed once; 32-bit offsets from a uniform base let the loads
+  // take the scalar-base form
+  uint32_t kof_full[2], vof_full[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    kof_full[j] = (32 * j + r_in) * RB + 16 * kchunk;
+    vof_full[j] = (32 * j + r_in) * RB + 16 * vchunk;
+  }
+  auto issue = [&](int u, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
+    const TileSrc ts = tile_src(min(u, ntiles - 1));
+    uint32_t kof[2], vof[2];
+    if (ts.nval == kTileKeys && ts.vstride == RB) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        kof[j] = kof_full[j];
+        vof[j] = vof_full[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = min(32 * j + r_in, ts.nval - 1);
+        kof[j] = row * RB + 16 * kchunk;
+        vof[j] = row * ts.vstride + 16 * vchunk;
+      }
+    }
+    // raw buffer descriptors over the tile's K and V (stride 0, a range the
+    // offsets never reach; 0x00020000 is the format word of untyped data)
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)ts.kb, 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)ts.vb, 0, 0x7fffffff, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk + 512 * j + 64 * wave),
+                                               16, kof[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv + 512 * j + 64 * wave),
+                                               16, vof[j], 0, 0, 0);
+    }
+  };
+  // the end of a phase: the wavefront's LDS reads have returned and, at the end
+  // of an even phase, its loads older than the last tile's four have landed;
+  // then every wavefront of the workgroup gets here (the loads of all of them
+  // are then in LDS). The signal fences keep the compiler from moving
+  // LDS accesses across the barrier, the scheduling barriers any other
+  // instruction (products of one phase must not sink into the next).
+  auto end_phase = [&](bool wait_loads) __attribute__((always_inline)) {
+    if (wait_loads) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0): tile u+2 may fly
+    else __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): this phase's LDS reads are done
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+
+  // Carried across the barrier from a tile's softmax phase to the next matrix
+  // phase: the tile's probabilities (pb) and the next tile's K operands of
+  // M-blocks 0, 1 (ka). Before the first tile pb is zero and the previous V
+  // buffer (lv3) holds zeros, so the first matrix phase's P V adds exact zeros
+  // and needs no branch.
+  uint4 pb[2][2], ka[2][4];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) pb[nb][kk] = make_uint4(0u, 0u, 0u, 0u);
+  TileOffsets to = tile_offsets(lane);
+  // The empty asm hides the lane offsets' values from the compiler, so that it
+  // adds them to each buffer's address at the read (an immediate offset)
+  // instead of keeping a register per buffer, and forms the XORed offsets of
+  // each phase inside it instead of keeping them live across the loop.
+  auto refresh = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+v"(to.kb));
+    asm volatile("" : "+v"(to.vb));
+  };
+  // matrix phase of tile u: Q K^T of tile u and P V of tile u-1, with no branch
+  // (past the last tile the products run on the spare buffer's repeated tile
+  // and are discarded). M-blocks 0, 1 come from registers; each group of
+  // operand reads is issued one group of products ahead of its use.
+  auto matrix = [&](const uint4* __restrict__ k0, const uint4* __restrict__ vm1, f32x4_t (&s)[4][2])
+      __attribute__((always_inline)) {
+    refresh();
+    uint4 vb[4][2], vc[4][2], kb[2][4];
+    WaveAttn::v_operands(vm1, to, 0, vb);
+    wa.qk_regs(ka, 0, s);
+    WaveAttn::k_operands(k0, to, 2, kb);
+    wa.pv_regs(vb, 0, pb);
+    WaveAttn::v_operands(vm1, to, 4, vc);
+    wa.qk_regs(kb, 2, s);
+    wa.pv_regs(vc, 4, pb);
+    // The order (mask 8: MFMA, 0x100: LDS read): each group of operand reads
+    // goes between the products before its use, at most 14 reads in flight so
+    // that the waits can name the reads a product needs (the LDS counter
+    // holds 15).
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {  // Q K^T of M-blocks 0, 1 with V^T reads 1..14 of dims 0..63
+      sched_mfma<1>();
+      sched_lds<1>();
+    }
+    sched_mfma<2>();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // P V of dims 0..63 with V^T reads 15, 16 and K reads 1..6
+      sched_mfma<2>();
+      sched_lds<1>();
+    }
+    sched_lds<2>();  // K reads 7, 8
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {  // Q K^T of M-blocks 2, 3 with V^T reads 1..14 of dims 64..127
+      sched_mfma<1>();
+      sched_lds<1>();
+    }
+    sched_mfma<2>();
+    sched_mfma<2>();  // P V of dims 64..127 with V^T reads 15, 16
+    sched_lds<2>();
+    sched_mfma<14>();
+  };
+  // softmax phase of tile u, then the K operands of M-blocks 0, 1 of tile u+1
+  // from its buffer k1 (in LDS since the barrier that began this phase)
+  auto vector = [&](int u, const uint4* __restrict__ k1, f32x4_t (&s)[4][2]) __attribute__((always_inline)) {
+    if (u >= ntiles) return;
+    refresh();
+    soft(u, s, pb);
+    WaveAttn::k_operands(k1, to, 0, ka);
+  };
+  // Tile u: its matrix phase, then its softmax phase; group 0 runs them as
+  // phases 2u and 2u+1, group 1 one phase later. Tile u is in buffer (k0, v0),
+  // tile u+1 in (k1, v1); at every even phase 2u each wavefront issues its share
+  // of tile u+2 (past the end it repeats the last tile into the spare buffer)
+  // and at the end of it waits for its share of tile u+1. Each group runs its
+  // own copy of the loop; both pass the same number of barriers.
+  auto tile0 = [&](int u, const uint4* __restrict__ k0, const uint4* __restrict__ vm1,
+                   const uint4* __restrict__ k1, uint4* __restrict__ k2, uint4* __restrict__ v2)
+      __attribute__((always_inline)) {
+    f32x4_t s[4][2];
+    issue(u + 2, k2, v2);
+    matrix(k0, vm1, s);
+    end_phase(true);
+    vector(u, k1, s);
+    end_phase(false);
+  };
+  auto tile1 = [&](int u, const uint4* __restrict__ k0, const uint4* __restrict__ vm1,
+                   const uint4* __restrict__ k1, uint4* __restrict__ k3, uint4* __restrict__ v3)
+      __attribute__((always_inline)) {
+    f32x4_t s[4][2];
+    matrix(k0, vm1, s);
+    end_phase(false);
+    issue(u + 3, k3, v3);
+    vector(u, k1, s);
+    end_phase(true);
+  };
+
+  if (ntiles > 0) {
+    issue(0, lk0, lv0);
+    issue(1, lk1, lv1);
+    // zeros in the V buffer that the first matrix phase reads as tile -1
+    lv3[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+    lv3[threadIdx.x + 512] = make_uint4(0u, 0u, 0u, 0u);
+    end_phase(true);  // tile 0 and the zeros are in
+    if (grp0) {
+      WaveAttn::k_operands(lk0, to, 0, ka);
+      for (int u = 0; u <= ntiles; u += 4) {
+        tile0(u, lk0, lv3, lk1, lk2, lv2);
+        if (u + 1 > ntiles) break;
+        tile0(u + 1, lk1, lv0, lk2, lk3, lv3);
+        if (u + 2 > ntiles) break;
+        tile0(u + 2, lk2, lv1, lk3, lk0, lv0);
+        if (u + 3 > ntiles) break;
+        tile0(u + 3, lk3, lv2, lk0, lk1, lv1);
+      }
+      end_phase(false);  // group 1's last softmax phase
+    } else {
+      issue(2, lk2, lv2);  // phase 0: group 0's first matrix phase
+      WaveAttn::k_operands(lk0, to, 0, ka);
+      end_phase(true);
+      for (int u = 0; u <= ntiles; u += 4) {
+        tile1(u, lk0, lv3, lk1, lk3, lv3);
+        if (u + 1 > ntiles) break;
+        tile1(u + 1, lk1, lv0, lk2, lk0, lv0);
+        if (u + 2 > ntiles) break;
+        tile1(u + 2, lk2, lv1, lk3, lk1, lv1);
+        if (u + 3 > ntiles) break;
+        tile1(u + 3, lk3, lv2, lk0, lk2, lv2);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load may land in LDS after the end
+  }
+}
 
 }  // namespace abk

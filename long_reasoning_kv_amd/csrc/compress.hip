@@ -191,20 +191,8 @@ __global__ void __launch_bounds__(64) compress_attn_simt_kernel(CompressArgs a) 
 // (persistent, then open), then the pause-key tiles. Masks are applied only to
 // partial and pause tiles.
 //
-// The wavefronts form two groups, one wavefront of each on every SIMD, kept
-// one phase apart by a workgroup barrier between phases. In a matrix phase a
-// wavefront runs the previous tile's O^T += V^T P^T and then this tile's
-// S^T = K Q^T (64 MFMAs); in a vector phase it runs this tile's softmax. The
-// groups alternate, so each SIMD's matrix core works on one group's products
-// while its vector unit runs the other group's softmax:
-//   phase 2u:   group 0 matrix (PV u-1, QK u)   group 1 softmax u-1
-//   phase 2u+1: group 0 softmax u               group 1 matrix (PV u-1, QK u)
-// for u = 0..ntiles (absent tiles skipped). Tiles stream straight into a ring
-// of four LDS buffers (32 KB each: K rows swizzled by kswz, V rows by vt_swz):
-// at phase 2u every wavefront issues its share of tile u+2, and before the
-// barrier that ends phase 2u it waits for its share of tile u+1. Tile u's
-// buffer is read from phase 2u to 2u+3, and the load into it is issued at
-// phase 2u-4, after the barrier that ends its previous tile's last read.
+// The tiles run on the ping-pong schedule of pingpong_attention (two groups of
+// four wavefronts, one phase apart, through a ring of four LDS buffers).
 
 __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs a) {
   constexpr int D = 128, G = 4, TK = kTileKeys, RB = D * 2, QR = kCompressRows;
@@ -215,7 +203,6 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
   const DevPool& P = a.P;
   const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  const bool grp0 = wave < 4;  // wavefronts w and w + 4 share a SIMD
   // workgroup -> (rank of its pair = sequence x KV head in the launch order,
   // query tile, context split); the workgroups of one pair share blockIdx.x
   // mod 8, i.e. one XCD and its L2
@@ -266,24 +253,25 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
   }
   wa.init();
 
-  // ---- tile t: 64 K rows and 64 V rows (a context page, or pause keys). The
-  // page table is read through the constant address space (scalar loads: it
-  // does not change while the kernel runs).
-  const __attribute__((address_space(4))) int32_t* ctab =
-      (const __attribute__((address_space(4))) int32_t*)tab;
-  auto page_of = [&](int t) __attribute__((always_inline)) {
+  // ---- tile t: 64 K rows and 64 V rows (a context page, or pause keys). A
+  // page id is fetched one tile ahead with a vector load (the template asks
+  // for tiles u = 0, 1, 2, ... in order, the last one repeated past the end),
+  // so no scalar-load wait sits at the start of a phase; a pending scalar load
+  // would also make every LDS wait of the phase a full one.
+  const __amdgpu_buffer_rsrc_t rtab = __builtin_amdgcn_make_buffer_rsrc((void*)tab, 0, 0x7fffffff, 0x00020000);
+  auto load_page = [&](int u) __attribute__((always_inline)) {
+    const int t = gt(min(u, ntiles - 1));
     const int idx = t < npp ? t : P.max_pers + min(t - npp, nop - 1);
-    return ctab[idx];
+    return t < ntc ? (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, idx * 4, 0, 0) : 0;
   };
-  struct TileSrc {
-    const char* kb;
-    const char* vb;
-    int vstride, nval;
-  };
-  auto tile_src = [&](int t) __attribute__((always_inline)) {
+  int next_page = ntiles > 0 ? load_page(0) : 0;  // page id of the tile asked for next
+  auto tile_src = [&](int u) __attribute__((always_inline)) {
+    const int t = gt(u);
+    const int page = __builtin_amdgcn_readfirstlane(next_page);
+    next_page = load_page(u + 1);
     TileSrc ts;
     if (t < ntc) {
-      const size_t off = (((size_t)page_of(t) * P.Hkv + hk) * TK) * RB;
+      const size_t off = (((size_t)page * P.Hkv + hk) * TK) * RB;
       ts.kb = (const char*)P.kpool + off;
       ts.vb = (const char*)P.vpool + off;
       ts.vstride = RB;
@@ -297,101 +285,9 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
     }
     return ts;
   };
-  // Tile t straight from global memory into LDS (global_load_lds_dwordx4): in
-  // load j of wavefront w, lane l fills LDS chunk 512j + 64w + l, i.e. row
-  // 32j + 4w + l/16 at swizzled position l%16, so it fetches the source chunk
-  // that belongs there (both swizzles ignore bit 5 of the row). Rows past the
-  // tile's valid count repeat its last row. Four loads per wavefront.
-  const int r_in = 4 * wave + (lane >> 4);
-  const int kchunk = (lane & 15) ^ kswz(r_in), vchunk = (lane & 15) ^ vt_swz(r_in);
-  // byte offsets of a whole context page's loads: the same for every such
-  // tile, so computed once; 32-bit offsets from a uniform base let the loads
-  // take the scalar-base form
-  uint32_t kof_full[2], vof_full[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    kof_full[j] = (32 * j + r_in) * RB + 16 * kchunk;
-    vof_full[j] = (32 * j + r_in) * RB + 16 * vchunk;
-  }
-  auto issue = [&](int u, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
-    const TileSrc ts = tile_src(gt(min(u, ntiles - 1)));
-    uint32_t kof[2], vof[2];
-    if (ts.nval == TK && ts.vstride == RB) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        kof[j] = kof_full[j];
-        vof[j] = vof_full[j];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = min(32 * j + r_in, ts.nval - 1);
-        kof[j] = row * RB + 16 * kchunk;
-        vof[j] = row * ts.vstride + 16 * vchunk;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      __builtin_amdgcn_global_load_lds((const void*)(ts.kb + kof[j]),
-                                       (__attribute__((address_space(3))) void*)(dk + 512 * j + 64 * wave),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(ts.vb + vof[j]),
-                                       (__attribute__((address_space(3))) void*)(dv + 512 * j + 64 * wave),
-                                       16, 0, 0);
-    }
-  };
-  // the end of a phase: the wavefront's LDS reads have returned and, at the end
-  // of an even phase, its loads older than the last tile's four have landed;
-  // then every wavefront of the workgroup gets here (the loads of all of them
-  // are then in LDS). The signal fences keep the compiler from moving
-  // LDS accesses across the barrier.
-  auto end_phase = [&](bool wait_loads) __attribute__((always_inline)) {
-    if (wait_loads) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0): tile u+2 may fly
-    else __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): this phase's LDS reads are done
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  };
-
-  uint4 pb[2][2];  // a tile's probabilities between its softmax and the next matrix phase
-  uint4 va[4][2];  // its V^T operands of dims 0..63, read at the end of the softmax phase
-  TileOffsets to = tile_offsets(lane);
-  // The empty asm hides the lane offsets' values from the compiler, so that it
-  // adds them to each buffer's address at the read (an immediate offset)
-  // instead of keeping a register per buffer.
-  auto refresh = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(to.k[j]));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(to.v[j]));
-  };
-  // matrix phase of tile u: P V of tile u-1 (dims 0..63 from the operands in
-  // registers, dims 64..127 read from its V buffer vm1 first), then Q K^T of
-  // tile u from its K buffer k0; each group of operand reads is issued one
-  // group of products ahead of its use
-  auto matrix = [&](int u, const uint4* __restrict__ k0, const uint4* __restrict__ vm1, f32x4_t (&s)[4][2])
-      __attribute__((always_inline)) {
-    refresh();
-    const bool has_pv = u >= 1, has_qk = u < ntiles;
-    uint4 vb[4][2], ka[2][4], kb[2][4];
-    if (has_pv) {
-      WaveAttn::v_operands(vm1, to, 4, vb);
-      wa.pv_regs(va, 0, pb);
-    }
-    if (has_qk) WaveAttn::k_operands(k0, to, 0, ka);
-    if (has_pv) wa.pv_regs(vb, 4, pb);
-    if (has_qk) {
-      WaveAttn::k_operands(k0, to, 2, kb);
-      wa.qk_regs(ka, 0, s);
-      wa.qk_regs(kb, 2, s);
-    }
-  };
-  // softmax phase of tile u: masks for partial context pages and pause tiles (a
-  // uniform test; in a pause tile a query sees pause keys up to its own), then
-  // the tile's V operands of dims 0..63 from buffer v_buf into registers
-  auto vector = [&](int u, const uint4* __restrict__ v_buf, f32x4_t (&s)[4][2]) __attribute__((always_inline)) {
-    if (u < 0 || u >= ntiles) return;
-    refresh();
+  // softmax of tile u: masks for partial context pages and pause tiles (a
+  // uniform test; in a pause tile a query sees pause keys up to its own)
+  auto soft = [&](int u, f32x4_t (&s)[4][2], uint4 (&pb)[2][2]) __attribute__((always_inline)) {
     const int t = gt(u);
     const bool ctx = t < ntc;
     const int nval = ctx ? (t == npp - 1 ? n_pers - t * TK : TK) : min(TK, a.Kp - (t - ntc) * TK);
@@ -401,65 +297,8 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
       for (int nb = 0; nb < 2; ++nb) lim[nb] = (ctx ? nval : min(nval, qpause[nb] - kbase + 1)) - 8 * g4;
     };
     wa.softmax(s, !ctx || nval < TK, limits, qs, lane, pb);
-    WaveAttn::v_operands(v_buf, to, 0, va);
   };
-  // Tile u: its matrix phase, then its softmax phase; group 0 runs them as
-  // phases 2u and 2u+1, group 1 one phase later. Tile u is in buffer (k0, v0);
-  // at every even phase 2u each wavefront issues its share of tile u+2 (past
-  // the end it repeats the last tile into the spare buffer) and at the end of
-  // it waits for its share of tile u+1. Each group runs its own copy of the
-  // loop; both pass the same number of barriers.
-  auto tile0 = [&](int u, const uint4* __restrict__ k0, const uint4* __restrict__ v0,
-                   const uint4* __restrict__ vm1, uint4* __restrict__ k2, uint4* __restrict__ v2)
-      __attribute__((always_inline)) {
-    f32x4_t s[4][2];
-    issue(u + 2, k2, v2);
-    matrix(u, k0, vm1, s);
-    end_phase(true);
-    vector(u, v0, s);
-    end_phase(false);
-  };
-  auto tile1 = [&](int u, const uint4* __restrict__ k0, const uint4* __restrict__ v0,
-                   const uint4* __restrict__ vm1, uint4* __restrict__ k3, uint4* __restrict__ v3)
-      __attribute__((always_inline)) {
-    f32x4_t s[4][2];
-    matrix(u, k0, vm1, s);
-    end_phase(false);
-    issue(u + 3, k3, v3);
-    vector(u, v0, s);
-    end_phase(true);
-  };
-
-  if (ntiles > 0) {
-    issue(0, lk0, lv0);
-    issue(1, lk1, lv1);
-    end_phase(true);  // tile 0 is in
-    if (grp0) {
-      for (int u = 0; u <= ntiles; u += 4) {
-        tile0(u, lk0, lv0, lv3, lk2, lv2);
-        if (u + 1 > ntiles) break;
-        tile0(u + 1, lk1, lv1, lv0, lk3, lv3);
-        if (u + 2 > ntiles) break;
-        tile0(u + 2, lk2, lv2, lv1, lk0, lv0);
-        if (u + 3 > ntiles) break;
-        tile0(u + 3, lk3, lv3, lv2, lk1, lv1);
-      }
-      end_phase(false);  // group 1's last softmax phase
-    } else {
-      issue(2, lk2, lv2);  // phase 0: group 0's first matrix phase
-      end_phase(true);
-      for (int u = 0; u <= ntiles; u += 4) {
-        tile1(u, lk0, lv0, lv3, lk3, lv3);
-        if (u + 1 > ntiles) break;
-        tile1(u + 1, lk1, lv1, lv0, lk0, lv0);
-        if (u + 2 > ntiles) break;
-        tile1(u + 2, lk2, lv2, lv1, lk1, lv1);
-        if (u + 3 > ntiles) break;
-        tile1(u + 3, lk3, lv3, lv2, lk2, lv2);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load may land in LDS after the end
-  }
+  pingpong_attention(wa, ntiles, lane, wave, lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3, tile_src, soft);
 
   // ---- output: O^T / l; lane holds dims 16 db + 4 g4 + e of query l16. With
   // context splits: the unnormalised partial (O, m, l) for compress_merge_kernel

@@ -124,10 +124,11 @@ struct CompressArgs {
 // at rows [prompt + blk * quota_h[h] + k] of its [npers] slab (npers sized for
 // the largest). The attention pass takes one workgroup per record of desc
 // (kBmRec ints): {KV head (-1: none), kind (0 prompt, 1 text, 2 pause), first
-// query row, query tokens (<= 32), index of the first query in its range
+// query row, query tokens (<= kBmTokens), index of the first query in its range
 // (prompt, text-in-block or pause index), persistent rows it sees, first row
 // of its block in kst, rows of the block it sees, block}.
 constexpr int kBmRec = 9;
+constexpr int kBmTokens = 64;  // query tokens per record (256 query rows)
 constexpr int kMaxPrefillHeads = 16;
 struct BlockMaskArgs {
   DevPool P;

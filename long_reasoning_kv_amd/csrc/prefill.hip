@@ -87,21 +87,21 @@ __global__ void __launch_bounds__(512) blockmask_stage_kernel(BlockMaskArgs a) {
 
 // ---- attention on bf16 MFMA ---------------------------------------------------
 //
-// Workgroup = one descriptor record: a KV head and up to 32 query tokens of one
-// kind inside one block (query row r is token r/4, head 4h + r%4; each of the 4
+// Workgroup = one descriptor record: a KV head and up to 64 query tokens of one
+// kind inside one block (query row r is token r/4, head 4h + r%4; each of the 8
 // wavefronts owns 32 rows). Its keys are two contiguous ranges: A, the layer's
 // persistent rows (kpers: the prompt, then the kept code rows in block order),
 // of which it sees the first nA (prompt tokens: causally); and B, its own
 // block in training order (kst from the block's first text row), of which it
 // sees the first nB rows, text causally and, for pause queries, pause keys up
-// to their own. Each range streams through LDS in 64-key tiles with the
-// per-tile math of attn_mfma.h, the next tile loading while the current one is
-// computed; a tile is masked only when one of its keys lies past the smallest
-// limit of the workgroup's queries.
-__global__ void __launch_bounds__(256, 2) blockmask_attn_mfma_kernel(BlockMaskArgs a) {
+// to their own. The ranges stream through LDS in 64-key tiles, A then B, on the
+// ping-pong schedule of attn_mfma.h; a tile is masked only when one of its keys
+// lies past the smallest limit of the workgroup's queries.
+__global__ void __launch_bounds__(512, 1) blockmask_attn_mfma_kernel(BlockMaskArgs a) {
   constexpr int D = 128, G = 4, TK = kTileKeys, RB = D * 2;
-  __shared__ uint4 lk0[TK * RB / 16], lk1[TK * RB / 16];
-  __shared__ uint4 lv0[TK * RB / 16], lv1[TK * RB / 16];
+  constexpr int TCH = TK * RB / 16;  // 16-byte chunks of a 64-row K (or V) tile
+  __shared__ uint4 lk0[TCH], lk1[TCH], lk2[TCH], lk3[TCH];
+  __shared__ uint4 lv0[TCH], lv1[TCH], lv2[TCH], lv3[TCH];
   const DevPool& P = a.P;
   const int lane = threadIdx.x & 63, wave = sgpr(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -117,7 +117,7 @@ __global__ void __launch_bounds__(256, 2) blockmask_attn_mfma_kernel(BlockMaskAr
   const int minB = kind == 1 ? tok0 + 1 : a.C + tok0 + 1;
 
   // ---- the wavefront's query rows (rotated at their positions, rounded once
-  // to bf16) and their limits in both ranges; rows past the tile's tokens
+  // to bf16) and their limits in both ranges; rows past the record's tokens
   // repeat its last token and are not written
   const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
   WaveAttn wa;
@@ -138,75 +138,26 @@ __global__ void __launch_bounds__(256, 2) blockmask_attn_mfma_kernel(BlockMaskAr
   }
   wa.init();
 
-  // ---- tile t: range A tile t (t < ntA), else range B tile t - ntA
-  struct TileSrc {
-    const char* kb;
-    const char* vb;
-    int nval, r0;
-    bool in_a;
-  };
-  auto tile_src = [&](int t) __attribute__((always_inline)) {
+  // ---- tile u: range A tile u (u < ntA), else range B tile u - ntA
+  auto tile_src = [&](int u) __attribute__((always_inline)) {
     TileSrc ts;
-    ts.in_a = t < ntA;
-    if (ts.in_a) {
-      ts.r0 = t * TK;
-      const size_t off = ((size_t)hk * a.npers + ts.r0) * RB;
+    ts.vstride = RB;
+    if (u < ntA) {
+      const int r0 = u * TK;
+      const size_t off = ((size_t)hk * a.npers + r0) * RB;
       ts.kb = (const char*)a.kpers + off;
       ts.vb = (const char*)a.vpers + off;
-      ts.nval = min(TK, rowsA - ts.r0);
+      ts.nval = min(TK, rowsA - r0);
     } else {
-      ts.r0 = (t - ntA) * TK;
-      const size_t off = ((size_t)hk * a.T + bstart + ts.r0) * RB;
+      const int r0 = (u - ntA) * TK;
+      const size_t off = ((size_t)hk * a.T + bstart + r0) * RB;
       ts.kb = (const char*)a.kst + off;
       ts.vb = (const char*)a.vst + off;
-      ts.nval = min(TK, nB - ts.r0);
+      ts.nval = min(TK, nB - r0);
     }
     return ts;
   };
-  // loads as in the compression kernel: in load j of wavefront w, lane l fills
-  // LDS chunk 256j + 64w + l (row 16j + 4w + l/16 at swizzled position l%16);
-  // rows past the tile's valid count repeat its last row
-  const int r_in = 4 * wave + (lane >> 4);
-  const int vchunk = (lane & 15) ^ vt_swz(r_in);
-  uint32_t kof_full[4], vof_full[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    kof_full[j] = (16 * j + r_in) * RB + 16 * ((lane & 15) ^ kswz(16 * j + r_in));
-    vof_full[j] = (16 * j + r_in) * RB + 16 * vchunk;
-  }
-  auto issue = [&](int t, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
-    const TileSrc ts = tile_src(t);
-    uint32_t kof[4], vof[4];
-    if (ts.nval == TK) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kof[j] = kof_full[j];
-        vof[j] = vof_full[j];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = min(16 * j + r_in, ts.nval - 1);
-        kof[j] = row * RB + 16 * ((lane & 15) ^ kswz(16 * j + r_in));
-        vof[j] = row * RB + 16 * vchunk;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_global_load_lds((const void*)(ts.kb + kof[j]),
-                                       (__attribute__((address_space(3))) void*)(dk + 256 * j + 64 * wave),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(ts.vb + vof[j]),
-                                       (__attribute__((address_space(3))) void*)(dv + 256 * j + 64 * wave),
-                                       16, 0, 0);
-    }
-  };
-
-  // one tile from (ck, cv) while the next loads into (nk, nv); the load is
-  // unconditional (past the end it repeats the last tile into the spare buffer)
-  auto step = [&](int u, const uint4* __restrict__ ck, const uint4* __restrict__ cv,
-                  uint4* __restrict__ nk, uint4* __restrict__ nv) __attribute__((always_inline)) {
-    issue(min(u + 1, ntiles - 1), nk, nv);
+  auto soft = [&](int u, f32x4_t (&s)[4][2], uint4 (&pb)[2][2]) __attribute__((always_inline)) {
     const bool in_a = u < ntA;
     const int r0 = in_a ? u * TK : (u - ntA) * TK;
     const int rows = in_a ? rowsA : nB;
@@ -214,20 +165,9 @@ __global__ void __launch_bounds__(256, 2) blockmask_attn_mfma_kernel(BlockMaskAr
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) lim[nb] = min(in_a ? limA[nb] : limB[nb], rows) - r0 - 8 * g4;
     };
-    wa.tile(ck, cv, r0 + TK > (in_a ? minA : minB), limits, qs, lane);
+    wa.softmax(s, r0 + TK > (in_a ? minA : minB), limits, qs, lane, pb);
   };
-
-  if (ntiles > 0) {
-    issue(0, lk0, lv0);
-    __syncthreads();
-    for (int u = 0; u < ntiles; u += 2) {
-      step(u, lk0, lv0, lk1, lv1);
-      __syncthreads();
-      if (u + 1 >= ntiles) break;
-      step(u + 1, lk1, lv1, lk0, lv0);
-      __syncthreads();
-    }
-  }
+  pingpong_attention(wa, ntiles, lane, wave, lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3, tile_src, soft);
 
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -245,7 +185,7 @@ bool blockmask_supported(const DevPool& P, int32_t G) { return P.dtype == 1 && P
 hipError_t launch_blockmask(const BlockMaskArgs& a, int32_t nrec, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   hipLaunchKernelGGL(blockmask_stage_kernel, dim3((a.T + kStageRows - 1) / kStageRows), dim3(512), 0, s, a);
-  if (nrec > 0) hipLaunchKernelGGL(blockmask_attn_mfma_kernel, dim3(nrec), dim3(256), 0, s, a);
+  if (nrec > 0) hipLaunchKernelGGL(blockmask_attn_mfma_kernel, dim3(nrec), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
