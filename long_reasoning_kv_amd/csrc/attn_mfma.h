@@ -306,11 +306,12 @@ struct TileSrc {
 // runs on a repeated tile and its scores are dropped, and no softmax phase runs
 // for u = ntiles). Tiles stream straight into a ring
 // of four LDS buffers (32 KB each: K rows swizzled by kswz, V rows by vt_swz):
-// at phase 2u every wavefront issues its share of tile u+2, and before the
-// barrier that ends phase 2u it waits for its share of tile u+1. Tile u's
-// buffer is read from phase 2u to 2u+3, and the load into it is issued at
-// phase 2u-4, after the barrier that ends its previous tile's last read.
-// tile_src(u) gives tile u's place; each wavefront asks for u = 0, 1, 2, ...
+// at phase 2u each wavefront of group 0 issues its share of tile u+2, and
+// before the barrier that ends phase 2u it waits for its share of tile u+1.
+// Tile u's buffer is read from phase 2u to 2u+3, and the load into it is
+// issued at phase 2u-4, after the barrier that ends its previous tile's last
+// read.
+// tile_src(u) gives tile u's place; each wavefront of group 0 asks for u = 0, 1, 2, ...
 // in order, once each, then for ntiles - 1 again past the end (a tile source
 // may fetch ahead). soft(u, s, pb) runs tile u's
 // softmax (wa.softmax with the tile's masks). The ring buffers are separate
@@ -326,37 +327,41 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
   const bool grp0 = wave < 4;
   // Tile t straight from global memory into LDS (buffer_load_dwordx4 ... lds,
   // the MUBUF form: the compiler's wait counting treats a FLAT load into LDS as
-  // an LDS access of unknown order and then waits for every LDS read): in
-  // load j of wavefront w, lane l fills LDS chunk 512j + 64w + l, i.e. row
-  // 32j + 4w + l/16 at swizzled position l%16, so it fetches the source chunk
-  // that belongs there (both swizzles ignore bit 5 of the row). Rows past the
-  // tile's valid count repeat its last row. Four loads per wavefront.
+  // an LDS access of unknown order and then waits for every LDS read). Group 0
+  // alone loads the tiles, in its matrix phases, where the address work takes
+  // issue slots between the products; group 1's softmax phases then carry no
+  // load work. In load j of wavefront w (w < 4), lane l fills LDS chunk 256j +
+  // 64w + l, i.e. row 16j + 4w + l/16 at swizzled position l%16, so it fetches
+  // the source chunk that belongs there (the V swizzle ignores bits 4 and 5 of
+  // the row, the K swizzle bit 5). Rows past the tile's valid count repeat its
+  // last row. Eight loads per wavefront of group 0.
   const int r_in = 4 * wave + (lane >> 4);
-  const int kchunk = (lane & 15) ^ kswz(r_in), vchunk = (lane & 15) ^ vt_swz(r_in);
-  // byte offsets of a whole tile of 256-byte rows: the same for every such
-  // tile, so computed once; 32-bit offsets from a uniform base let the loads
-  // take the scalar-base form
-  uint32_t kof_full[2], vof_full[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    kof_full[j] = (32 * j + r_in) * RB + 16 * kchunk;
-    vof_full[j] = (32 * j + r_in) * RB + 16 * vchunk;
-  }
+  const int kchunk0 = (lane & 15) ^ kswz(r_in), kchunk1 = (lane & 15) ^ kswz(16 + r_in);
+  const int vchunk = (lane & 15) ^ vt_swz(r_in);
+  // byte offsets of loads 0 and 1 of a whole tile of 256-byte rows, the same
+  // for every such tile (loads 2 and 3 add 32 rows through the scalar offset);
+  // 32-bit offsets from a uniform base let the loads take the scalar-base form
+  const uint32_t kof_full0 = r_in * RB + 16 * kchunk0, kof_full1 = (16 + r_in) * RB + 16 * kchunk1;
+  const uint32_t vof_full = r_in * RB + 16 * vchunk;
   auto issue = [&](int u, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
     const TileSrc ts = tile_src(min(u, ntiles - 1));
-    uint32_t kof[2], vof[2];
+    uint32_t kof[4], vof[4];
+    int ksoff[4], vsoff[4];
     if (ts.nval == kTileKeys && ts.vstride == RB) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        kof[j] = kof_full[j];
-        vof[j] = vof_full[j];
+      for (int j = 0; j < 4; ++j) {
+        kof[j] = (j & 1) ? kof_full1 : kof_full0;
+        ksoff[j] = (j >> 1) * 32 * RB;
+        vof[j] = vof_full;
+        vsoff[j] = j * 16 * RB;
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = min(32 * j + r_in, ts.nval - 1);
-        kof[j] = row * RB + 16 * kchunk;
+      for (int j = 0; j < 4; ++j) {
+        const int row = min(16 * j + r_in, ts.nval - 1);
+        kof[j] = row * RB + 16 * ((j & 1) ? kchunk1 : kchunk0);
         vof[j] = row * ts.vstride + 16 * vchunk;
+        ksoff[j] = vsoff[j] = 0;
       }
     }
     // raw buffer descriptors over the tile's K and V (stride 0, a range the
@@ -364,21 +369,21 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)ts.kb, 0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)ts.vb, 0, 0x7fffffff, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk + 512 * j + 64 * wave),
-                                               16, kof[j], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv + 512 * j + 64 * wave),
-                                               16, vof[j], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk + 256 * j + 64 * wave),
+                                               16, kof[j], ksoff[j], 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv + 256 * j + 64 * wave),
+                                               16, vof[j], vsoff[j], 0, 0);
     }
   };
   // the end of a phase: the wavefront's LDS reads have returned and, at the end
-  // of an even phase, its loads older than the last tile's four have landed;
-  // then every wavefront of the workgroup gets here (the loads of all of them
-  // are then in LDS). The signal fences keep the compiler from moving
+  // of group 0's matrix phase, its loads older than the last tile's eight have
+  // landed; then every wavefront of the workgroup gets here (the loads of
+  // group 0 are then in LDS). The signal fences keep the compiler from moving
   // LDS accesses across the barrier, the scheduling barriers any other
   // instruction (products of one phase must not sink into the next).
   auto end_phase = [&](bool wait_loads) __attribute__((always_inline)) {
-    if (wait_loads) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0): tile u+2 may fly
+    if (wait_loads) __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): tile u+2 may fly
     else __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): this phase's LDS reads are done
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_sched_barrier(0);
@@ -457,10 +462,11 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
   };
   // Tile u: its matrix phase, then its softmax phase; group 0 runs them as
   // phases 2u and 2u+1, group 1 one phase later. Tile u is in buffer (k0, v0),
-  // tile u+1 in (k1, v1); at every even phase 2u each wavefront issues its share
-  // of tile u+2 (past the end it repeats the last tile into the spare buffer)
-  // and at the end of it waits for its share of tile u+1. Each group runs its
-  // own copy of the loop; both pass the same number of barriers.
+  // tile u+1 in (k1, v1); at every even phase 2u each wavefront of group 0
+  // issues its share of tile u+2 (past the end it repeats the last tile into
+  // the spare buffer) and at the end of it waits for its share of tile u+1.
+  // Each group runs its own copy of the loop; both pass the same number of
+  // barriers.
   auto tile0 = [&](int u, const uint4* __restrict__ k0, const uint4* __restrict__ vm1,
                    const uint4* __restrict__ k1, uint4* __restrict__ k2, uint4* __restrict__ v2)
       __attribute__((always_inline)) {
@@ -472,23 +478,23 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
     end_phase(false);
   };
   auto tile1 = [&](int u, const uint4* __restrict__ k0, const uint4* __restrict__ vm1,
-                   const uint4* __restrict__ k1, uint4* __restrict__ k3, uint4* __restrict__ v3)
-      __attribute__((always_inline)) {
+                   const uint4* __restrict__ k1) __attribute__((always_inline)) {
     f32x4_t s[4][2];
     matrix(k0, vm1, s);
     end_phase(false);
-    issue(u + 3, k3, v3);
     vector(u, k1, s);
-    end_phase(true);
+    end_phase(false);
   };
 
   if (ntiles > 0) {
-    issue(0, lk0, lv0);
-    issue(1, lk1, lv1);
+    if (grp0) {
+      issue(0, lk0, lv0);
+      issue(1, lk1, lv1);
+    }
     // zeros in the V buffer that the first matrix phase reads as tile -1
     lv3[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
     lv3[threadIdx.x + 512] = make_uint4(0u, 0u, 0u, 0u);
-    end_phase(true);  // tile 0 and the zeros are in
+    end_phase(grp0);  // tile 0 and the zeros are in
     if (grp0) {
       WaveAttn::k_operands(lk0, to, 0, ka);
       for (int u = 0; u <= ntiles; u += 4) {
@@ -502,17 +508,16 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
       }
       end_phase(false);  // group 1's last softmax phase
     } else {
-      issue(2, lk2, lv2);  // phase 0: group 0's first matrix phase
       WaveAttn::k_operands(lk0, to, 0, ka);
-      end_phase(true);
+      end_phase(false);  // phase 0: group 0's first matrix phase
       for (int u = 0; u <= ntiles; u += 4) {
-        tile1(u, lk0, lv3, lk1, lk3, lv3);
+        tile1(u, lk0, lv3, lk1);
         if (u + 1 > ntiles) break;
-        tile1(u + 1, lk1, lv0, lk2, lk0, lv0);
+        tile1(u + 1, lk1, lv0, lk2);
         if (u + 2 > ntiles) break;
-        tile1(u + 2, lk2, lv1, lk3, lk1, lv1);
+        tile1(u + 2, lk2, lv1, lk3);
         if (u + 3 > ntiles) break;
-        tile1(u + 3, lk3, lv2, lk0, lk2, lv2);
+        tile1(u + 3, lk3, lv2, lk0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load may land in LDS after the end

@@ -224,15 +224,13 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
   const int q0 = qt * QR;     // first query row of the workgroup
   const int nq = min(QR, 4 * a.Kp - q0);
   const int last_pause = (q0 + nq - 1) >> 2;
-  // this split's tiles: context tiles [tc0, tc1), then, in the last split, the
-  // pause-key tiles; local tile u maps to tile index gt(u) (pause tiles follow
-  // the ntc context tiles)
+  // this split's tiles: local tile u < nct is context tile tc0 + u (of
+  // [tc0, tc1)); in the last split, pause-key tile u - nct follows
   const int cps = (ntc + ns - 1) / ns;
   const int tc0 = min(ntc, sp * cps), tc1 = min(ntc, tc0 + cps);
   const int nct = tc1 - tc0;
   const int ntp = sp == ns - 1 ? last_pause / TK + 1 : 0;  // pause-key tiles
   const int ntiles = nct + ntp;
-  auto gt = [&](int u) { return u < nct ? tc0 + u : ntc + (u - nct); };
 
   // ---- the wavefront's query rows: rotated at the bitrev position, rounded
   // once to bf16 (like stored keys); the softmax scale goes on the fp32 scores.
@@ -259,25 +257,34 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
   // so no scalar-load wait sits at the start of a phase; a pending scalar load
   // would also make every LDS wait of the phase a full one.
   const __amdgpu_buffer_rsrc_t rtab = __builtin_amdgcn_make_buffer_rsrc((void*)tab, 0, 0x7fffffff, 0x00020000);
+  // Per-tile address work is kept small (it takes issue slots in the loop):
+  // local tile u < nct is context tile tc0 + u, whose page id sits at table
+  // index tc0 + u (persistent) or tc0 + u + open_shift (open block); its K and
+  // V rows start page * pstride past the head's bases.
+  const int open_shift = P.max_pers - npp;
+  const uint64_t pstride = (uint64_t)P.Hkv * TK * RB;
+  const char* kbase_h = (const char*)P.kpool + (size_t)hk * TK * RB;
+  const char* vbase_h = (const char*)P.vpool + (size_t)hk * TK * RB;
+  const int last_local = min(ntiles, nct) - 1;                  // last local context tile
+  const int nval_last = n_pers - (npp - 1) * TK;
   auto load_page = [&](int u) __attribute__((always_inline)) {
-    const int t = gt(min(u, ntiles - 1));
-    const int idx = t < npp ? t : P.max_pers + min(t - npp, nop - 1);
-    return t < ntc ? (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, idx * 4, 0, 0) : 0;
+    const int t = tc0 + u;
+    return u <= last_local ? (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, (t < npp ? t : t + open_shift) * 4, 0, 0)
+                           : 0;
   };
   int next_page = ntiles > 0 ? load_page(0) : 0;  // page id of the tile asked for next
   auto tile_src = [&](int u) __attribute__((always_inline)) {
-    const int t = gt(u);
     const int page = __builtin_amdgcn_readfirstlane(next_page);
-    next_page = load_page(u + 1);
+    next_page = load_page(min(u + 1, ntiles - 1));
     TileSrc ts;
-    if (t < ntc) {
-      const size_t off = (((size_t)page * P.Hkv + hk) * TK) * RB;
-      ts.kb = (const char*)P.kpool + off;
-      ts.vb = (const char*)P.vpool + off;
+    if (u < nct) {
+      const uint64_t off = (uint64_t)(uint32_t)page * pstride;
+      ts.kb = kbase_h + off;
+      ts.vb = vbase_h + off;
       ts.vstride = RB;
-      ts.nval = (t == npp - 1) ? n_pers - t * TK : TK;
+      ts.nval = tc0 + u == npp - 1 ? nval_last : TK;
     } else {
-      const int k0 = (t - ntc) * TK;
+      const int k0 = (u - nct) * TK;
       ts.kb = (const char*)a.kp_rot + (((size_t)i * P.Hkv + hk) * a.Kp + k0) * RB;
       ts.vb = (const char*)a.vp + (((size_t)ir * a.Kp + k0) * HkvR + H) * RB;
       ts.vstride = HkvR * RB;
@@ -288,10 +295,9 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
   // softmax of tile u: masks for partial context pages and pause tiles (a
   // uniform test; in a pause tile a query sees pause keys up to its own)
   auto soft = [&](int u, f32x4_t (&s)[4][2], uint4 (&pb)[2][2]) __attribute__((always_inline)) {
-    const int t = gt(u);
-    const bool ctx = t < ntc;
-    const int nval = ctx ? (t == npp - 1 ? n_pers - t * TK : TK) : min(TK, a.Kp - (t - ntc) * TK);
-    const int kbase = ctx ? 0 : (t - ntc) * TK;  // pause index of key 0 of a pause tile
+    const bool ctx = u < nct;
+    const int kbase = ctx ? 0 : (u - nct) * TK;  // pause index of key 0 of a pause tile
+    const int nval = ctx ? (tc0 + u == npp - 1 ? nval_last : TK) : min(TK, a.Kp - kbase);
     auto limits = [&](int (&lim)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) lim[nb] = (ctx ? nval : min(nval, qpause[nb] - kbase + 1)) - 8 * g4;
