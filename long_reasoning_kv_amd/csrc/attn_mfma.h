@@ -134,21 +134,52 @@ struct WaveAttn {
     }
   }
 
+  // Plain v_max_f32 / v_min_f32 / v_max3_f32. fmaxf under IEEE mode must quiet a
+  // signalling NaN, so the compiler puts a canonicalising v_max x, x in front
+  // of every operand it cannot prove canonical (MFMA and lane-swap results);
+  // the scores here are finite or -inf.
+  __device__ __forceinline__ static float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+  }
+  __device__ __forceinline__ static float vmin(float a, float b) {
+    float r;
+    asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+  }
+  __device__ __forceinline__ static float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+  }
   // Maximum of query column nb's 16 scores in this lane, as a tree.
   __device__ __forceinline__ static float col_max(const f32x4_t (&s)[4][2], int nb) {
-    const float a = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), s[0][nb][2]);
-    const float b = fmaxf(fmaxf(s[0][nb][3], s[1][nb][0]), s[1][nb][1]);
-    const float c = fmaxf(fmaxf(s[1][nb][2], s[1][nb][3]), s[2][nb][0]);
-    const float d = fmaxf(fmaxf(s[2][nb][1], s[2][nb][2]), s[2][nb][3]);
-    const float e = fmaxf(fmaxf(s[3][nb][0], s[3][nb][1]), s[3][nb][2]);
-    return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[3][nb][3]));
+    const float a = vmax3(s[0][nb][0], s[0][nb][1], s[0][nb][2]);
+    const float b = vmax3(s[0][nb][3], s[1][nb][0], s[1][nb][1]);
+    const float c = vmax3(s[1][nb][2], s[1][nb][3], s[2][nb][0]);
+    const float d = vmax3(s[2][nb][1], s[2][nb][2], s[2][nb][3]);
+    const float e = vmax3(s[3][nb][0], s[3][nb][1], s[3][nb][2]);
+    return vmax(vmax3(a, b, c), vmax3(d, e, s[3][nb][3]));
+  }
+  // The maxima over the four lanes l%16 + 16r (r = 0..3) of both columns at
+  // once: the first swap pairs column 0's odd rows with column 1's even rows,
+  // so that after it and the 32-lane swap rows 0, 2 hold column 0's maximum
+  // and rows 1, 3 column 1's; the last swap hands every lane both.
+  __device__ __forceinline__ static void rows4_max2(float& x0, float& x1) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x0), __float_as_uint(x1), false, false);
+    const float m = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    const float y = vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    x0 = __uint_as_float(c[0]);
+    x1 = __uint_as_float(c[1]);
   }
 
   // Online softmax of a tile's scores. When `masked`, key tile_key(mb, 4 g4 +
   // e) = 8 g4 + (32(mb/2) + 4(mb%2) + e) of query column nb is kept only if
   // 32(mb/2) + 4(mb%2) + e < lim[nb], the bound in this lane's key
-  // coordinates that limits(lim) fills (called only then): one compare per
-  // element. qs = log2(e)/sqrt(d). Moves the running maximum (rescaling O^T
+  // coordinates that limits(lim) fills (called only then). qs = log2(e)/sqrt(d). Moves the running maximum (rescaling O^T
   // and the sum) when needed, adds the tile's probabilities to the sum and
   // leaves them, as bf16, in pb[nb][kk] (keys 32 kk + 8 g4 + 0..7).
   template <class Limits>
@@ -156,15 +187,26 @@ struct WaveAttn {
                                           uint4 (&pb)[2][2]) {
     (void)lane;
     if (masked) {
+      // key position k (0..39) is kept if k < lim, i.e. if (lim - 0.5 - k)
+      // 2^120 is positive: that bound is then at least 2^119 and min(s, bound)
+      // = s (the scores are far smaller); for a dropped key it is at most
+      // -2^119, which the exponential turns into exactly 0. With lim clamped
+      // to [-1, 64] no bound overflows. One FMA and one min per score, with
+      // no compare-to-mask hazard between them.
       int lim[2];
       limits(lim);
+      constexpr float big = 0x1p120f;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < 2; ++nb) {
+        const float fl = ((float)min(max(lim[nb], -1), 64) - 0.5f) * big;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            s[mb][nb][e] = 32 * (mb >> 1) + 4 * (mb & 1) + e < lim[nb] ? s[mb][nb][e] : -INFINITY;
+          for (int e = 0; e < 4; ++e) {
+            const float k = (float)(32 * (mb >> 1) + 4 * (mb & 1) + e);
+            s[mb][nb][e] = vmin(s[mb][nb][e], fmaf(-k, big, fl));
+          }
+      }
     }
     // per query column (lane-local after the row swaps). The phase runs on
     // one wavefront per SIMD, which hides no latency, so the reductions are
@@ -172,8 +214,9 @@ struct WaveAttn {
     float mx[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) mx[nb] = col_max(s, nb);
+    rows4_max2(mx[0], mx[1]);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) mx[nb] = rows4_max(mx[nb]) * qs;  // log2 units
+    for (int nb = 0; nb < 2; ++nb) mx[nb] *= qs;  // log2 units
     float mn[2], alpha[2];
     bool moved = false;
 #pragma unroll
