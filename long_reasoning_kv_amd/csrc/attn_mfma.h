@@ -495,13 +495,15 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
     sched_lds<2>();
     sched_mfma<14>();
   };
-  // softmax phase of tile u, then the K operands of M-blocks 0, 1 of tile u+1
-  // from its buffer k1 (in LDS since the barrier that began this phase)
+  // softmax phase of tile u, with the K operands of M-blocks 0, 1 of tile u+1
+  // read from its buffer k1 (in LDS since the barrier that began this phase)
   auto vector = [&](int u, const uint4* __restrict__ k1, f32x4_t (&s)[4][2]) __attribute__((always_inline)) {
     if (u >= ntiles) return;
     refresh();
-    soft(u, s, pb);
+    // the reads first, so that their latency passes under the softmax
     WaveAttn::k_operands(k1, to, 0, ka);
+    __builtin_amdgcn_sched_barrier(0);
+    soft(u, s, pb);
   };
   // Tile u: its matrix phase, then its softmax phase; group 0 runs them as
   // phases 2u and 2u+1, group 1 one phase later. Tile u is in buffer (k0, v0),
