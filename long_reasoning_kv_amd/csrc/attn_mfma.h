@@ -21,6 +21,8 @@
 // evenly.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace abk {
@@ -208,33 +210,33 @@ struct WaveAttn {
           }
       }
     }
-    // per query column (lane-local after the row swaps). The phase runs on
-    // one wavefront per SIMD, which hides no latency, so the reductions are
-    // trees and the two columns' chains are independent.
+    // The running maximum of a column moves only when the tile's maximum
+    // exceeds it by more than 8 (log2 units). Each lane first tests its own
+    // scores' maximum, a tree over lane-local registers; only when some lane
+    // of the wavefront passes the test does the maximum over the column's four
+    // lanes (three lane swaps, a serial chain) run, with the rescale. A column
+    // whose lanes all stay below the bound cannot move, so the decisions are
+    // the same as with the reduction on every tile. Multiplying by qs > 0 keeps
+    // the order of the rounded products, so the lane test agrees with the test
+    // of the reduced maximum.
     float mx[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) mx[nb] = col_max(s, nb);
-    rows4_max2(mx[0], mx[1]);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) mx[nb] *= qs;  // log2 units
-    float mn[2], alpha[2];
-    bool moved = false;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const bool up = mx[nb] > m[nb] + 8.f;
-      mn[nb] = up ? mx[nb] : m[nb];
-      alpha[nb] = fast_exp2(m[nb] - mn[nb]);
-      moved = moved || up;
-      m[nb] = mn[nb];
-    }
-    if (__builtin_amdgcn_ballot_w64(moved)) {
+    const bool over = mx[0] * qs > m[0] + 8.f || mx[1] * qs > m[1] + 8.f;
+    if (__builtin_amdgcn_ballot_w64(over)) {
+      rows4_max2(mx[0], mx[1]);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        l[nb] *= alpha[nb];
+        const float t = mx[nb] * qs;  // log2 units
+        const float mn = t > m[nb] + 8.f ? t : m[nb];
+        const float alpha = fast_exp2(m[nb] - mn);
+        m[nb] = mn;
+        l[nb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) acc[nb][db] *= alpha[nb];
+        for (int db = 0; db < 8; ++db) acc[nb][db] *= alpha;
       }
     }
+    const float mn[2] = {m[0], m[1]};
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -356,16 +358,17 @@ struct TileSrc {
 // read.
 // tile_src(u) gives tile u's place; each wavefront of group 0 asks for u = 0, 1, 2, ...
 // in order, once each, then for ntiles - 1 again past the end (a tile source
-// may fetch ahead). soft(u, s, pb) runs tile u's
+// may fetch ahead: it then issues kSrcLoads memory loads per call, at most 7). soft(u, s, pb) runs tile u's
 // softmax (wa.softmax with the tile's masks). The ring buffers are separate
 // __shared__ arrays of the kernel, so that the compiler can tell them apart.
-template <class TileFn, class SoftFn>
+template <int kSrcLoads, class TileFn, class SoftFn>
 __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int lane, int wave,
                                                    uint4* __restrict__ lk0, uint4* __restrict__ lk1,
                                                    uint4* __restrict__ lk2, uint4* __restrict__ lk3,
                                                    uint4* __restrict__ lv0, uint4* __restrict__ lv1,
                                                    uint4* __restrict__ lv2, uint4* __restrict__ lv3,
                                                    TileFn tile_src, SoftFn soft) {
+  static_assert(kSrcLoads >= 0 && kSrcLoads <= 7, "the wait count holds 15 loads");
   constexpr int RB = 256;  // bytes of a bf16 row of 128 dims
   const bool grp0 = wave < 4;
   // Tile t straight from global memory into LDS (buffer_load_dwordx4 ... lds,
@@ -379,54 +382,36 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
   // the row, the K swizzle bit 5). Rows past the tile's valid count repeat its
   // last row. Eight loads per wavefront of group 0.
   const int r_in = 4 * wave + (lane >> 4);
-  const int kchunk0 = (lane & 15) ^ kswz(r_in), kchunk1 = (lane & 15) ^ kswz(16 + r_in);
-  const int vchunk = (lane & 15) ^ vt_swz(r_in);
-  // byte offsets of loads 0 and 1 of a whole tile of 256-byte rows, the same
-  // for every such tile (loads 2 and 3 add 32 rows through the scalar offset);
-  // 32-bit offsets from a uniform base let the loads take the scalar-base form
-  const uint32_t kof_full0 = r_in * RB + 16 * kchunk0, kof_full1 = (16 + r_in) * RB + 16 * kchunk1;
-  const uint32_t vof_full = r_in * RB + 16 * vchunk;
+  const int kc0 = 16 * ((lane & 15) ^ kswz(r_in)), kc1 = 16 * ((lane & 15) ^ kswz(16 + r_in));
+  const int vc = 16 * ((lane & 15) ^ vt_swz(r_in));
+  // One form for every tile, without branches, so that its instructions can
+  // be spread between the products: load j takes row min(16 j + r_in, nval -
+  // 1) of the tile (a row of a whole tile is its own), at a per-lane offset.
   auto issue = [&](int u, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
     const TileSrc ts = tile_src(min(u, ntiles - 1));
-    uint32_t kof[4], vof[4];
-    int ksoff[4], vsoff[4];
-    if (ts.nval == kTileKeys && ts.vstride == RB) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kof[j] = (j & 1) ? kof_full1 : kof_full0;
-        ksoff[j] = (j >> 1) * 32 * RB;
-        vof[j] = vof_full;
-        vsoff[j] = j * 16 * RB;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = min(16 * j + r_in, ts.nval - 1);
-        kof[j] = row * RB + 16 * ((j & 1) ? kchunk1 : kchunk0);
-        vof[j] = row * ts.vstride + 16 * vchunk;
-        ksoff[j] = vsoff[j] = 0;
-      }
-    }
+    const int last = ts.nval - 1;
     // raw buffer descriptors over the tile's K and V (stride 0, a range the
     // offsets never reach; 0x00020000 is the format word of untyped data)
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)ts.kb, 0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)ts.vb, 0, 0x7fffffff, 0x00020000);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const int row = min(16 * j + r_in, last);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk + 256 * j + 64 * wave),
-                                               16, kof[j], ksoff[j], 0, 0);
+                                               16, row * RB + ((j & 1) ? kc1 : kc0), 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv + 256 * j + 64 * wave),
-                                               16, vof[j], vsoff[j], 0, 0);
+                                               16, row * ts.vstride + vc, 0, 0, 0);
     }
   };
   // the end of a phase: the wavefront's LDS reads have returned and, at the end
-  // of group 0's matrix phase, its loads older than the last tile's eight have
-  // landed; then every wavefront of the workgroup gets here (the loads of
+  // of group 0's matrix phase, its loads older than this phase's (eight rows
+  // and the tile source's own kSrcLoads, in any order) have landed; then every wavefront of the workgroup gets here (the loads of
   // group 0 are then in LDS). The signal fences keep the compiler from moving
   // LDS accesses across the barrier, the scheduling barriers any other
   // instruction (products of one phase must not sink into the next).
   auto end_phase = [&](bool wait_loads) __attribute__((always_inline)) {
-    if (wait_loads) __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0): tile u+2 may fly
+    // vmcnt(8 + kSrcLoads) lgkmcnt(0): this phase's loads may fly
+    if (wait_loads) __builtin_amdgcn_s_waitcnt(0x0070 | (8 + kSrcLoads));
     else __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): this phase's LDS reads are done
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_sched_barrier(0);
@@ -458,9 +443,13 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
   // (past the last tile the products run on the spare buffer's repeated tile
   // and are discarded). M-blocks 0, 1 come from registers; each group of
   // operand reads is issued one group of products ahead of its use.
-  auto matrix = [&](const uint4* __restrict__ k0, const uint4* __restrict__ vm1, f32x4_t (&s)[4][2])
-      __attribute__((always_inline)) {
+  // With `loads` (group 0) the phase also issues tile u+2 (`pre`), in the same
+  // scheduling region, its scalar and load instructions spread between the
+  // first products instead of ahead of them.
+  auto matrix = [&](auto loads, auto pre, const uint4* __restrict__ k0, const uint4* __restrict__ vm1,
+                    f32x4_t (&s)[4][2]) __attribute__((always_inline)) {
     refresh();
+    pre();
     uint4 vb[4][2], vc[4][2], kb[2][4];
     WaveAttn::v_operands(vm1, to, 0, vb);
     wa.qk_regs(ka, 0, s);
@@ -473,10 +462,23 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
     // goes between the products before its use, at most 14 reads in flight so
     // that the waits can name the reads a product needs (the LDS counter
     // holds 15).
+    if constexpr (decltype(loads)::value) {
+      // and (mask 0x20: memory load) the tile issue: the page id's load after
+      // the fourth product, a row load after each from the seventh on; the
+      // address work in between is left to the scheduler (scalar groups as
+      // well make it gather all the loads in one place)
 #pragma unroll
-    for (int i = 0; i < 14; ++i) {  // Q K^T of M-blocks 0, 1 with V^T reads 1..14 of dims 0..63
-      sched_mfma<1>();
-      sched_lds<1>();
+      for (int i = 0; i < 14; ++i) {
+        sched_mfma<1>();
+        sched_lds<1>();
+        if (i == 3 || i >= 6) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 14; ++i) {  // Q K^T of M-blocks 0, 1 with V^T reads 1..14 of dims 0..63
+        sched_mfma<1>();
+        sched_lds<1>();
+      }
     }
     sched_mfma<2>();
 #pragma unroll
@@ -516,8 +518,7 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
                    const uint4* __restrict__ k1, uint4* __restrict__ k2, uint4* __restrict__ v2)
       __attribute__((always_inline)) {
     f32x4_t s[4][2];
-    issue(u + 2, k2, v2);
-    matrix(k0, vm1, s);
+    matrix(std::true_type{}, [&]() __attribute__((always_inline)) { issue(u + 2, k2, v2); }, k0, vm1, s);
     end_phase(true);
     vector(u, k1, s);
     end_phase(false);
@@ -525,7 +526,7 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
   auto tile1 = [&](int u, const uint4* __restrict__ k0, const uint4* __restrict__ vm1,
                    const uint4* __restrict__ k1) __attribute__((always_inline)) {
     f32x4_t s[4][2];
-    matrix(k0, vm1, s);
+    matrix(std::false_type{}, []() {}, k0, vm1, s);
     end_phase(false);
     vector(u, k1, s);
     end_phase(false);

@@ -256,40 +256,48 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
   // for tiles u = 0, 1, 2, ... in order, the last one repeated past the end),
   // so no scalar-load wait sits at the start of a phase; a pending scalar load
   // would also make every LDS wait of the phase a full one.
-  const __amdgpu_buffer_rsrc_t rtab = __builtin_amdgcn_make_buffer_rsrc((void*)tab, 0, 0x7fffffff, 0x00020000);
-  // Per-tile address work is kept small (it takes issue slots in the loop):
-  // local tile u < nct is context tile tc0 + u, whose page id sits at table
-  // index tc0 + u (persistent) or tc0 + u + open_shift (open block); its K and
-  // V rows start page * pstride past the head's bases.
+  // The table holds tstride entries; an index past it reads 0.
+  const __amdgpu_buffer_rsrc_t rtab = __builtin_amdgcn_make_buffer_rsrc((void*)tab, 0, P.tstride * 4, 0x00020000);
+  // Per-tile address work is kept small and free of branches: it takes issue
+  // slots between the products of a matrix phase. Local tile u < nct is
+  // context tile tc0 + u, whose page id sits at table index tc0 + u
+  // (persistent) or tc0 + u + open_shift (open block); its K and V rows start
+  // page * pstride past the head's bases. Pause-key tile u - nct starts at
+  // pause key k0 = 64 (u - nct) of the staged rotated keys and of the caller's
+  // values.
   const int open_shift = P.max_pers - npp;
-  const uint64_t pstride = (uint64_t)P.Hkv * TK * RB;
+  const uint32_t pstride = (uint32_t)P.Hkv * TK * RB;
   const char* kbase_h = (const char*)P.kpool + (size_t)hk * TK * RB;
   const char* vbase_h = (const char*)P.vpool + (size_t)hk * TK * RB;
+  const char* kbase_p = (const char*)a.kp_rot + ((size_t)i * P.Hkv + hk) * a.Kp * RB;
+  const char* vbase_p = (const char*)a.vp + ((size_t)ir * a.Kp * HkvR + H) * RB;
+  const uint32_t vrow_p = HkvR * RB;
   const int last_local = min(ntiles, nct) - 1;                  // last local context tile
   const int nval_last = n_pers - (npp - 1) * TK;
+  // page id of local tile u, clamped to the context tiles (past them the
+  // value goes unused)
   auto load_page = [&](int u) __attribute__((always_inline)) {
-    const int t = tc0 + u;
-    return u <= last_local ? (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, (t < npp ? t : t + open_shift) * 4, 0, 0)
-                           : 0;
+    const int t = tc0 + max(min(u, last_local), 0);
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, (t < npp ? t : t + open_shift) * 4, 0, 0);
   };
-  int next_page = ntiles > 0 ? load_page(0) : 0;  // page id of the tile asked for next
+  int next_page = load_page(0);  // page id of the tile asked for next
+  // Both kinds of tile start at base + index * stride: the selects pick the
+  // operands, so that no branch forms around the products.
   auto tile_src = [&](int u) __attribute__((always_inline)) {
     const int page = __builtin_amdgcn_readfirstlane(next_page);
-    next_page = load_page(min(u + 1, ntiles - 1));
+    next_page = load_page(u + 1);
+    // both sides are computed first, so that the compiler picks with selects
+    // instead of forming branches around them
+    const bool ctx = u < nct;
+    const int k0 = max(u - nct, 0) * TK;
+    const int nval_c = tc0 + u == npp - 1 ? nval_last : TK;
+    const int nval_p = min(TK, a.Kp - k0);
+    const uint32_t idx = ctx ? (uint32_t)page : (uint32_t)k0;
     TileSrc ts;
-    if (u < nct) {
-      const uint64_t off = (uint64_t)(uint32_t)page * pstride;
-      ts.kb = kbase_h + off;
-      ts.vb = vbase_h + off;
-      ts.vstride = RB;
-      ts.nval = tc0 + u == npp - 1 ? nval_last : TK;
-    } else {
-      const int k0 = (u - nct) * TK;
-      ts.kb = (const char*)a.kp_rot + (((size_t)i * P.Hkv + hk) * a.Kp + k0) * RB;
-      ts.vb = (const char*)a.vp + (((size_t)ir * a.Kp + k0) * HkvR + H) * RB;
-      ts.vstride = HkvR * RB;
-      ts.nval = min(TK, a.Kp - k0);
-    }
+    ts.kb = (ctx ? kbase_h : kbase_p) + (uint64_t)idx * (ctx ? pstride : (uint32_t)RB);
+    ts.vb = (ctx ? vbase_h : vbase_p) + (uint64_t)idx * (ctx ? pstride : vrow_p);
+    ts.vstride = ctx ? RB : vrow_p;
+    ts.nval = ctx ? nval_c : nval_p;
     return ts;
   };
   // softmax of tile u: masks for partial context pages and pause tiles (a
@@ -304,7 +312,7 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
     };
     wa.softmax(s, !ctx || nval < TK, limits, qs, lane, pb);
   };
-  pingpong_attention(wa, ntiles, lane, wave, lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3, tile_src, soft);
+  pingpong_attention<1>(wa, ntiles, lane, wave, lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3, tile_src, soft);
 
   // ---- output: O^T / l; lane holds dims 16 db + 4 g4 + e of query l16. With
   // context splits: the unnormalised partial (O, m, l) for compress_merge_kernel

@@ -139,22 +139,23 @@ __global__ void __launch_bounds__(512, 1) blockmask_attn_mfma_kernel(BlockMaskAr
   wa.init();
 
   // ---- tile u: range A tile u (u < ntA), else range B tile u - ntA
+  // Range A's rows start at the persistent list's head row, range B's at the
+  // block's first staged row; both sides are computed first, so that the
+  // compiler picks with selects instead of forming branches.
+  const char* kbase_a = (const char*)a.kpers + (size_t)hk * a.npers * RB;
+  const char* vbase_a = (const char*)a.vpers + (size_t)hk * a.npers * RB;
+  const char* kbase_b = (const char*)a.kst + ((size_t)hk * a.T + bstart) * RB;
+  const char* vbase_b = (const char*)a.vst + ((size_t)hk * a.T + bstart) * RB;
   auto tile_src = [&](int u) __attribute__((always_inline)) {
+    const bool in_a = u < ntA;
+    const int r0a = u * TK, r0b = max(u - ntA, 0) * TK;
+    const int r0 = in_a ? r0a : r0b;
+    const int rows = in_a ? rowsA : nB;
     TileSrc ts;
     ts.vstride = RB;
-    if (u < ntA) {
-      const int r0 = u * TK;
-      const size_t off = ((size_t)hk * a.npers + r0) * RB;
-      ts.kb = (const char*)a.kpers + off;
-      ts.vb = (const char*)a.vpers + off;
-      ts.nval = min(TK, rowsA - r0);
-    } else {
-      const int r0 = (u - ntA) * TK;
-      const size_t off = ((size_t)hk * a.T + bstart + r0) * RB;
-      ts.kb = (const char*)a.kst + off;
-      ts.vb = (const char*)a.vst + off;
-      ts.nval = min(TK, nB - r0);
-    }
+    ts.kb = (in_a ? kbase_a : kbase_b) + (size_t)r0 * RB;
+    ts.vb = (in_a ? vbase_a : vbase_b) + (size_t)r0 * RB;
+    ts.nval = min(TK, rows - r0);
     return ts;
   };
   auto soft = [&](int u, f32x4_t (&s)[4][2], uint4 (&pb)[2][2]) __attribute__((always_inline)) {
@@ -167,7 +168,7 @@ __global__ void __launch_bounds__(512, 1) blockmask_attn_mfma_kernel(BlockMaskAr
     };
     wa.softmax(s, r0 + TK > (in_a ? minA : minB), limits, qs, lane, pb);
   };
-  pingpong_attention(wa, ntiles, lane, wave, lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3, tile_src, soft);
+  pingpong_attention<0>(wa, ntiles, lane, wave, lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3, tile_src, soft);
 
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
