@@ -181,9 +181,10 @@ struct WaveAttn {
   // Online softmax of a tile's scores. When `masked`, key tile_key(mb, 4 g4 +
   // e) = 8 g4 + (32(mb/2) + 4(mb%2) + e) of query column nb is kept only if
   // 32(mb/2) + 4(mb%2) + e < lim[nb], the bound in this lane's key
-  // coordinates that limits(lim) fills (called only then). qs = log2(e)/sqrt(d). Moves the running maximum (rescaling O^T
-  // and the sum) when needed, adds the tile's probabilities to the sum and
-  // leaves them, as bf16, in pb[nb][kk] (keys 32 kk + 8 g4 + 0..7).
+  // coordinates that limits(lim) fills (called only then). qs =
+  // log2(e)/sqrt(d). Moves the running maximum (rescaling O^T and the sum)
+  // when needed, adds the tile's probabilities to the sum and leaves them, as
+  // bf16, in pb[nb][kk] (keys 32 kk + 8 g4 + 0..7).
   template <class Limits>
   __device__ __forceinline__ void softmax(f32x4_t (&s)[4][2], bool masked, Limits limits, float qs, int lane,
                                           uint4 (&pb)[2][2]) {
@@ -211,19 +212,40 @@ struct WaveAttn {
       }
     }
     // The running maximum of a column moves only when the tile's maximum
-    // exceeds it by more than 8 (log2 units). Each lane first tests its own
-    // scores' maximum, a tree over lane-local registers; only when some lane
-    // of the wavefront passes the test does the maximum over the column's four
-    // lanes (three lane swaps, a serial chain) run, with the rescale. A column
-    // whose lanes all stay below the bound cannot move, so the decisions are
-    // the same as with the reduction on every tile. Multiplying by qs > 0 keeps
-    // the order of the rounded products, so the lane test agrees with the test
-    // of the reduced maximum.
-    float mx[2];
+    // exceeds it by more than 8 (log2 units). The probabilities are first
+    // taken against the current maximum, with the scores kept; such a score
+    // gives a probability above 256, so a lane whose column sum stays at most
+    // 255 holds none (nor an overflow, which the first tile, with m = -1e30,
+    // always has). Only when some lane of the wavefront passes that test
+    // does the exact step run: per column the maximum of its lanes' scores
+    // (a lane-local tree, then three lane swaps), the move and the rescale,
+    // and the probabilities again. A wavefront that stays below the bound
+    // ends with the values that step would give; the test on the sums
+    // replaces the maximum's tree and swaps on most tiles.
+    f32x4_t p[4][2];
+    float st[2];
+    auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) mx[nb] = col_max(s, nb);
-    const bool over = mx[0] * qs > m[0] + 8.f || mx[1] * qs > m[1] + 8.f;
-    if (__builtin_amdgcn_ballot_w64(over)) {
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[mb][nb][e] = fast_exp2(fmaf(s[mb][nb][e], qs, -m[nb]));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float q4[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) q4[mb] = (p[mb][nb][0] + p[mb][nb][1]) + (p[mb][nb][2] + p[mb][nb][3]);
+        st[nb] = (q4[0] + q4[1]) + (q4[2] + q4[3]);
+      }
+    };
+    probs();
+    // (written so that a NaN sum, from an infinite probability, passes too)
+    const bool big = !(st[0] <= 255.f) || !(st[1] <= 255.f);
+    if (__builtin_amdgcn_ballot_w64(big)) {
+      float mx[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) mx[nb] = col_max(s, nb);
       rows4_max2(mx[0], mx[1]);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -235,25 +257,15 @@ struct WaveAttn {
 #pragma unroll
         for (int db = 0; db < 8; ++db) acc[nb][db] *= alpha;
       }
+      probs();
     }
-    const float mn[2] = {m[0], m[1]};
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)  // the score register now holds its probability
-          s[mb][nb][e] = fast_exp2(fmaf(s[mb][nb][e], qs, -mn[nb]));
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float q4[4];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) q4[mb] = (s[mb][nb][0] + s[mb][nb][1]) + (s[mb][nb][2] + s[mb][nb][3]);
-      l[nb] += (q4[0] + q4[1]) + (q4[2] + q4[3]);
+      l[nb] += st[nb];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         // keys 32kk + 8 g4 + j: j < 4 from M-block 2kk, j >= 4 from 2kk+1
-        const f32x4_t u0 = s[2 * kk][nb], u1 = s[2 * kk + 1][nb];
+        const f32x4_t u0 = p[2 * kk][nb], u1 = p[2 * kk + 1][nb];
         pb[nb][kk] = make_uint4(pack_bf16x2(u0[0], u0[1]), pack_bf16x2(u0[2], u0[3]),
                                 pack_bf16x2(u1[0], u1[1]), pack_bf16x2(u1[2], u1[3]));
       }
