@@ -407,12 +407,13 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)ts.kb, 0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)ts.vb, 0, 0x7fffffff, 0x00020000);
 #pragma unroll
+    // (row < 64 and the strides below 2^24: 24-bit products, one multiply-add)
     for (int j = 0; j < 4; ++j) {
       const int row = min(16 * j + r_in, last);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk + 256 * j + 64 * wave),
                                                16, row * RB + ((j & 1) ? kc1 : kc0), 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv + 256 * j + 64 * wave),
-                                               16, row * ts.vstride + vc, 0, 0, 0);
+                                               16, (int)__umul24(row, ts.vstride) + vc, 0, 0, 0);
     }
   };
   // the end of a phase: the wavefront's LDS reads have returned and, at the end

@@ -272,12 +272,11 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
   const char* kbase_p = (const char*)a.kp_rot + ((size_t)i * P.Hkv + hk) * a.Kp * RB;
   const char* vbase_p = (const char*)a.vp + ((size_t)ir * a.Kp * HkvR + H) * RB;
   const uint32_t vrow_p = HkvR * RB;
-  const int last_local = min(ntiles, nct) - 1;                  // last local context tile
   const int nval_last = n_pers - (npp - 1) * TK;
-  // page id of local tile u, clamped to the context tiles (past them the
-  // value goes unused)
+  // page id of local tile u; past the context tiles the value goes unused
+  // (the load reads another entry of the table, or 0 past its end)
   auto load_page = [&](int u) __attribute__((always_inline)) {
-    const int t = tc0 + max(min(u, last_local), 0);
+    const int t = tc0 + u;
     return (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, (t < npp ? t : t + open_shift) * 4, 0, 0);
   };
   int next_page = load_page(0);  // page id of the tile asked for next
