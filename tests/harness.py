@@ -35,6 +35,7 @@ class Run:
                  compress=True, max_seqs=64, pool_bytes=None, max_position=40960,
                  split_rows=0, base=1e6, seed=0, head_quota=None, budget_pool_pages=None):
         self.L, self.Hq, self.Hkv, self.D, self.C = L, Hq, Hkv, D, C
+        self.pause_q_scale = 1.0  # multiplies the pause queries' normals (both sides)
         self.quota = list(quota)
         self.head_quota = [list(r) for r in head_quota] if head_quota is not None else None
         self.pause = list(pause) if pause is not None else [Kp] * L
@@ -99,7 +100,8 @@ class Run:
     def pause_inputs(self, sids, layer):
         Kp = self.pause[layer]
         ks = np.arange(Kp)
-        q = np.stack([self.rows(s, layer, PAUSE, np.full(Kp, self.nb[s]), ks, synth.WHICH_Q) for s in sids])
+        q = np.stack([self.rows(s, layer, PAUSE, np.full(Kp, self.nb[s]), ks, synth.WHICH_Q,
+                                scale=self.pause_q_scale) for s in sids])
         k = np.stack([self.rows(s, layer, PAUSE, np.full(Kp, self.nb[s]), ks, synth.WHICH_K) for s in sids])
         v = np.stack([self.rows(s, layer, PAUSE, np.full(Kp, self.nb[s]), ks, synth.WHICH_V) for s in sids])
         return q, k, v
@@ -198,7 +200,7 @@ class Run:
         """Oracle of compressing block nb[sid] (its open block, full)."""
         b = self.nb[sid]
         Kp = self.pause[layer]
-        q = self.rows(sid, layer, PAUSE, np.full(Kp, b), np.arange(Kp), synth.WHICH_Q)
+        q = self.rows(sid, layer, PAUSE, np.full(Kp, b), np.arange(Kp), synth.WHICH_Q, scale=self.pause_q_scale)
         if self.head_quota is not None:
             return oracle.compress_heads(self.views(sid, layer), self.G[sid], b, b, q, self.fetch(sid, layer),
                                          ORC_DT[self.dtype], self.base)

@@ -170,6 +170,30 @@ def test_bf16_compress_then_decode_uses_code_rows(pr, C, Kp, quota):
 
 
 @pytest.mark.parametrize("pr,C,Kp,quota", [COMPRESS_CASES[0], COMPRESS_CASES[2]])
+def test_peaky_pause_queries_move_the_maximum_on_later_tiles(pr, C, Kp, quota):
+    """Pause queries four times larger: scores spread over about 6 log2 units,
+    so a column's running maximum also moves on later tiles (the rescale path
+    of the tile loop, not only its first tile), on the SIMT (16-row pages) and
+    MFMA (64-row pages) paths. (At eight times, single keys carry nearly all of
+    a row's weight and the MFMA path's bf16 probabilities put its output just
+    past the bar.)"""
+    run = _bf16_run(seed=13, pr=pr, C=C, Kp=Kp, quota=quota, split_rows=0)
+    run.pause_q_scale = 4.0
+    sids = [run.new_seq(P, i) for i, P in enumerate([5, 64])]
+    for s in sids:
+        run.write_prompts(s)
+    run.grow({s: 2 * C for s in sids})
+    outs = [run.compress_layer(sids, l) for l in range(run.L)]
+    torch.cuda.synchronize()
+    for l, (out, lse) in enumerate(outs):
+        out, lse = host(out), host(lse)
+        for i, s in enumerate(sids):
+            o_ref, l_ref, _ = run.oracle_compress(s, l)
+            _close(f"peaky compress out seq{s} L{l}", out[i], o_ref, 2e-2)
+            _close(f"peaky compress lse seq{s} L{l}", lse[i], l_ref, 1e-3)
+
+
+@pytest.mark.parametrize("pr,C,Kp,quota", [COMPRESS_CASES[0], COMPRESS_CASES[2]])
 def test_first_block_compression_with_empty_and_one_row_prompts(pr, C, Kp, quota):
     """Block 0 compressed with no prompt (the context is the block alone and the
     pause keys sit at bitrev(k)·C/K) and with a one-row prompt, on the SIMT

@@ -80,6 +80,28 @@ def test_blockmask_prefill_every_row(P, G, compress):
     pool.close()
 
 
+@pytest.mark.parametrize("P,G", [(37, 3 * 64 + 45), (0, 4 * 64)])
+def test_blockmask_prefill_peaky_queries(P, G):
+    """Queries eight times larger (a power of two: the bf16 values stay exact):
+    scores spread over about 11 log2 units, so running maxima move on later
+    tiles too, not only on each column's first tile."""
+    C, Kp, quotas = 64, 16, [16, 8]
+    pool = _pool(C, Kp, quotas, True)
+    for layer in range(2):
+        L = LayerView(P, C, Kp, quotas[layer], True)
+        kind, a, b, q, k, v = _synth_inputs(L, G, layer, seed=21 + layer)
+        q = q * 8.0
+        T = len(kind)
+        out = torch.empty((T, HQ, D), device="cuda", dtype=torch.bfloat16)
+        lse = torch.empty((T, HQ), device="cuda", dtype=torch.float32)
+        pool.blockmask_attention(layer, P, G, dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), out, lse)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.blockmask_prefill(L, G, q, _fetcher(L, G, k, v), oracle.BF16, 1e6)
+        _close(f"peaky prefill out P{P} G{G} L{layer} ({T} rows)", host(out), o_ref, 2e-2)
+        _close(f"peaky prefill lse P{P} G{G} L{layer}", host(lse), l_ref, 1e-3)
+    pool.close()
+
+
 def test_blockmask_prefill_fig9_shape_sampled():
     """16K text tokens after a 256-token prompt, C = 512, K = 256, three layers
     with quotas 64 / 128 / 256: T = 24,832 rows."""
