@@ -69,28 +69,38 @@ __device__ __forceinline__ int tile_key(int mb, int m) {
 
 // B operand of S^T for one 16-row N-block: the query row (bf16, pre-RoPE)
 // rotated in fp64 with the position's cos/sin row and rounded once to bf16;
-// qh[ks] holds dims 32ks + 8 g4 + 0..7.
-__device__ __forceinline__ void query_operand(const bf16_t* qrow, const double2* rope, int g4,
-                                              uint4 (&qh)[4]) {
-  constexpr int D = 128;
+// qh[ks] holds dims 32ks + 8 g4 + 0..7. In two steps, so that the loads can be
+// issued ahead of other loads and the rotation done later: query_load fetches
+// the lane's query dims and cos/sin pairs, query_rotate rotates and rounds.
+struct QueryRaw {
+  uint4 q[4];        // dims 32ks + 8 g4 + 0..7 (bf16)
+  double2 cs[2][8];  // cos/sin of pairs 32ks + 8 g4 + j, ks < 2
+};
+__device__ __forceinline__ void query_load(const bf16_t* qrow, const double2* rope, int g4, QueryRaw& r) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) r.q[ks] = *(const uint4*)(qrow + 32 * ks + 8 * g4);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r.cs[ks][j] = rope[32 * ks + 8 * g4 + j];
+}
+__device__ __forceinline__ void query_rotate(const QueryRaw& r, uint4 (&qh)[4]) {
   float x[4][8];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) unpack16(*(const uint4*)(qrow + 32 * ks + 8 * g4), x[ks], bf16_t());
+  for (int ks = 0; ks < 4; ++ks) unpack16(r.q[ks], x[ks], bf16_t());
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     double y0[8], y1[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const double2 cs = rope[32 * ks + 8 * g4 + j];
-      y0[j] = rot_first(x[ks][j], x[ks + 2][j], cs);
-      y1[j] = rot_second(x[ks][j], x[ks + 2][j], cs);
+      y0[j] = rot_first(x[ks][j], x[ks + 2][j], r.cs[ks][j]);
+      y1[j] = rot_second(x[ks][j], x[ks + 2][j], r.cs[ks][j]);
     }
     qh[ks] = make_uint4(pack_bf16x2_f64(y0[0], y0[1]), pack_bf16x2_f64(y0[2], y0[3]),
                         pack_bf16x2_f64(y0[4], y0[5]), pack_bf16x2_f64(y0[6], y0[7]));
     qh[ks + 2] = make_uint4(pack_bf16x2_f64(y1[0], y1[1]), pack_bf16x2_f64(y1[2], y1[3]),
                             pack_bf16x2_f64(y1[4], y1[5]), pack_bf16x2_f64(y1[6], y1[7]));
   }
-  (void)D;
 }
 
 // Per-lane byte offsets of the operand reads of a 64-key tile. They depend on
@@ -373,13 +383,18 @@ struct TileSrc {
 // may fetch ahead: it then issues kSrcLoads memory loads per call, at most 7). soft(u, s, pb) runs tile u's
 // softmax (wa.softmax with the tile's masks). The ring buffers are separate
 // __shared__ arrays of the kernel, so that the compiler can tell them apart.
-template <int kSrcLoads, class TileFn, class SoftFn>
+// qload() issues the loads of the wavefront's query rows and qfinish() turns
+// them into wa's query operands and initial state: the query loads go out
+// between the first two tiles' and the rotation follows, so that both pass
+// under the first tile's latency.
+template <int kSrcLoads, class TileFn, class SoftFn, class QLoadFn, class QFinishFn>
 __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int lane, int wave,
                                                    uint4* __restrict__ lk0, uint4* __restrict__ lk1,
                                                    uint4* __restrict__ lk2, uint4* __restrict__ lk3,
                                                    uint4* __restrict__ lv0, uint4* __restrict__ lv1,
                                                    uint4* __restrict__ lv2, uint4* __restrict__ lv3,
-                                                   TileFn tile_src, SoftFn soft) {
+                                                   TileFn tile_src, SoftFn soft, QLoadFn qload,
+                                                   QFinishFn qfinish) {
   static_assert(kSrcLoads >= 0 && kSrcLoads <= 7, "the wait count holds 15 loads");
   constexpr int RB = 256;  // bytes of a bf16 row of 128 dims
   const bool grp0 = wave < 4;
@@ -545,14 +560,34 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
     end_phase(false);
   };
 
-  if (ntiles > 0) {
-    if (grp0) {
-      issue(0, lk0, lv0);
-      issue(1, lk1, lv1);
-    }
+  if (ntiles <= 0) {
+    qload();
+    qfinish();
+    return;
+  }
+  {
     // zeros in the V buffer that the first matrix phase reads as tile -1
+    // (before any load into LDS is in flight, which a store would wait for)
     lv3[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
     lv3[threadIdx.x + 512] = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_sched_barrier(0);
+    // tile 0, the query loads, then tile 1: a tile source that fetches its
+    // next page id ahead (one load of its own) has that id ahead of the query
+    // loads too, so taking it waits for none of them
+    if (grp0) issue(0, lk0, lv0);
+    __builtin_amdgcn_sched_barrier(0);
+    qload();
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp0) issue(1, lk1, lv1);
+    __builtin_amdgcn_sched_barrier(0);
+    qfinish();
+    // the empty asm uses the query operands, so that the rotation is done here,
+    // under the tiles' latency, not sunk below the wait that follows
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        asm volatile("" ::"v"(wa.qh[nb][ks].x), "v"(wa.qh[nb][ks].y), "v"(wa.qh[nb][ks].z), "v"(wa.qh[nb][ks].w));
     end_phase(grp0);  // tile 0 and the zeros are in
     if (grp0) {
       WaveAttn::k_operands(lk0, to, 0, ka);

@@ -235,21 +235,29 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
   // ---- the wavefront's query rows: rotated at the bitrev position, rounded
   // once to bf16 (like stored keys); the softmax scale goes on the fp32 scores.
   // Rows past the workgroup's last are computed on its first row, not stored.
+  // Loaded and rotated by the schedule around the first tiles' issue.
   const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
   WaveAttn wa;
   int qpause[2];
+  QueryRaw qraw[2];
+  auto qload = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    int r = q0 + wave * 32 + nb * 16 + l16;
-    const bool rv = r < q0 + nq;
-    r = rv ? r : q0;
-    const int pz = r >> 2, hh = r & 3;
-    qpause[nb] = rv ? pz : -1;
-    const int pos = prompt + blk * P.C + bitrev_dev(pz, a.log2Kp) * (P.C / a.Kp);
-    const bf16_t* qrow = (const bf16_t*)a.qp + (((size_t)ir * a.Kp + pz) * a.Hq + H * G + hh) * D;
-    query_operand(qrow, P.rope + (size_t)pos * (D / 2), g4, wa.qh[nb]);
-  }
-  wa.init();
+    for (int nb = 0; nb < 2; ++nb) {
+      int r = q0 + wave * 32 + nb * 16 + l16;
+      const bool rv = r < q0 + nq;
+      r = rv ? r : q0;
+      const int pz = r >> 2, hh = r & 3;
+      qpause[nb] = rv ? pz : -1;
+      const int pos = prompt + blk * P.C + bitrev_dev(pz, a.log2Kp) * (P.C / a.Kp);
+      const bf16_t* qrow = (const bf16_t*)a.qp + (((size_t)ir * a.Kp + pz) * a.Hq + H * G + hh) * D;
+      query_load(qrow, P.rope + (size_t)pos * (D / 2), g4, qraw[nb]);
+    }
+  };
+  auto qfinish = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) query_rotate(qraw[nb], wa.qh[nb]);
+    wa.init();
+  };
 
   // ---- tile t: 64 K rows and 64 V rows (a context page, or pause keys). A
   // page id is fetched one tile ahead with a vector load (the template asks
@@ -311,7 +319,7 @@ __global__ void __launch_bounds__(512, 1) compress_attn_mfma_kernel(CompressArgs
     };
     wa.softmax(s, !ctx || nval < TK, limits, qs, lane, pb);
   };
-  pingpong_attention<1>(wa, ntiles, lane, wave, lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3, tile_src, soft);
+  pingpong_attention<1>(wa, ntiles, lane, wave, lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3, tile_src, soft, qload, qfinish);
 
   // ---- output: O^T / l; lane holds dims 16 db + 4 g4 + e of query l16. With
   // context splits: the unnormalised partial (O, m, l) for compress_merge_kernel

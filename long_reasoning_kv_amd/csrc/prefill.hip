@@ -119,24 +119,39 @@ __global__ void __launch_bounds__(512, 1) blockmask_attn_mfma_kernel(BlockMaskAr
   // ---- the wavefront's query rows (rotated at their positions, rounded once
   // to bf16) and their limits in both ranges; rows past the record's tokens
   // repeat its last token and are not written
+  // (loaded and rotated by the schedule around the first tiles' issue)
   const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
   WaveAttn wa;
-  int limA[2], limB[2];
+  QueryRaw qraw[2];
+  auto qload = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int r = wave * 32 + nb * 16 + l16;
-    const int tok = min(r >> 2, ntok - 1), hh = r & 3;
-    const int qi = tok0 + tok;  // the query's index in its range
-    int pos;
-    if (kind == 0) pos = row0 + tok;
-    else if (kind == 1) pos = a.prompt + blk * a.C + qi;
-    else pos = a.prompt + blk * a.C + bitrev_dev(qi, a.log2Kp) * (a.C / a.Kp);
-    const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)(row0 + tok) * a.Hq + hk * G + hh) * D;
-    query_operand(qrow, P.rope + (size_t)pos * (D / 2), g4, wa.qh[nb]);
-    limA[nb] = kind == 0 ? qi + 1 : nA;
-    limB[nb] = kind == 1 ? qi + 1 : (kind == 2 ? a.C + qi + 1 : 0);
-  }
-  wa.init();
+    for (int nb = 0; nb < 2; ++nb) {
+      const int r = wave * 32 + nb * 16 + l16;
+      const int tok = min(r >> 2, ntok - 1), hh = r & 3;
+      const int qi = tok0 + tok;  // the query's index in its range
+      int pos;
+      if (kind == 0) pos = row0 + tok;
+      else if (kind == 1) pos = a.prompt + blk * a.C + qi;
+      else pos = a.prompt + blk * a.C + bitrev_dev(qi, a.log2Kp) * (a.C / a.Kp);
+      const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)(row0 + tok) * a.Hq + hk * G + hh) * D;
+      query_load(qrow, P.rope + (size_t)pos * (D / 2), g4, qraw[nb]);
+    }
+  };
+  auto qfinish = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) query_rotate(qraw[nb], wa.qh[nb]);
+    wa.init();
+  };
+  // the limits of query column nb in ranges A and B (recomputed on the rare
+  // masked tile rather than kept in registers across the loop; the empty asm
+  // keeps the compiler from hoisting them out of it)
+  auto lim_ab = [&](int nb, bool in_a) __attribute__((always_inline)) {
+    int l = l16;
+    asm volatile("" : "+v"(l));
+    const int r = wave * 32 + nb * 16 + l;
+    const int qi = tok0 + min(r >> 2, ntok - 1);
+    return in_a ? (kind == 0 ? qi + 1 : nA) : (kind == 1 ? qi + 1 : (kind == 2 ? a.C + qi + 1 : 0));
+  };
 
   // ---- tile u: range A tile u (u < ntA), else range B tile u - ntA
   // Range A's rows start at the persistent list's head row, range B's at the
@@ -164,11 +179,11 @@ __global__ void __launch_bounds__(512, 1) blockmask_attn_mfma_kernel(BlockMaskAr
     const int rows = in_a ? rowsA : nB;
     auto limits = [&](int (&lim)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) lim[nb] = min(in_a ? limA[nb] : limB[nb], rows) - r0 - 8 * g4;
+      for (int nb = 0; nb < 2; ++nb) lim[nb] = min(lim_ab(nb, in_a), rows) - r0 - 8 * g4;
     };
     wa.softmax(s, r0 + TK > (in_a ? minA : minB), limits, qs, lane, pb);
   };
-  pingpong_attention<0>(wa, ntiles, lane, wave, lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3, tile_src, soft);
+  pingpong_attention<0>(wa, ntiles, lane, wave, lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3, tile_src, soft, qload, qfinish);
 
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
