@@ -595,7 +595,7 @@ __global__ void __launch_bounds__(256) decode_bf16_d128_g4_kernel(DecodeArgs a) 
   const int prow0 = threadIdx.x >> 4, pchunk = threadIdx.x & 15;
   const int lds0 = prow0 * 16 + (pchunk ^ (prow0 & 7));  // swizzled LDS slot (rows +16 for ch 1)
   uint4 ak0, av0, ak1, av1, bk0, bv0, bk1, bv1;
-  auto gload = [&](int u, uint4* k0, uint4* v0, uint4* k1, uint4* v1) __attribute__((always_inline)) {
+  auto gload = [&](int u, bool fresh, uint4* k0, uint4* v0, uint4* k1, uint4* v1) __attribute__((always_inline)) {
     size_t off;
     int nval;
     locate(u, &off, &nval);
@@ -607,10 +607,17 @@ __global__ void __launch_bounds__(256) decode_bf16_d128_g4_kernel(DecodeArgs a) 
     }
     const char* kb = kbase + off + pchunk * 16;
     const char* vb = vbase + off + pchunk * 16;
-    *k0 = load_stream16(kb + r0 * RB);
-    *v0 = load_stream16(vb + r0 * RB);
-    *k1 = load_stream16(kb + r1 * RB);
-    *v1 = load_stream16(vb + r1 * RB);
+    if (fresh) {
+      *k0 = load_stream16(kb + r0 * RB);
+      *v0 = load_stream16(vb + r0 * RB);
+      *k1 = load_stream16(kb + r1 * RB);
+      *v1 = load_stream16(vb + r1 * RB);
+    } else {  // a repeat of the last unit: the default policy finds it in L2
+      *k0 = *(const uint4*)(kb + r0 * RB);
+      *v0 = *(const uint4*)(vb + r0 * RB);
+      *k1 = *(const uint4*)(kb + r1 * RB);
+      *v1 = *(const uint4*)(vb + r1 * RB);
+    }
   };
   auto swrite = [&](int b, const uint4& k0, const uint4& v0, const uint4& k1, const uint4& v1)
       __attribute__((always_inline)) {
@@ -677,18 +684,19 @@ __global__ void __launch_bounds__(256) decode_bf16_d128_g4_kernel(DecodeArgs a) 
 
   // Prologue: unit 0 in LDS buffer 0, units 1 (stage a) and 2 (stage b) in
   // flight. Every step issues the same loads and stores whatever the unit count
-  // (indices past the end re-read the last unit, which is still in L2), so the
+  // (indices past the end re-read the last unit, under the default cache policy
+  // so that it comes from L2), so the
   // waits before each store can count exactly the newer stage's loads.
   const int ulast = nunits - 1;
-  gload(0, &ak0, &av0, &ak1, &av1);
+  gload(0, true, &ak0, &av0, &ak1, &av1);
   swrite(0, ak0, av0, ak1, av1);
-  gload(min(1, ulast), &ak0, &av0, &ak1, &av1);
-  gload(min(2, ulast), &bk0, &bv0, &bk1, &bv1);
+  gload(min(1, ulast), 1 <= ulast, &ak0, &av0, &ak1, &av1);
+  gload(min(2, ulast), 2 <= ulast, &bk0, &bv0, &bk1, &bv1);
   __syncthreads();
   auto step = [&](int u, uint4& k0, uint4& v0, uint4& k1, uint4& v1) __attribute__((always_inline)) {
     const int b = u & 1;
     swrite(b ^ 1, k0, v0, k1, v1);  // its buffer was last read before the previous barrier
-    gload(min(u + 3, ulast), &k0, &v0, &k1, &v1);
+    gload(min(u + 3, ulast), u + 3 <= ulast, &k0, &v0, &k1, &v1);
     if (u < nunits) {
       size_t off;
       int nval;
@@ -830,7 +838,7 @@ __global__ void __launch_bounds__(256) decode_stream_kernel(StreamArgs a) {
       *nval = rows - qq * UR;
     };
     uint4 ak0, av0, ak1, av1, bk0, bv0, bk1, bv1;
-    auto gload = [&](int u, uint4* k0, uint4* v0, uint4* k1, uint4* v1) __attribute__((always_inline)) {
+    auto gload = [&](int u, bool fresh, uint4* k0, uint4* v0, uint4* k1, uint4* v1) __attribute__((always_inline)) {
       size_t off;
       int nval;
       locate(u, &off, &nval);
@@ -842,10 +850,17 @@ __global__ void __launch_bounds__(256) decode_stream_kernel(StreamArgs a) {
       }
       const char* kb = kbase + off + pchunk * 16;
       const char* vb = vbase + off + pchunk * 16;
-      *k0 = load_stream16(kb + r0 * RB);
-      *v0 = load_stream16(vb + r0 * RB);
-      *k1 = load_stream16(kb + r1 * RB);
-      *v1 = load_stream16(vb + r1 * RB);
+      if (fresh) {
+        *k0 = load_stream16(kb + r0 * RB);
+        *v0 = load_stream16(vb + r0 * RB);
+        *k1 = load_stream16(kb + r1 * RB);
+        *v1 = load_stream16(vb + r1 * RB);
+      } else {  // a repeat of the last unit: the default policy finds it in L2
+        *k0 = *(const uint4*)(kb + r0 * RB);
+        *v0 = *(const uint4*)(vb + r0 * RB);
+        *k1 = *(const uint4*)(kb + r1 * RB);
+        *v1 = *(const uint4*)(vb + r1 * RB);
+      }
     };
     auto swrite = [&](int b, const uint4& k0, const uint4& v0, const uint4& k1, const uint4& v1)
         __attribute__((always_inline)) {
@@ -910,15 +925,15 @@ __global__ void __launch_bounds__(256) decode_stream_kernel(StreamArgs a) {
     };
 
     const int ulast = nunits - 1;
-    gload(0, &ak0, &av0, &ak1, &av1);
+    gload(0, true, &ak0, &av0, &ak1, &av1);
     swrite(0, ak0, av0, ak1, av1);
-    gload(min(1, ulast), &ak0, &av0, &ak1, &av1);
-    gload(min(2, ulast), &bk0, &bv0, &bk1, &bv1);
+    gload(min(1, ulast), 1 <= ulast, &ak0, &av0, &ak1, &av1);
+    gload(min(2, ulast), 2 <= ulast, &bk0, &bv0, &bk1, &bv1);
     __syncthreads();
     auto step = [&](int u, uint4& k0, uint4& v0, uint4& k1, uint4& v1) __attribute__((always_inline)) {
       const int b = u & 1;
       swrite(b ^ 1, k0, v0, k1, v1);
-      gload(min(u + 3, ulast), &k0, &v0, &k1, &v1);
+      gload(min(u + 3, ulast), u + 3 <= ulast, &k0, &v0, &k1, &v1);
       if (u < nunits) {
         size_t off;
         int nval;
@@ -1322,10 +1337,14 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(StreamArgs a) {
       va[db] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
     }
-    // ---- the next tile into the same LDS (once every read above has landed)
+    // ---- the next tile into the same LDS (once every read above has landed).
+    // The last tile of the run issues nothing: a repeated tile would come from
+    // HBM again, since the nontemporal loads do not keep it in L2
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    if (t + 1 < Fend) advance(ci);
-    issue(ci);  // unconditional: past the end it repeats the last tile
+    if (t + 1 < Fend) {
+      advance(ci);
+      issue(ci);
+    }
     // ---- S^T, softmax, O^T
     if (nval > 0) {
     f32x4_t sc[2];
