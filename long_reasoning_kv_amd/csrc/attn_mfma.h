@@ -414,23 +414,40 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
   // One form for every tile, without branches, so that its instructions can
   // be spread between the products: load j takes row min(16 j + r_in, nval -
   // 1) of the tile (a row of a whole tile is its own), at a per-lane offset.
-  auto issue = [&](int u, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
+  // The issue in two parts: prep (the tile source and the buffer descriptors,
+  // scalar work) and fire (the eight row loads). Group 0 preps tile u+3 in its
+  // softmax phase of tile u, where the scalar instructions take issue slots
+  // between dependent vector ones, and fires it in its next matrix phase.
+  struct Prepped {
+    __amdgpu_buffer_rsrc_t rk, rv;
+    int last, vstride;
+  };
+  auto prep = [&](int u) __attribute__((always_inline)) {
     const TileSrc ts = tile_src(min(u, ntiles - 1));
-    const int last = ts.nval - 1;
+    Prepped p;
+    p.last = ts.nval - 1;
+    p.vstride = ts.vstride;
     // raw buffer descriptors over the tile's K and V (stride 0, a range the
     // offsets never reach; 0x00020000 is the format word of untyped data)
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)ts.kb, 0, 0x7fffffff, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)ts.vb, 0, 0x7fffffff, 0x00020000);
+    p.rk = __builtin_amdgcn_make_buffer_rsrc((void*)ts.kb, 0, 0x7fffffff, 0x00020000);
+    p.rv = __builtin_amdgcn_make_buffer_rsrc((void*)ts.vb, 0, 0x7fffffff, 0x00020000);
+    return p;
+  };
+  auto fire = [&](const Prepped& p, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
 #pragma unroll
     // (row < 64 and the strides below 2^24: 24-bit products, one multiply-add)
     for (int j = 0; j < 4; ++j) {
-      const int row = min(16 * j + r_in, last);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk + 256 * j + 64 * wave),
+      const int row = min(16 * j + r_in, p.last);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rk, (__attribute__((address_space(3))) void*)(dk + 256 * j + 64 * wave),
                                                16, row * RB + ((j & 1) ? kc1 : kc0), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv + 256 * j + 64 * wave),
-                                               16, (int)__umul24(row, ts.vstride) + vc, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rv, (__attribute__((address_space(3))) void*)(dv + 256 * j + 64 * wave),
+                                               16, (int)__umul24(row, p.vstride) + vc, 0, 0, 0);
     }
   };
+  auto issue = [&](int u, uint4* __restrict__ dk, uint4* __restrict__ dv) __attribute__((always_inline)) {
+    fire(prep(u), dk, dv);
+  };
+  Prepped next;  // group 0: the tile its next matrix phase issues
   // the end of a phase: the wavefront's LDS reads have returned and, at the end
   // of group 0's matrix phase, its loads older than this phase's (eight rows
   // and the tile source's own kSrcLoads, in any order) have landed; then every wavefront of the workgroup gets here (the loads of
@@ -491,15 +508,15 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
     // that the waits can name the reads a product needs (the LDS counter
     // holds 15).
     if constexpr (decltype(loads)::value) {
-      // and (mask 0x20: memory load) the tile issue: the page id's load after
-      // the fourth product, a row load after each from the seventh on; the
-      // address work in between is left to the scheduler (scalar groups as
+      // and (mask 0x20: memory load) the tile issue, prepared in the softmax
+      // phase before: a row load after each product from the seventh on; the
+      // per-lane offsets in between are left to the scheduler (scalar groups as
       // well make it gather all the loads in one place)
 #pragma unroll
       for (int i = 0; i < 14; ++i) {
         sched_mfma<1>();
         sched_lds<1>();
-        if (i == 3 || i >= 6) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (i >= 6) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     } else {
 #pragma unroll
@@ -526,13 +543,17 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
     sched_mfma<14>();
   };
   // softmax phase of tile u, with the K operands of M-blocks 0, 1 of tile u+1
-  // read from its buffer k1 (in LDS since the barrier that began this phase)
-  auto vector = [&](int u, const uint4* __restrict__ k1, f32x4_t (&s)[4][2]) __attribute__((always_inline)) {
+  // read from its buffer k1 (in LDS since the barrier that began this phase),
+  // and (`pre`, group 0) the scalar work of the next tile issue, which the
+  // scheduler spreads between the softmax's dependent vector instructions
+  auto vector = [&](int u, const uint4* __restrict__ k1, f32x4_t (&s)[4][2], auto pre)
+      __attribute__((always_inline)) {
     if (u >= ntiles) return;
     refresh();
     // the reads first, so that their latency passes under the softmax
     WaveAttn::k_operands(k1, to, 0, ka);
     __builtin_amdgcn_sched_barrier(0);
+    pre();
     soft(u, s, pb);
   };
   // Tile u: its matrix phase, then its softmax phase; group 0 runs them as
@@ -546,9 +567,9 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
                    const uint4* __restrict__ k1, uint4* __restrict__ k2, uint4* __restrict__ v2)
       __attribute__((always_inline)) {
     f32x4_t s[4][2];
-    matrix(std::true_type{}, [&]() __attribute__((always_inline)) { issue(u + 2, k2, v2); }, k0, vm1, s);
+    matrix(std::true_type{}, [&]() __attribute__((always_inline)) { fire(next, k2, v2); }, k0, vm1, s);
     end_phase(true);
-    vector(u, k1, s);
+    vector(u, k1, s, [&]() __attribute__((always_inline)) { next = prep(u + 3); });
     end_phase(false);
   };
   auto tile1 = [&](int u, const uint4* __restrict__ k0, const uint4* __restrict__ vm1,
@@ -556,7 +577,7 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
     f32x4_t s[4][2];
     matrix(std::false_type{}, []() {}, k0, vm1, s);
     end_phase(false);
-    vector(u, k1, s);
+    vector(u, k1, s, []() {});
     end_phase(false);
   };
 
@@ -588,6 +609,10 @@ __device__ __forceinline__ void pingpong_attention(WaveAttn& wa, int ntiles, int
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         asm volatile("" ::"v"(wa.qh[nb][ks].x), "v"(wa.qh[nb][ks].y), "v"(wa.qh[nb][ks].z), "v"(wa.qh[nb][ks].w));
+    // tile 2's scalar work (its page id, fetched with tile 1's, is older than
+    // tile 1's row loads, so taking it waits for those of tile 0 and the query)
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp0) next = prep(2);
     end_phase(grp0);  // tile 0 and the zeros are in
     if (grp0) {
       WaveAttn::k_operands(lk0, to, 0, ka);
