@@ -373,8 +373,10 @@ struct TileSrc {
 // runs on a repeated tile and its scores are dropped, and no softmax phase runs
 // for u = ntiles). Tiles stream straight into a ring
 // of four LDS buffers (32 KB each: K rows swizzled by kswz, V rows by vt_swz):
-// at phase 2u each wavefront of group 0 issues its share of tile u+2, and
-// before the barrier that ends phase 2u it waits for its share of tile u+1.
+// at phase 2u each wavefront of group 0 issues its share of tile u+2 (whose
+// scalar part, the tile source and buffer descriptors, it prepared in its
+// softmax phase of tile u-1), and before the barrier that ends phase 2u it
+// waits for its share of tile u+1.
 // Tile u's buffer is read from phase 2u to 2u+3, and the load into it is
 // issued at phase 2u-4, after the barrier that ends its previous tile's last
 // read.
