@@ -213,12 +213,16 @@ struct WaveAttn {
       for (int nb = 0; nb < 2; ++nb) {
         const float fl = ((float)min(max(lim[nb], -1), 64) - 0.5f) * big;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 4; ++mb) {
+          // four bounds, then their four minima (the empty asm takes all four,
+          // so that no min issues right behind the product it reads)
+          float bnd[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float k = (float)(32 * (mb >> 1) + 4 * (mb & 1) + e);
-            s[mb][nb][e] = vmin(s[mb][nb][e], fmaf(-k, big, fl));
-          }
+          for (int e = 0; e < 4; ++e) bnd[e] = fmaf(-(float)(32 * (mb >> 1) + 4 * (mb & 1) + e), big, fl);
+          asm volatile("" : "+v"(bnd[0]), "+v"(bnd[1]), "+v"(bnd[2]), "+v"(bnd[3]));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[mb][nb][e] = vmin(s[mb][nb][e], bnd[e]);
+        }
       }
     }
     // The running maximum of a column moves only when the tile's maximum
@@ -235,12 +239,20 @@ struct WaveAttn {
     f32x4_t p[4][2];
     float st[2];
     auto probs = [&]() __attribute__((always_inline)) {
+      // four exponent arguments, then their four exponentials: the empty asm
+      // takes all four, so that each exponential issues three instructions
+      // after the product it reads instead of right behind it
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 4; ++mb) {
+          float x[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) p[mb][nb][e] = fast_exp2(fmaf(s[mb][nb][e], qs, -m[nb]));
+          for (int e = 0; e < 4; ++e) x[e] = fmaf(s[mb][nb][e], qs, -m[nb]);
+          asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[mb][nb][e] = fast_exp2(x[e]);
+        }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         float q4[4];
