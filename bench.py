@@ -342,11 +342,11 @@ def mix_summary(d, prof):
         lines.append(f"  ratios: sequences x{j['sequences_ratio']:.2f}, tokens/s x{j['tokens_per_s_ratio']:.2f}")
         if name == "mix_full":
             tr = j["abridgekv"]["occupancy_trace"]
-            kv = tr["seq0_kv_mb"]
-            lines += ["", "occupancy (untraced run, AbridgeKV): first sequence's resident K/V in MB, "
+            kv = tr["seq_kv_mb"]
+            lines += ["", f"occupancy (untraced run, AbridgeKV): sequence {tr['sequence']}'s resident K/V in MB, "
                           "every 16th step, with its generated count:",
                       "  " + ", ".join(f"{g}:{x:.0f}" for g, x in
-                                       list(zip(tr["seq0_generated"], kv))[::16]),
+                                       list(zip(tr["seq_generated"], kv))[::16]),
                       "pool pages by layer budget (rows kept per block) every 32 steps:"]
             for q, v in tr["pages_by_quota"].items():
                 lines.append(f"  {q:>3s}-row layers: " + ", ".join(str(x) for x in v))
@@ -811,6 +811,13 @@ def budget_pool_split(by_quota: dict, pool_pages: int):
     return qs, pages
 
 
+def traced_sequence(G, warm: int) -> int:
+    """Index of the sequence whose block completes first at or after step
+    `warm` (in step t a sequence with G generated tokens before the first step
+    compresses when G + t is a multiple of C)."""
+    return int(np.argmin([(-(int(x) + warm)) % C for x in G]))
+
+
 def run_serving_mix(args, torch, abk, compress: bool):
     """The saturated serving mix: a 200 GiB pool filled with as many sequences
     as fit, then `steps` decode steps of all of them (one fused append + decode
@@ -862,18 +869,25 @@ def run_serving_mix(args, torch, abk, compress: bool):
     lse = torch.empty((B, HQ), device="cuda", dtype=torch.float32)
     views = [[(q_in[t, l], k_in[t, l], v_in[t, l]) for l in range(L)] for t in range(nsets)]
     stats = {"compressions": 0, "rows": 0}
-    # occupancy trace (host bookkeeping only, no GPU synchronisation): the first
-    # sequence's resident K/V summed over layers every step, and the pool's
-    # pages by budget class (layers keeping 64 / 128 / 256 rows per block)
-    # every 32 steps
+    # occupancy trace (host bookkeeping only, no GPU synchronisation): one
+    # sequence's resident K/V summed over layers after every timed step, and
+    # the pool's pages by budget class (layers keeping 64 / 128 / 256 rows per
+    # block) every 32 steps. The traced sequence is the one whose block
+    # completes earliest in the timed steps (in step t a sequence compresses
+    # when G + t is a multiple of C), so that its drop falls inside the trace.
     row_bytes = 2 * HKV * D * 2
-    trace = {"seq0_kv_mb": [], "seq0_generated": [], "budget_steps": [],
-             "pages_by_quota": {str(q): [] for q in sorted(set(quotas.tolist()))}, "pages_used": []}
+    ti = traced_sequence(G, warm + 1)  # a drop after the first timed step shows in the trace
+    trace = {"sequence": ti, "seq_kv_mb": [], "seq_generated": [], "budget_steps": [],
+             "pages_by_quota": {str(q): [] for q in sorted(set(quotas.tolist()))}, "pages_used": [],
+             # a compression step: each layer's C open rows become q_l code rows,
+             # then the step's token adds one row per layer
+             "drop_closed_form_mb": round(sum(C - int(q) - 1 for q in quotas) * row_bytes / 1e6, 3)
+             if compress else None}
 
     def record(t):
-        rows = sum(pool.seq_query(sids[0], l)["resident_rows"] for l in range(L))
-        trace["seq0_kv_mb"].append(round(rows * row_bytes / 1e6, 3))
-        trace["seq0_generated"].append(int(g[0]))
+        rows = sum(pool.seq_query(sids[ti], l)["resident_rows"] for l in range(L))
+        trace["seq_kv_mb"].append(round(rows * row_bytes / 1e6, 3))
+        trace["seq_generated"].append(int(g[ti]))
         if t % 32 == 0:
             by = {q: 0 for q in trace["pages_by_quota"]}
             if split:
@@ -936,9 +950,21 @@ def run_serving_mix(args, torch, abk, compress: bool):
             "occupancy_trace": trace}
 
 
+def occupancy_summary(tr: dict) -> dict:
+    """The traced sequence's resident K/V per timed step (MB, one decimal) and
+    the steps where it drops, beside the closed-form drop of one compression."""
+    kv = tr["seq_kv_mb"]
+    drops = [{"step": t, "generated": tr["seq_generated"][t], "from_mb": kv[t - 1], "to_mb": kv[t]}
+             for t in range(1, len(kv)) if kv[t] < kv[t - 1]]
+    return {"sequence": tr["sequence"], "generated_at_first_step": tr["seq_generated"][0] if kv else None,
+            "kv_mb": [round(x, 1) for x in kv], "drops": drops,
+            "drop_closed_form_mb": tr["drop_closed_form_mb"]}
+
+
 def serving_mix_leg(a: dict, f: dict) -> dict:
-    """The serving mix's two modes as the default bench line reports them
-    (without the occupancy traces)."""
+    """The serving mix's two modes as the default bench line reports them, each
+    with its traced sequence's occupancy (the pool's per-budget page counts
+    are left to the long form)."""
     keys = ("sequences_resident", "tokens_per_s", "ms_per_step", "steps", "compressions_in_timed_steps",
             "decode_kv_gb_per_step", "kv_gbps_incl_compression", "pool_pages_used_at_end", "pool_pages")
     return {"metric": "serving mix: decode tokens/s and sequences resident, AbridgeKV vs full KV",
@@ -947,7 +973,8 @@ def serving_mix_leg(a: dict, f: dict) -> dict:
                                    "6x256/12x64/18x128, P ~ U[128,512], G ~ U[1024,32768], one fused "
                                    "append+decode call per layer per step, compress+free at block "
                                    "boundaries inside the steps; full KV: the same kernels, compression off"},
-            "abridgekv": {k: a[k] for k in keys}, "full_kv": {k: f[k] for k in keys},
+            "abridgekv": {**{k: a[k] for k in keys}, "occupancy": occupancy_summary(a["occupancy_trace"])},
+            "full_kv": {**{k: f[k] for k in keys}, "occupancy": occupancy_summary(f["occupancy_trace"])},
             "tokens_per_s_ratio": a["tokens_per_s"] / f["tokens_per_s"],
             "sequences_ratio": a["sequences_resident"] / f["sequences_resident"]}
 

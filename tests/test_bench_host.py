@@ -69,3 +69,25 @@ def test_budget_pool_split_covers_the_admitted_needs():
     qs, split = bench.budget_pool_split(by, pages)
     assert qs == sorted(set(int(q) for q in quotas))
     assert all(n >= by[q] for q, n in zip(qs, split)) and sum(split) <= pages
+
+
+def test_traced_sequence_compresses_first():
+    """The serving mix traces the sequence whose block completes earliest at
+    or after the warmup: brute force over the steps of the compression rule."""
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        G = rng.integers(1, 40000, int(rng.integers(1, 50)))
+        warm = int(rng.integers(0, 4))
+        first = [next(t for t in range(warm, warm + bench.C + 1) if (int(x) + t) % bench.C == 0) for x in G]
+        assert first[bench.traced_sequence(G, warm)] == min(first)
+
+
+def test_occupancy_summary_finds_the_drop():
+    """A trace that grows by one row per layer and falls at a compression
+    step reports that step, its sizes and the closed-form drop it carries."""
+    tr = {"sequence": 3, "seq_kv_mb": [10.0, 10.147, 2.0, 2.147], "seq_generated": [511, 512, 513, 514],
+          "drop_closed_form_mb": 8.1}
+    s = bench.occupancy_summary(tr)
+    assert s["sequence"] == 3 and s["generated_at_first_step"] == 511
+    assert s["drops"] == [{"step": 2, "generated": 513, "from_mb": 10.147, "to_mb": 2.0}]
+    assert s["kv_mb"] == [10.0, 10.1, 2.0, 2.1] and s["drop_closed_form_mb"] == 8.1
