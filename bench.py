@@ -717,17 +717,19 @@ def run_prefill(args, torch, abk):
     """Block-mask prefill at the Fig. 9 shape: one sequence of 16,384 text
     tokens after a 256-token prompt, C = 512, K = 256 pause tokens per block,
     every one of the 36 layers (its own quota); the same kernel with
-    compression off (plain causal attention over the same text) beside it."""
-    P, G, Kp = 256, 16384, 256
-    quotas = layer_quotas(2)
+    compression off (plain causal attention over the same text) beside it,
+    and the same text at C = 256 (K = 128, every quota halved: 4:1 as well),
+    the block size Fig. 9 reports as costlier from partly filled tiles."""
+    P, G = 256, 16384
     bf = torch.bfloat16
-    res = {}
-    for comp in ((True,) if args.no_prefill_causal else (True, False)):
-        pool = abk.Pool(num_layers=L, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_tokens=C,
+
+    def forward(Cb, Kp, quotas, comp):
+        """ms per 36-layer forward (mean of two after a warmup), flops, rows"""
+        pool = abk.Pool(num_layers=L, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, block_tokens=Cb,
                         num_pause=Kp, layer_quota=quotas.tolist(), page_rows=PR, max_seqs=1,
                         pool_bytes=2 * HKV * PR * D * 2 * 16, max_position=P + G, dtype="bf16",
                         rope_base=1e6, compress=comp)
-        T = P + G + ((G // C) * Kp if comp else 0)
+        T = P + G + ((G // Cb) * Kp if comp else 0)
         gen = torch.Generator(device="cuda")
         gen.manual_seed(5)
         q = torch.randn((T, HQ, D), device="cuda", dtype=bf, generator=gen)
@@ -747,12 +749,23 @@ def run_prefill(args, torch, abk):
                 times.append(e0.elapsed_time(e1))
         pool.close()
         del q, k, v, out, lse
-        keys = sum(blockmask_visible_keys(P, G, C, Kp, int(qq), comp) for qq in quotas)
-        flops = 4.0 * D * HQ * keys
-        ms = float(np.mean(times))
-        res[comp] = (ms, flops, T)
-    ms, flops, T = res[True]
-    ms_c, flops_c, _ = res.get(False, (float("nan"), float("nan"), 0))
+        keys = sum(blockmask_visible_keys(P, G, Cb, Kp, int(qq), comp) for qq in quotas)
+        return float(np.mean(times)), 4.0 * D * HQ * keys, T
+
+    quotas = layer_quotas(2)
+    ms, flops, T = forward(C, 256, quotas, True)
+    ms_c, flops_c = float("nan"), float("nan")
+    if not args.no_prefill_causal:
+        ms_c, flops_c, _ = forward(C, 256, quotas, False)
+    b256 = None
+    if not args.no_prefill_c256:
+        ms_b, flops_b, T_b = forward(256, 128, quotas // 2, True)
+        tf_b = flops_b / (ms_b * 1e-3) / 1e12
+        b256 = {"ms_per_forward": ms_b, "rows": T_b, "tflop_per_forward": flops_b / 1e12,
+                "achieved_tflops": tf_b, "frac": tf_b / BF16_PEAK_TFLOPS, "time_vs_c512": ms_b / ms,
+                "config": {"workload": "the same 256-token prompt + 16,384 text tokens at C = 256, "
+                                       "K = 128 pause tokens per block, quotas 6x128/12x32/18x64 "
+                                       "(4:1 mean quota), 36 layers"}}
     tflops = flops / (ms * 1e-3) / 1e12
     # algorithmic bytes per launch (one layer): q, out and lse of every row, k
     # and v of every row once
@@ -766,6 +779,7 @@ def run_prefill(args, torch, abk):
                      "traffic": traffic_from_profiles("blockmask_attn_mfma", nbytes)},
         "causal_ms_per_forward": ms_c, "causal_tflop_per_forward": flops_c / 1e12,
         "causal_tflops": flops_c / (ms_c * 1e-3) / 1e12, "time_vs_causal": ms / ms_c,
+        "block_size_256": b256,
         "config": {"workload": "Fig. 9 shape: 256-token prompt + 16,384 text tokens, C = 512, "
                                "K = 256 pause tokens per block (4:1 mean quota), 36 layers with "
                                "quotas 6x256/12x64/18x128; causal: the same kernel with "
@@ -1073,6 +1087,8 @@ def main():
                     help="skip the compression event and the one-layer decode call (the decode "
                          "step alone, as the decode profile runs it)")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-prefill-c256", action="store_true",
+                    help="skip the prefill leg at block size C = 256")
     ap.add_argument("--no-prefill-causal", action="store_true",
                     help="skip the plain-causal comparison of the prefill (profiled runs)")
     ap.add_argument("--no-single-sequence", action="store_true",

@@ -102,10 +102,12 @@ def test_blockmask_prefill_peaky_queries(P, G):
     pool.close()
 
 
-def test_blockmask_prefill_fig9_shape_sampled():
-    """16K text tokens after a 256-token prompt, C = 512, K = 256, three layers
-    with quotas 64 / 128 / 256: T = 24,832 rows."""
-    P, G, C, Kp, quotas = 256, 16384, 512, 256, [64, 128, 256]
+@pytest.mark.parametrize("C,Kp,quotas", [(512, 256, [64, 128, 256]), (256, 128, [32, 64, 128])])
+def test_blockmask_prefill_fig9_shape_sampled(C, Kp, quotas):
+    """16K text tokens after a 256-token prompt, three layers, at the bench's
+    two block sizes (4:1 mean quota at each): C = 512, K = 256 and C = 256,
+    K = 128, both T = 24,832 rows."""
+    P, G = 256, 16384
     pool = _pool(C, Kp, quotas, max_position=P + G, pr=64)
     gen = torch.Generator().manual_seed(9)
     for layer in range(3):
@@ -120,17 +122,17 @@ def test_blockmask_prefill_fig9_shape_sampled():
         lse = torch.empty((T, HQ), device="cuda", dtype=torch.float32)
         pool.blockmask_attention(layer, P, G, q.cuda(), k.cuda(), v.cuda(), out, lse)
         torch.cuda.synchronize()
-        per = C + Kp
-        rows = [0, P - 1,                                       # prompt
-                P, P + 300, P + 511,                            # block 0 text
-                P + 512, P + 600, P + per - 1,                  # block 0 pause
-                P + 15 * per + 17, P + 15 * per + 512 + 100,    # block 15
-                P + 31 * per + 511, P + 31 * per + 512, T - 1]  # last block
+        per, nb = C + Kp, G // C
+        rows = [0, P - 1,                                                  # prompt
+                P, P + C // 2 + 44, P + C - 1,                             # block 0 text
+                P + C, P + C + Kp // 3, P + per - 1,                       # block 0 pause
+                P + 15 * per + 17, P + 15 * per + C + Kp // 2 - 28,        # block 15
+                P + (nb - 1) * per + C - 1, P + (nb - 1) * per + C, T - 1]  # last block
         qn, kn, vn = (x.float().numpy().astype(np.float64) for x in (q, k, v))
         o_ref, l_ref = oracle.blockmask_prefill(L, G, qn, _fetcher(L, G, kn, vn), oracle.BF16, 1e6,
                                                 rows=rows)
-        _close(f"fig9 prefill out L{layer} q{quotas[layer]}", host(out[rows]), o_ref, 2e-2)
-        _close(f"fig9 prefill lse L{layer} q{quotas[layer]}", host(lse[rows]), l_ref, 1e-3)
+        _close(f"fig9 prefill out C{C} L{layer} q{quotas[layer]}", host(out[rows]), o_ref, 2e-2)
+        _close(f"fig9 prefill lse C{C} L{layer} q{quotas[layer]}", host(lse[rows]), l_ref, 1e-3)
         assert np.isfinite(host(out)).all() and np.isfinite(host(lse)).all()
     pool.close()
 
