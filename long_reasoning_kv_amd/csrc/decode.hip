@@ -1011,16 +1011,20 @@ __global__ void __launch_bounds__(512) decode_stream_merge_kernel(StreamArgs a) 
   if (ns == 1) return;
   const float* base = a.part + ((size_t)i * Hkv + h) * (a.maxp + a.fused) * G * (D + 2);
   for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
-    const int g = t / D, d = t % D;
+    // a wavefront's 64 threads share the query head (D = 128), so its partials'
+    // maxima and sums are wavefront-uniform: scalar loads, one per wavefront
+    const int g = sgpr(t / D), d = t % D;
     float M = -INFINITY, Ls = 0.f, O = 0.f;
     for (int s0 = 0; s0 < ns; s0 += K) {
       float mv[K], lv[K], ov[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        const float* pp = base + (min(s0 + k, ns - 1) * G + g) * (D + 2);
-        mv[k] = pp[D];
-        lv[k] = pp[D + 1];
-        ov[k] = pp[d];
+        const int off = (min(s0 + k, ns - 1) * G + g) * (D + 2);
+        // (read-only here: written by the decode launch before this one)
+        const __attribute__((address_space(4))) float* pc = (const __attribute__((address_space(4))) float*)(base + off);
+        mv[k] = pc[D];
+        lv[k] = pc[D + 1];
+        ov[k] = base[off + d];
       }
       float cm = M;
 #pragma unroll
