@@ -8,7 +8,8 @@ automatic decode schedule), on outputs the oracle computes one by one.
   36 layers, K = 256 pause tokens; and one or two sequences alone (the
   context-split schedule).
 - The serving mix's shape: more sequences than one launch takes, fused calls,
-  blocks completing between steps; AbridgeKV and full-KV modes.
+  blocks completing between steps; AbridgeKV and full-KV modes; and the mix at
+  its benchmarked size (the 200 GiB pool of bench.py's admitted sequences).
 
 Bars as everywhere: out max-abs 2e-2, lse 1e-3; stored values and rotated keys
 bit-exact (both sides round the same fp64 rotation once); row counts and
@@ -226,6 +227,53 @@ def test_serving_mix_more_sequences_than_one_launch(compress):
             _close(f"mix out seq{i} L{l}", out[i], o_ref, 2e-2)
             _close(f"mix lse seq{i} L{l}", lse[i], l_ref, 1e-3)
     run.pool.close()
+
+
+def test_serving_mix_full_size_sampled():
+    """The saturated serving mix at the size bench.py times: the 200 GiB pool
+    holding the sequences bench.py admits (prompts U[128, 512], U[1024, 32768]
+    generated tokens, the 36-layer quotas), fused steps up to and past the
+    first block that completes (compressed at every layer and freed inside the
+    step, as in serving). Row counts of every sequence exact; sampled
+    (sequence, layer) outputs of the last step against the oracle, the
+    compressed sequence among them."""
+    torch.cuda.empty_cache()
+    quotas = bench.layer_quotas(2)
+    pool_bytes = 200 << 30
+    P, G, _ = bench.serving_mix_admit(quotas, 66, True, pool_bytes // (2 * HKV * PR * D * 2))
+    B = len(P)
+    first = bench.traced_sequence(G, 0)
+    steps = (-int(G[first])) % C + 2  # it compresses in the step before the last
+    run = Run(L=L, Hq=HQ, Hkv=HKV, D=D, C=C, Kp=int(quotas.max()), quota=quotas.tolist(), pr=PR,
+              dtype="bf16", max_seqs=B, pool_bytes=pool_bytes, max_position=33792, seed=4)
+    sids = [run.new_seq(int(P[i]), i) for i in range(B)]
+    for s, g in zip(sids, G):
+        run.fill(s, int(g))
+    print(f"[fullsize] serving mix: {B} sequences filled, {steps} steps", flush=True)
+    crossed = set()
+    for t in range(steps):
+        full = [s for s in sids if run.G[s] - run.nb[s] * C == C]
+        if full:
+            run.compress_and_free(full)
+            crossed.update(full)
+        results = run.step_fused(sids)
+    assert sids[first] in crossed
+    layers = _sample_layers(quotas)[::2]  # one layer of each quota class
+    seqs = sorted({first, 0, B - 1})
+    for l in range(L):
+        out, lse, q = results[l]
+        assert np.isfinite(out).all() and np.isfinite(lse).all(), l
+        for i, s in enumerate(sids):
+            nb = run.nb[s]
+            want = int(P[i]) + nb * int(quotas[l]) + (run.G[s] - nb * C)
+            assert run.pool.seq_query(s, l)["resident_rows"] == want, (i, l)
+        if l in layers:
+            for i in seqs:
+                o_ref, l_ref, _ = run.oracle_decode(sids[i], l, q[i])
+                _close(f"mix200 out seq{i} L{l} q{quotas[l]}", out[i], o_ref, 2e-2)
+                _close(f"mix200 lse seq{i} L{l} q{quotas[l]}", lse[i], l_ref, 1e-3)
+    run.pool.close()
+    torch.cuda.empty_cache()
 
 
 def test_36_layer_per_head_decode_step_sampled():
